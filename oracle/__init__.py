@@ -1,0 +1,137 @@
+"""fp64 CPU oracle for the gated delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check in the package entry file and the
+benchmark's CPU-baseline leg may import this module.  The product path (the
+HIP library and its Python binding) never imports it and shares no code with
+it; the only thing both sides consume is the seeded input generator, which
+holds none of the method's arithmetic.
+
+The arithmetic lives in ``gdn_oracle.c`` (plain C, fp64, OpenMP over the
+independent (sequence, head) units).  This module is argument marshalling
+through ctypes plus the build-on-demand of that C file.
+
+Parity status: every function here is pinned by tests/test_oracle.py against
+closed forms, invariants and a hand-worked example (see that file's header).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_L = ctypes.c_long
+
+
+def _lib():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = _build.LIB
+    src = _build.SRC
+    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(src):
+        _build.build()
+    lib = ctypes.CDLL(path)
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_gdn_recurrent.restype = ctypes.c_int
+    lib.oracle_gdn_recurrent.argtypes = [
+        _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_void_p, _f64p, _f64p,
+        _L, _L, _L, _L, ctypes.c_int]
+    lib.oracle_gdn_chunked.restype = ctypes.c_int
+    lib.oracle_gdn_chunked.argtypes = [
+        _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_void_p, _f64p, _f64p,
+        _L, _L, _L, _L, _L, ctypes.c_int]
+    lib.oracle_gdn_chunk_stages.restype = ctypes.c_int
+    lib.oracle_gdn_chunk_stages.argtypes = [
+        _f32p, _f32p, _f32p, _f32p, _f32p, _f64p, _L, _L] + [ctypes.c_void_p] * 8
+    _LIB = lib
+    return lib
+
+
+def max_threads() -> int:
+    """Threads the oracle's OpenMP runtime would use by default."""
+    return int(_lib().oracle_max_threads())
+
+
+def _prep(q, k, v, g, beta, state):
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share shape (n_seqs, n_tokens, n_heads, d)")
+    S, T, H, d = q.shape
+    if g.shape != (S, T, H) or beta.shape != (S, T, H):
+        raise ValueError("g and beta must be (n_seqs, n_tokens, n_heads)")
+    if state is not None:
+        state = np.ascontiguousarray(state, dtype=np.float64)
+        if state.shape != (S, H, d, d):
+            raise ValueError("state must be (n_seqs, n_heads, d, d), [value][key]")
+    return q, k, v, g, beta, state, (S, T, H, d)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def gdn_recurrent(q, k, v, g, beta, state=None, threads: int = 0):
+    """Token-sequential fp64 recurrence.  Returns (out, final_state) as float64.
+
+    q, k, v: (n_seqs, n_tokens, n_heads, d); g, beta: (n_seqs, n_tokens,
+    n_heads); state: (n_seqs, n_heads, d, d) stored [value][key] or None for
+    zeros.  Values are taken as given (bf16 inputs should be passed already
+    rounded); all arithmetic is fp64.
+    """
+    q, k, v, g, beta, state, (S, T, H, d) = _prep(q, k, v, g, beta, state)
+    out = np.empty((S, T, H, d), dtype=np.float64)
+    fin = np.empty((S, H, d, d), dtype=np.float64)
+    rc = _lib().oracle_gdn_recurrent(q, k, v, g, beta, _ptr(state), out, fin,
+                                     S, T, H, d, int(threads))
+    if rc != 0:
+        raise MemoryError("oracle_gdn_recurrent failed (%d)" % rc)
+    return out, fin
+
+
+def gdn_chunked(q, k, v, g, beta, state=None, chunk: int = 64, threads: int = 0):
+    """The same result via the chunked (block) form, fp64.  Returns (out, final)."""
+    q, k, v, g, beta, state, (S, T, H, d) = _prep(q, k, v, g, beta, state)
+    out = np.empty((S, T, H, d), dtype=np.float64)
+    fin = np.empty((S, H, d, d), dtype=np.float64)
+    rc = _lib().oracle_gdn_chunked(q, k, v, g, beta, _ptr(state), out, fin,
+                                   S, T, H, d, int(chunk), int(threads))
+    if rc != 0:
+        raise MemoryError("oracle_gdn_chunked failed (%d)" % rc)
+    return out, fin
+
+
+def chunk_stages(q, k, v, g, beta, state=None):
+    """Stage values of ONE chunk for a single (seq, head).
+
+    q, k, v: (n, d); g, beta: (n,); state: (d, d) [value][key] or None.
+    Returns a dict with gam (n), A, T, P (n x n), W, U, Delta, out (n x d) and
+    state (d x d, after the chunk).
+    """
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    n, d = q.shape
+    M = np.zeros((d, d)) if state is None else np.array(state, dtype=np.float64)
+    M = np.ascontiguousarray(M)
+    res = {"gam": np.empty(n), "A": np.empty((n, n)), "T": np.empty((n, n)),
+           "P": np.empty((n, n)), "W": np.empty((n, d)), "U": np.empty((n, d)),
+           "Delta": np.empty((n, d)), "out": np.empty((n, d))}
+    rc = _lib().oracle_gdn_chunk_stages(
+        q, np.ascontiguousarray(k, dtype=np.float32),
+        np.ascontiguousarray(v, dtype=np.float32),
+        np.ascontiguousarray(g, dtype=np.float32),
+        np.ascontiguousarray(beta, dtype=np.float32), M, n, d,
+        *[_ptr(res[key]) for key in ("gam", "A", "T", "P", "W", "U", "Delta", "out")])
+    if rc != 0:
+        raise MemoryError("oracle_gdn_chunk_stages failed (%d)" % rc)
+    res["state"] = M
+    return res

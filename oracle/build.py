@@ -1,0 +1,27 @@
+"""Compile the fp64 CPU oracle (test infrastructure) into oracle/libgdn_oracle.so.
+
+Plain gcc; no GPU code is involved.  Run as ``python oracle/build.py`` or via
+``build()`` in the package entry file.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "gdn_oracle.c")
+LIB = os.path.join(HERE, "libgdn_oracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c99",
+           "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
+    print(LIB)

@@ -1,0 +1,282 @@
+"""Pins for the fp64 CPU oracle (runs without a GPU).
+
+Each test fixes the oracle to something other than itself: a hand-worked
+example, closed forms that hold for special inputs, exact invariants of the
+rule, a library matrix inverse and brute-force agreement between the token
+recurrence and the independently written chunked form.  Together they would
+catch a dropped term, a wrong sign, a transposed state, a gate applied after
+the retrieval instead of before it, a readout taken before the write, or a
+missing 1/sqrt(head_dim).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_attention_recurrence_03_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, scale=1.0):
+    return (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32)
+
+
+def _unit(x):
+    x = x.astype(np.float64)
+    return (x / np.linalg.norm(x, axis=-1, keepdims=True)).astype(np.float32)
+
+
+def _problem(S, T, H, d, seed, state=True):
+    rng = np.random.default_rng(seed)
+    q = _unit(rng.standard_normal((S, T, H, d)))
+    k = _unit(rng.standard_normal((S, T, H, d)))
+    v = rng.standard_normal((S, T, H, d)).astype(np.float32)
+    g = (-np.logaddexp(0, rng.standard_normal((S, T, H)))).astype(np.float32)
+    beta = (1 / (1 + np.exp(-rng.standard_normal((S, T, H))))).astype(np.float32)
+    st = (rng.standard_normal((S, H, d, d)) * 0.1).astype(np.float32) if state else None
+    return q, k, v, g, beta, st
+
+
+def test_hand_worked_example():
+    """tests/golden/hand_d2.json: three tokens at head_dim 2 derived by hand."""
+    with open(os.path.join(GOLDEN, "hand_d2.json")) as f:
+        case = json.load(f)
+    q = np.array(case["q"], np.float32)[None, :, None, :]
+    k = np.array(case["k"], np.float32)[None, :, None, :]
+    v = np.array(case["v"], np.float32)[None, :, None, :]
+    g = np.array(case["g"], np.float32)[None, :, None]
+    beta = np.array(case["beta"], np.float32)[None, :, None]
+    tol = case["tolerance"]
+    for fn in (oracle.gdn_recurrent, lambda *a: oracle.gdn_chunked(*a, chunk=2)):
+        out, fin = fn(q, k, v, g, beta, None)
+        np.testing.assert_allclose(out[0, :, 0, :] * np.sqrt(2.0),
+                                   np.array(case["out_times_sqrt2"]), rtol=0, atol=tol * 10)
+        np.testing.assert_allclose(fin[0, 0], np.array(case["final_state"]),
+                                   rtol=0, atol=tol * 10)
+
+
+@pytest.mark.parametrize("d", [4, 16, 32])
+def test_beta_zero_closed_form(d):
+    """beta = 0: no write ever happens, so the state is only decayed.
+
+    out_t = (1/sqrt(d)) exp(G_t) M0 q_t with G_t the inclusive sum of g over the
+    call's tokens, and final = exp(G_T) M0.  M0 is deliberately non-symmetric so
+    a transposed layout fails.
+    """
+    S, T, H = 2, 37, 3
+    q, k, v, g, beta, st = _problem(S, T, H, d, seed=d)
+    beta = np.zeros_like(beta)
+    st = st + np.triu(np.ones((d, d), np.float32))  # clearly non-symmetric
+    out, fin = oracle.gdn_recurrent(q, k, v, g, beta, st)
+    G = np.cumsum(g.astype(np.float64), axis=1)            # (S, T, H)
+    M0 = st.astype(np.float64)
+    expect = np.einsum("sth,shij,sthj->sthi", np.exp(G), M0, q.astype(np.float64)) / np.sqrt(d)
+    np.testing.assert_allclose(out, expect, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(fin, np.exp(G[:, -1, :])[:, :, None, None] * M0,
+                               rtol=1e-12, atol=1e-14)
+    assert not np.allclose(M0, np.swapaxes(M0, -1, -2))
+
+
+@pytest.mark.parametrize("d", [8, 32])
+def test_beta_one_unit_key_overwrites(d):
+    """beta = 1 and |k| = 1: after each token the state maps k_t exactly to v_t,
+    whatever the gate and the previous state.  With q = k the output is v/sqrt(d).
+    """
+    S, T, H = 2, 20, 2
+    q, k, v, g, beta, st = _problem(S, T, H, d, seed=100 + d)
+    k64 = k.astype(np.float64)
+    k = (k64 / np.linalg.norm(k64, axis=-1, keepdims=True)).astype(np.float32)
+    beta = np.ones_like(beta)
+    g = g * 3  # strong, varied decay
+    out, fin = oracle.gdn_recurrent(k, k, v, g, beta, st)
+    # fp32 keys are unit only to ~1e-7, which bounds how exact the overwrite is
+    nk = np.sum(k.astype(np.float64) ** 2, axis=-1, keepdims=True)
+    np.testing.assert_allclose(out * np.sqrt(d), v.astype(np.float64), rtol=0, atol=5e-6)
+    retrieved = np.einsum("shij,shj->shi", fin, k[:, -1].astype(np.float64))
+    np.testing.assert_allclose(retrieved, v[:, -1].astype(np.float64), atol=5e-6)
+    assert np.max(np.abs(nk - 1)) < 1e-6
+
+
+def _hadamard(n):
+    h = np.array([[1.0]])
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+@pytest.mark.parametrize("basis", ["hadamard16", "signed_perm32"])
+def test_orthonormal_keys_overwrite_not_add(basis):
+    """g = 0, beta = 1, M0 = 0, keys cycling through an exactly orthonormal
+    basis: reading with a basis vector returns the LAST value written under it
+    (plain additive linear attention would return the sum of all of them).
+    """
+    if basis == "hadamard16":
+        d = 16
+        B = (_hadamard(16) / 4.0).astype(np.float32)      # rows orthonormal, exact
+    else:
+        d = 32
+        rng = np.random.default_rng(7)
+        B = np.zeros((d, d), np.float32)
+        B[np.arange(d), rng.permutation(d)] = rng.choice([-1.0, 1.0], d)
+    T = 2 * d
+    kidx = np.arange(T) % d
+    k = B[kidx][None, :, None, :]
+    # read with the previous token's key: that slot was written one step ago
+    qidx = (np.arange(T) - 1) % d
+    q = B[qidx][None, :, None, :]
+    v = _rand((1, T, 1, d), 11)
+    g = np.zeros((1, T, 1), np.float32)
+    beta = np.ones((1, T, 1), np.float32)
+    out, fin = oracle.gdn_recurrent(q, k, v, g, beta, None)
+    expect = np.zeros((T, d))
+    for t in range(T):
+        writes = [u for u in range(t + 1) if kidx[u] == qidx[t]]
+        if writes:
+            expect[t] = v[0, writes[-1], 0]
+    np.testing.assert_allclose(out[0, :, 0] * np.sqrt(d), expect, atol=1e-12)
+    # final state = sum_j v_last(j) b_j^T, stored [value][key]
+    last = {int(kidx[u]): u for u in range(T)}
+    M = sum(np.outer(v[0, last[j], 0].astype(np.float64), B[j].astype(np.float64))
+            for j in range(d))
+    np.testing.assert_allclose(fin[0, 0], M, atol=1e-12)
+
+
+def test_single_token_from_zero():
+    """One token from a zero state: M = beta v k^T and out = (beta/sqrt(d)) (k.q) v."""
+    d = 32
+    q, k, v, g, beta, _ = _problem(1, 1, 4, d, seed=5)
+    k = k * 1.7  # keys need not be unit for this identity
+    out, fin = oracle.gdn_recurrent(q, k, v, g, beta, None)
+    for h in range(4):
+        kk, qq, vv = (x[0, 0, h].astype(np.float64) for x in (k, q, v))
+        b = float(beta[0, 0, h])
+        np.testing.assert_allclose(fin[0, h], b * np.outer(vv, kk), rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(out[0, 0, h], b * (kk @ qq) * vv / np.sqrt(d),
+                                   rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("d", [4, 16, 32])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130])
+@pytest.mark.parametrize("C", [1, 4, 16, 64])
+def test_recurrent_equals_chunked(d, T, C):
+    """Brute force: the token recurrence and the chunked form agree to rounding."""
+    q, k, v, g, beta, st = _problem(1, T, 2, d, seed=1000 * d + T + C)
+    o1, f1 = oracle.gdn_recurrent(q, k, v, g, beta, st)
+    o2, f2 = oracle.gdn_chunked(q, k, v, g, beta, st, chunk=C)
+    scale = max(np.max(np.abs(o1)), 1e-300)
+    assert np.max(np.abs(o1 - o2)) / scale < 1e-12
+    assert np.max(np.abs(f1 - f2)) / max(np.max(np.abs(f1)), 1e-300) < 1e-12
+
+
+def test_recurrent_equals_chunked_strong_and_weak_decay():
+    """Chunked form under the mixed strong-decay gates and under very weak decay."""
+    for gate in ("mixed", "weak"):
+        x = inputs.custom(1, 150, 2, 16, dtype="bf16", state="normal", gate=gate,
+                          beta_std=2.0, seed=3)
+        o1, f1 = oracle.gdn_recurrent(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"])
+        o2, f2 = oracle.gdn_chunked(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"],
+                                    chunk=64)
+        assert np.max(np.abs(o1 - o2)) / np.max(np.abs(o1)) < 1e-12
+        assert np.max(np.abs(f1 - f2)) / np.max(np.abs(f1)) < 1e-12
+
+
+@pytest.mark.parametrize("n", [1, 5, 16, 64])
+def test_chunk_T_matches_library_inverse(n):
+    """The forward-substitution T equals numpy.linalg.inv(I + A); A is strictly
+    lower triangular and P lower triangular (causal masks)."""
+    d = 16
+    q, k, v, g, beta, st = _problem(1, n, 1, d, seed=n)
+    r = oracle.chunk_stages(q[0, :, 0], k[0, :, 0], v[0, :, 0], g[0, :, 0],
+                            beta[0, :, 0], st[0, 0].astype(np.float64))
+    A, T = r["A"], r["T"]
+    assert np.all(np.triu(A) == 0)
+    assert np.all(np.triu(r["P"], 1) == 0)
+    np.testing.assert_allclose(T, np.linalg.inv(np.eye(n) + A), rtol=1e-12, atol=1e-14)
+    # gate sums are the inclusive prefix sums of this chunk's g
+    np.testing.assert_allclose(r["gam"], np.cumsum(g[0, :, 0].astype(np.float64)), rtol=1e-15)
+
+
+def test_chunk_stages_single_chunk_matches_recurrence():
+    """Stage output of one whole chunk equals the recurrence's out and state."""
+    n, d = 40, 16
+    q, k, v, g, beta, st = _problem(1, n, 1, d, seed=9)
+    r = oracle.chunk_stages(q[0, :, 0], k[0, :, 0], v[0, :, 0], g[0, :, 0],
+                            beta[0, :, 0], st[0, 0].astype(np.float64))
+    o, f = oracle.gdn_recurrent(q, k, v, g, beta, st)
+    np.testing.assert_allclose(r["out"], o[0, :, 0], rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(r["state"], f[0, 0], rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("T1", [1, 17, 64])
+def test_split_invariance(T1):
+    """Running T tokens at once equals T1 tokens then the rest with the state
+    carried (the state is the checkpoint)."""
+    T, d = 100, 16
+    q, k, v, g, beta, st = _problem(2, T, 3, d, seed=T1)
+    o, f = oracle.gdn_recurrent(q, k, v, g, beta, st)
+    oa, fa = oracle.gdn_recurrent(q[:, :T1], k[:, :T1], v[:, :T1], g[:, :T1],
+                                  beta[:, :T1], st)
+    ob, fb = oracle.gdn_recurrent(q[:, T1:], k[:, T1:], v[:, T1:], g[:, T1:],
+                                  beta[:, T1:], fa)
+    np.testing.assert_allclose(np.concatenate([oa, ob], axis=1), o, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(fb, f, rtol=1e-13, atol=1e-15)
+
+
+def test_independence_of_value_rows_heads_and_seqs():
+    """Perturbing v[..., i] changes only out[..., i] and row i of the state;
+    perturbing one (seq, head) leaves every other one bit-identical."""
+    S, T, H, d = 2, 30, 3, 16
+    q, k, v, g, beta, st = _problem(S, T, H, d, seed=77)
+    o, f = oracle.gdn_recurrent(q, k, v, g, beta, st)
+    i = 5
+    v2 = v.copy()
+    v2[..., i] += 1.0
+    o2, f2 = oracle.gdn_recurrent(q, k, v2, g, beta, st)
+    other = [j for j in range(d) if j != i]
+    assert np.array_equal(o[..., other], o2[..., other])
+    assert np.array_equal(f[:, :, other, :], f2[:, :, other, :])
+    assert not np.array_equal(o[..., i], o2[..., i])
+    k2 = k.copy()
+    k2[1, :, 2] = k2[1, ::-1, 2]
+    o3, f3 = oracle.gdn_recurrent(q, k2, v, g, beta, st)
+    mask = np.ones((S, H), bool)
+    mask[1, 2] = False
+    for s in range(S):
+        for h in range(H):
+            same = np.array_equal(o[s, :, h], o3[s, :, h]) and np.array_equal(f[s, h], f3[s, h])
+            assert same == mask[s, h]
+
+
+def test_linear_in_q():
+    """q -> c q scales out by c and leaves the state untouched."""
+    q, k, v, g, beta, st = _problem(1, 25, 2, 16, seed=3)
+    o, f = oracle.gdn_recurrent(q, k, v, g, beta, st)
+    o2, f2 = oracle.gdn_recurrent(q * 2, k, v, g, beta, st)
+    assert np.array_equal(o2, 2 * o) and np.array_equal(f2, f)
+    o3, f3 = oracle.gdn_recurrent((q * np.float32(0.3)), k, v, g, beta, st)
+    # 0.3 q is rounded to fp32 (6e-8 relative per element), hence the bound
+    assert np.max(np.abs(o3 - 0.3 * o)) / np.max(np.abs(o)) < 1e-6
+    assert np.array_equal(f3, f)
+
+
+def test_zero_tokens_returns_state():
+    """No tokens: the state passes through unchanged."""
+    d = 8
+    st = _rand((1, 2, d, d), 1)
+    z = np.zeros((1, 0, 2, d), np.float32)
+    zg = np.zeros((1, 0, 2), np.float32)
+    o, f = oracle.gdn_recurrent(z, z, z, zg, zg, st)
+    assert o.shape == (1, 0, 2, d)
+    assert np.array_equal(f, st.astype(np.float64))
+    o, f = oracle.gdn_chunked(z, z, z, zg, zg, st)
+    assert np.array_equal(f, st.astype(np.float64))
+
+
+def test_threads_do_not_change_results():
+    q, k, v, g, beta, st = _problem(2, 40, 4, 16, seed=8)
+    o1, f1 = oracle.gdn_recurrent(q, k, v, g, beta, st, threads=1)
+    o2, f2 = oracle.gdn_recurrent(q, k, v, g, beta, st, threads=4)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
