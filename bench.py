@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of libgdn on one MI355X.
+
+Headline: chunked prefill tokens/s on n_seqs=1, n_tokens=4096, n_heads=32,
+head_dim=128, bf16 q/k/v, fp32 g/beta/state (one GDN layer of a 4B hybrid
+model; "ggml attention kernels" model card, section "Measured").  A step is one
+gdn_forward call over that batch: every stage of the chunked path runs inside
+it.  Also reported (extra keys on the same JSON line): single-token decode
+microseconds per layer over 24 sequential layer calls, batched decode, and the
+long batched prefill (4 x 32768 tokens, 16 heads).
+
+Cold-cache protocol: MI355X has 256 MB of Infinity Cache in front of HBM and
+every workload here except the long prefill would fit in it, so timed loops
+rotate through enough input copies (or scrub a 1 GiB buffer first) that each
+call reads inputs the cache no longer holds.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+CHUNK = 64
+
+
+def algorithmic_bytes(S, T, H, D, esz, state_read=True):
+    """Each input read once, each output written once, the state read+written once."""
+    tok = S * T * H * D * esz
+    gate = S * T * H * 4
+    st = S * H * D * D * 4
+    return 4 * tok + 2 * gate + st * (2 if state_read else 1)
+
+
+def algorithmic_flops_chunked(S, T, H, D, C=CHUNK):
+    """Per token-head 5 C d + 6 d^2 + C^2/3 (triangular work the chunked form needs)."""
+    return S * T * H * (5 * C * D + 6 * D * D + C * C / 3.0)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_recurrence_03_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_key):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def to_dev(x, dtype, torch):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    d = {}
+    for n in ("q", "k", "v"):
+        d[n] = torch.from_numpy(x[n]).to("cuda").to(tdt).contiguous()
+    for n in ("g", "beta", "state"):
+        d[n] = torch.from_numpy(x[n]).to("cuda").contiguous()
+    return d
+
+
+class Slot:
+    """One resident copy of a workload's inputs plus its output buffers."""
+
+    def __init__(self, gdn, d, torch):
+        self.d = d
+        q = d["q"]
+        S, T, H, D = q.shape
+        self.out = torch.empty_like(q)
+        self.state_out = torch.empty((S, H, D, D), dtype=torch.float32, device="cuda")
+        need = gdn.workspace_size("bf16" if q.dtype == torch.bfloat16 else "f32", S, T, H, D)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+
+    def run(self, gdn):
+        d = self.d
+        gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], out=self.out,
+                    state_out=self.state_out, workspace=self.ws)
+
+
+def clone_dev(d):
+    return {n: t.clone() for n, t in d.items()}
+
+
+def time_loop(torch, fn, n):
+    """HIP-event time of n calls of fn() on the current stream, in ms per call."""
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def bench_prefill(gdn, torch, wl, steps, warmup, nbuf):
+    from linear_attention_recurrence_03_amd import inputs
+    x = inputs.make(wl)
+    base = to_dev(x, wl.dtype, torch)
+    slots = [Slot(gdn, base if i == 0 else clone_dev(base), torch) for i in range(nbuf)]
+    del x
+    for i in range(warmup):
+        slots[i % nbuf].run(gdn)
+    ms = time_loop(torch, lambda i: slots[i % nbuf].run(gdn), steps)
+    return ms, slots
+
+
+def bench_decode_layers(gdn, torch, wl, reps, n_layers=24):
+    """24 sequential single-token layer calls, each with its own inputs and state;
+    a 1 GiB scrub before each timed batch; median over reps."""
+    from linear_attention_recurrence_03_amd import inputs
+    slots = [Slot(gdn, to_dev(inputs.make(wl, layer=l), wl.dtype, torch), torch)
+             for l in range(n_layers)]
+    scrub = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    for s in slots:
+        s.run(gdn)
+    dev_us, host_us = [], []
+    for _ in range(reps):
+        scrub.fill_(1.0)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        t0 = time.perf_counter()
+        for s in slots:
+            s.run(gdn)
+        t1 = time.perf_counter()
+        b.record()
+        torch.cuda.synchronize()
+        dev_us.append(a.elapsed_time(b) * 1e3 / n_layers)
+        host_us.append((t1 - t0) * 1e6 / n_layers)
+    return statistics.median(dev_us), min(dev_us), max(dev_us), statistics.median(host_us)
+
+
+def cpu_baseline(wl):
+    """The fp64 oracle on this host's cores over the whole prefill workload."""
+    import oracle
+    from linear_attention_recurrence_03_amd import inputs
+    x = inputs.make(wl)
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    oracle.gdn_recurrent(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"], threads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": wl.n_seqs * wl.n_tokens / dt, "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "the whole workload (%d seq x %d tokens x %d heads, d=%d), fp64 token "
+                      "recurrence, OpenMP over (seq, head)" % (wl.n_seqs, wl.n_tokens,
+                                                              wl.n_heads, wl.head_dim)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the decode and long-prefill extras")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus %d (WORLD_SIZE=%d) is not "
+              "supported.  Each (sequence, head) is independent, so a multi-GPU run would "
+              "shard heads with no communication; it is not measured here." % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_recurrence_03_amd as gdn
+    from linear_attention_recurrence_03_amd import inputs
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    gdn._lib()
+
+    wl = inputs.WORKLOADS[4]
+    S, T, H, D = wl.shape()
+    ms, _ = bench_prefill(gdn, torch, wl, args.steps, args.warmup, nbuf=4)
+    tok_s = S * T / (ms * 1e-3)
+    nbytes = algorithmic_bytes(S, T, H, D, 2)
+    flops = algorithmic_flops_chunked(S, T, H, D)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    traffic = load_traffic("prefill_bf16")
+    line = {
+        "metric": "GDN prefill tokens/s @T=4096,H=32,d=128",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_bf16: n_seqs=1 n_tokens=4096 n_heads=32 head_dim=128, "
+                               "bf16 q/k/v/out, fp32 g/beta/state, chunk 64",
+                   "n_seqs": S, "n_tokens": T, "n_heads": H, "head_dim": D},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "scope": "one gdn_forward call (all kernels of the chunked path)"},
+    }
+
+    if not args.headline_only:
+        extras = {}
+        # single-token decode, 24 layers
+        wl2 = inputs.WORKLOADS[2]
+        med, lo, hi, host = bench_decode_layers(gdn, torch, wl2, reps=30)
+        b2 = algorithmic_bytes(*wl2.shape(), 4)
+        extras["decode_1tok"] = {
+            "us_per_layer_device": round(med, 3), "us_min": round(lo, 3), "us_max": round(hi, 3),
+            "us_per_layer_host": round(host, 3), "bytes_per_call": b2,
+            "hbm_frac": round(b2 / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "workload": "1 seq x 1 token x 32 heads x d128 fp32, 24 sequential layer calls, "
+                        "1 GiB scrub before each batch"}
+        # batched decode
+        wl3 = inputs.WORKLOADS[3]
+        ms3, _ = bench_prefill(gdn, torch, wl3, steps=50, warmup=5, nbuf=3)
+        b3 = algorithmic_bytes(*wl3.shape(), 4)
+        extras["decode_batched"] = {
+            "us_per_call": round(ms3 * 1e3, 3), "bytes_per_call": b3,
+            "achieved_GBs": round(b3 / (ms3 * 1e-3) / 1e9, 1),
+            "hbm_frac": round(b3 / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "workload": "64 seqs x 1 token x 32 heads x d128 fp32, 3 rotating input copies"}
+        torch.cuda.empty_cache()
+        # long prefill
+        wl5 = inputs.WORKLOADS[5]
+        ms5, slots = bench_prefill(gdn, torch, wl5, steps=10, warmup=2, nbuf=1)
+        del slots
+        torch.cuda.empty_cache()
+        S5, T5, H5, D5 = wl5.shape()
+        b5 = algorithmic_bytes(S5, T5, H5, D5, 2)
+        f5 = algorithmic_flops_chunked(S5, T5, H5, D5)
+        extras["prefill_long"] = {
+            "tokens_per_s": round(S5 * T5 / (ms5 * 1e-3), 1), "ms_per_call": round(ms5, 4),
+            "hbm_frac": round(b5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(f5 / (ms5 * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "workload": "4 seqs x 32768 tokens x 16 heads x d128 bf16, carried N(0,0.1) state"}
+        line["extras"] = extras
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+/*
+ * gdn.h -- libgdn: the gated delta rule recurrence on AMD MI355X (gfx950).
+ *
+ * One call runs a whole span of gated-delta-rule steps for every sequence and
+ * head ("ggml attention kernels" model card, huggingface.co/marcsun13/
+ * ggml-gated-delta-net, section "Ops": one dispatch for a whole run of steps,
+ * signature (q, k, v, g, beta, state) -> (out, final_state), plus a supports
+ * predicate on head_dim).
+ *
+ * Per sequence s and head h, with the state M stored [value][key] (row i is a
+ * value channel, column j a key channel) and d = head_dim, each token t does
+ *     M     <- exp(g_t) * M                      (gate; g is log-domain)
+ *     delta  = beta_t * (v_t - M k_t)            (what the key now retrieves)
+ *     M     <- M + delta k_t^T                   (delta-rule overwrite)
+ *     out_t  = M q_t / sqrt(d)                   (readout after the write)
+ * The gate and the overwrite are the two ideas described in "Gated Delta Net
+ * on AMD: why ROCm stumbles on hybrid-attention LLMs" (velstech.net, section
+ * "What Gated Delta Net is, in plain language"); the op exponentiates g itself
+ * and applies the 1/sqrt(head_dim) output scaling itself (model card, the
+ * paragraph after the contract bullets).  The retrieval uses the gated state
+ * and the readout follows the write: the pages leave that order open and this
+ * is the reading taken.
+ *
+ * All arrays are dense, row-major ("torch order", model card section "Shapes,
+ * in torch order"):
+ *     q, k, v, out : (n_seqs, n_tokens, n_heads, head_dim)   dtype gdn_dtype
+ *     g, beta      : (n_seqs, n_tokens, n_heads)             fp32
+ *     state_in/out : (n_seqs, n_heads, head_dim, head_dim)   fp32, [value][key]
+ * q and k carry one head per value head, already expanded (first contract
+ * bullet): head h of q and k pairs with head h of v, in the caller's order.
+ * q and k are used as given (no normalisation inside the op).
+ *
+ * Ownership and streams.  Every data pointer is a DEVICE pointer owned by the
+ * caller.  The library keeps no pointer after a call returns and never
+ * allocates device memory: scratch space for the chunked algorithm is the
+ * caller's workspace.  Work is enqueued on the caller's stream and the call
+ * returns without synchronising; results are ready when that stream reaches
+ * the end of the enqueued work (the model card, section "Where the kernels
+ * come from", explains why kernels must join the caller's own queue).
+ *
+ * Errors.  Every entry point validates its arguments on the host first and
+ * launches nothing when it returns an error.  Device faults, if any, surface
+ * at the caller's next synchronisation of the stream.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage dtype of q, k, v and out.  g, beta and the state are always fp32. */
+typedef enum {
+    GDN_F32 = 0,
+    GDN_BF16 = 1
+} gdn_dtype;
+
+/* Algorithm choice.  AUTO takes the token recurrence for n_tokens < 64 and the
+ * chunked form (chunks of 64 tokens) otherwise.  The two forced values exist so
+ * that tests can run either algorithm on any input. */
+typedef enum {
+    GDN_ALGO_AUTO = 0,
+    GDN_ALGO_RECURRENT = 1,
+    GDN_ALGO_CHUNKED = 2
+} gdn_algo;
+
+/* Status codes: GDN_OK or a negative error. */
+enum {
+    GDN_OK = 0,
+    GDN_ERR_UNSUPPORTED_HEAD_DIM = -1, /* head_dim not accepted by gdn_supports */
+    GDN_ERR_BAD_SHAPE = -2,            /* a size is negative or too large     */
+    GDN_ERR_NULL_POINTER = -3,         /* a needed pointer is NULL            */
+    GDN_ERR_BAD_DTYPE = -4,            /* dtype is not a gdn_dtype value      */
+    GDN_ERR_WORKSPACE_TOO_SMALL = -5,  /* workspace_bytes < gdn_workspace_size */
+    GDN_ERR_ALGO_UNAVAILABLE = -6,     /* algo is not a gdn_algo value        */
+    GDN_ERR_MISALIGNED = -7,           /* a pointer is not 16-byte aligned    */
+    GDN_ERR_ALIASING = -8,             /* out overlaps an input, or state_out
+                                          overlaps state_in without being equal */
+    GDN_ERR_HIP = -9                   /* the HIP runtime refused a launch     */
+};
+
+/* 1 if head_dim is supported, else 0.  Supported widths are the multiples of 32
+ * from 32 to 128 (32, 64, 96, 128): a state row is covered by 32 lanes holding
+ * head_dim/32 values each, and widths above 128 are not built (model card, the
+ * paragraph after the contract bullets, on asking rather than assuming). */
+int gdn_supports(int head_dim);
+
+/* Bytes of device workspace gdn_forward needs for these sizes, dtype and
+ * algorithm (0 for the token recurrence).  Returns 0 for arguments
+ * gdn_forward would reject.  The workspace's contents are internal and need no
+ * initialisation; it may be reused by later calls on the same stream. */
+size_t gdn_workspace_size(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens,
+                          int64_t n_heads, int head_dim, gdn_algo algo);
+
+/* Run n_tokens gated-delta-rule steps for every (sequence, head).
+ *
+ *   dtype        storage dtype of q, k, v, out
+ *   q, k, v      (n_seqs, n_tokens, n_heads, head_dim), device, read only
+ *   g, beta      (n_seqs, n_tokens, n_heads) fp32, device, read only; g is the
+ *                log-domain gate and must be finite (exp(g) is the decay)
+ *   state_in     (n_seqs, n_heads, head_dim, head_dim) fp32 [value][key],
+ *                device, read only; NULL means a zero initial state
+ *   out          like q, device, written; the output includes 1/sqrt(head_dim)
+ *   state_out    like state_in, device, written with the state after the last
+ *                token.  state_out == state_in is allowed (in-place update);
+ *                any other overlap, and any overlap of out with an input, is
+ *                rejected with GDN_ERR_ALIASING
+ *   workspace    device scratch of at least gdn_workspace_size(...) bytes
+ *                (may be NULL when that size is 0)
+ *   algo         GDN_ALGO_AUTO, or a forced algorithm
+ *   stream       a hipStream_t (NULL = the default stream)
+ *
+ * n_seqs == 0 or n_heads == 0 is a no-op.  n_tokens == 0 copies state_in to
+ * state_out (or zero-fills it when state_in is NULL) and writes no output.
+ * Every pointer must be 16-byte aligned.  Returns GDN_OK or a negative status;
+ * on error nothing is launched. */
+int gdn_forward(gdn_dtype dtype, const void *q, const void *k, const void *v,
+                const float *g, const float *beta, const float *state_in,
+                void *out, float *state_out, int64_t n_seqs, int64_t n_tokens,
+                int64_t n_heads, int head_dim, void *workspace,
+                size_t workspace_bytes, gdn_algo algo, void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *gdn_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

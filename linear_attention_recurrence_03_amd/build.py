@@ -1,0 +1,55 @@
+"""Build libgdn.so (HIP kernels for gfx950 + the C-ABI) in-tree with hipcc.
+
+Usage: ``python -m linear_attention_recurrence_03_amd.build`` (or ``build()``
+from the package entry file).  Always recompiles.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libgdn.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_chunk.hip"]
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
+# Device code: gfx950 only; packed-fp32 instruction selection disabled.
+DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-fgpu-flush-denormals-to-zero", "-munsafe-fp-atomics"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    with tempfile.TemporaryDirectory(prefix="gdn_build_") as tmp:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            flags = COMMON + (DEVICE if src.endswith(".hip") else ["-D__HIP_PLATFORM_AMD__"])
+            cmd = [HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append(subprocess.Popen(cmd))
+            objs.append(obj)
+        bad = [p.wait() for p in procs]
+        if any(bad):
+            raise RuntimeError("hipcc failed (exit codes %s)" % bad)
+        tmp_lib = LIB + ".tmp"
+        _run([HIPCC, "-shared", "--offload-arch=" + ARCH, "-fPIC", "-o", tmp_lib] + objs, verbose)
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,200 @@
+// gdn_api.cpp -- the C-ABI of libgdn: host-side validation and dispatch.
+//
+// Every check runs before any HIP call, so that a rejected call launches
+// nothing (and so that the checks can be exercised on a machine without a
+// GPU).  The contract is documented in include/gdn.h.
+#include "gdn.h"
+
+#include <limits.h>
+#include <stdint.h>
+
+#include "gdn_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+// Largest element count accepted for one tensor: far beyond any device memory,
+// small enough that every byte offset fits comfortably in int64.
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool mul_ok(int64_t a, int64_t b, int64_t *r)
+{
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > kMaxElems / a) return false;
+    *r = a * b;
+    return *r <= kMaxElems;
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void *p, int64_t bytes)
+{
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(Range a, Range b)
+{
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned16(const void *p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+gdn_algo pick_algo(gdn_algo algo, int64_t n_tokens)
+{
+    if (algo != GDN_ALGO_AUTO) return algo;
+    return n_tokens >= gdn::kChunk ? GDN_ALGO_CHUNKED : GDN_ALGO_RECURRENT;
+}
+
+// Shape checks shared by gdn_workspace_size and gdn_forward.  On success fills
+// the element counts of a token tensor, a gate tensor and the state.
+int check_shape(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens, int64_t n_heads,
+                int head_dim, gdn_algo algo, int64_t *tok_elems, int64_t *gate_elems,
+                int64_t *state_elems)
+{
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+    if (algo != GDN_ALGO_AUTO && algo != GDN_ALGO_RECURRENT && algo != GDN_ALGO_CHUNKED)
+        return GDN_ERR_ALGO_UNAVAILABLE;
+    if (!gdn_supports(head_dim)) return GDN_ERR_UNSUPPORTED_HEAD_DIM;
+    if (n_seqs < 0 || n_tokens < 0 || n_heads < 0) return GDN_ERR_BAD_SHAPE;
+    int64_t a, b;
+    if (!mul_ok(n_seqs, n_tokens, &a) || !mul_ok(a, n_heads, gate_elems) ||
+        !mul_ok(*gate_elems, head_dim, tok_elems))
+        return GDN_ERR_BAD_SHAPE;
+    if (!mul_ok(n_seqs, n_heads, &b) || !mul_ok(b, int64_t(head_dim) * head_dim, state_elems))
+        return GDN_ERR_BAD_SHAPE;
+    // launch grids index (seq, head, row block) with 32-bit block ids
+    if (b > (int64_t(1) << 24)) return GDN_ERR_BAD_SHAPE;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_supports(int head_dim)
+{
+    return (head_dim >= 32 && head_dim <= 128 && head_dim % 32 == 0) ? 1 : 0;
+}
+
+size_t gdn_workspace_size(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens,
+                          int64_t n_heads, int head_dim, gdn_algo algo)
+{
+    int64_t te, ge, se;
+    if (check_shape(dtype, n_seqs, n_tokens, n_heads, head_dim, algo, &te, &ge, &se) != GDN_OK)
+        return 0;
+    if (n_seqs == 0 || n_heads == 0 || n_tokens == 0) return 0;
+    if (pick_algo(algo, n_tokens) != GDN_ALGO_CHUNKED) return 0;
+    return gdn::chunk_workspace_bytes(dtype == GDN_BF16, n_seqs, n_tokens, n_heads, head_dim);
+}
+
+int gdn_forward(gdn_dtype dtype, const void *q, const void *k, const void *v, const float *g,
+                const float *beta, const float *state_in, void *out, float *state_out,
+                int64_t n_seqs, int64_t n_tokens, int64_t n_heads, int head_dim,
+                void *workspace, size_t workspace_bytes, gdn_algo algo, void *stream)
+{
+    int64_t tok_elems, gate_elems, state_elems;
+    int rc = check_shape(dtype, n_seqs, n_tokens, n_heads, head_dim, algo, &tok_elems,
+                         &gate_elems, &state_elems);
+    if (rc != GDN_OK) return rc;
+    if (n_seqs == 0 || n_heads == 0) return GDN_OK;
+
+    const int64_t esz = (dtype == GDN_BF16) ? 2 : 4;
+    const bool have_tokens = n_tokens > 0;
+    if (!state_out) return GDN_ERR_NULL_POINTER;
+    if (have_tokens && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL_POINTER;
+
+    const void *ptrs[] = {q, k, v, g, beta, state_in, out, state_out, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_MISALIGNED;
+
+    const Range r_state_out = range_of(state_out, state_elems * 4);
+    const Range r_state_in = state_in ? range_of(state_in, state_elems * 4) : Range{0, 0};
+    if (state_in && state_in != state_out && overlap(r_state_in, r_state_out))
+        return GDN_ERR_ALIASING;
+    if (have_tokens) {
+        const Range r_out = range_of(out, tok_elems * esz);
+        const Range reads[] = {range_of(q, tok_elems * esz), range_of(k, tok_elems * esz),
+                               range_of(v, tok_elems * esz), range_of(g, gate_elems * 4),
+                               range_of(beta, gate_elems * 4)};
+        for (const Range &r : reads)
+            if (overlap(r_out, r) || overlap(r_state_out, r)) return GDN_ERR_ALIASING;
+        if (overlap(r_out, r_state_in) || overlap(r_out, r_state_out)) return GDN_ERR_ALIASING;
+    }
+
+    const gdn_algo chosen = pick_algo(algo, n_tokens);
+    size_t need = 0;
+    if (have_tokens && chosen == GDN_ALGO_CHUNKED) {
+        need = gdn::chunk_workspace_bytes(dtype == GDN_BF16, n_seqs, n_tokens, n_heads, head_dim);
+        if (workspace_bytes < need) return GDN_ERR_WORKSPACE_TOO_SMALL;
+        if (need > 0 && !workspace) return GDN_ERR_NULL_POINTER;
+        if (need > 0) {
+            const Range r_ws = range_of(workspace, static_cast<int64_t>(need));
+            const Range all[] = {range_of(q, tok_elems * esz), range_of(k, tok_elems * esz),
+                                 range_of(v, tok_elems * esz), range_of(g, gate_elems * 4),
+                                 range_of(beta, gate_elems * 4), r_state_in, r_state_out,
+                                 range_of(out, tok_elems * esz)};
+            for (const Range &r : all)
+                if (overlap(r_ws, r)) return GDN_ERR_ALIASING;
+        }
+    }
+
+    // ---- validated: from here on only launches ----
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (!have_tokens) {
+        if (state_in == state_out) return GDN_OK;
+        err = gdn::launch_state_copy(state_in, state_out, state_elems, st);
+        return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    }
+    gdn::Problem p;
+    p.bf16 = (dtype == GDN_BF16);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.state_in = state_in;
+    p.out = out;
+    p.state_out = state_out;
+    p.n_seqs = n_seqs;
+    p.n_tokens = n_tokens;
+    p.n_heads = n_heads;
+    p.head_dim = head_dim;
+    if (chosen == GDN_ALGO_CHUNKED)
+        err = gdn::launch_chunked(p, workspace, st);
+    else
+        err = gdn::launch_recurrent(p, st);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+const char *gdn_status_string(int status)
+{
+    switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head_dim (need 32, 64, 96 or 128)";
+    case GDN_ERR_BAD_SHAPE: return "bad shape (negative or too large size)";
+    case GDN_ERR_NULL_POINTER: return "required pointer is NULL";
+    case GDN_ERR_BAD_DTYPE: return "bad dtype (need GDN_F32 or GDN_BF16)";
+    case GDN_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than gdn_workspace_size()";
+    case GDN_ERR_ALGO_UNAVAILABLE: return "algorithm value not recognised";
+    case GDN_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case GDN_ERR_ALIASING: return "output overlaps an input (only state_out == state_in is allowed)";
+    case GDN_ERR_HIP: return "HIP runtime refused a launch";
+    default: return "unknown status";
+    }
+}
+
+int gdn_version(void)
+{
+    return kVersion;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// gdn_common.h -- small device helpers used by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// bf16 <-> fp32.  bf16 is the top half of an fp32 bit pattern.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b)
+{
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even.  Inputs are finite in this library; NaN is
+// kept a NaN by forcing a mantissa bit.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Sum over each aligned group of 32 lanes of a wave64; every lane of the group
+// receives the total.  Four DPP steps reduce within rows of 16 lanes (swap
+// neighbours, swap pairs, mirror within 8, mirror within 16); one ds_swizzle
+// (xor 16, bit mode) folds the two rows of the 32-lane group.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL,
+                                                      0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float sum32(float x)
+{
+    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_mov<0x141>(x);  // row_half_mirror
+    x += dpp_mov<0x140>(x);  // row_mirror
+    x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+    return x;
+}
+
+}  // namespace gdn

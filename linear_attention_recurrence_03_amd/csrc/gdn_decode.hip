@@ -1,0 +1,283 @@
+// gdn_decode.hip -- token recurrence of the gated delta rule for gfx950.
+//
+// The step (per sequence, head and token; state M stored [value][key]):
+//     M <- exp(g) M;  delta = beta (v - M k);  M <- M + delta k^T;
+//     out = M q / sqrt(d)
+// ("Gated Delta Net on AMD", velstech.net, section "What Gated Delta Net is,
+// in plain language": a gate on the state and a delta-rule overwrite; state
+// layout, log-domain g and the 1/sqrt(head_dim) scaling from the "ggml
+// attention kernels" model card, contract notes under "Shapes, in torch
+// order").
+//
+// Value rows of M are independent given (k, q, g, beta) of the token, so each
+// state row is one unit of work.  A row of d fp32 values is held by 32 lanes
+// with d/32 consecutive values each (the width rule of the model card's
+// supports predicate), so one wave64 load instruction covers two adjacent rows
+// -- 2*d*4 contiguous bytes, fully coalesced.  A wave keeps 2*NP rows in
+// registers for the whole call: the state is read once and written once, which
+// is all of the HBM traffic that matters (the model card notes that a 2 MB
+// state copy per layer per token is most of the cost).  Per token each row
+// needs two dot products over its keys (M_i.k and M_i.q), done as lane
+// partials plus a 32-lane DPP reduction; k.q is reduced alongside.  Since
+// M_new q = exp(g) M q + delta (k.q), the readout needs no second pass over
+// the row.
+#include "gdn_common.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kWaves = 4;   // waves per workgroup
+
+template <int NV>
+struct Vec {
+    float x[NV];
+};
+
+template <int NV>
+__device__ __forceinline__ Vec<NV> load_f32(const float *p)
+{
+    Vec<NV> r;
+    if constexpr (NV == 4) {
+        const float4 t = *reinterpret_cast<const float4 *>(p);
+        r.x[0] = t.x; r.x[1] = t.y; r.x[2] = t.z; r.x[3] = t.w;
+    } else if constexpr (NV == 2) {
+        const float2 t = *reinterpret_cast<const float2 *>(p);
+        r.x[0] = t.x; r.x[1] = t.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) r.x[i] = p[i];
+    }
+    return r;
+}
+
+template <int NV>
+__device__ __forceinline__ void store_f32(float *p, const Vec<NV> &r)
+{
+    if constexpr (NV == 4) {
+        *reinterpret_cast<float4 *>(p) = make_float4(r.x[0], r.x[1], r.x[2], r.x[3]);
+    } else if constexpr (NV == 2) {
+        *reinterpret_cast<float2 *>(p) = make_float2(r.x[0], r.x[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) p[i] = r.x[i];
+    }
+}
+
+template <int NV, bool BF16>
+__device__ __forceinline__ Vec<NV> load_in(const void *base, int64_t off)
+{
+    if constexpr (!BF16) {
+        return load_f32<NV>(static_cast<const float *>(base) + off);
+    } else {
+        const uint16_t *p = static_cast<const uint16_t *>(base) + off;
+        Vec<NV> r;
+        if constexpr (NV == 4) {
+            const uint2 t = *reinterpret_cast<const uint2 *>(p);
+            r.x[0] = __uint_as_float(t.x << 16);
+            r.x[1] = __uint_as_float(t.x & 0xffff0000u);
+            r.x[2] = __uint_as_float(t.y << 16);
+            r.x[3] = __uint_as_float(t.y & 0xffff0000u);
+        } else if constexpr (NV == 2) {
+            const uint32_t t = *reinterpret_cast<const uint32_t *>(p);
+            r.x[0] = __uint_as_float(t << 16);
+            r.x[1] = __uint_as_float(t & 0xffff0000u);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) r.x[i] = bf16_to_f32(p[i]);
+        }
+        return r;
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_scalar_in(const void *base, int64_t off)
+{
+    if constexpr (BF16)
+        return bf16_to_f32(static_cast<const uint16_t *>(base)[off]);
+    else
+        return static_cast<const float *>(base)[off];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_scalar_out(void *base, int64_t off, float x)
+{
+    if constexpr (BF16)
+        static_cast<uint16_t *>(base)[off] = f32_to_bf16(x);
+    else
+        static_cast<float *>(base)[off] = x;
+}
+
+// One workgroup = kWaves waves = kWaves*2*NP consecutive value rows of one
+// (seq, head).  Grid: n_seqs * n_heads * (D / rows_per_block) workgroups.
+template <int D, int NP, bool BF16>
+__global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
+    const void *__restrict__ q, const void *__restrict__ k,
+    const void *__restrict__ v, const float *__restrict__ g,
+    const float *__restrict__ beta, const float *state_in, void *__restrict__ out,
+    float *state_out, int64_t n_tokens, int64_t n_heads, float scale)
+{
+    constexpr int NV = D / 32;
+    constexpr int kRowsPerWave = 2 * NP;
+    constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
+    constexpr int kBlocksPerHead = D / kRowsPerBlock;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int col = (lane & 31) * NV;
+    const int64_t sh = blockIdx.x / kBlocksPerHead;   // s * n_heads + h
+    const int rb = blockIdx.x % kBlocksPerHead;
+    const int64_t s = sh / n_heads;
+    const int64_t h = sh - s * n_heads;
+    // rows of this lane: row0 + 2p, p < NP (the two half-waves interleave)
+    const int row0 = rb * kRowsPerBlock + wave * kRowsPerWave + (lane >> 5);
+    const int64_t st_base = sh * D * D;
+
+    Vec<NV> M[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        if (state_in) {
+            M[p] = load_f32<NV>(state_in + st_base + (int64_t)(row0 + 2 * p) * D + col);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) M[p].x[i] = 0.f;
+        }
+    }
+
+    // token t of (s, h): vectors at ((s*T + t)*H + h)*D, gates at (s*T + t)*H + h
+    int64_t gi = s * n_tokens * n_heads + h;
+    Vec<NV> kv = load_in<NV, BF16>(k, gi * D + col);
+    Vec<NV> qv = load_in<NV, BF16>(q, gi * D + col);
+    float vr[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) vr[p] = load_scalar_in<BF16>(v, gi * D + row0 + 2 * p);
+    float gt = g[gi], bt = beta[gi];
+
+    for (int64_t t = 0; t < n_tokens; ++t) {
+        // prefetch the next token's inputs while this one is computed
+        const int64_t gn = gi + n_heads;
+        const bool more = (t + 1 < n_tokens);
+        Vec<NV> kn, qn;
+        float vn[NP], gnext = 0.f, bnext = 0.f;
+        if (more) {
+            kn = load_in<NV, BF16>(k, gn * D + col);
+            qn = load_in<NV, BF16>(q, gn * D + col);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) vn[p] = load_scalar_in<BF16>(v, gn * D + row0 + 2 * p);
+            gnext = g[gn];
+            bnext = beta[gn];
+        }
+
+        const float alpha = expf(gt);
+        float a[NP], b[NP], kq = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) kq = fmaf(kv.x[i], qv.x[i], kq);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            a[p] = 0.f;
+            b[p] = 0.f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                a[p] = fmaf(M[p].x[i], kv.x[i], a[p]);
+                b[p] = fmaf(M[p].x[i], qv.x[i], b[p]);
+            }
+        }
+        kq = sum32(kq);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            a[p] = sum32(a[p]);
+            b[p] = sum32(b[p]);
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            // retrieval from the gated state: (alpha M) k = alpha (M k)
+            const float delta = bt * (vr[p] - alpha * a[p]);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) M[p].x[i] = fmaf(alpha, M[p].x[i], delta * kv.x[i]);
+            const float o = scale * fmaf(alpha, b[p], delta * kq);
+            if ((lane & 31) == 0) store_scalar_out<BF16>(out, gi * D + row0 + 2 * p, o);
+        }
+
+        if (more) {
+            kv = kn;
+            qv = qn;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) vr[p] = vn[p];
+            gt = gnext;
+            bt = bnext;
+        }
+        gi = gn;
+    }
+
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+        store_f32<NV>(state_out + st_base + (int64_t)(row0 + 2 * p) * D + col, M[p]);
+}
+
+template <int D, int NP, bool BF16>
+hipError_t launch_rec(const Problem &p, hipStream_t stream)
+{
+    constexpr int kRowsPerBlock = kWaves * 2 * NP;
+    static_assert(D % kRowsPerBlock == 0, "rows per block must divide head_dim");
+    const int64_t blocks = p.n_seqs * p.n_heads * (D / kRowsPerBlock);
+    if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const float scale = 1.0f / sqrtf(static_cast<float>(D));
+    hipLaunchKernelGGL((recurrent_kernel<D, NP, BF16>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kWaves * 64), 0, stream, p.q, p.k, p.v, p.g, p.beta,
+                       p.state_in, p.out, p.state_out, p.n_tokens, p.n_heads, scale);
+    return hipGetLastError();
+}
+
+// Rows per wave: 8 (NP = 4) once there are enough rows to fill the chip with
+// workgroups, else 2 (NP = 1) so that small problems still spread over many
+// compute units.
+template <int D, bool BF16>
+hipError_t launch_rec_d(const Problem &p, hipStream_t stream)
+{
+    const int64_t rows = p.n_seqs * p.n_heads * D;
+    if (rows >= 256 * 32 * 4)
+        return launch_rec<D, 4, BF16>(p, stream);
+    return launch_rec<D, 1, BF16>(p, stream);
+}
+
+template <bool BF16>
+hipError_t launch_rec_t(const Problem &p, hipStream_t stream)
+{
+    switch (p.head_dim) {
+    case 32: return launch_rec_d<32, BF16>(p, stream);
+    case 64: return launch_rec_d<64, BF16>(p, stream);
+    case 96: return launch_rec_d<96, BF16>(p, stream);
+    case 128: return launch_rec_d<128, BF16>(p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+__global__ __launch_bounds__(256) void state_copy_kernel(const float *__restrict__ src,
+                                                         float *__restrict__ dst,
+                                                         int64_t count)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
+         i += stride)
+        dst[i] = src ? src[i] : 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_recurrent(const Problem &p, hipStream_t stream)
+{
+    return p.bf16 ? launch_rec_t<true>(p, stream) : launch_rec_t<false>(p, stream);
+}
+
+hipError_t launch_state_copy(const float *state_in, float *state_out, int64_t count,
+                             hipStream_t stream)
+{
+    if (count <= 0) return hipSuccess;
+    int64_t blocks = (count + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(state_copy_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       stream, state_in, state_out, count);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

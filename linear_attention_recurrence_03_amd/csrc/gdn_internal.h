@@ -1,0 +1,37 @@
+// gdn_internal.h -- launchers shared between the C-ABI layer and the kernels.
+// Not installed; the public interface is include/gdn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Chunk length of the chunked algorithm (tokens per block of the sequence).
+constexpr int kChunk = 64;
+
+struct Problem {
+    int bf16;               // 1: q, k, v, out are bf16; 0: fp32
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const float *state_in;  // may be null (zero initial state)
+    void *out;
+    float *state_out;
+    int64_t n_seqs, n_tokens, n_heads;
+    int head_dim;
+};
+
+// Token recurrence, any n_tokens >= 1.
+hipError_t launch_recurrent(const Problem &p, hipStream_t stream);
+
+// Chunked algorithm, n_tokens >= 1.  Needs chunk_workspace_bytes(p) bytes.
+size_t chunk_workspace_bytes(int bf16, int64_t n_seqs, int64_t n_tokens,
+                             int64_t n_heads, int head_dim);
+hipError_t launch_chunked(const Problem &p, void *workspace, hipStream_t stream);
+
+// n_tokens == 0: state_out = state_in (or zeros when state_in is null).
+hipError_t launch_state_copy(const float *state_in, float *state_out,
+                             int64_t count, hipStream_t stream);
+
+}  // namespace gdn

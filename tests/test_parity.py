@@ -1,0 +1,215 @@
+"""GPU parity: libgdn (through the C-ABI) against the fp64 oracle.
+
+Error metric, per tensor X in {out, final_state}:
+    err(X) = max |X_gpu - X_oracle| / max |X_oracle|
+with the limits 1e-4 for fp32 q/k/v and 2e-2 for bf16 q/k/v (fp32 state in
+both cases).  The oracle always runs on exactly the values the GPU received
+(bf16 inputs already rounded, widened to fp64).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from linear_attention_recurrence_03_amd import inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible to torch")
+    import linear_attention_recurrence_03_amd as m
+    m._lib()   # fail loudly if the HIP library is missing
+    return m
+
+
+def to_dev(x, dtype):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    d = {n: torch.from_numpy(np.ascontiguousarray(x[n])).cuda() for n in ("g", "beta")}
+    for n in ("q", "k", "v"):
+        d[n] = torch.from_numpy(np.ascontiguousarray(x[n])).to("cuda").to(tdt)
+    d["state"] = None if x["state"] is None else torch.from_numpy(
+        np.ascontiguousarray(x["state"])).cuda()
+    return d
+
+
+def run_gpu(gdn, x, dtype, algo="auto", state=True):
+    d = to_dev(x, dtype)
+    out, fin = gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                           d["state"] if state else None, algo=algo)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), fin.cpu().numpy().astype(np.float64)
+
+
+def rel_err(a, b):
+    den = np.max(np.abs(b))
+    num = np.max(np.abs(a - b)) if a.size else 0.0
+    return num / den if den > 0 else num
+
+
+def check(gdn, x, dtype, algo, state=True, what=""):
+    print("case:", what, dtype, algo, x["q"].shape, flush=True)
+    out, fin = run_gpu(gdn, x, dtype, algo, state)
+    ro, rf = oracle.gdn_recurrent(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                                  x["state"] if state else None)
+    eo, ef = rel_err(out, ro), rel_err(fin, rf)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(fin))
+    assert eo <= TOL[dtype], "out err %.3e > %.1e (%s)" % (eo, TOL[dtype], what)
+    assert ef <= TOL[dtype], "state err %.3e > %.1e (%s)" % (ef, TOL[dtype], what)
+    return eo, ef
+
+
+# ---- the five workloads -------------------------------------------------------
+
+@pytest.mark.parametrize("algo", ["auto", "recurrent", "chunked"])
+def test_workload1_tiny(gdn, algo):
+    check(gdn, inputs.make(inputs.WORKLOADS[1]), "f32", algo, what="tiny")
+
+
+@pytest.mark.parametrize("layer", [0, 7, 23])
+def test_workload2_decode(gdn, layer):
+    check(gdn, inputs.make(inputs.WORKLOADS[2], layer=layer), "f32", "auto",
+          what="decode layer %d" % layer)
+
+
+def test_workload3_batched_decode(gdn):
+    check(gdn, inputs.make(inputs.WORKLOADS[3]), "f32", "auto", what="batched decode")
+
+
+@pytest.mark.parametrize("algo", ["auto", "recurrent"])
+def test_workload4_prefill(gdn, algo):
+    check(gdn, inputs.make(inputs.WORKLOADS[4]), "bf16", algo, what="prefill 4096")
+
+
+def test_workload5_long_prefill_sampled(gdn):
+    """Full workload on the GPU (all 4 sequences, the launch the benchmark
+    times); the oracle recomputes a sample of (sequence, head) pairs."""
+    wl = inputs.WORKLOADS[5]
+    x = inputs.make(wl)
+    print("case: long prefill full", flush=True)
+    out, fin = run_gpu(gdn, x, "bf16", "auto")
+    rng = np.random.default_rng(0)
+    picks = [(0, 0), (3, 15)] + [(int(rng.integers(4)), int(rng.integers(16))) for _ in range(2)]
+    for s, h in picks:
+        sub = {n: x[n][s:s + 1, :, h:h + 1] for n in ("q", "k", "v", "g", "beta")}
+        ro, rf = oracle.gdn_recurrent(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"],
+                                      x["state"][s:s + 1, h:h + 1])
+        eo = rel_err(out[s:s + 1, :, h:h + 1], ro)
+        ef = rel_err(fin[s:s + 1, h:h + 1], rf)
+        assert eo <= TOL["bf16"] and ef <= TOL["bf16"], (s, h, eo, ef)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(fin))
+
+
+# ---- tails, widths, decay regimes -------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
+@pytest.mark.parametrize("T", [1, 2, 63, 65, 130])
+@pytest.mark.parametrize("algo", ["recurrent", "chunked"])
+def test_tails_and_widths(gdn, dtype, D, T, algo):
+    x = inputs.custom(2, T, 3, D, dtype=dtype, state="normal", seed=T * 1000 + D)
+    check(gdn, x, dtype, algo, what="tail T=%d D=%d" % (T, D))
+
+
+@pytest.mark.parametrize("gate", ["weak", "mixed"])
+@pytest.mark.parametrize("algo", ["recurrent", "chunked"])
+def test_decay_regimes(gdn, gate, algo):
+    """Weak decay makes the carried state matter across many chunks; the mixed
+    recipe has within-chunk gate sums far below -70."""
+    x = inputs.custom(1, 1000, 4, 128, dtype="bf16", state="normal", gate=gate,
+                      beta_std=2.0, seed=42)
+    check(gdn, x, "bf16", algo, what="gate " + gate)
+    xf = inputs.custom(1, 200, 2, 64, dtype="f32", state="normal", gate=gate, seed=43)
+    check(gdn, xf, "f32", algo, what="gate f32 " + gate)
+
+
+def test_zero_initial_state_pointer(gdn):
+    x = inputs.custom(1, 70, 2, 64, dtype="f32", state="zeros", seed=1)
+    check(gdn, x, "f32", "auto", state=False, what="state None")
+
+
+# ---- contract properties ------------------------------------------------------
+
+def test_in_place_state_update(gdn):
+    x = inputs.custom(2, 5, 4, 128, dtype="f32", seed=3)
+    d = to_dev(x, "f32")
+    ref_o, ref_f = gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"].clone())
+    st = d["state"].clone()
+    o, f = gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], st, state_out=st)
+    torch.cuda.synchronize()
+    assert f.data_ptr() == st.data_ptr()
+    assert torch.equal(o, ref_o) and torch.equal(st, ref_f)
+
+
+def test_zero_tokens_copies_state(gdn):
+    x = inputs.custom(2, 0, 3, 64, dtype="bf16", seed=4)
+    d = to_dev(x, "bf16")
+    o, f = gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"])
+    o2, f2 = gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], None)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(f, d["state"])
+    assert torch.count_nonzero(f2).item() == 0
+
+
+def test_deterministic(gdn):
+    x = inputs.custom(1, 300, 4, 128, dtype="bf16", seed=5)
+    a = run_gpu(gdn, x, "bf16", "auto")
+    b = run_gpu(gdn, x, "bf16", "auto")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("algo", ["recurrent", "chunked"])
+def test_value_row_independence(gdn, algo):
+    """Perturbing value channel i changes only out[..., i] and state row i."""
+    x = inputs.custom(1, 130, 2, 128, dtype="bf16", seed=6)
+    o1, f1 = run_gpu(gdn, x, "bf16", algo)
+    y = dict(x)
+    y["v"] = x["v"].copy()
+    y["v"][..., 17] = inputs.bf16_round(y["v"][..., 17] + 1.0)
+    o2, f2 = run_gpu(gdn, y, "bf16", algo)
+    other = [j for j in range(128) if j != 17]
+    assert np.array_equal(o1[..., other], o2[..., other])
+    assert np.array_equal(f1[:, :, other, :], f2[:, :, other, :])
+    assert not np.array_equal(o1[..., 17], o2[..., 17])
+
+
+def test_runs_on_callers_stream(gdn):
+    """Inputs produced by a torch op on a side stream and consumed there with no
+    synchronisation in between: the library must join that stream's queue."""
+    x = inputs.custom(2, 100, 8, 128, dtype="bf16", seed=7)
+    ref_o, ref_f = run_gpu(gdn, x, "bf16", "auto")
+    d = to_dev(x, "bf16")
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        big = torch.randn(4096, 4096, device="cuda")
+        for _ in range(3):
+            big = big @ big * 1e-3                       # keep the stream busy
+        v2 = d["v"] + (big[0, 0] * 0).to(torch.bfloat16)  # depends on the busy work
+        out, fin = gdn.forward(d["q"], d["k"], v2, d["g"], d["beta"], d["state"])
+    side.synchronize()
+    assert np.array_equal(out.float().cpu().numpy().astype(np.float64), ref_o)
+    assert np.array_equal(fin.cpu().numpy().astype(np.float64), ref_f)
+
+
+def test_empty_batch_noop(gdn):
+    q = torch.empty((0, 5, 2, 64), device="cuda")
+    g = torch.empty((0, 5, 2), device="cuda")
+    o, f = gdn.forward(q, q, q, g, g, None)
+    assert o.shape == q.shape and f.shape == (0, 2, 64, 64)
+
+
+def test_rejects_bad_arguments(gdn):
+    x = inputs.custom(1, 4, 2, 64, dtype="f32", seed=8)
+    d = to_dev(x, "f32")
+    with pytest.raises(gdn.GdnError):
+        gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"],
+                    out=d["q"])   # output aliases an input
+    q48 = torch.zeros((1, 4, 2, 48), device="cuda")
+    g = torch.zeros((1, 4, 2), device="cuda")
+    with pytest.raises(gdn.GdnError):
+        gdn.forward(q48, q48, q48, g, g, None)
