@@ -33,8 +33,9 @@
 //                         needs no communication.  Each wave owns 16 value rows
 //                         and does K M^T, Q M^T, T E, P Delta and the state
 //                         update on MFMA (16x16x32 bf16 for bf16 inputs,
-//                         16x16x4 fp32 for fp32 inputs), with the chunk's K, K^T,
-//                         Q, T, P and V staged in LDS; the next chunk's loads
+//                         16x16x4 fp32 for fp32 inputs), with the chunk's K, Q, T,
+//                         P and V staged in LDS (K^T operands come from
+//                         transposing LDS reads); the next chunk's loads
 //                         are in flight while the current one is computed.
 //
 // MFMA fragments.  An A operand (16 rows x 32 k) gives lane l row l%16 and eight
@@ -74,7 +75,7 @@ __device__ __forceinline__ T from_f(float x);
 template <>
 __device__ __forceinline__ uint16_t from_f<uint16_t>(float x)
 {
-    return f32_to_bf16(x);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 template <>
 __device__ __forceinline__ float from_f<float>(float x)
@@ -95,9 +96,13 @@ struct Frag<false> {
     float v[8];
 };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack2(float a, float b)
 {
-    return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf16x2_t));
 }
 
 // k order of a fragment: element j of lane group g is k = 4g+j (j<4), 16+4g+j-4.
@@ -121,7 +126,40 @@ __device__ __forceinline__ Frag<BF16> lds_frag(const typename Elem<BF16>::T *bas
     return f;
 }
 
-// B operand from two stacked accumulator tiles, element-wise scaled by s0/s1.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// A operand whose rows are the key channels of a token-major LDS matrix: lane
+// (g, i) gets base[t0 + k(g, j)][key0 + i] for the eight j, i.e. eight tokens of
+// one key.  For bf16 this is two ds_read_b64_tr_b16: inside each group of 16
+// lanes, lane i receives element j = (i mod 4)-th 16-bit value fetched by lane
+// 4j + i/4, so lane p of group g fetches row t0 + 4g + p/4 (then 16 rows lower),
+// keys key0 + 4 (p mod 4) .. +3.
+template <bool BF16>
+__device__ __forceinline__ Frag<BF16> lds_frag_tr(const typename Elem<BF16>::T *base, int ld,
+                                                  int t0, int key0, int lane)
+{
+    Frag<BF16> f;
+    const int g = lane >> 4, p = lane & 15;
+    if constexpr (BF16) {
+        const uint16_t *a1 = base + (t0 + 4 * g + (p >> 2)) * ld + key0 + 4 * (p & 3);
+        const uint16_t *a2 = a1 + 16 * ld;
+        typedef __attribute__((address_space(3))) short4_t lds_short4;
+        const short4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a1));
+        const short4_t r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a2));
+        const uint2 u1 = __builtin_bit_cast(uint2, r1);
+        const uint2 u2 = __builtin_bit_cast(uint2, r2);
+        f.u = make_uint4(u1.x, u1.y, u2.x, u2.y);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f.v[j] = base[(t0 + 4 * g + j) * ld + key0 + p];
+            f.v[4 + j] = base[(t0 + 16 + 4 * g + j) * ld + key0 + p];
+        }
+    }
+    return f;
+}
+
+// B operand from two stacked accumulator tiles (rows 0-15 and 16-31 of the k range).
 template <bool BF16>
 __device__ __forceinline__ Frag<BF16> acc_frag(const floatx4 &c0, const floatx4 &c1)
 {
@@ -152,6 +190,16 @@ __device__ __forceinline__ floatx4 mma(const Frag<false> &a, const Frag<false> &
     return c;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
+// outstanding global load and store of the wave, which would stall on the next
+// chunk's prefetch and on output stores that nothing in the workgroup reads.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---- workspace layout, per (seq, head, chunk) ----------------------------------
 //   T     [C][C] elements   (fp32 or bf16, like q/k/v)
 //   P     [C][C] elements
@@ -179,9 +227,7 @@ struct PrepSmem {
     static constexpr int kQ = kK + C * LDK * sizeof(E);
     static constexpr int kA = kQ + C * LDK * sizeof(E);
     static constexpr int kT = kA + C * LDA * 4;
-    static constexpr int kP = kT + C * LDA * 4;
-    static constexpr int kX = kP + C * LDA * 4;  // 3 blocks of 16x17 fp32
-    static constexpr int kG = kX + 3 * 16 * 17 * 4;
+    static constexpr int kG = kT + C * LDA * 4;
     static constexpr int kBytes = kG + (4 * C + 4) * 4;
 };
 
@@ -190,6 +236,13 @@ __device__ __forceinline__ void lower_tile(int ix, int &tr, int &tc)
 {
     tr = (ix >= 6) ? 3 : (ix >= 3) ? 2 : (ix >= 1) ? 1 : 0;
     tc = ix - tr * (tr + 1) / 2;
+}
+
+// Upper 16x16 tiles (tr < tc), fixed order.
+__device__ __forceinline__ void upper_tile(int ix, int &tr, int &tc)
+{
+    tr = (ix >= 5) ? 2 : (ix >= 3) ? 1 : 0;
+    tc = tr + 1 + (ix - (tr == 0 ? 0 : tr == 1 ? 3 : 5));
 }
 
 template <int D, bool BF16>
@@ -207,8 +260,6 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     E *sQ = reinterpret_cast<E *>(smem + L::kQ);
     float *sA = reinterpret_cast<float *>(smem + L::kA);
     float *sT = reinterpret_cast<float *>(smem + L::kT);
-    float *sP = reinterpret_cast<float *>(smem + L::kP);
-    float *sX = reinterpret_cast<float *>(smem + L::kX);
     float *sG = reinterpret_cast<float *>(smem + L::kG);  // gam, beta, e^gam, e^{last-gam}, e^last
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -218,6 +269,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const int64_t s = sh / n_heads, h = sh - s * n_heads;
     const int64_t t0 = int64_t(n) * C;
     const int nv = static_cast<int>(min<int64_t>(C, n_tokens - t0));
+    unsigned char *dst = ws + chunk_id * W::kBytes;
+    E *wT = reinterpret_cast<E *>(dst + W::kT);
+    E *wP = reinterpret_cast<E *>(dst + W::kP);
 
     // 1. K and Q rows of the chunk (zero past the end of the sequence)
     constexpr int VE = 16 / sizeof(E);
@@ -255,38 +309,35 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
         sG[3 * C + lane] = ok ? expf(glast - x) : 0.f;
         if (lane == 0) sG[4 * C] = expf(glast);
     }
-    __syncthreads();
+    lds_barrier();
 
-    // 3. K K^T and Q K^T on the 10 lower tiles each (MFMA), decay masks applied
     const int gq = lane >> 4, cl = lane & 15;
-    for (int job = wave; job < 20; job += kPrepThreads / 64) {
-        const bool isq = job >= 10;
+    // 3. A = beta e^{gam_r - gam_s} K K^T (strictly lower), on the 10 lower tiles
+    for (int job = wave; job < 10; job += kPrepThreads / 64) {
         int tr, tc;
-        lower_tile(isq ? job - 10 : job, tr, tc);
-        const E *Am = isq ? sQ : sK;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        lower_tile(job, tr, tc);
+        Frag<BF16> fa[D / 32], fb[D / 32];
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
-            const Frag<BF16> a = lds_frag<BF16>(Am, LDK, 16 * tr + cl, 32 * ks, gq);
-            const Frag<BF16> b = lds_frag<BF16>(sK, LDK, 16 * tc + cl, 32 * ks, gq);
-            acc = mma(a, b, acc);
+            fa[ks] = lds_frag<BF16>(sK, LDK, 16 * tr + cl, 32 * ks, gq);
+            fb[ks] = lds_frag<BF16>(sK, LDK, 16 * tc + cl, 32 * ks, gq);
         }
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) acc = mma(fa[ks], fb[ks], acc);
         const int col = 16 * tc + cl;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 16 * tr + 4 * gq + j;
-            const float dec = (col <= row) ? expf(sG[row] - sG[col]) : 0.f;
-            if (isq)
-                sP[row * LDA + col] = dec * acc[j];
-            else
-                sA[row * LDA + col] = (col < row) ? sG[C + row] * dec * acc[j] : 0.f;
+            sA[row * LDA + col] =
+                (col < row) ? sG[C + row] * __expf(sG[row] - sG[col]) * acc[j] : 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // 4. T = (I + A)^{-1}.  (a) 16x16 diagonal blocks: lane = (block, column),
-    //    forward substitution down the column.
     if (wave == 0) {
+        // 4a. 16x16 diagonal blocks of T = (I + A)^{-1}: lane = (block, column),
+        //     forward substitution down the column.
         const int b = lane >> 4, c = lane & 15;
         const float *Ab = sA + (16 * b) * LDA + 16 * b;
         float x[16];
@@ -299,217 +350,397 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) sT[(16 * b + r) * LDA + 16 * b + c] = x[r];
-    }
-    __syncthreads();
-    // (b) off-diagonal blocks, one block diagonal at a time:
-    //     X = A[i-rows][16j : 16i] T[16j : 16i][j-cols],  T_ij = -T_ii X
-    for (int dd = 1; dd < 4; ++dd) {
-        const int nb = 4 - dd;
-        for (int e = tid; e < nb * 256; e += kPrepThreads) {
-            const int blk = e >> 8, r = (e >> 4) & 15, c = e & 15;
-            const int i = blk + dd, j = blk;
-            const float *arow = sA + (16 * i + r) * LDA;
-            float acc = 0.f;
-            for (int u = 16 * j; u < 16 * i; ++u) acc = fmaf(arow[u], sT[u * LDA + 16 * j + c], acc);
-            sX[(blk * 16 + r) * 17 + c] = acc;
-        }
-        __syncthreads();
-        for (int e = tid; e < nb * 256; e += kPrepThreads) {
-            const int blk = e >> 8, r = (e >> 4) & 15, c = e & 15;
-            const int i = blk + dd, j = blk;
-            const float *trow = sT + (16 * i + r) * LDA + 16 * i;
-            float acc = 0.f;
+    } else {
+        // 3b (other waves, meanwhile). P = e^{gam_r - gam_s} Q K^T (lower incl.
+        //    diagonal), written straight from the accumulators; upper tiles zero.
+        for (int job = wave - 1; job < 16; job += kPrepThreads / 64 - 1) {
+            int tr, tc;
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (job < 10) {
+                lower_tile(job, tr, tc);
+                Frag<BF16> fa[D / 32], fb[D / 32];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) acc = fmaf(trow[m], sX[(blk * 16 + m) * 17 + c], acc);
-            sT[(16 * i + r) * LDA + 16 * j + c] = -acc;
+                for (int ks = 0; ks < D / 32; ++ks) {
+                    fa[ks] = lds_frag<BF16>(sQ, LDK, 16 * tr + cl, 32 * ks, gq);
+                    fb[ks] = lds_frag<BF16>(sK, LDK, 16 * tc + cl, 32 * ks, gq);
+                }
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks) acc = mma(fa[ks], fb[ks], acc);
+            } else {
+                upper_tile(job - 10, tr, tc);
+            }
+            const int col = 16 * tc + cl;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * tr + 4 * gq + j;
+                const float pv = (col <= row) ? __expf(sG[row] - sG[col]) * acc[j] : 0.f;
+                wP[row * C + col] = from_f<E>(pv);
+            }
         }
-        __syncthreads();
+    }
+    lds_barrier();
+
+    // 4b. off-diagonal blocks of T, one block diagonal at a time, on fp32 MFMA:
+    //     X = A[i rows][16j : 16i] T[16j : 16i][j cols] (inner length 16 (i-j)),
+    //     T_ij = -T_ii X.  X stays in accumulator registers: for the second
+    //     product, k step jj pairs lane group g with row 4g + jj of X.
+    for (int dd = 1; dd < 4; ++dd) {
+        if (wave < 4 - dd) {
+            const int j = wave, i = wave + dd;
+            floatx4 X = {0.f, 0.f, 0.f, 0.f};
+            for (int st = 0; st < 4 * dd; ++st) {
+                const int u = 16 * j + 4 * st + gq;
+                X = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * i + cl) * LDA + u],
+                                                         sT[u * LDA + 16 * j + cl], X, 0, 0, 0);
+            }
+            floatx4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                Y = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                    sT[(16 * i + cl) * LDA + 16 * i + 4 * gq + jj], X[jj], Y, 0, 0, 0);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) sT[(16 * i + 4 * gq + jj) * LDA + 16 * j + cl] = -Y[jj];
+        }
+        lds_barrier();
     }
 
-    // 5. T, P (upper triangles written as zeros) and gates to the workspace
-    unsigned char *dst = ws + chunk_id * W::kBytes;
-    E *wT = reinterpret_cast<E *>(dst + W::kT);
-    E *wP = reinterpret_cast<E *>(dst + W::kP);
+    // 5. T (upper triangle as zeros) and gates to the workspace
     for (int i = tid; i < C * C / VE; i += kPrepThreads) {
         const int r = (i * VE) / C, c0 = (i * VE) % C;
-        E vt[VE], vp[VE];
+        E vt[VE];
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
             const int c = c0 + e;
             vt[e] = from_f<E>(c <= r ? sT[r * LDA + c] : 0.f);
-            vp[e] = from_f<E>(c <= r ? sP[r * LDA + c] : 0.f);
         }
         *reinterpret_cast<uint4 *>(wT + i * VE) = *reinterpret_cast<const uint4 *>(vt);
-        *reinterpret_cast<uint4 *>(wP + i * VE) = *reinterpret_cast<const uint4 *>(vp);
     }
     float4 *wG = reinterpret_cast<float4 *>(dst + W::kGates);
     if (tid < C) wG[tid] = make_float4(sG[C + tid], sG[2 * C + tid], sG[3 * C + tid], sG[4 * C]);
 }
 
 // ---- the chunk-to-chunk scan -----------------------------------------------------
+//
+// One workgroup = four waves for 32 value rows of one (seq, head):
+//   waves 0, 1  "chain" waves, 16 value rows each: carry M^T in registers and
+//               per chunk do X = K M^T, E, Delta = T E and the state update --
+//               the serial dependency from one chunk to the next;
+//   waves 2, 3  "output" waves, paired with waves 0, 1: one chunk behind, they
+//               take the M^T and Delta fragments the chain wave published in
+//               LDS and form O = (e^gam Q M^T + P Delta) / sqrt(d).
+// Each wave sits on its own SIMD, so the chain's MFMA work is not shared with the
+// output products.  Chunk inputs (K, Q, T, P, V, gates) are staged through
+// registers into double-buffered LDS (bf16); the next chunk's global loads are in
+// flight during the current step.  The fp32 variant (parity path) has room for
+// one LDS stage only and runs chain and output phases back to back.
 
-template <int D, int NW, bool BF16>
-struct ScanSmem {
+constexpr int kScanThreads = 256;
+constexpr int kScanRows = 32;
+
+template <int D, bool BF16>
+struct ScanCfg {
     using E = typename Elem<BF16>::T;
-    static constexpr int RW = 16 * NW;               // value rows per workgroup
+    static constexpr int kStages = BF16 ? 2 : 1;
     static constexpr int PAD = BF16 ? 8 : 4;
-    static constexpr int LDK = D + PAD;               // sK, sQ rows
-    static constexpr int LDT = C + PAD;               // sKt, sT, sP rows
-    static constexpr int LDV = RW + PAD;              // sV rows
+    static constexpr int LDK = D + PAD;        // sK, sQ rows (elements)
+    static constexpr int LDT = C + PAD;        // sT, sP rows
+    static constexpr int LDV = kScanRows + PAD;
     static constexpr int kK = 0;
     static constexpr int kQ = kK + C * LDK * sizeof(E);
-    static constexpr int kKt = kQ + C * LDK * sizeof(E);
-    static constexpr int kT = kKt + D * LDT * sizeof(E);
+    static constexpr int kT = kQ + C * LDK * sizeof(E);
     static constexpr int kP = kT + C * LDT * sizeof(E);
     static constexpr int kV = kP + C * LDT * sizeof(E);
     static constexpr int kG = kV + C * LDV * sizeof(E);
-    static constexpr int kBytes = kG + 4 * C * 4;
+    static constexpr int kStage = kG + C * 16;                          // bytes per stage
+    static constexpr int kFrags = D / 32 + 2;                           // M^T and Delta fragments
+    static constexpr int kPubWave = 64 * kFrags * int(sizeof(Frag<BF16>));
+    static constexpr int kPub = kStages * kStage;                       // published fragments
+    static constexpr int kBytes = kPub + kStages * 2 * kPubWave;
     static_assert(kBytes <= 160 * 1024, "LDS budget");
-};
-
-// Per-thread staging registers for one chunk (global -> registers -> LDS).
-template <int D, int NW, bool BF16>
-struct Stage {
-    using E = typename Elem<BF16>::T;
-    static constexpr int NT = NW * 64;
+    // staging: 16-byte vectors per thread
     static constexpr int VE = 16 / sizeof(E);
-    static constexpr int RW = 16 * NW;
-    static constexpr int NK = (C * D / VE + NT - 1) / NT;      // K (and Q) vectors
-    static constexpr int NTP = (C * C / VE + NT - 1) / NT;     // T (and P) vectors
-    static constexpr int NV = (C * RW / VE + NT - 1) / NT;     // V vectors
-    static constexpr int NG = (4 * C / 4 + NT - 1) / NT;       // gate float4 vectors
-    uint4 k[NK], q[NK], t[NTP], p[NTP], v[NV], gt[NG];
+    static constexpr int VPR = D / VE;
+    static constexpr int NK = C * VPR / kScanThreads;                   // K (and Q)
+    static constexpr int NTP = C * C / VE / kScanThreads;               // T (and P)
+    static constexpr int VPV = kScanRows / VE;
+    static constexpr int NV = (C * VPV + kScanThreads - 1) / kScanThreads;
+    static_assert(C * VPR % kScanThreads == 0 && C * C / VE % kScanThreads == 0, "staging split");
 };
 
-template <int D, int NW, bool BF16>
-__device__ __forceinline__ void stage_fetch(Stage<D, NW, BF16> &st, const void *q, const void *k,
-                                            const void *v, const unsigned char *wsc,
-                                            int64_t s, int64_t h, int64_t t0, int nv,
-                                            int64_t n_tokens, int64_t n_heads, int v0, int tid)
+template <int D, bool BF16>
+struct ScanStage {
+    using F = ScanCfg<D, BF16>;
+    uint4 k[F::NK], q[F::NK], t[F::NTP], p[F::NTP], v[F::NV], g;
+};
+
+// Global loads through explicit global-address-space pointers.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_t global_u32x4;
+
+__device__ __forceinline__ uint4 ldg16(const void *p)
 {
-    using S = Stage<D, NW, BF16>;
-    using E = typename Elem<BF16>::T;
-    using W = WsLayout<BF16>;
-    constexpr int VPR = D / S::VE;
-#pragma unroll
-    for (int i = 0; i < S::NK; ++i) {
-        const int idx = tid + i * S::NT;
-        st.k[i] = st.q[i] = make_uint4(0, 0, 0, 0);
-        if (idx < C * VPR) {
-            const int r = idx / VPR, c = (idx - r * VPR) * S::VE;
-            if (r < nv) {
-                const int64_t off = ((s * n_tokens + t0 + r) * n_heads + h) * D + c;
-                st.k[i] = *reinterpret_cast<const uint4 *>(static_cast<const E *>(k) + off);
-                st.q[i] = *reinterpret_cast<const uint4 *>(static_cast<const E *>(q) + off);
-            }
-        }
-    }
-    const uint4 *wT = reinterpret_cast<const uint4 *>(wsc + W::kT);
-    const uint4 *wP = reinterpret_cast<const uint4 *>(wsc + W::kP);
-#pragma unroll
-    for (int i = 0; i < S::NTP; ++i) {
-        const int idx = tid + i * S::NT;
-        if (idx < C * C / S::VE) {
-            st.t[i] = wT[idx];
-            st.p[i] = wP[idx];
-        }
-    }
-    constexpr int VPV = S::RW / S::VE;  // vectors per V row of this workgroup
-#pragma unroll
-    for (int i = 0; i < S::NV; ++i) {
-        const int idx = tid + i * S::NT;
-        st.v[i] = make_uint4(0, 0, 0, 0);
-        if (idx < C * VPV) {
-            const int r = idx / VPV, c = (idx - r * VPV) * S::VE;
-            if (r < nv) {
-                const int64_t off = ((s * n_tokens + t0 + r) * n_heads + h) * D + v0 + c;
-                st.v[i] = *reinterpret_cast<const uint4 *>(static_cast<const E *>(v) + off);
-            }
-        }
-    }
-    const uint4 *wG = reinterpret_cast<const uint4 *>(wsc + W::kGates);
-#pragma unroll
-    for (int i = 0; i < S::NG; ++i) {
-        const int idx = tid + i * S::NT;
-        if (idx < C) st.gt[i] = wG[idx];
-    }
+    const u32x4_t x = *reinterpret_cast<global_u32x4 *>(reinterpret_cast<uintptr_t>(p));
+    return make_uint4(x.x, x.y, x.z, x.w);
 }
 
-template <int D, int NW, bool BF16>
-__device__ __forceinline__ void stage_commit(const Stage<D, NW, BF16> &st, unsigned char *smem,
-                                             int tid)
+__device__ __forceinline__ uint4 zero_unless(bool keep, uint4 x)
 {
-    using S = Stage<D, NW, BF16>;
-    using L = ScanSmem<D, NW, BF16>;
+    return keep ? x : make_uint4(0, 0, 0, 0);
+}
+
+// Global -> registers for the chunk starting at token t0 with nv valid tokens.
+// kp, qp, vp point at token 0 of this (seq, head) (vp already offset to the
+// workgroup's first value row); hd is n_heads * head_dim, the token stride.
+// Rows past the end are read from the last valid row (every address stays
+// inside the tensors) and zeroed when committed to LDS: using a loaded value
+// here would make the wave wait for the load instead of overlapping it.
+template <int D, bool BF16>
+__device__ __forceinline__ void scan_fetch(ScanStage<D, BF16> &st, const typename Elem<BF16>::T *kp,
+                                           const typename Elem<BF16>::T *qp,
+                                           const typename Elem<BF16>::T *vp,
+                                           const unsigned char *wsc, int64_t hd, int64_t t0,
+                                           int nv, int tid)
+{
+    using F = ScanCfg<D, BF16>;
+    using W = WsLayout<BF16>;
+    const int64_t base = t0 * hd;
+#pragma unroll
+    for (int i = 0; i < F::NK; ++i) {
+        const int idx = tid + i * kScanThreads;
+        const int r = idx / F::VPR, c = (idx % F::VPR) * F::VE;
+        const int64_t off = base + min(r, nv - 1) * hd + c;
+        st.k[i] = ldg16(kp + off);
+        st.q[i] = ldg16(qp + off);
+    }
+#pragma unroll
+    for (int i = 0; i < F::NTP; ++i) {
+        st.t[i] = ldg16(wsc + W::kT + 16 * (tid + i * kScanThreads));
+        st.p[i] = ldg16(wsc + W::kP + 16 * (tid + i * kScanThreads));
+    }
+#pragma unroll
+    for (int i = 0; i < F::NV; ++i) {
+        const int idx = min(tid + i * kScanThreads, C * F::VPV - 1);
+        const int r = idx / F::VPV, c = (idx % F::VPV) * F::VE;
+        st.v[i] = ldg16(vp + base + min(r, nv - 1) * hd + c);
+    }
+    st.g = ldg16(wsc + W::kGates + 16 * (tid & (C - 1)));
+}
+
+template <int D, bool BF16>
+__device__ __forceinline__ void scan_commit(const ScanStage<D, BF16> &st, unsigned char *buf, int nv,
+                                            int tid)
+{
+    using F = ScanCfg<D, BF16>;
     using E = typename Elem<BF16>::T;
-    E *sK = reinterpret_cast<E *>(smem + L::kK);
-    E *sQ = reinterpret_cast<E *>(smem + L::kQ);
-    E *sKt = reinterpret_cast<E *>(smem + L::kKt);
-    E *sT = reinterpret_cast<E *>(smem + L::kT);
-    E *sP = reinterpret_cast<E *>(smem + L::kP);
-    E *sV = reinterpret_cast<E *>(smem + L::kV);
-    float *sG = reinterpret_cast<float *>(smem + L::kG);
-    constexpr int VPR = D / S::VE;
+    E *sK = reinterpret_cast<E *>(buf + F::kK);
+    E *sQ = reinterpret_cast<E *>(buf + F::kQ);
+    E *sT = reinterpret_cast<E *>(buf + F::kT);
+    E *sP = reinterpret_cast<E *>(buf + F::kP);
+    E *sV = reinterpret_cast<E *>(buf + F::kV);
 #pragma unroll
-    for (int i = 0; i < S::NK; ++i) {
-        const int idx = tid + i * S::NT;
-        if (idx < C * VPR) {
-            const int r = idx / VPR, c = (idx - r * VPR) * S::VE;
-            *reinterpret_cast<uint4 *>(sK + r * L::LDK + c) = st.k[i];
-            *reinterpret_cast<uint4 *>(sQ + r * L::LDK + c) = st.q[i];
-            const E *ke = reinterpret_cast<const E *>(&st.k[i]);
+    for (int i = 0; i < F::NK; ++i) {
+        const int idx = tid + i * kScanThreads;
+        const int r = idx / F::VPR, c = (idx % F::VPR) * F::VE;
+        *reinterpret_cast<uint4 *>(sK + r * F::LDK + c) = zero_unless(r < nv, st.k[i]);
+        *reinterpret_cast<uint4 *>(sQ + r * F::LDK + c) = zero_unless(r < nv, st.q[i]);
+    }
 #pragma unroll
-            for (int e = 0; e < S::VE; ++e) sKt[(c + e) * L::LDT + r] = ke[e];
+    for (int i = 0; i < F::NTP; ++i) {
+        const int idx = (tid + i * kScanThreads) * F::VE;
+        const int r = idx / C, c = idx % C;
+        *reinterpret_cast<uint4 *>(sT + r * F::LDT + c) = st.t[i];
+        *reinterpret_cast<uint4 *>(sP + r * F::LDT + c) = st.p[i];
+    }
+#pragma unroll
+    for (int i = 0; i < F::NV; ++i) {
+        const int idx = tid + i * kScanThreads;
+        if (C * F::VPV % kScanThreads == 0 || idx < C * F::VPV) {
+            const int r = idx / F::VPV, c = (idx % F::VPV) * F::VE;
+            *reinterpret_cast<uint4 *>(sV + r * F::LDV + c) = zero_unless(r < nv, st.v[i]);
         }
     }
+    if (tid < C) reinterpret_cast<uint4 *>(buf + F::kG)[tid] = st.g;
+}
+
+template <int D, bool BF16>
+__device__ __forceinline__ void scan_load(ScanStage<D, BF16> &st, const typename Elem<BF16>::T *kp,
+                                          const typename Elem<BF16>::T *qp,
+                                          const typename Elem<BF16>::T *vp,
+                                          const unsigned char *wsc, int64_t hd, int64_t t0,
+                                          int nv, int tid)
+{
+    scan_fetch<D, BF16>(st, kp, qp, vp, wsc, hd, t0, nv, tid);
+}
+
+// Chain step for one chunk: publishes this chunk's M^T and Delta fragments and
+// advances Mt (accumulator layout: Mt[kt][j] = M[vrow][16 kt + 4 g + j]).
+// Every phase first issues all of its LDS reads, then runs its MFMAs with the
+// k step outermost, so that independent accumulators interleave and LDS latency
+// is paid once per phase rather than once per product.
+template <int D, bool BF16>
+__device__ __forceinline__ void chain_step(floatx4 (&Mt)[D / 16], const unsigned char *buf,
+                                           Frag<BF16> *pub, int vcol, int lane)
+{
+    using F = ScanCfg<D, BF16>;
+    using E = typename Elem<BF16>::T;
+    constexpr int KS = D / 32;
+    const E *sK = reinterpret_cast<const E *>(buf + F::kK);
+    const E *sT = reinterpret_cast<const E *>(buf + F::kT);
+    const E *sV = reinterpret_cast<const E *>(buf + F::kV);
+    const float4 *sG = reinterpret_cast<const float4 *>(buf + F::kG);
+    const int gq = lane >> 4, cl = lane & 15;
+
+    // LDS reads for X = K M^T, E and Delta = T E
+    Frag<BF16> ak[4][KS];
 #pragma unroll
-    for (int i = 0; i < S::NTP; ++i) {
-        const int idx = tid + i * S::NT;
-        if (idx < C * C / S::VE) {
-            const int r = (idx * S::VE) / C, c = (idx * S::VE) % C;
-            *reinterpret_cast<uint4 *>(sT + r * L::LDT + c) = st.t[i];
-            *reinterpret_cast<uint4 *>(sP + r * L::LDT + c) = st.p[i];
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) ak[tt][ks] = lds_frag<BF16>(sK, F::LDK, 16 * tt + cl, 32 * ks, gq);
+    Frag<BF16> at[6];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        at[tt] = lds_frag<BF16>(sT, F::LDT, 16 * tt + cl, 0, gq);
+        if (tt >= 2) at[2 + tt] = lds_frag<BF16>(sT, F::LDT, 16 * tt + cl, 32, gq);
+    }
+    float4 gt[4][4];
+    float vv[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = 16 * tt + 4 * gq + j;
+            gt[tt][j] = sG[t];
+            vv[tt][j] = to_f(sV[t * F::LDV + vcol]);
         }
-    }
-    constexpr int VPV = S::RW / S::VE;
+
+    Frag<BF16> bm[KS];
 #pragma unroll
-    for (int i = 0; i < S::NV; ++i) {
-        const int idx = tid + i * S::NT;
-        if (idx < C * VPV) {
-            const int r = idx / VPV, c = (idx - r * VPV) * S::VE;
-            *reinterpret_cast<uint4 *>(sV + r * L::LDV + c) = st.v[i];
+    for (int ks = 0; ks < KS; ++ks) {
+        bm[ks] = acc_frag<BF16>(Mt[2 * ks], Mt[2 * ks + 1]);
+        pub[ks * 64 + lane] = bm[ks];
+    }
+    floatx4 xk[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) xk[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) xk[tt] = mma(ak[tt][ks], bm[ks], xk[tt]);
+
+    // transposed K reads for the state update, issued before they are needed
+    Frag<BF16> akt[D / 16][2];
+#pragma unroll
+    for (int kt = 0; kt < D / 16; ++kt) {
+        akt[kt][0] = lds_frag_tr<BF16>(sK, F::LDK, 0, 16 * kt, lane);
+        akt[kt][1] = lds_frag_tr<BF16>(sK, F::LDK, 32, 16 * kt, lane);
+    }
+
+    // E = beta (V - e^gam X)
+    floatx4 e[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) e[tt][j] = gt[tt][j].x * (vv[tt][j] - gt[tt][j].y * xk[tt][j]);
+    const Frag<BF16> be0 = acc_frag<BF16>(e[0], e[1]);
+    const Frag<BF16> be1 = acc_frag<BF16>(e[2], e[3]);
+    // Delta = T E  (T lower triangular)
+    floatx4 dl[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) dl[tt] = mma(at[tt], be0, floatx4{0.f, 0.f, 0.f, 0.f});
+    dl[2] = mma(at[4], be1, dl[2]);
+    dl[3] = mma(at[5], be1, dl[3]);
+    pub[KS * 64 + lane] = acc_frag<BF16>(dl[0], dl[1]);
+    pub[(KS + 1) * 64 + lane] = acc_frag<BF16>(dl[2], dl[3]);
+    // M^T <- e^{gam_last} M^T + K^T diag(e^{gam_last - gam}) Delta
+    floatx4 ds[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ds[tt][j] = gt[tt][j].z * dl[tt][j];
+    const Frag<BF16> bs0 = acc_frag<BF16>(ds[0], ds[1]);
+    const Frag<BF16> bs1 = acc_frag<BF16>(ds[2], ds[3]);
+    const float eC = gt[0][0].w;
+#pragma unroll
+    for (int kt = 0; kt < D / 16; ++kt) Mt[kt] = mma(akt[kt][0], bs0, Mt[kt] * eC);
+#pragma unroll
+    for (int kt = 0; kt < D / 16; ++kt) Mt[kt] = mma(akt[kt][1], bs1, Mt[kt]);
+}
+
+// Output step for one chunk from the published fragments of its chain wave.
+// op points at out[(s, chunk token 0, h, vrow)]; hd is the token stride.
+template <int D, bool BF16>
+__device__ __forceinline__ void output_step(const unsigned char *buf, const Frag<BF16> *pub,
+                                            typename Elem<BF16>::T *op, int64_t hd, int nv,
+                                            float scale, int lane)
+{
+    using F = ScanCfg<D, BF16>;
+    using E = typename Elem<BF16>::T;
+    constexpr int KS = D / 32;
+    const E *sQ = reinterpret_cast<const E *>(buf + F::kQ);
+    const E *sP = reinterpret_cast<const E *>(buf + F::kP);
+    const float4 *sG = reinterpret_cast<const float4 *>(buf + F::kG);
+    const int gq = lane >> 4, cl = lane & 15;
+    Frag<BF16> aq[4][KS], ap[6], bm[KS];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) aq[tt][ks] = lds_frag<BF16>(sQ, F::LDK, 16 * tt + cl, 32 * ks, gq);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        ap[tt] = lds_frag<BF16>(sP, F::LDT, 16 * tt + cl, 0, gq);
+        if (tt >= 2) ap[2 + tt] = lds_frag<BF16>(sP, F::LDT, 16 * tt + cl, 32, gq);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bm[ks] = pub[ks * 64 + lane];
+    const Frag<BF16> bd0 = pub[KS * 64 + lane];
+    const Frag<BF16> bd1 = pub[(KS + 1) * 64 + lane];
+    float eg[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) eg[tt][j] = sG[16 * tt + 4 * gq + j].y;
+
+    floatx4 xq[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) xq[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) xq[tt] = mma(aq[tt][ks], bm[ks], xq[tt]);
+    floatx4 o[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[tt][j] = eg[tt][j] * xq[tt][j];
+        o[tt] = mma(ap[tt], bd0, o[tt]);
+    }
+    o[2] = mma(ap[4], bd1, o[2]);
+    o[3] = mma(ap[5], bd1, o[3]);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = 16 * tt + 4 * gq + j;
+            if (t < nv) op[t * hd] = from_f<E>(scale * o[tt][j]);
         }
-    }
-#pragma unroll
-    for (int i = 0; i < S::NG; ++i) {
-        const int idx = tid + i * S::NT;
-        if (idx < C) *reinterpret_cast<uint4 *>(sG + 4 * idx) = st.gt[i];
-    }
 }
 
 // Workgroups are numbered so that the row blocks of one (seq, head) share the
 // low three bits of the block id: consecutive ids go to different XCDs, so this
 // keeps a head's workgroups on one XCD, where its K, Q, T and P hit in L2.
-template <int D, int NW, bool BF16>
-__global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(
+template <int D, bool BF16>
+__global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *state_in, void *__restrict__ out, float *state_out,
     const unsigned char *__restrict__ ws, int64_t n_tokens, int64_t n_heads, int64_t n_sh,
     int n_chunks, float scale)
 {
+    using F = ScanCfg<D, BF16>;
     using E = typename Elem<BF16>::T;
-    using L = ScanSmem<D, NW, BF16>;
     using W = WsLayout<BF16>;
-    constexpr int RW = L::RW;
-    constexpr int NRB = D / RW;  // row blocks per head
+    constexpr int NRB = D / kScanRows;  // row blocks per head
+    constexpr int S = F::kStages;
     extern __shared__ __align__(16) unsigned char smem[];
-    const E *sK = reinterpret_cast<const E *>(smem + L::kK);
-    const E *sQ = reinterpret_cast<const E *>(smem + L::kQ);
-    const E *sKt = reinterpret_cast<const E *>(smem + L::kKt);
-    const E *sT = reinterpret_cast<const E *>(smem + L::kT);
-    const E *sP = reinterpret_cast<const E *>(smem + L::kP);
-    const E *sV = reinterpret_cast<const E *>(smem + L::kV);
-    const float *sG = reinterpret_cast<const float *>(smem + L::kG);
 
     const int64_t b = blockIdx.x;
     const int64_t sh = (b / (8 * NRB)) * 8 + (b & 7);
@@ -517,119 +748,77 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(
     if (sh >= n_sh) return;  // whole workgroup leaves before any barrier
     const int64_t s = sh / n_heads, h = sh - s * n_heads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int gq = lane >> 4, cl = lane & 15;
-    const int v0 = rb * RW;                 // first value row of the workgroup
-    const int vrow = v0 + 16 * wave + cl;   // this lane's value row (column of M^T)
-
-    // M^T tiles in accumulator layout: Mt[kt][j] = M[vrow][16 kt + 4 gq + j]
-    floatx4 Mt[D / 16];
-    const int64_t st_off = sh * D * D + int64_t(vrow) * D;
-#pragma unroll
-    for (int kt = 0; kt < D / 16; ++kt) {
-        if (state_in) {
-            const float4 m = *reinterpret_cast<const float4 *>(state_in + st_off + 16 * kt + 4 * gq);
-            Mt[kt] = floatx4{m.x, m.y, m.z, m.w};
-        } else {
-            Mt[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-
+    const bool is_chain = wave < 2;
+    const int pair = wave & 1;                       // which 16-row half
+    const int v0 = rb * kScanRows;                   // first value row of the workgroup
+    const int vcol = 16 * pair + (lane & 15);        // row within the workgroup
+    const int vrow = v0 + vcol;                      // this lane's value row
+    const int64_t hd = n_heads * D;
+    const E *kp = static_cast<const E *>(k) + (s * n_tokens * n_heads + h) * D;
+    const E *qp = static_cast<const E *>(q) + (s * n_tokens * n_heads + h) * D;
+    const E *vp = static_cast<const E *>(v) + (s * n_tokens * n_heads + h) * D + v0;
+    E *op = static_cast<E *>(out) + (s * n_tokens * n_heads + h) * D + vrow;
     const unsigned char *wsh = ws + sh * n_chunks * W::kBytes;
-    Stage<D, NW, BF16> st;
-    stage_fetch<D, NW, BF16>(st, q, k, v, wsh, s, h, 0, static_cast<int>(min<int64_t>(C, n_tokens)),
-                             n_tokens, n_heads, v0, tid);
-    for (int n = 0; n < n_chunks; ++n) {
-        const int64_t t0 = int64_t(n) * C;
-        const int nv = static_cast<int>(min<int64_t>(C, n_tokens - t0));
-        stage_commit<D, NW, BF16>(st, smem, tid);
-        __syncthreads();
-        if (n + 1 < n_chunks) {
-            const int64_t t1 = t0 + C;
-            stage_fetch<D, NW, BF16>(st, q, k, v, wsh + (n + 1) * W::kBytes, s, h, t1,
-                                     static_cast<int>(min<int64_t>(C, n_tokens - t1)), n_tokens,
-                                     n_heads, v0, tid);
-        }
+    auto pub_of = [&](int stage, int which) {
+        return reinterpret_cast<Frag<BF16> *>(smem + F::kPub + (stage * 2 + which) * F::kPubWave);
+    };
 
-        // B operands of M^T, one per 32 keys
-        Frag<BF16> bm[D / 32];
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) bm[ks] = acc_frag<BF16>(Mt[2 * ks], Mt[2 * ks + 1]);
-
-        // X_K = K M^T, X_Q = Q M^T  (tokens x this wave's 16 value rows)
-        floatx4 xk[4], xq[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            xk[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-            xq[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) {
-                xk[tt] = mma(lds_frag<BF16>(sK, L::LDK, 16 * tt + cl, 32 * ks, gq), bm[ks], xk[tt]);
-                xq[tt] = mma(lds_frag<BF16>(sQ, L::LDK, 16 * tt + cl, 32 * ks, gq), bm[ks], xq[tt]);
-            }
-        }
-        // E = beta (V - e^gam X_K)
-        floatx4 e[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = 16 * tt + 4 * gq + j;
-                const float vv = to_f(sV[t * L::LDV + 16 * wave + cl]);
-                e[tt][j] = sG[4 * t] * (vv - sG[4 * t + 1] * xk[tt][j]);
-            }
-        }
-        const Frag<BF16> be0 = acc_frag<BF16>(e[0], e[1]);
-        const Frag<BF16> be1 = acc_frag<BF16>(e[2], e[3]);
-        // Delta = T E (T lower triangular: token tiles 0-1 need only k block 0)
-        floatx4 dl[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            dl[tt] = mma(lds_frag<BF16>(sT, L::LDT, 16 * tt + cl, 0, gq), be0,
-                         floatx4{0.f, 0.f, 0.f, 0.f});
-            if (tt >= 2) dl[tt] = mma(lds_frag<BF16>(sT, L::LDT, 16 * tt + cl, 32, gq), be1, dl[tt]);
-        }
-        // O = (e^gam X_Q + P Delta) / sqrt(d)
-        const Frag<BF16> bd0 = acc_frag<BF16>(dl[0], dl[1]);
-        const Frag<BF16> bd1 = acc_frag<BF16>(dl[2], dl[3]);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            floatx4 o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = sG[4 * (16 * tt + 4 * gq + j) + 1] * xq[tt][j];
-            o = mma(lds_frag<BF16>(sP, L::LDT, 16 * tt + cl, 0, gq), bd0, o);
-            if (tt >= 2) o = mma(lds_frag<BF16>(sP, L::LDT, 16 * tt + cl, 32, gq), bd1, o);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = 16 * tt + 4 * gq + j;
-                if (t < nv) {
-                    const int64_t off = ((s * n_tokens + t0 + t) * n_heads + h) * D + vrow;
-                    static_cast<E *>(out)[off] = from_f<E>(scale * o[j]);
-                }
-            }
-        }
-        // M^T <- e^{gam_last} M^T + K^T diag(e^{gam_last - gam}) Delta
-        floatx4 ds[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ds[tt][j] = sG[4 * (16 * tt + 4 * gq + j) + 2] * dl[tt][j];
-        const Frag<BF16> bs0 = acc_frag<BF16>(ds[0], ds[1]);
-        const Frag<BF16> bs1 = acc_frag<BF16>(ds[2], ds[3]);
-        const float eC = sG[3];
+    floatx4 Mt[D / 16];
+    const int64_t st_off = sh * D * D + int64_t(vrow) * D + 4 * (lane >> 4);
+    if (is_chain) {
 #pragma unroll
         for (int kt = 0; kt < D / 16; ++kt) {
-            floatx4 m = Mt[kt] * eC;
-            m = mma(lds_frag<BF16>(sKt, L::LDT, 16 * kt + cl, 0, gq), bs0, m);
-            m = mma(lds_frag<BF16>(sKt, L::LDT, 16 * kt + cl, 32, gq), bs1, m);
-            Mt[kt] = m;
+            if (state_in) {
+                const float4 m = *reinterpret_cast<const float4 *>(state_in + st_off + 16 * kt);
+                Mt[kt] = floatx4{m.x, m.y, m.z, m.w};
+            } else {
+                Mt[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
         }
-        __syncthreads();
     }
 
+    ScanStage<D, BF16> st;
+    auto nv_of = [&](int n) { return static_cast<int>(min<int64_t>(C, n_tokens - int64_t(n) * C)); };
+    if constexpr (S == 2) {
+        scan_load<D, BF16>(st, kp, qp, vp, wsh, hd, 0, nv_of(0), tid);
+        for (int n = 0; n <= n_chunks; ++n) {
+            if (n < n_chunks) scan_commit<D, BF16>(st, smem + (n & 1) * F::kStage, nv_of(n), tid);
+            lds_barrier();
+            if (n + 1 < n_chunks)
+                scan_load<D, BF16>(st, kp, qp, vp, wsh + (n + 1) * W::kBytes, hd,
+                                   int64_t(n + 1) * C, nv_of(n + 1), tid);
+            if (is_chain) {
+                if (n < n_chunks)
+                    chain_step<D, BF16>(Mt, smem + (n & 1) * F::kStage, pub_of(n & 1, pair), vcol,
+                                        lane);
+            } else if (n >= 1) {
+                const int m = n - 1;
+                output_step<D, BF16>(smem + (m & 1) * F::kStage, pub_of(m & 1, pair),
+                                     op + int64_t(m) * C * hd, hd, nv_of(m), scale, lane);
+            }
+            lds_barrier();
+        }
+    } else {
+        for (int n = 0; n < n_chunks; ++n) {
+            scan_load<D, BF16>(st, kp, qp, vp, wsh + n * W::kBytes, hd, int64_t(n) * C, nv_of(n),
+                               tid);
+            scan_commit<D, BF16>(st, smem, nv_of(n), tid);
+            lds_barrier();
+            if (is_chain) chain_step<D, BF16>(Mt, smem, pub_of(0, pair), vcol, lane);
+            lds_barrier();
+            if (!is_chain)
+                output_step<D, BF16>(smem, pub_of(0, pair), op + int64_t(n) * C * hd, hd, nv_of(n),
+                                     scale, lane);
+            lds_barrier();
+        }
+    }
+
+    if (is_chain) {
 #pragma unroll
-    for (int kt = 0; kt < D / 16; ++kt)
-        *reinterpret_cast<float4 *>(state_out + st_off + 16 * kt + 4 * gq) =
-            make_float4(Mt[kt][0], Mt[kt][1], Mt[kt][2], Mt[kt][3]);
+        for (int kt = 0; kt < D / 16; ++kt)
+            *reinterpret_cast<float4 *>(state_out + st_off + 16 * kt) =
+                make_float4(Mt[kt][0], Mt[kt][1], Mt[kt][2], Mt[kt][3]);
+    }
 }
 
 template <int D, bool BF16>
@@ -650,42 +839,35 @@ hipError_t launch_prep(const Problem &p, unsigned char *ws, int n_chunks, hipStr
     return hipGetLastError();
 }
 
-template <int D, int NW, bool BF16>
+template <int D, bool BF16>
 hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, hipStream_t stream)
 {
-    using L = ScanSmem<D, NW, BF16>;
-    auto kern = chunk_scan_kernel<D, NW, BF16>;
+    using F = ScanCfg<D, BF16>;
+    auto kern = chunk_scan_kernel<D, BF16>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::kBytes);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, F::kBytes);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    constexpr int NRB = D / (16 * NW);
+    constexpr int NRB = D / kScanRows;
     const int64_t n_sh = p.n_seqs * p.n_heads;
     const int64_t blocks = (n_sh + 7) / 8 * 8 * NRB;
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
-    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(NW * 64), L::kBytes, stream,
-                       p.q, p.k, p.v, p.state_in, p.out, p.state_out, ws, p.n_tokens, p.n_heads,
-                       n_sh, n_chunks, scale);
+    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kScanThreads), F::kBytes,
+                       stream, p.q, p.k, p.v, p.state_in, p.out, p.state_out, ws, p.n_tokens,
+                       p.n_heads, n_sh, n_chunks, scale);
     return hipGetLastError();
 }
 
-// Waves per scan workgroup: as many as still leave at least 256 workgroups
-// (one per compute unit), at least one.
 template <int D, bool BF16>
 hipError_t launch_chunk_d(const Problem &p, unsigned char *ws, hipStream_t stream)
 {
     const int n_chunks = static_cast<int>((p.n_tokens + C - 1) / C);
     hipError_t e = launch_prep<D, BF16>(p, ws, n_chunks, stream);
     if (e != hipSuccess) return e;
-    const int64_t n_sh = p.n_seqs * p.n_heads;
-    if constexpr (D % 64 == 0) {
-        if (n_sh * (D / 64) >= 256) return launch_scan<D, 4, BF16>(p, ws, n_chunks, stream);
-    }
-    if (n_sh * (D / 32) >= 256) return launch_scan<D, 2, BF16>(p, ws, n_chunks, stream);
-    return launch_scan<D, 1, BF16>(p, ws, n_chunks, stream);
+    return launch_scan<D, BF16>(p, ws, n_chunks, stream);
 }
 
 template <bool BF16>
