@@ -128,14 +128,26 @@ def bench_prefill(gdn, torch, wl, steps, warmup, nbuf):
 
 
 def bench_decode_layers(gdn, torch, wl, reps, n_layers=24):
-    """24 sequential single-token layer calls, each with its own inputs and state;
-    a 1 GiB scrub before each timed batch; median over reps."""
+    """24 sequential single-token layer calls, each with its own inputs and state.
+
+    Device time comes from replaying the 24 calls captured in one HIP graph
+    (so host-side Python overhead does not starve the GPU), with a 1 GiB scrub
+    before each timed replay; host time is the wall time of eager calls.
+    Median over reps."""
     from linear_attention_recurrence_03_amd import inputs
     slots = [Slot(gdn, to_dev(inputs.make(wl, layer=l), wl.dtype, torch), torch)
              for l in range(n_layers)]
     scrub = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
-    for s in slots:
-        s.run(gdn)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):           # warm up outside capture
+        for s in slots:
+            s.run(gdn)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in slots:
+            s.run(gdn)
     dev_us, host_us = [], []
     for _ in range(reps):
         scrub.fill_(1.0)
@@ -143,15 +155,69 @@ def bench_decode_layers(gdn, torch, wl, reps, n_layers=24):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        t0 = time.perf_counter()
-        for s in slots:
-            s.run(gdn)
-        t1 = time.perf_counter()
+        graph.replay()
         b.record()
         torch.cuda.synchronize()
         dev_us.append(a.elapsed_time(b) * 1e3 / n_layers)
-        host_us.append((t1 - t0) * 1e6 / n_layers)
+        scrub.fill_(1.0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in slots:
+            s.run(gdn)
+        host_us.append((time.perf_counter() - t0) * 1e6 / n_layers)
+        torch.cuda.synchronize()
     return statistics.median(dev_us), min(dev_us), max(dev_us), statistics.median(host_us)
+
+
+def profile_pass(gdn, torch, wl, launches=10):
+    """Short run for hardware-counter passes: an elementwise multiply by one over
+    512 MiB (known bytes: reads 512 MiB, writes 512 MiB; it calibrates FETCH_SIZE
+    and WRITE_SIZE) and a few launches of the headline workload."""
+    src = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)          # the calibration kernel: 512 MiB in, 512 MiB out
+    torch.cuda.synchronize()
+    _, slots = bench_prefill(gdn, torch, wl, steps=launches, warmup=0, nbuf=4)
+    torch.cuda.synchronize()
+    print("profile pass done: copy %d bytes, %d launches" % (src.numel() * 4, launches), flush=True)
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Turn two rocprofv3 --pmc runs of --profile-pass (FETCH_SIZE, WRITE_SIZE, in
+    KiB per dispatch) into HBM bytes per launch of each libgdn kernel, scaled by
+    what the same counters read for the 512 MiB copy; writes profiles/traffic.json."""
+    import csv
+    copy_bytes = 2 * 512 * 1024 * 1024   # read + write of the calibration copy
+
+    def per_kernel(d, counter):
+        vals = {}
+        path = os.path.join(d, "run_counter_collection.csv")
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = ("copy" if "MulFunctor" in name else
+                   "chunk_scan" if "chunk_scan" in name else
+                   "chunk_prep" if "chunk_prep" in name else
+                   "recurrent" if "recurrent_kernel" in name else None)
+            if key:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: statistics.median(v) for k, v in vals.items()}
+
+    f = per_kernel(fetch_dir, "FETCH_SIZE")
+    w = per_kernel(write_dir, "WRITE_SIZE")
+    scale = copy_bytes / (f["copy"] + w["copy"])
+    kernels = {k: {"fetch_bytes": f.get(k, 0) * scale, "write_bytes": w.get(k, 0) * scale}
+               for k in ("chunk_prep", "chunk_scan")}
+    total = sum(v["fetch_bytes"] + v["write_bytes"] for v in kernels.values())
+    rec = {"prefill_bf16": {"source_hash": kernel_source_hash(), "bytes_per_launch": round(total),
+                            "kernels": kernels, "copy_calibration_factor": scale,
+                            "note": "FETCH_SIZE + WRITE_SIZE per dispatch, scaled by the factor "
+                                    "that maps the 512 MiB copy's counters to its 1 GiB of traffic"}}
+    out = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def cpu_baseline(wl):
@@ -178,7 +244,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the decode and long-prefill extras")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="short run for rocprofv3 --pmc passes (copy calibration + 10 launches)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two --pmc runs of --profile-pass")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus %d (WORLD_SIZE=%d) is not "
@@ -196,6 +269,9 @@ def main():
     gdn._lib()
 
     wl = inputs.WORKLOADS[4]
+    if args.profile_pass:
+        profile_pass(gdn, torch, wl)
+        return
     S, T, H, D = wl.shape()
     ms, _ = bench_prefill(gdn, torch, wl, args.steps, args.warmup, nbuf=4)
     tok_s = S * T / (ms * 1e-3)
@@ -237,8 +313,8 @@ def main():
             "us_per_layer_device": round(med, 3), "us_min": round(lo, 3), "us_max": round(hi, 3),
             "us_per_layer_host": round(host, 3), "bytes_per_call": b2,
             "hbm_frac": round(b2 / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "workload": "1 seq x 1 token x 32 heads x d128 fp32, 24 sequential layer calls, "
-                        "1 GiB scrub before each batch"}
+            "workload": "1 seq x 1 token x 32 heads x d128 fp32, 24 sequential layer calls "
+                        "replayed from one HIP graph, 1 GiB scrub before each replay"}
         # batched decode
         wl3 = inputs.WORKLOADS[3]
         ms3, _ = bench_prefill(gdn, torch, wl3, steps=50, warmup=5, nbuf=3)
