@@ -203,8 +203,8 @@ __device__ __forceinline__ void lds_barrier()
 // ---- workspace layout, per (seq, head, chunk) ----------------------------------
 //   T     [C][C] elements   (fp32 or bf16, like q/k/v)
 //   P     [C][C] elements
-//   gates [C][4] fp32: per token r {beta_r, e^{gam_r}, e^{gam_last - gam_r},
-//                      e^{gam_last}}
+//   gates [4][C] fp32: beta_r, e^{gam_r}, e^{gam_last - gam_r}, then e^{gam_last}
+//                      repeated C times
 // Rows past the end of a partial last chunk carry beta = e^gam = 0, so they add
 // nothing to the state or to valid outputs.
 template <bool BF16>
@@ -415,330 +415,399 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
         }
         *reinterpret_cast<uint4 *>(wT + i * VE) = *reinterpret_cast<const uint4 *>(vt);
     }
-    float4 *wG = reinterpret_cast<float4 *>(dst + W::kGates);
-    if (tid < C) wG[tid] = make_float4(sG[C + tid], sG[2 * C + tid], sG[3 * C + tid], sG[4 * C]);
+    float *wG = reinterpret_cast<float *>(dst + W::kGates);
+    if (tid < C) {
+        wG[tid] = sG[C + tid];
+        wG[C + tid] = sG[2 * C + tid];
+        wG[2 * C + tid] = sG[3 * C + tid];
+        wG[3 * C + tid] = sG[4 * C];
+    }
 }
 
 // ---- the chunk-to-chunk scan -----------------------------------------------------
 //
-// One workgroup = four waves for 32 value rows of one (seq, head):
-//   waves 0, 1  "chain" waves, 16 value rows each: carry M^T in registers and
-//               per chunk do X = K M^T, E, Delta = T E and the state update --
-//               the serial dependency from one chunk to the next;
-//   waves 2, 3  "output" waves, paired with waves 0, 1: one chunk behind, they
-//               take the M^T and Delta fragments the chain wave published in
-//               LDS and form O = (e^gam Q M^T + P Delta) / sqrt(d).
-// Each wave sits on its own SIMD, so the chain's MFMA work is not shared with the
-// output products.  Chunk inputs (K, Q, T, P, V, gates) are staged through
-// registers into double-buffered LDS (bf16); the next chunk's global loads are in
-// flight during the current step.  The fp32 variant (parity path) has room for
-// one LDS stage only and runs chain and output phases back to back.
+// One workgroup = three waves for RW = 16 VT value rows of one (seq, head):
+//   wave 0  "chain": carries those rows of M^T in registers and per chunk does
+//           X = K M^T, E = beta (V - e^gam X), Delta = T E and the state update --
+//           the serial dependency from chunk to chunk;
+//   wave 1  "output": while the chain wave works on X, E and Delta it forms
+//           e^gam Q M^T from the M^T fragments the chain wave published, then
+//           after a mid-step barrier adds P Delta and stores O;
+//   wave 2  "producer": issues the next chunk's loads (K, Q, T, P, V, gates)
+//           global -> LDS with global_load_lds (16 bytes per lane) into the
+//           stage not in use, and waits for them.
+// Each wave sits on its own SIMD.  K, Q, T and P are read from LDS once per
+// workgroup per chunk; LDS rows are padded by 16 bytes so that fragment reads
+// spread over the banks.  Rows past the end of a partial chunk are loaded from
+// the last valid row: the prep kernel gives them beta = e^gam = 0, so they
+// contribute nothing, and finite data keeps 0 * x = 0.
 
-constexpr int kScanThreads = 256;
-constexpr int kScanRows = 32;
+constexpr int kScanThreads = 192;
 
-template <int D, bool BF16>
+template <int D, bool BF16, int VT>
 struct ScanCfg {
     using E = typename Elem<BF16>::T;
+    static constexpr int RW = 16 * VT;               // value rows per workgroup
     static constexpr int kStages = BF16 ? 2 : 1;
-    static constexpr int PAD = BF16 ? 8 : 4;
-    static constexpr int LDK = D + PAD;        // sK, sQ rows (elements)
-    static constexpr int LDT = C + PAD;        // sT, sP rows
-    static constexpr int LDV = kScanRows + PAD;
+    static constexpr int ES = sizeof(E);
+    static constexpr int RK = D * ES + 16;          // sK, sQ row stride (bytes)
+    static constexpr int RT = C * ES + 16;          // sT, sP row stride
+    static constexpr int RV = RW * ES + 16;         // sV row stride
     static constexpr int kK = 0;
-    static constexpr int kQ = kK + C * LDK * sizeof(E);
-    static constexpr int kT = kQ + C * LDK * sizeof(E);
-    static constexpr int kP = kT + C * LDT * sizeof(E);
-    static constexpr int kV = kP + C * LDT * sizeof(E);
-    static constexpr int kG = kV + C * LDV * sizeof(E);
-    static constexpr int kStage = kG + C * 16;                          // bytes per stage
-    static constexpr int kFrags = D / 32 + 2;                           // M^T and Delta fragments
-    static constexpr int kPubWave = 64 * kFrags * int(sizeof(Frag<BF16>));
-    static constexpr int kPub = kStages * kStage;                       // published fragments
-    static constexpr int kBytes = kPub + kStages * 2 * kPubWave;
+    static constexpr int kQ = kK + C * RK;
+    static constexpr int kT = kQ + C * RK;
+    static constexpr int kP = kT + C * RT;
+    static constexpr int kV = kP + C * RT;
+    static constexpr int kG = kV + C * RV;
+    static constexpr int kStage = (kG + 4 * C * 4 + 1023) / 1024 * 1024;
+    static constexpr int KS = D / 32;
+    static constexpr int kFrags = (KS + 2) * VT;    // M^T and Delta fragments
+    static constexpr int kPub = kStages * kStage;
+    static constexpr int kBytes = kPub + 64 * kFrags * int(sizeof(Frag<BF16>));
     static_assert(kBytes <= 160 * 1024, "LDS budget");
-    // staging: 16-byte vectors per thread
-    static constexpr int VE = 16 / sizeof(E);
-    static constexpr int VPR = D / VE;
-    static constexpr int NK = C * VPR / kScanThreads;                   // K (and Q)
-    static constexpr int NTP = C * C / VE / kScanThreads;               // T (and P)
-    static constexpr int VPV = kScanRows / VE;
-    static constexpr int NV = (C * VPV + kScanThreads - 1) / kScanThreads;
-    static_assert(C * VPR % kScanThreads == 0 && C * C / VE % kScanThreads == 0, "staging split");
+    // 1 KiB LDS-DMA blocks per region (64 padded rows are a whole number of blocks)
+    static constexpr int NBK = C * RK / 1024;
+    static constexpr int NBT = C * RT / 1024;
+    static constexpr int NBV = C * RV / 1024;
+    static_assert(C * RK % 1024 == 0 && C * RT % 1024 == 0 && C * RV % 1024 == 0, "blocks");
 };
 
-template <int D, bool BF16>
-struct ScanStage {
-    using F = ScanCfg<D, BF16>;
-    uint4 k[F::NK], q[F::NK], t[F::NTP], p[F::NTP], v[F::NV], g;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
+
+// One 16-byte-per-lane LDS-DMA: lane l's 16 bytes (from base + off) land at
+// lds + 16 l.  base is wave-uniform; off is a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16(const unsigned char *base, uint32_t off, void *lds)
+{
+    __builtin_amdgcn_global_load_lds((global_cvoid *)(base + off), (lds_void *)(lds), 16, 0, 0);
+}
+
+// Wait for this wave's outstanding global loads (LDS-DMA included).
+__device__ __forceinline__ void wait_vmem()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unconstrained
+}
+
+// Byte offset, inside one chunk's data, of the 16 bytes lane `lane` loads for LDS
+// block `blk` of a padded region: rows of `rowb` valid bytes stored with stride
+// `stride`; pad slots read row 0.  `gstride` is the source row stride; rows past
+// nv read row nv - 1.
+__device__ __forceinline__ uint32_t dma_src_offset(int blk, int lane, int rowb, int stride,
+                                                   uint32_t gstride, int nv)
+{
+    const int o = blk * 1024 + lane * 16;
+    const int r = o / stride, b = o - r * stride;
+    const uint32_t v = uint32_t(min(r, nv - 1)) * gstride + uint32_t(b);
+    return b < rowb ? v : 0u;
+}
+
+struct ScanPtrs {
+    const unsigned char *k, *q, *v;   // token 0 of this (seq, head); v at the first value row
+    const unsigned char *ws;          // this (seq, head)'s chunk 0 in the workspace
+    int64_t hd_bytes;                 // token stride in bytes (64 of them fit in 32 bits)
 };
 
-// Global loads through explicit global-address-space pointers.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) const u32x4_t global_u32x4;
-
-__device__ __forceinline__ uint4 ldg16(const void *p)
+// Producer wave: issue the LDS-DMA loads of chunk n into stage buffer `buf`.
+template <int D, bool BF16, int VT>
+__device__ __forceinline__ void scan_issue(const ScanPtrs &pt, unsigned char *buf, int n, int nv,
+                                           int lane)
 {
-    const u32x4_t x = *reinterpret_cast<global_u32x4 *>(reinterpret_cast<uintptr_t>(p));
-    return make_uint4(x.x, x.y, x.z, x.w);
-}
-
-__device__ __forceinline__ uint4 zero_unless(bool keep, uint4 x)
-{
-    return keep ? x : make_uint4(0, 0, 0, 0);
-}
-
-// Global -> registers for the chunk starting at token t0 with nv valid tokens.
-// kp, qp, vp point at token 0 of this (seq, head) (vp already offset to the
-// workgroup's first value row); hd is n_heads * head_dim, the token stride.
-// Rows past the end are read from the last valid row (every address stays
-// inside the tensors) and zeroed when committed to LDS: using a loaded value
-// here would make the wave wait for the load instead of overlapping it.
-template <int D, bool BF16>
-__device__ __forceinline__ void scan_fetch(ScanStage<D, BF16> &st, const typename Elem<BF16>::T *kp,
-                                           const typename Elem<BF16>::T *qp,
-                                           const typename Elem<BF16>::T *vp,
-                                           const unsigned char *wsc, int64_t hd, int64_t t0,
-                                           int nv, int tid)
-{
-    using F = ScanCfg<D, BF16>;
+    using F = ScanCfg<D, BF16, VT>;
     using W = WsLayout<BF16>;
-    const int64_t base = t0 * hd;
+    const int64_t tb = int64_t(n) * C * pt.hd_bytes;
+    const uint32_t hdb = static_cast<uint32_t>(pt.hd_bytes);
+    const unsigned char *kb = pt.k + tb, *qb = pt.q + tb, *vb = pt.v + tb;
 #pragma unroll
-    for (int i = 0; i < F::NK; ++i) {
-        const int idx = tid + i * kScanThreads;
-        const int r = idx / F::VPR, c = (idx % F::VPR) * F::VE;
-        const int64_t off = base + min(r, nv - 1) * hd + c;
-        st.k[i] = ldg16(kp + off);
-        st.q[i] = ldg16(qp + off);
+    for (int blk = 0; blk < F::NBK; ++blk) {
+        const uint32_t off = dma_src_offset(blk, lane, D * F::ES, F::RK, hdb, nv);
+        dma16(kb, off, buf + F::kK + 1024 * blk);
+        dma16(qb, off, buf + F::kQ + 1024 * blk);
+    }
+    const unsigned char *wsc = pt.ws + int64_t(n) * W::kBytes;
+#pragma unroll
+    for (int blk = 0; blk < F::NBT; ++blk) {
+        const uint32_t off = dma_src_offset(blk, lane, C * F::ES, F::RT, C * F::ES, C);
+        dma16(wsc + W::kT, off, buf + F::kT + 1024 * blk);
+        dma16(wsc + W::kP, off, buf + F::kP + 1024 * blk);
     }
 #pragma unroll
-    for (int i = 0; i < F::NTP; ++i) {
-        st.t[i] = ldg16(wsc + W::kT + 16 * (tid + i * kScanThreads));
-        st.p[i] = ldg16(wsc + W::kP + 16 * (tid + i * kScanThreads));
-    }
-#pragma unroll
-    for (int i = 0; i < F::NV; ++i) {
-        const int idx = min(tid + i * kScanThreads, C * F::VPV - 1);
-        const int r = idx / F::VPV, c = (idx % F::VPV) * F::VE;
-        st.v[i] = ldg16(vp + base + min(r, nv - 1) * hd + c);
-    }
-    st.g = ldg16(wsc + W::kGates + 16 * (tid & (C - 1)));
+    for (int blk = 0; blk < F::NBV; ++blk)
+        dma16(vb, dma_src_offset(blk, lane, F::RW * F::ES, F::RV, hdb, nv), buf + F::kV + 1024 * blk);
+    dma16(wsc + W::kGates, 16u * lane, buf + F::kG);
 }
 
-template <int D, bool BF16>
-__device__ __forceinline__ void scan_commit(const ScanStage<D, BF16> &st, unsigned char *buf, int nv,
-                                            int tid)
+// Fragment loaders on the padded LDS layout.  A operand row `row`, k elements
+// k0 + {4g..4g+3} and k0 + 16 + {4g..4g+3}.
+template <bool BF16>
+__device__ __forceinline__ Frag<BF16> frag_rows(const unsigned char *base, int stride, int row,
+                                                int k0, int g)
 {
-    using F = ScanCfg<D, BF16>;
-    using E = typename Elem<BF16>::T;
-    E *sK = reinterpret_cast<E *>(buf + F::kK);
-    E *sQ = reinterpret_cast<E *>(buf + F::kQ);
-    E *sT = reinterpret_cast<E *>(buf + F::kT);
-    E *sP = reinterpret_cast<E *>(buf + F::kP);
-    E *sV = reinterpret_cast<E *>(buf + F::kV);
-#pragma unroll
-    for (int i = 0; i < F::NK; ++i) {
-        const int idx = tid + i * kScanThreads;
-        const int r = idx / F::VPR, c = (idx % F::VPR) * F::VE;
-        *reinterpret_cast<uint4 *>(sK + r * F::LDK + c) = zero_unless(r < nv, st.k[i]);
-        *reinterpret_cast<uint4 *>(sQ + r * F::LDK + c) = zero_unless(r < nv, st.q[i]);
+    Frag<BF16> f;
+    constexpr int ES = BF16 ? 2 : 4;
+    const unsigned char *p = base + row * stride + (k0 + 4 * g) * ES;
+    if constexpr (BF16) {
+        const uint2 lo = *reinterpret_cast<const uint2 *>(p);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(p + 32);
+        f.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+        const float4 lo = *reinterpret_cast<const float4 *>(p);
+        const float4 hi = *reinterpret_cast<const float4 *>(p + 64);
+        f.v[0] = lo.x; f.v[1] = lo.y; f.v[2] = lo.z; f.v[3] = lo.w;
+        f.v[4] = hi.x; f.v[5] = hi.y; f.v[6] = hi.z; f.v[7] = hi.w;
     }
+    return f;
+}
+
+// Operand whose rows are columns c0 + (lane mod 16) of a row-major LDS matrix and
+// whose k values are rows t0 + {4g..4g+3}, t0 + 16 + {4g..4g+3} (eight rows of
+// one column).  bf16: two ds_read_b64_tr_b16 (see lds_frag_tr).
+template <bool BF16>
+__device__ __forceinline__ Frag<BF16> frag_cols(const unsigned char *base, int stride, int t0,
+                                                int c0, int lane)
+{
+    Frag<BF16> f;
+    const int g = lane >> 4, p = lane & 15;
+    if constexpr (BF16) {
+        const unsigned char *a1 = base + (t0 + 4 * g + (p >> 2)) * stride + (c0 + 4 * (p & 3)) * 2;
+        typedef __attribute__((address_space(3))) short4_t lds_short4;
+        const short4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a1));
+        const short4_t r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a1 + 16 * stride));
+        const uint2 u1 = __builtin_bit_cast(uint2, r1);
+        const uint2 u2 = __builtin_bit_cast(uint2, r2);
+        f.u = make_uint4(u1.x, u1.y, u2.x, u2.y);
+    } else {
+        const float *col = reinterpret_cast<const float *>(base + (c0 + p) * 4);
 #pragma unroll
-    for (int i = 0; i < F::NTP; ++i) {
-        const int idx = (tid + i * kScanThreads) * F::VE;
-        const int r = idx / C, c = idx % C;
-        *reinterpret_cast<uint4 *>(sT + r * F::LDT + c) = st.t[i];
-        *reinterpret_cast<uint4 *>(sP + r * F::LDT + c) = st.p[i];
-    }
-#pragma unroll
-    for (int i = 0; i < F::NV; ++i) {
-        const int idx = tid + i * kScanThreads;
-        if (C * F::VPV % kScanThreads == 0 || idx < C * F::VPV) {
-            const int r = idx / F::VPV, c = (idx % F::VPV) * F::VE;
-            *reinterpret_cast<uint4 *>(sV + r * F::LDV + c) = zero_unless(r < nv, st.v[i]);
+        for (int j = 0; j < 4; ++j) {
+            f.v[j] = *reinterpret_cast<const float *>(reinterpret_cast<const unsigned char *>(col) +
+                                                      (t0 + 4 * g + j) * stride);
+            f.v[4 + j] = *reinterpret_cast<const float *>(reinterpret_cast<const unsigned char *>(col) +
+                                                          (t0 + 16 + 4 * g + j) * stride);
         }
     }
-    if (tid < C) reinterpret_cast<uint4 *>(buf + F::kG)[tid] = st.g;
+    return f;
 }
 
-template <int D, bool BF16>
-__device__ __forceinline__ void scan_load(ScanStage<D, BF16> &st, const typename Elem<BF16>::T *kp,
-                                          const typename Elem<BF16>::T *qp,
-                                          const typename Elem<BF16>::T *vp,
-                                          const unsigned char *wsc, int64_t hd, int64_t t0,
-                                          int nv, int tid)
+// Values of one LDS column at four consecutive rows t..t+3 (accumulator layout
+// rows 4g+j of a tile): lane (g, i) gets base[t0 + 4g + j][c0 + i], j = 0..3.
+template <bool BF16>
+__device__ __forceinline__ floatx4 col4(const unsigned char *base, int stride, int t0, int c0,
+                                        int lane)
 {
-    scan_fetch<D, BF16>(st, kp, qp, vp, wsc, hd, t0, nv, tid);
+    const int g = lane >> 4, p = lane & 15;
+    floatx4 r;
+    if constexpr (BF16) {
+        // one transposing read: lane 4j + i/4 fetches row t0 + 4g + j, columns
+        // c0 + 4 (i/4) .. +3; lane i receives column c0 + i of the four rows
+        const unsigned char *a = base + (t0 + 4 * g + (p >> 2)) * stride + (c0 + 4 * (p & 3)) * 2;
+        typedef __attribute__((address_space(3))) short4_t lds_short4;
+        const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = bf16_to_f32(static_cast<uint16_t>(v[j]));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            r[j] = *reinterpret_cast<const float *>(base + (t0 + 4 * g + j) * stride + (c0 + p) * 4);
+    }
+    return r;
 }
 
-// Chain step for one chunk: publishes this chunk's M^T and Delta fragments and
-// advances Mt (accumulator layout: Mt[kt][j] = M[vrow][16 kt + 4 g + j]).
-// Every phase first issues all of its LDS reads, then runs its MFMAs with the
-// k step outermost, so that independent accumulators interleave and LDS latency
-// is paid once per phase rather than once per product.
-template <int D, bool BF16>
-__device__ __forceinline__ void chain_step(floatx4 (&Mt)[D / 16], const unsigned char *buf,
-                                           Frag<BF16> *pub, int vcol, int lane)
+// Chain wave, first half of a step: X = K M^T, E, Delta = T E for VT tiles of
+// 16 value rows; publishes Delta.  Also returns the gate rows it read.
+template <int D, bool BF16, int VT>
+__device__ __forceinline__ void chain_first(const floatx4 (&Mt)[VT][D / 16],
+                                            const unsigned char *buf, Frag<BF16> *pub, int lane,
+                                            floatx4 (&dl)[VT][4], floatx4 (&edec)[4], float &eC)
 {
-    using F = ScanCfg<D, BF16>;
-    using E = typename Elem<BF16>::T;
-    constexpr int KS = D / 32;
-    const E *sK = reinterpret_cast<const E *>(buf + F::kK);
-    const E *sT = reinterpret_cast<const E *>(buf + F::kT);
-    const E *sV = reinterpret_cast<const E *>(buf + F::kV);
-    const float4 *sG = reinterpret_cast<const float4 *>(buf + F::kG);
+    using F = ScanCfg<D, BF16, VT>;
+    constexpr int KS = F::KS;
     const int gq = lane >> 4, cl = lane & 15;
-
-    // LDS reads for X = K M^T, E and Delta = T E
+    const float *sG = reinterpret_cast<const float *>(buf + F::kG);
     Frag<BF16> ak[4][KS];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) ak[tt][ks] = lds_frag<BF16>(sK, F::LDK, 16 * tt + cl, 32 * ks, gq);
+        for (int ks = 0; ks < KS; ++ks) ak[tt][ks] = frag_rows<BF16>(buf + F::kK, F::RK, 16 * tt + cl, 32 * ks, gq);
     Frag<BF16> at[6];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-        at[tt] = lds_frag<BF16>(sT, F::LDT, 16 * tt + cl, 0, gq);
-        if (tt >= 2) at[2 + tt] = lds_frag<BF16>(sT, F::LDT, 16 * tt + cl, 32, gq);
+        at[tt] = frag_rows<BF16>(buf + F::kT, F::RT, 16 * tt + cl, 0, gq);
+        if (tt >= 2) at[2 + tt] = frag_rows<BF16>(buf + F::kT, F::RT, 16 * tt + cl, 32, gq);
     }
-    float4 gt[4][4];
-    float vv[4][4];
+    floatx4 bt[4], eg[4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = 16 * tt + 4 * gq + j;
-            gt[tt][j] = sG[t];
-            vv[tt][j] = to_f(sV[t * F::LDV + vcol]);
-        }
-
-    Frag<BF16> bm[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        bm[ks] = acc_frag<BF16>(Mt[2 * ks], Mt[2 * ks + 1]);
-        pub[ks * 64 + lane] = bm[ks];
+    for (int tt = 0; tt < 4; ++tt) {
+        const int t = 16 * tt + 4 * gq;
+        const float4 b4 = *reinterpret_cast<const float4 *>(sG + t);
+        const float4 e4 = *reinterpret_cast<const float4 *>(sG + C + t);
+        const float4 d4 = *reinterpret_cast<const float4 *>(sG + 2 * C + t);
+        bt[tt] = floatx4{b4.x, b4.y, b4.z, b4.w};
+        eg[tt] = floatx4{e4.x, e4.y, e4.z, e4.w};
+        edec[tt] = floatx4{d4.x, d4.y, d4.z, d4.w};
     }
-    floatx4 xk[4];
+    eC = sG[3 * C];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) xk[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int vt = 0; vt < VT; ++vt) {
+        floatx4 vv[4];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+        for (int tt = 0; tt < 4; ++tt) vv[tt] = col4<BF16>(buf + F::kV, F::RV, 16 * tt, 16 * vt, lane);
+        Frag<BF16> bm[KS];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) xk[tt] = mma(ak[tt][ks], bm[ks], xk[tt]);
-
-    // transposed K reads for the state update, issued before they are needed
-    Frag<BF16> akt[D / 16][2];
+        for (int ks = 0; ks < KS; ++ks) bm[ks] = acc_frag<BF16>(Mt[vt][2 * ks], Mt[vt][2 * ks + 1]);
+        floatx4 xk[4];
 #pragma unroll
-    for (int kt = 0; kt < D / 16; ++kt) {
-        akt[kt][0] = lds_frag_tr<BF16>(sK, F::LDK, 0, 16 * kt, lane);
-        akt[kt][1] = lds_frag_tr<BF16>(sK, F::LDK, 32, 16 * kt, lane);
+        for (int tt = 0; tt < 4; ++tt) xk[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) xk[tt] = mma(ak[tt][ks], bm[ks], xk[tt]);
+        floatx4 e[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) e[tt][j] = bt[tt][j] * fmaf(-eg[tt][j], xk[tt][j], vv[tt][j]);
+        const Frag<BF16> be0 = acc_frag<BF16>(e[0], e[1]);
+        const Frag<BF16> be1 = acc_frag<BF16>(e[2], e[3]);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) dl[vt][tt] = mma(at[tt], be0, floatx4{0.f, 0.f, 0.f, 0.f});
+        dl[vt][2] = mma(at[4], be1, dl[vt][2]);
+        dl[vt][3] = mma(at[5], be1, dl[vt][3]);
+        pub[(VT * KS + 2 * vt) * 64 + lane] = acc_frag<BF16>(dl[vt][0], dl[vt][1]);
+        pub[(VT * KS + 2 * vt + 1) * 64 + lane] = acc_frag<BF16>(dl[vt][2], dl[vt][3]);
     }
-
-    // E = beta (V - e^gam X)
-    floatx4 e[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) e[tt][j] = gt[tt][j].x * (vv[tt][j] - gt[tt][j].y * xk[tt][j]);
-    const Frag<BF16> be0 = acc_frag<BF16>(e[0], e[1]);
-    const Frag<BF16> be1 = acc_frag<BF16>(e[2], e[3]);
-    // Delta = T E  (T lower triangular)
-    floatx4 dl[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) dl[tt] = mma(at[tt], be0, floatx4{0.f, 0.f, 0.f, 0.f});
-    dl[2] = mma(at[4], be1, dl[2]);
-    dl[3] = mma(at[5], be1, dl[3]);
-    pub[KS * 64 + lane] = acc_frag<BF16>(dl[0], dl[1]);
-    pub[(KS + 1) * 64 + lane] = acc_frag<BF16>(dl[2], dl[3]);
-    // M^T <- e^{gam_last} M^T + K^T diag(e^{gam_last - gam}) Delta
-    floatx4 ds[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ds[tt][j] = gt[tt][j].z * dl[tt][j];
-    const Frag<BF16> bs0 = acc_frag<BF16>(ds[0], ds[1]);
-    const Frag<BF16> bs1 = acc_frag<BF16>(ds[2], ds[3]);
-    const float eC = gt[0][0].w;
-#pragma unroll
-    for (int kt = 0; kt < D / 16; ++kt) Mt[kt] = mma(akt[kt][0], bs0, Mt[kt] * eC);
-#pragma unroll
-    for (int kt = 0; kt < D / 16; ++kt) Mt[kt] = mma(akt[kt][1], bs1, Mt[kt]);
 }
 
-// Output step for one chunk from the published fragments of its chain wave.
-// op points at out[(s, chunk token 0, h, vrow)]; hd is the token stride.
-template <int D, bool BF16>
-__device__ __forceinline__ void output_step(const unsigned char *buf, const Frag<BF16> *pub,
-                                            typename Elem<BF16>::T *op, int64_t hd, int nv,
-                                            float scale, int lane)
+// Chain wave, second half: M^T <- e^{gam_last} M^T + K^T diag(e^{gam_last - gam})
+// Delta; publishes the new M^T fragments for the next step.
+template <int D, bool BF16, int VT>
+__device__ __forceinline__ void chain_second(floatx4 (&Mt)[VT][D / 16], const unsigned char *buf,
+                                             Frag<BF16> *pub, int lane, const floatx4 (&dl)[VT][4],
+                                             const floatx4 (&edec)[4], float eC)
 {
-    using F = ScanCfg<D, BF16>;
-    using E = typename Elem<BF16>::T;
-    constexpr int KS = D / 32;
-    const E *sQ = reinterpret_cast<const E *>(buf + F::kQ);
-    const E *sP = reinterpret_cast<const E *>(buf + F::kP);
-    const float4 *sG = reinterpret_cast<const float4 *>(buf + F::kG);
-    const int gq = lane >> 4, cl = lane & 15;
-    Frag<BF16> aq[4][KS], ap[6], bm[KS];
+    using F = ScanCfg<D, BF16, VT>;
+    constexpr int KS = F::KS;
+    Frag<BF16> bs[VT][2];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int vt = 0; vt < VT; ++vt) {
+        floatx4 ds[4];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) aq[tt][ks] = lds_frag<BF16>(sQ, F::LDK, 16 * tt + cl, 32 * ks, gq);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        ap[tt] = lds_frag<BF16>(sP, F::LDT, 16 * tt + cl, 0, gq);
-        if (tt >= 2) ap[2 + tt] = lds_frag<BF16>(sP, F::LDT, 16 * tt + cl, 32, gq);
+        for (int tt = 0; tt < 4; ++tt) ds[tt] = edec[tt] * dl[vt][tt];
+        bs[vt][0] = acc_frag<BF16>(ds[0], ds[1]);
+        bs[vt][1] = acc_frag<BF16>(ds[2], ds[3]);
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bm[ks] = pub[ks * 64 + lane];
-    const Frag<BF16> bd0 = pub[KS * 64 + lane];
-    const Frag<BF16> bd1 = pub[(KS + 1) * 64 + lane];
-    float eg[4][4];
+    for (int kt = 0; kt < D / 16; ++kt) {
+        const Frag<BF16> a0 = frag_cols<BF16>(buf + F::kK, F::RK, 0, 16 * kt, lane);
+        const Frag<BF16> a1 = frag_cols<BF16>(buf + F::kK, F::RK, 32, 16 * kt, lane);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) eg[tt][j] = sG[16 * tt + 4 * gq + j].y;
-
-    floatx4 xq[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) xq[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) xq[tt] = mma(aq[tt][ks], bm[ks], xq[tt]);
-    floatx4 o[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[tt][j] = eg[tt][j] * xq[tt][j];
-        o[tt] = mma(ap[tt], bd0, o[tt]);
-    }
-    o[2] = mma(ap[4], bd1, o[2]);
-    o[3] = mma(ap[5], bd1, o[3]);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = 16 * tt + 4 * gq + j;
-            if (t < nv) op[t * hd] = from_f<E>(scale * o[tt][j]);
+        for (int vt = 0; vt < VT; ++vt) {
+            Mt[vt][kt] = mma(a0, bs[vt][0], Mt[vt][kt] * eC);
+            Mt[vt][kt] = mma(a1, bs[vt][1], Mt[vt][kt]);
         }
+    }
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            pub[(vt * KS + ks) * 64 + lane] = acc_frag<BF16>(Mt[vt][2 * ks], Mt[vt][2 * ks + 1]);
+}
+
+// Output wave, first half: e^gam Q M^T for the chunk (M^T from the publication).
+template <int D, bool BF16, int VT>
+__device__ __forceinline__ void output_first(const unsigned char *buf, const Frag<BF16> *pub,
+                                             int lane, floatx4 (&o)[VT][4])
+{
+    using F = ScanCfg<D, BF16, VT>;
+    constexpr int KS = F::KS;
+    const int gq = lane >> 4, cl = lane & 15;
+    const float *sG = reinterpret_cast<const float *>(buf + F::kG);
+    Frag<BF16> aq[4][KS];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            aq[tt][ks] = frag_rows<BF16>(buf + F::kQ, F::RK, 16 * tt + cl, 32 * ks, gq);
+    floatx4 eg[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const float4 e4 = *reinterpret_cast<const float4 *>(sG + C + 16 * tt + 4 * gq);
+        eg[tt] = floatx4{e4.x, e4.y, e4.z, e4.w};
+    }
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+        Frag<BF16> bm[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bm[ks] = pub[(vt * KS + ks) * 64 + lane];
+        floatx4 xq[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) xq[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) xq[tt] = mma(aq[tt][ks], bm[ks], xq[tt]);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) o[vt][tt] = eg[tt] * xq[tt];
+    }
+}
+
+// Output wave, second half: O = (o + P Delta) / sqrt(d), stored for valid tokens.
+// orow points at out[(s, first token of the chunk, h, first value row + lane%16)].
+template <int D, bool BF16, int VT>
+__device__ __forceinline__ void output_second(const unsigned char *buf, const Frag<BF16> *pub,
+                                              int lane, floatx4 (&o)[VT][4],
+                                              typename Elem<BF16>::T *orow, int64_t hd, int nv,
+                                              float scale)
+{
+    using F = ScanCfg<D, BF16, VT>;
+    using E = typename Elem<BF16>::T;
+    constexpr int KS = F::KS;
+    const int gq = lane >> 4, cl = lane & 15;
+    Frag<BF16> ap[6];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        ap[tt] = frag_rows<BF16>(buf + F::kP, F::RT, 16 * tt + cl, 0, gq);
+        if (tt >= 2) ap[2 + tt] = frag_rows<BF16>(buf + F::kP, F::RT, 16 * tt + cl, 32, gq);
+    }
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+        const Frag<BF16> bd0 = pub[(VT * KS + 2 * vt) * 64 + lane];
+        const Frag<BF16> bd1 = pub[(VT * KS + 2 * vt + 1) * 64 + lane];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) o[vt][tt] = mma(ap[tt], bd0, o[vt][tt]);
+        o[vt][2] = mma(ap[4], bd1, o[vt][2]);
+        o[vt][3] = mma(ap[5], bd1, o[vt][3]);
+        E *ov = orow + 16 * vt;
+        if (nv == C) {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ov[(16 * tt + 4 * gq + j) * hd] = from_f<E>(scale * o[vt][tt][j]);
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int t = 16 * tt + 4 * gq + j;
+                    if (t < nv) ov[t * hd] = from_f<E>(scale * o[vt][tt][j]);
+                }
+        }
+    }
 }
 
 // Workgroups are numbered so that the row blocks of one (seq, head) share the
 // low three bits of the block id: consecutive ids go to different XCDs, so this
 // keeps a head's workgroups on one XCD, where its K, Q, T and P hit in L2.
-template <int D, bool BF16>
+template <int D, bool BF16, int VT>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *state_in, void *__restrict__ out, float *state_out,
     const unsigned char *__restrict__ ws, int64_t n_tokens, int64_t n_heads, int64_t n_sh,
     int n_chunks, float scale)
 {
-    using F = ScanCfg<D, BF16>;
+    using F = ScanCfg<D, BF16, VT>;
     using E = typename Elem<BF16>::T;
     using W = WsLayout<BF16>;
-    constexpr int NRB = D / kScanRows;  // row blocks per head
+    constexpr int NRB = D / F::RW;  // row blocks per head
     constexpr int S = F::kStages;
     extern __shared__ __align__(16) unsigned char smem[];
 
@@ -748,76 +817,85 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     if (sh >= n_sh) return;  // whole workgroup leaves before any barrier
     const int64_t s = sh / n_heads, h = sh - s * n_heads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool is_chain = wave < 2;
-    const int pair = wave & 1;                       // which 16-row half
-    const int v0 = rb * kScanRows;                   // first value row of the workgroup
-    const int vcol = 16 * pair + (lane & 15);        // row within the workgroup
-    const int vrow = v0 + vcol;                      // this lane's value row
+    const int v0 = rb * F::RW;                       // first value row of the workgroup
     const int64_t hd = n_heads * D;
-    const E *kp = static_cast<const E *>(k) + (s * n_tokens * n_heads + h) * D;
-    const E *qp = static_cast<const E *>(q) + (s * n_tokens * n_heads + h) * D;
-    const E *vp = static_cast<const E *>(v) + (s * n_tokens * n_heads + h) * D + v0;
-    E *op = static_cast<E *>(out) + (s * n_tokens * n_heads + h) * D + vrow;
-    const unsigned char *wsh = ws + sh * n_chunks * W::kBytes;
-    auto pub_of = [&](int stage, int which) {
-        return reinterpret_cast<Frag<BF16> *>(smem + F::kPub + (stage * 2 + which) * F::kPubWave);
-    };
-
-    floatx4 Mt[D / 16];
-    const int64_t st_off = sh * D * D + int64_t(vrow) * D + 4 * (lane >> 4);
-    if (is_chain) {
-#pragma unroll
-        for (int kt = 0; kt < D / 16; ++kt) {
-            if (state_in) {
-                const float4 m = *reinterpret_cast<const float4 *>(state_in + st_off + 16 * kt);
-                Mt[kt] = floatx4{m.x, m.y, m.z, m.w};
-            } else {
-                Mt[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-    }
-
-    ScanStage<D, BF16> st;
+    const int64_t tok0 = (s * n_tokens * n_heads + h) * D;
+    ScanPtrs pt;
+    pt.k = static_cast<const unsigned char *>(k) + tok0 * F::ES;
+    pt.q = static_cast<const unsigned char *>(q) + tok0 * F::ES;
+    pt.v = static_cast<const unsigned char *>(v) + (tok0 + v0) * F::ES;
+    pt.ws = ws + sh * n_chunks * W::kBytes;
+    pt.hd_bytes = hd * F::ES;
+    Frag<BF16> *pub = reinterpret_cast<Frag<BF16> *>(smem + F::kPub);
     auto nv_of = [&](int n) { return static_cast<int>(min<int64_t>(C, n_tokens - int64_t(n) * C)); };
-    if constexpr (S == 2) {
-        scan_load<D, BF16>(st, kp, qp, vp, wsh, hd, 0, nv_of(0), tid);
-        for (int n = 0; n <= n_chunks; ++n) {
-            if (n < n_chunks) scan_commit<D, BF16>(st, smem + (n & 1) * F::kStage, nv_of(n), tid);
-            lds_barrier();
-            if (n + 1 < n_chunks)
-                scan_load<D, BF16>(st, kp, qp, vp, wsh + (n + 1) * W::kBytes, hd,
-                                   int64_t(n + 1) * C, nv_of(n + 1), tid);
-            if (is_chain) {
-                if (n < n_chunks)
-                    chain_step<D, BF16>(Mt, smem + (n & 1) * F::kStage, pub_of(n & 1, pair), vcol,
-                                        lane);
-            } else if (n >= 1) {
-                const int m = n - 1;
-                output_step<D, BF16>(smem + (m & 1) * F::kStage, pub_of(m & 1, pair),
-                                     op + int64_t(m) * C * hd, hd, nv_of(m), scale, lane);
-            }
-            lds_barrier();
-        }
-    } else {
+
+    if (wave == 2) {
+        // producer
+        if constexpr (S == 2) scan_issue<D, BF16, VT>(pt, smem, 0, nv_of(0), lane);
         for (int n = 0; n < n_chunks; ++n) {
-            scan_load<D, BF16>(st, kp, qp, vp, wsh + n * W::kBytes, hd, int64_t(n) * C, nv_of(n),
-                               tid);
-            scan_commit<D, BF16>(st, smem, nv_of(n), tid);
-            lds_barrier();
-            if (is_chain) chain_step<D, BF16>(Mt, smem, pub_of(0, pair), vcol, lane);
-            lds_barrier();
-            if (!is_chain)
-                output_step<D, BF16>(smem, pub_of(0, pair), op + int64_t(n) * C * hd, hd, nv_of(n),
-                                     scale, lane);
-            lds_barrier();
+            if constexpr (S == 1) scan_issue<D, BF16, VT>(pt, smem, n, nv_of(n), lane);
+            wait_vmem();
+            lds_barrier();  // A: chunk n is in LDS
+            if constexpr (S == 2) {
+                if (n + 1 < n_chunks)
+                    scan_issue<D, BF16, VT>(pt, smem + ((n + 1) & 1) * F::kStage, n + 1,
+                                            nv_of(n + 1), lane);
+            }
+            lds_barrier();  // B
+            if constexpr (S == 1) lds_barrier();
         }
+        return;
     }
 
-    if (is_chain) {
+    // M^T tiles in accumulator layout: Mt[vt][kt][j] = M[v0 + 16 vt + lane%16][16 kt + 4 g + j]
+    const int64_t st_off = sh * D * D + int64_t(v0 + (lane & 15)) * D + 4 * (lane >> 4);
+    if (wave == 0) {
+        floatx4 Mt[VT][D / 16];
 #pragma unroll
-        for (int kt = 0; kt < D / 16; ++kt)
-            *reinterpret_cast<float4 *>(state_out + st_off + 16 * kt) =
-                make_float4(Mt[kt][0], Mt[kt][1], Mt[kt][2], Mt[kt][3]);
+        for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+            for (int kt = 0; kt < D / 16; ++kt) {
+                if (state_in) {
+                    const float4 m = *reinterpret_cast<const float4 *>(state_in + st_off +
+                                                                       16 * vt * D + 16 * kt);
+                    Mt[vt][kt] = floatx4{m.x, m.y, m.z, m.w};
+                } else {
+                    Mt[vt][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+            for (int ks = 0; ks < F::KS; ++ks)
+                pub[(vt * F::KS + ks) * 64 + lane] = acc_frag<BF16>(Mt[vt][2 * ks], Mt[vt][2 * ks + 1]);
+        for (int n = 0; n < n_chunks; ++n) {
+            const unsigned char *buf = smem + (S == 2 ? (n & 1) : 0) * F::kStage;
+            lds_barrier();  // A: chunk n is in LDS; M^T_n is published
+            floatx4 dl[VT][4], edec[4];
+            float eC;
+            chain_first<D, BF16, VT>(Mt, buf, pub, lane, dl, edec, eC);
+            lds_barrier();  // B: Delta_n is published
+            chain_second<D, BF16, VT>(Mt, buf, pub, lane, dl, edec, eC);
+            if constexpr (S == 1) lds_barrier();
+        }
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+            for (int kt = 0; kt < D / 16; ++kt)
+                *reinterpret_cast<float4 *>(state_out + st_off + 16 * vt * D + 16 * kt) =
+                    make_float4(Mt[vt][kt][0], Mt[vt][kt][1], Mt[vt][kt][2], Mt[vt][kt][3]);
+    } else {
+        E *orow = static_cast<E *>(out) + tok0 + v0 + (lane & 15);
+        for (int n = 0; n < n_chunks; ++n) {
+            const unsigned char *buf = smem + (S == 2 ? (n & 1) : 0) * F::kStage;
+            lds_barrier();  // A
+            floatx4 o[VT][4];
+            output_first<D, BF16, VT>(buf, pub, lane, o);
+            lds_barrier();  // B
+            output_second<D, BF16, VT>(buf, pub, lane, o, orow + int64_t(n) * C * hd, hd, nv_of(n),
+                                       scale);
+            if constexpr (S == 1) lds_barrier();
+        }
     }
 }
 
@@ -839,11 +917,11 @@ hipError_t launch_prep(const Problem &p, unsigned char *ws, int n_chunks, hipStr
     return hipGetLastError();
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, int VT>
 hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, hipStream_t stream)
 {
-    using F = ScanCfg<D, BF16>;
-    auto kern = chunk_scan_kernel<D, BF16>;
+    using F = ScanCfg<D, BF16, VT>;
+    auto kern = chunk_scan_kernel<D, BF16, VT>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -851,7 +929,7 @@ hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, 
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    constexpr int NRB = D / kScanRows;
+    constexpr int NRB = D / F::RW;
     const int64_t n_sh = p.n_seqs * p.n_heads;
     const int64_t blocks = (n_sh + 7) / 8 * 8 * NRB;
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
@@ -861,13 +939,17 @@ hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, 
     return hipGetLastError();
 }
 
+// Scan workgroups hold 16 value rows each while that still leaves at most one
+// workgroup per compute unit (few heads: more parallel chains), else 32.
 template <int D, bool BF16>
 hipError_t launch_chunk_d(const Problem &p, unsigned char *ws, hipStream_t stream)
 {
     const int n_chunks = static_cast<int>((p.n_tokens + C - 1) / C);
     hipError_t e = launch_prep<D, BF16>(p, ws, n_chunks, stream);
     if (e != hipSuccess) return e;
-    return launch_scan<D, BF16>(p, ws, n_chunks, stream);
+    const int64_t n_sh = p.n_seqs * p.n_heads;
+    if (n_sh * (D / 16) <= 256) return launch_scan<D, BF16, 1>(p, ws, n_chunks, stream);
+    return launch_scan<D, BF16, 2>(p, ws, n_chunks, stream);
 }
 
 template <bool BF16>

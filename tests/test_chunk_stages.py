@@ -4,8 +4,8 @@ The chunked algorithm first computes, for every (sequence, head, chunk), the
 state-independent matrices T = (I + A)^{-1} and the decay-masked P, plus the
 per-token gate factors, into the caller's workspace.  This test decodes that
 workspace (its layout is internal to the library and mirrored here: per chunk
-T[64][64] and P[64][64] in the input dtype, then 64 x {beta, e^gam,
-e^(gam_last - gam), e^gam_last} fp32) and compares it with the oracle's stage
+T[64][64] and P[64][64] in the input dtype, then four fp32 rows of 64:
+beta, e^gam, e^(gam_last - gam) and e^gam_last repeated) and compares it with the oracle's stage
 values, so that a parity failure can be attributed to the first or the second
 half of the path.
 """
@@ -30,7 +30,7 @@ def _decode_ws(ws, dtype, n_units):
         m = bits.view(np.float32).reshape(n_units, 2, C, C)
     else:
         m = mats.view(np.float32).reshape(n_units, 2, C, C)
-    gates = raw[:, 2 * C * C * esz:].view(np.float32).reshape(n_units, C, 4)
+    gates = raw[:, 2 * C * C * esz:].view(np.float32).reshape(n_units, 4, C).transpose(0, 2, 1)
     return m[:, 0].astype(np.float64), m[:, 1].astype(np.float64), gates.astype(np.float64)
 
 
