@@ -426,23 +426,24 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
 
 // ---- the chunk-to-chunk scan -----------------------------------------------------
 //
-// One workgroup = three waves for RW = 16 VT value rows of one (seq, head):
+// One workgroup = four waves for RW = 16 VT value rows of one (seq, head):
 //   wave 0  "chain": carries those rows of M^T in registers and per chunk does
 //           X = K M^T, E = beta (V - e^gam X), Delta = T E and the state update --
 //           the serial dependency from chunk to chunk;
 //   wave 1  "output": while the chain wave works on X, E and Delta it forms
 //           e^gam Q M^T from the M^T fragments the chain wave published, then
 //           after a mid-step barrier adds P Delta and stores O;
-//   wave 2  "producer": issues the next chunk's loads (K, Q, T, P, V, gates)
-//           global -> LDS with global_load_lds (16 bytes per lane) into the
-//           stage not in use, and waits for them.
+//   waves 2, 3  "producers": issue the next chunk's loads (K, Q, T, P, V,
+//           gates) global -> LDS with global_load_lds (16 bytes per lane) into
+//           the stage not in use, and wait for them; a compute unit ingests
+//           these loads faster when more than one wave issues them.
 // Each wave sits on its own SIMD.  K, Q, T and P are read from LDS once per
 // workgroup per chunk; LDS rows are padded by 16 bytes so that fragment reads
 // spread over the banks.  Rows past the end of a partial chunk are loaded from
 // the last valid row: the prep kernel gives them beta = e^gam = 0, so they
 // contribute nothing, and finite data keeps 0 * x = 0.
 
-constexpr int kScanThreads = 192;
+constexpr int kScanThreads = 256;
 
 template <int D, bool BF16, int VT>
 struct ScanCfg {
@@ -507,33 +508,34 @@ struct ScanPtrs {
     int64_t hd_bytes;                 // token stride in bytes (64 of them fit in 32 bits)
 };
 
-// Producer wave: issue the LDS-DMA loads of chunk n into stage buffer `buf`.
+// Producer waves: issue the LDS-DMA loads of chunk n into stage buffer `buf`;
+// producer `part` of 2 takes every other 1 KiB block.
 template <int D, bool BF16, int VT>
 __device__ __forceinline__ void scan_issue(const ScanPtrs &pt, unsigned char *buf, int n, int nv,
-                                           int lane)
+                                           int part, int lane)
 {
     using F = ScanCfg<D, BF16, VT>;
     using W = WsLayout<BF16>;
     const int64_t tb = int64_t(n) * C * pt.hd_bytes;
     const uint32_t hdb = static_cast<uint32_t>(pt.hd_bytes);
     const unsigned char *kb = pt.k + tb, *qb = pt.q + tb, *vb = pt.v + tb;
+    const unsigned char *wsc = pt.ws + int64_t(n) * W::kBytes;
+    // K on producer 0, Q on producer 1 (same lane offsets); T/P/V blocks alternate
 #pragma unroll
     for (int blk = 0; blk < F::NBK; ++blk) {
         const uint32_t off = dma_src_offset(blk, lane, D * F::ES, F::RK, hdb, nv);
-        dma16(kb, off, buf + F::kK + 1024 * blk);
-        dma16(qb, off, buf + F::kQ + 1024 * blk);
+        dma16(part == 0 ? kb : qb, off, buf + (part == 0 ? F::kK : F::kQ) + 1024 * blk);
     }
-    const unsigned char *wsc = pt.ws + int64_t(n) * W::kBytes;
 #pragma unroll
     for (int blk = 0; blk < F::NBT; ++blk) {
         const uint32_t off = dma_src_offset(blk, lane, C * F::ES, F::RT, C * F::ES, C);
-        dma16(wsc + W::kT, off, buf + F::kT + 1024 * blk);
-        dma16(wsc + W::kP, off, buf + F::kP + 1024 * blk);
+        dma16(wsc + (part == 0 ? W::kT : W::kP), off, buf + (part == 0 ? F::kT : F::kP) + 1024 * blk);
     }
 #pragma unroll
     for (int blk = 0; blk < F::NBV; ++blk)
-        dma16(vb, dma_src_offset(blk, lane, F::RW * F::ES, F::RV, hdb, nv), buf + F::kV + 1024 * blk);
-    dma16(wsc + W::kGates, 16u * lane, buf + F::kG);
+        if ((blk & 1) == part)
+            dma16(vb, dma_src_offset(blk, lane, F::RW * F::ES, F::RV, hdb, nv), buf + F::kV + 1024 * blk);
+    if (part == (F::NBV & 1)) dma16(wsc + W::kGates, 16u * lane, buf + F::kG);
 }
 
 // Fragment loaders on the padded LDS layout.  A operand row `row`, k elements
@@ -612,12 +614,14 @@ __device__ __forceinline__ floatx4 col4(const unsigned char *base, int stride, i
     return r;
 }
 
-// Chain wave, first half of a step: X = K M^T, E, Delta = T E for VT tiles of
-// 16 value rows; publishes Delta.  Also returns the gate rows it read.
+// Chain wave, one chunk.  All LDS reads of the step (K rows, T, gates, V and the
+// transposed K for the update) are issued first; then X = K M^T, E = beta (V -
+// e^gam X), Delta = T E (published, then barrier B for the output wave) and the
+// state update M^T <- e^{gam_last} M^T + K^T diag(e^{gam_last - gam}) Delta,
+// whose new fragments are published for the next step.
 template <int D, bool BF16, int VT>
-__device__ __forceinline__ void chain_first(const floatx4 (&Mt)[VT][D / 16],
-                                            const unsigned char *buf, Frag<BF16> *pub, int lane,
-                                            floatx4 (&dl)[VT][4], floatx4 (&edec)[4], float &eC)
+__device__ __forceinline__ void chain_step(floatx4 (&Mt)[VT][D / 16], const unsigned char *buf,
+                                           Frag<BF16> *pub, int lane)
 {
     using F = ScanCfg<D, BF16, VT>;
     constexpr int KS = F::KS;
@@ -634,7 +638,7 @@ __device__ __forceinline__ void chain_first(const floatx4 (&Mt)[VT][D / 16],
         at[tt] = frag_rows<BF16>(buf + F::kT, F::RT, 16 * tt + cl, 0, gq);
         if (tt >= 2) at[2 + tt] = frag_rows<BF16>(buf + F::kT, F::RT, 16 * tt + cl, 32, gq);
     }
-    floatx4 bt[4], eg[4];
+    floatx4 bt[4], eg[4], edec[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         const int t = 16 * tt + 4 * gq;
@@ -645,12 +649,22 @@ __device__ __forceinline__ void chain_first(const floatx4 (&Mt)[VT][D / 16],
         eg[tt] = floatx4{e4.x, e4.y, e4.z, e4.w};
         edec[tt] = floatx4{d4.x, d4.y, d4.z, d4.w};
     }
-    eC = sG[3 * C];
+    const float eC = sG[3 * C];
+    floatx4 vv[VT][4];
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) vv[vt][tt] = col4<BF16>(buf + F::kV, F::RV, 16 * tt, 16 * vt, lane);
+    Frag<BF16> akt[D / 16][2];
+#pragma unroll
+    for (int kt = 0; kt < D / 16; ++kt) {
+        akt[kt][0] = frag_cols<BF16>(buf + F::kK, F::RK, 0, 16 * kt, lane);
+        akt[kt][1] = frag_cols<BF16>(buf + F::kK, F::RK, 32, 16 * kt, lane);
+    }
+
+    floatx4 dl[VT][4];
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
-        floatx4 vv[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) vv[tt] = col4<BF16>(buf + F::kV, F::RV, 16 * tt, 16 * vt, lane);
         Frag<BF16> bm[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) bm[ks] = acc_frag<BF16>(Mt[vt][2 * ks], Mt[vt][2 * ks + 1]);
@@ -665,7 +679,7 @@ __device__ __forceinline__ void chain_first(const floatx4 (&Mt)[VT][D / 16],
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) e[tt][j] = bt[tt][j] * fmaf(-eg[tt][j], xk[tt][j], vv[tt][j]);
+            for (int j = 0; j < 4; ++j) e[tt][j] = bt[tt][j] * fmaf(-eg[tt][j], xk[tt][j], vv[vt][tt][j]);
         const Frag<BF16> be0 = acc_frag<BF16>(e[0], e[1]);
         const Frag<BF16> be1 = acc_frag<BF16>(e[2], e[3]);
 #pragma unroll
@@ -675,17 +689,7 @@ __device__ __forceinline__ void chain_first(const floatx4 (&Mt)[VT][D / 16],
         pub[(VT * KS + 2 * vt) * 64 + lane] = acc_frag<BF16>(dl[vt][0], dl[vt][1]);
         pub[(VT * KS + 2 * vt + 1) * 64 + lane] = acc_frag<BF16>(dl[vt][2], dl[vt][3]);
     }
-}
-
-// Chain wave, second half: M^T <- e^{gam_last} M^T + K^T diag(e^{gam_last - gam})
-// Delta; publishes the new M^T fragments for the next step.
-template <int D, bool BF16, int VT>
-__device__ __forceinline__ void chain_second(floatx4 (&Mt)[VT][D / 16], const unsigned char *buf,
-                                             Frag<BF16> *pub, int lane, const floatx4 (&dl)[VT][4],
-                                             const floatx4 (&edec)[4], float eC)
-{
-    using F = ScanCfg<D, BF16, VT>;
-    constexpr int KS = F::KS;
+    lds_barrier();  // B: Delta_n is published
     Frag<BF16> bs[VT][2];
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
@@ -696,15 +700,13 @@ __device__ __forceinline__ void chain_second(floatx4 (&Mt)[VT][D / 16], const un
         bs[vt][1] = acc_frag<BF16>(ds[2], ds[3]);
     }
 #pragma unroll
-    for (int kt = 0; kt < D / 16; ++kt) {
-        const Frag<BF16> a0 = frag_cols<BF16>(buf + F::kK, F::RK, 0, 16 * kt, lane);
-        const Frag<BF16> a1 = frag_cols<BF16>(buf + F::kK, F::RK, 32, 16 * kt, lane);
+    for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
-        for (int vt = 0; vt < VT; ++vt) {
-            Mt[vt][kt] = mma(a0, bs[vt][0], Mt[vt][kt] * eC);
-            Mt[vt][kt] = mma(a1, bs[vt][1], Mt[vt][kt]);
-        }
-    }
+        for (int kt = 0; kt < D / 16; ++kt) Mt[vt][kt] = mma(akt[kt][0], bs[vt][0], Mt[vt][kt] * eC);
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+        for (int kt = 0; kt < D / 16; ++kt) Mt[vt][kt] = mma(akt[kt][1], bs[vt][1], Mt[vt][kt]);
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
@@ -712,12 +714,17 @@ __device__ __forceinline__ void chain_second(floatx4 (&Mt)[VT][D / 16], const un
             pub[(vt * KS + ks) * 64 + lane] = acc_frag<BF16>(Mt[vt][2 * ks], Mt[vt][2 * ks + 1]);
 }
 
-// Output wave, first half: e^gam Q M^T for the chunk (M^T from the publication).
+// Output wave, one chunk: reads Q, P and gates, forms e^gam Q M^T from the
+// published M^T fragments, waits at barrier B for Delta, adds P Delta and stores
+// O / sqrt(d) for valid tokens.  orow points at out[(s, first token of the chunk,
+// h, first value row + lane%16)].
 template <int D, bool BF16, int VT>
-__device__ __forceinline__ void output_first(const unsigned char *buf, const Frag<BF16> *pub,
-                                             int lane, floatx4 (&o)[VT][4])
+__device__ __forceinline__ void output_step(const unsigned char *buf, const Frag<BF16> *pub,
+                                            int lane, typename Elem<BF16>::T *orow, int64_t hd,
+                                            int nv, float scale)
 {
     using F = ScanCfg<D, BF16, VT>;
+    using E = typename Elem<BF16>::T;
     constexpr int KS = F::KS;
     const int gq = lane >> 4, cl = lane & 15;
     const float *sG = reinterpret_cast<const float *>(buf + F::kG);
@@ -727,12 +734,19 @@ __device__ __forceinline__ void output_first(const unsigned char *buf, const Fra
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             aq[tt][ks] = frag_rows<BF16>(buf + F::kQ, F::RK, 16 * tt + cl, 32 * ks, gq);
+    Frag<BF16> ap[6];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        ap[tt] = frag_rows<BF16>(buf + F::kP, F::RT, 16 * tt + cl, 0, gq);
+        if (tt >= 2) ap[2 + tt] = frag_rows<BF16>(buf + F::kP, F::RT, 16 * tt + cl, 32, gq);
+    }
     floatx4 eg[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         const float4 e4 = *reinterpret_cast<const float4 *>(sG + C + 16 * tt + 4 * gq);
         eg[tt] = floatx4{e4.x, e4.y, e4.z, e4.w};
     }
+    floatx4 o[VT][4];
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
         Frag<BF16> bm[KS];
@@ -748,26 +762,7 @@ __device__ __forceinline__ void output_first(const unsigned char *buf, const Fra
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) o[vt][tt] = eg[tt] * xq[tt];
     }
-}
-
-// Output wave, second half: O = (o + P Delta) / sqrt(d), stored for valid tokens.
-// orow points at out[(s, first token of the chunk, h, first value row + lane%16)].
-template <int D, bool BF16, int VT>
-__device__ __forceinline__ void output_second(const unsigned char *buf, const Frag<BF16> *pub,
-                                              int lane, floatx4 (&o)[VT][4],
-                                              typename Elem<BF16>::T *orow, int64_t hd, int nv,
-                                              float scale)
-{
-    using F = ScanCfg<D, BF16, VT>;
-    using E = typename Elem<BF16>::T;
-    constexpr int KS = F::KS;
-    const int gq = lane >> 4, cl = lane & 15;
-    Frag<BF16> ap[6];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        ap[tt] = frag_rows<BF16>(buf + F::kP, F::RT, 16 * tt + cl, 0, gq);
-        if (tt >= 2) ap[2 + tt] = frag_rows<BF16>(buf + F::kP, F::RT, 16 * tt + cl, 32, gq);
-    }
+    lds_barrier();  // B: Delta_n is published
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
         const Frag<BF16> bd0 = pub[(VT * KS + 2 * vt) * 64 + lane];
@@ -829,17 +824,18 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     Frag<BF16> *pub = reinterpret_cast<Frag<BF16> *>(smem + F::kPub);
     auto nv_of = [&](int n) { return static_cast<int>(min<int64_t>(C, n_tokens - int64_t(n) * C)); };
 
-    if (wave == 2) {
-        // producer
-        if constexpr (S == 2) scan_issue<D, BF16, VT>(pt, smem, 0, nv_of(0), lane);
+    if (wave >= 2) {
+        // producers
+        const int part = wave - 2;
+        if constexpr (S == 2) scan_issue<D, BF16, VT>(pt, smem, 0, nv_of(0), part, lane);
         for (int n = 0; n < n_chunks; ++n) {
-            if constexpr (S == 1) scan_issue<D, BF16, VT>(pt, smem, n, nv_of(n), lane);
+            if constexpr (S == 1) scan_issue<D, BF16, VT>(pt, smem, n, nv_of(n), part, lane);
             wait_vmem();
             lds_barrier();  // A: chunk n is in LDS
             if constexpr (S == 2) {
                 if (n + 1 < n_chunks)
                     scan_issue<D, BF16, VT>(pt, smem + ((n + 1) & 1) * F::kStage, n + 1,
-                                            nv_of(n + 1), lane);
+                                            nv_of(n + 1), part, lane);
             }
             lds_barrier();  // B
             if constexpr (S == 1) lds_barrier();
@@ -871,11 +867,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
         for (int n = 0; n < n_chunks; ++n) {
             const unsigned char *buf = smem + (S == 2 ? (n & 1) : 0) * F::kStage;
             lds_barrier();  // A: chunk n is in LDS; M^T_n is published
-            floatx4 dl[VT][4], edec[4];
-            float eC;
-            chain_first<D, BF16, VT>(Mt, buf, pub, lane, dl, edec, eC);
-            lds_barrier();  // B: Delta_n is published
-            chain_second<D, BF16, VT>(Mt, buf, pub, lane, dl, edec, eC);
+            chain_step<D, BF16, VT>(Mt, buf, pub, lane);  // contains barrier B
             if constexpr (S == 1) lds_barrier();
         }
 #pragma unroll
@@ -889,11 +881,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
         for (int n = 0; n < n_chunks; ++n) {
             const unsigned char *buf = smem + (S == 2 ? (n & 1) : 0) * F::kStage;
             lds_barrier();  // A
-            floatx4 o[VT][4];
-            output_first<D, BF16, VT>(buf, pub, lane, o);
-            lds_barrier();  // B
-            output_second<D, BF16, VT>(buf, pub, lane, o, orow + int64_t(n) * C * hd, hd, nv_of(n),
-                                       scale);
+            output_step<D, BF16, VT>(buf, pub, lane, orow + int64_t(n) * C * hd, hd, nv_of(n),
+                                     scale);  // contains barrier B
             if constexpr (S == 1) lds_barrier();
         }
     }
