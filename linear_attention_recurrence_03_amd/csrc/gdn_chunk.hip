@@ -200,18 +200,50 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// ---- fragment blocks -------------------------------------------------------------
+// A fragment block is the image of one 16-row x 32-k A operand, laid out so that
+// each lane's fragment is one contiguous unit (its eight elements: 16 bytes for
+// bf16, 32 for fp32) and a wave's read of the whole operand touches every LDS
+// bank equally: the unit of row r for lane group g sits at position
+// 4 r + (g ^ (r >> 2)).  Inside a unit the elements follow the fragment k order
+// (4g+j for j < 4, 16+4g+j-4 for j >= 4), so the block multiplies B operands
+// built from accumulator tiles.  The lower-triangular T and P are stored as the
+// six blocks (row tile tt, k half h) with 32 h <= 16 tt + 15, in the order
+// (0,0) (1,0) (2,0) (2,1) (3,0) (3,1); the other two are zero.
+template <bool BF16>
+constexpr int kFragBytes = BF16 ? 16 : 32;
+template <bool BF16>
+constexpr int kBlkBytes = 64 * kFragBytes<BF16>;
+
+__device__ __forceinline__ int blk_unit(int r, int g) { return 4 * r + (g ^ (r >> 2)); }
+
+template <bool BF16>
+__device__ __forceinline__ Frag<BF16> frag_blk(const unsigned char *blk, int lane)
+{
+    return *reinterpret_cast<const Frag<BF16> *>(blk + kFragBytes<BF16> * blk_unit(lane & 15, lane >> 4));
+}
+
+// Byte offset of element (r, c), c < 32 (r / 32 + 1), in a triangular block image.
+template <bool BF16>
+__device__ __forceinline__ int tri_offset(int r, int c)
+{
+    const int tt = r >> 4, i = r & 15, h = c >> 5, kk = c & 31;
+    const int b = tt < 2 ? tt : 2 * tt - 2 + h;
+    const int g = (kk & 15) >> 2, j = (kk & 3) + ((kk >> 4) << 2);
+    return b * kBlkBytes<BF16> + kFragBytes<BF16> * blk_unit(i, g) + j * (BF16 ? 2 : 4);
+}
+
 // ---- workspace layout, per (seq, head, chunk) ----------------------------------
-//   T     [C][C] elements   (fp32 or bf16, like q/k/v)
-//   P     [C][C] elements
+//   T     six fragment blocks (elements like q/k/v: fp32 or bf16)
+//   P     six fragment blocks
 //   gates [4][C] fp32: beta_r, e^{gam_r}, e^{gam_last - gam_r}, then e^{gam_last}
 //                      repeated C times
 // Rows past the end of a partial last chunk carry beta = e^gam = 0, so they add
 // nothing to the state or to valid outputs.
 template <bool BF16>
 struct WsLayout {
-    using E = typename Elem<BF16>::T;
     static constexpr int64_t kT = 0;
-    static constexpr int64_t kP = int64_t(C) * C * sizeof(E);
+    static constexpr int64_t kP = 6 * kBlkBytes<BF16>;
     static constexpr int64_t kGates = 2 * kP;
     static constexpr int64_t kBytes = kGates + 4 * C * 4;
 };
@@ -238,12 +270,6 @@ __device__ __forceinline__ void lower_tile(int ix, int &tr, int &tc)
     tc = ix - tr * (tr + 1) / 2;
 }
 
-// Upper 16x16 tiles (tr < tc), fixed order.
-__device__ __forceinline__ void upper_tile(int ix, int &tr, int &tc)
-{
-    tr = (ix >= 5) ? 2 : (ix >= 3) ? 1 : 0;
-    tc = tr + 1 + (ix - (tr == 0 ? 0 : tr == 1 ? 3 : 5));
-}
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
@@ -270,7 +296,6 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const int64_t t0 = int64_t(n) * C;
     const int nv = static_cast<int>(min<int64_t>(C, n_tokens - t0));
     unsigned char *dst = ws + chunk_id * W::kBytes;
-    E *wT = reinterpret_cast<E *>(dst + W::kT);
     E *wP = reinterpret_cast<E *>(dst + W::kP);
 
     // 1. K and Q rows of the chunk (zero past the end of the sequence)
@@ -353,7 +378,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     } else {
         // 3b (other waves, meanwhile). P = e^{gam_r - gam_s} Q K^T (lower incl.
         //    diagonal), written straight from the accumulators; upper tiles zero.
-        for (int job = wave - 1; job < 16; job += kPrepThreads / 64 - 1) {
+        for (int job = wave - 1; job < 12; job += kPrepThreads / 64 - 1) {
             int tr, tc;
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
             if (job < 10) {
@@ -367,14 +392,16 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
 #pragma unroll
                 for (int ks = 0; ks < D / 32; ++ks) acc = mma(fa[ks], fb[ks], acc);
             } else {
-                upper_tile(job - 10, tr, tc);
+                tr = job == 10 ? 0 : 2;  // upper tiles (0,1) and (2,3): zeros inside stored blocks
+                tc = tr + 1;
             }
             const int col = 16 * tc + cl;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * tr + 4 * gq + j;
                 const float pv = (col <= row) ? __expf(sG[row] - sG[col]) * acc[j] : 0.f;
-                wP[row * C + col] = from_f<E>(pv);
+                *reinterpret_cast<E *>(reinterpret_cast<unsigned char *>(wP) + tri_offset<BF16>(row, col)) =
+                    from_f<E>(pv);
             }
         }
     }
@@ -404,16 +431,24 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
         lds_barrier();
     }
 
-    // 5. T (upper triangle as zeros) and gates to the workspace
-    for (int i = tid; i < C * C / VE; i += kPrepThreads) {
-        const int r = (i * VE) / C, c0 = (i * VE) % C;
-        E vt[VE];
+    // 5. T as six fragment blocks (zeros above the diagonal), then the gates
+    constexpr int FB = kFragBytes<BF16>;
+    for (int u = tid; u < 6 * 64; u += kPrepThreads) {
+        const int b = u >> 6, p = u & 63;
+        const int tt = b < 2 ? b : 2 + ((b - 2) >> 1), hh = b < 2 ? 0 : (b - 2) & 1;
+        const int i = p >> 2, gg = (p & 3) ^ (i >> 2);
+        const int r = 16 * tt + i;
+        E vt[8];
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            const int c = c0 + e;
+        for (int e = 0; e < 8; ++e) {
+            const int c = 32 * hh + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
             vt[e] = from_f<E>(c <= r ? sT[r * LDA + c] : 0.f);
         }
-        *reinterpret_cast<uint4 *>(wT + i * VE) = *reinterpret_cast<const uint4 *>(vt);
+        uint4 w[FB / 16];
+        __builtin_memcpy(w, vt, FB);
+        uint4 *ub = reinterpret_cast<uint4 *>(dst + W::kT + b * kBlkBytes<BF16> + FB * p);
+#pragma unroll
+        for (int x = 0; x < FB / 16; ++x) ub[x] = w[x];
     }
     float *wG = reinterpret_cast<float *>(dst + W::kGates);
     if (tid < C) {
@@ -426,73 +461,146 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
 
 // ---- the chunk-to-chunk scan -----------------------------------------------------
 //
-// One workgroup = four waves for RW = 16 VT value rows of one (seq, head):
-//   wave 0  "chain": carries those rows of M^T in registers and per chunk does
-//           X = K M^T, E = beta (V - e^gam X), Delta = T E and the state update --
-//           the serial dependency from chunk to chunk;
-//   wave 1  "output": while the chain wave works on X, E and Delta it forms
-//           e^gam Q M^T from the M^T fragments the chain wave published, then
-//           after a mid-step barrier adds P Delta and stores O;
-//   waves 2, 3  "producers": issue the next chunk's loads (K, Q, T, P, V,
-//           gates) global -> LDS with global_load_lds (16 bytes per lane) into
-//           the stage not in use, and wait for them; a compute unit ingests
-//           these loads faster when more than one wave issues them.
-// Each wave sits on its own SIMD.  K, Q, T and P are read from LDS once per
-// workgroup per chunk; LDS rows are padded by 16 bytes so that fragment reads
-// spread over the banks.  Rows past the end of a partial chunk are loaded from
-// the last valid row: the prep kernel gives them beta = e^gam = 0, so they
-// contribute nothing, and finite data keeps 0 * x = 0.
+// One workgroup handles RW = 16 VT value rows of one (seq, head) and walks the
+// chunks in order.  Value tile vt (16 rows) has three waves of its own:
+//   X_vt  X = K M_n^T, E = beta (V - e^gam X), Delta = T E; publishes Delta (for
+//         the output) and diag(e^{gam_last - gam}) Delta (for the update);
+//   U_vt  holds its rows of M^T in fp32 and applies
+//         M^T <- e^{gam_last} M^T + K^T (scaled Delta), publishing the new M^T
+//         as B-operand fragment blocks;
+//   O_vt  e^gam Q M_n^T, then + P Delta, staged through LDS and stored as
+//         O / sqrt(d) with 16-byte stores;
+// and four producer waves move the chunk data global -> LDS with
+// global_load_lds (16 bytes per lane; a compute unit ingests faster the more
+// waves keep such loads in flight).
+//
+// Two workgroup barriers per chunk n split the dependency chain between X and U,
+// so that each one's LDS operand reads are done while the other computes:
+//   A_n  M^T_n published                       X, O: products with M^T_n
+//   B_n  Delta_n published                     U: state update; O: P Delta
+// Between B_{n-1} and A_n, X reads its operands of chunk n into registers;
+// between A_n and B_n, U reads its transposed K and O its Q and P of chunk n.
+// Chunk data live in rings of SK (K, T, V, gates) and SQ (Q, P) slots, chunk m
+// in slot m mod S.  The K/T slot of chunk m is read during [B_{m-1}, B_m) and
+// refilled with chunk m+SK from B_m on; the Q/P slot is read during [A_m, B_m)
+// and refilled with chunk m+SQ from A_{m+1} on.  A load thus has SK - 1 (SQ - 1)
+// chunk steps to land, and the two kinds of loads are issued half a step apart.  The fp32 variant (parity path) keeps
+// one slot of each: a third barrier L_n per chunk marks the slot as loaded and
+// the phases of a chunk run back to back.
+//
+// K and Q rows are padded by 16 bytes, which makes both the 16-byte row reads
+// (k order 8g..8g+7 per lane group, matched by the key order of the published
+// M^T blocks) and the transposing reads of K spread over the LDS banks.  T and
+// P arrive as fragment blocks.  Rows past the end of a partial chunk are loaded
+// from the last valid row: the prep kernel gives them beta = e^gam = 0, so they
+// contribute nothing, and the data stay finite so that 0 * x = 0.
 
-constexpr int kScanThreads = 256;
+constexpr int kProducers = 4;
 
 template <int D, bool BF16, int VT>
 struct ScanCfg {
+    static_assert(VT == 1 || VT == 2, "one or two value tiles per workgroup");
     using E = typename Elem<BF16>::T;
-    static constexpr int RW = 16 * VT;               // value rows per workgroup
-    static constexpr int kStages = BF16 ? 2 : 1;
+    static constexpr bool PIPE = BF16;
+    static constexpr int RW = 16 * VT;              // value rows per workgroup
     static constexpr int ES = sizeof(E);
-    static constexpr int RK = D * ES + 16;          // sK, sQ row stride (bytes)
-    static constexpr int RT = C * ES + 16;          // sT, sP row stride
-    static constexpr int RV = RW * ES + 16;         // sV row stride
-    static constexpr int kK = 0;
-    static constexpr int kQ = kK + C * RK;
-    static constexpr int kT = kQ + C * RK;
-    static constexpr int kP = kT + C * RT;
-    static constexpr int kV = kP + C * RT;
-    static constexpr int kG = kV + C * RV;
-    static constexpr int kStage = (kG + 4 * C * 4 + 1023) / 1024 * 1024;
     static constexpr int KS = D / 32;
-    static constexpr int kFrags = (KS + 2) * VT;    // M^T and Delta fragments
-    static constexpr int kPub = kStages * kStage;
-    static constexpr int kBytes = kPub + 64 * kFrags * int(sizeof(Frag<BF16>));
-    static_assert(kBytes <= 160 * 1024, "LDS budget");
-    // 1 KiB LDS-DMA blocks per region (64 padded rows are a whole number of blocks)
+    static constexpr int FB = kFragBytes<BF16>;
+    static constexpr int BLK = kBlkBytes<BF16>;
+    static constexpr int RK = D * ES + 16;          // K, Q row stride (bytes)
+    static constexpr int RV = RW * ES + 16;         // V row stride
+    // K/T/V/gates slot
+    static constexpr int kK = 0;
+    static constexpr int kT = kK + C * RK;
+    static constexpr int kV = kT + 6 * BLK;
+    static constexpr int kG = kV + C * RV;
+    static constexpr int kSlotKT = kG + 1024;
+    // Q/P slot
+    static constexpr int kQ = 0;
+    static constexpr int kP = kQ + C * RK;
+    static constexpr int kSlotQP = kP + 6 * BLK;
+    // published values: M^T blocks, Delta and scaled Delta (accumulator-pair
+    // fragments), output staging [C][16] per value tile
+    static constexpr int kPubBytes = VT * KS * BLK + 4 * VT * 64 * FB + VT * C * 16 * ES;
+    static constexpr int kLds = 160 * 1024;
+    static constexpr bool fits(int sk, int sq) { return sk * kSlotKT + sq * kSlotQP + kPubBytes <= kLds; }
+    static constexpr int SK = !PIPE ? 1 : fits(3, 2) ? 3 : 2;
+    static constexpr int SQ = !PIPE ? 1 : fits(3, 3) ? 3 : 2;
+    static constexpr int kRingKT = 0;
+    static constexpr int kRingQP = kRingKT + SK * kSlotKT;
+    static constexpr int kPubM = kRingQP + SQ * kSlotQP;
+    static constexpr int kPubD = kPubM + VT * KS * BLK;
+    static constexpr int kPubS = kPubD + 2 * VT * 64 * FB;
+    static constexpr int kOut = kPubS + 2 * VT * 64 * FB;
+    static constexpr int kBytes = kOut + VT * C * 16 * ES;
+    static_assert(kBytes <= kLds, "LDS budget");
+    // 1 KiB DMA blocks.  The regions of a slot are contiguous multiples of 1 KiB,
+    // so block i of a slot's list lands at slot + 1024 i.
     static constexpr int NBK = C * RK / 1024;
-    static constexpr int NBT = C * RT / 1024;
+    static constexpr int NBT = 6 * BLK / 1024;
     static constexpr int NBV = C * RV / 1024;
-    static_assert(C * RK % 1024 == 0 && C * RT % 1024 == 0 && C * RV % 1024 == 0, "blocks");
+    static_assert(C * RK % 1024 == 0 && C * RV % 1024 == 0, "blocks");
+    static constexpr int NKT = NBK + NBT + NBV + 1;  // K, T, V, gates
+    static constexpr int NQP = NBK + NBT;            // Q, P
+    // producer p takes blocks p, p + 4, ...: its instruction counts
+    static constexpr int nkt(int p) { return (NKT + kProducers - 1 - p) / kProducers; }
+    static constexpr int nqp(int p) { return (NQP + kProducers - 1 - p) / kProducers; }
+    // Issue times (barrier A_j = time 2j, B_j = 2j + 1): right after A_j the
+    // producers issue Q/P of chunk j + SQ - 1, right after B_j K/T of chunk j + SK;
+    // the prologue issues the events of times t < 0 that have a chunk >= 0.
+    static constexpr int qp_chunk(int t) { return t / 2 + SQ - 1; }          // t even
+    static constexpr int kt_chunk(int t) { return (t - 1) / 2 + SK; }        // t odd
+    // Number of a producer's load instructions issued at times in (lo, hi] for
+    // chunks >= 0 (assuming every such chunk < n_chunks).
+    static constexpr int issued(int lo, int hi, int p)
+    {
+        int c = 0;
+        for (int t = lo + 1; t <= hi; ++t) {
+            if (t % 2 == 0)
+                c += qp_chunk(t) >= 0 ? nqp(p) : 0;
+            else
+                c += kt_chunk(t) >= 0 ? nkt(p) : 0;
+        }
+        return c;
+    }
+    // Loads that may stay in flight at each wait, counted at n = 0 (a later n's
+    // windows hold at least as many loads, so these counts stay safe):
+    //   before B_{-1}: K/T of chunk 0 (issued at time 1 - 2 SK) has landed;
+    //   before A_n:    Q/P of chunk n (issued at 2n + 2 - 2 SQ) has landed;
+    //   before B_n:    K/T of chunk n+1 (issued at 2n + 3 - 2 SK) has landed.
+    static constexpr int wait_prologue(int p) { return issued(1 - 2 * SK, -1, p); }
+    static constexpr int wait_a(int p) { return issued(2 - 2 * SQ, -1, p); }
+    static constexpr int wait_b(int p) { return issued(3 - 2 * SK, 0, p); }
+    static_assert(wait_prologue(0) < 64 && wait_a(0) < 64 && wait_b(0) < 64, "vmcnt range");
+    static_assert(qp_chunk(2 - 2 * SQ) == 0 && kt_chunk(1 - 2 * SK) == 0, "issue times");
+    static constexpr int kWaves = 3 * VT + kProducers;  // also in chunk_scan_kernel's launch bounds
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void global_cvoid;
 
 // One 16-byte-per-lane LDS-DMA: lane l's 16 bytes (from base + off) land at
-// lds + 16 l.  base is wave-uniform; off is a 32-bit per-lane byte offset.
+// lds + 16 l.  base and lds are wave-uniform; off is a per-lane byte offset.
 __device__ __forceinline__ void dma16(const unsigned char *base, uint32_t off, void *lds)
 {
     __builtin_amdgcn_global_load_lds((global_cvoid *)(base + off), (lds_void *)(lds), 16, 0, 0);
 }
 
-// Wait for this wave's outstanding global loads (LDS-DMA included).
-__device__ __forceinline__ void wait_vmem()
+// Wait until at most N of this wave's global loads (LDS-DMA included) are
+// outstanding; they complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le()
 {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unconstrained
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // s_waitcnt fields: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8]
+    // (15 = no wait), vmcnt[5:4] in bits 15:14
+    __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
 }
 
 // Byte offset, inside one chunk's data, of the 16 bytes lane `lane` loads for LDS
 // block `blk` of a padded region: rows of `rowb` valid bytes stored with stride
-// `stride`; pad slots read row 0.  `gstride` is the source row stride; rows past
-// nv read row nv - 1.
+// `stride`; pad slots read offset 0.  `gstride` is the source row stride; rows at
+// or past nv read row nv - 1.
 __device__ __forceinline__ uint32_t dma_src_offset(int blk, int lane, int rowb, int stride,
                                                    uint32_t gstride, int nv)
 {
@@ -502,67 +610,85 @@ __device__ __forceinline__ uint32_t dma_src_offset(int blk, int lane, int rowb, 
     return b < rowb ? v : 0u;
 }
 
+// Workgroup barrier for the producer waves.  Their only LDS writes are the
+// LDS-DMA loads, and a release fence would wait for every one of them to land
+// (vmcnt 0), draining the prefetch pipeline at each barrier.  Instead each
+// producer waits explicitly (wait_vmem_le) for exactly the loads that the
+// barrier publishes; the loads still in flight write slots that no other wave
+// reads before a later barrier.
+__device__ __forceinline__ void dma_barrier() { __builtin_amdgcn_s_barrier(); }
+
 struct ScanPtrs {
     const unsigned char *k, *q, *v;   // token 0 of this (seq, head); v at the first value row
     const unsigned char *ws;          // this (seq, head)'s chunk 0 in the workspace
     int64_t hd_bytes;                 // token stride in bytes (64 of them fit in 32 bits)
 };
 
-// Producer waves: issue the LDS-DMA loads of chunk n into stage buffer `buf`;
-// producer `part` of 2 takes every other 1 KiB block.
-template <int D, bool BF16, int VT>
-__device__ __forceinline__ void scan_issue(const ScanPtrs &pt, unsigned char *buf, int n, int nv,
-                                           int part, int lane)
+// Producer PART's blocks of chunk n's K, T, V and gates.
+template <int D, bool BF16, int VT, int PART>
+__device__ __forceinline__ void issue_kt(const ScanPtrs &pt, unsigned char *slot, int n, int nv,
+                                        int lane)
 {
     using F = ScanCfg<D, BF16, VT>;
     using W = WsLayout<BF16>;
     const int64_t tb = int64_t(n) * C * pt.hd_bytes;
     const uint32_t hdb = static_cast<uint32_t>(pt.hd_bytes);
-    const unsigned char *kb = pt.k + tb, *qb = pt.q + tb, *vb = pt.v + tb;
     const unsigned char *wsc = pt.ws + int64_t(n) * W::kBytes;
-    // K on producer 0, Q on producer 1 (same lane offsets); T/P/V blocks alternate
 #pragma unroll
-    for (int blk = 0; blk < F::NBK; ++blk) {
-        const uint32_t off = dma_src_offset(blk, lane, D * F::ES, F::RK, hdb, nv);
-        dma16(part == 0 ? kb : qb, off, buf + (part == 0 ? F::kK : F::kQ) + 1024 * blk);
+    for (int i = PART; i < F::NKT; i += kProducers) {
+        uint32_t off;
+        const unsigned char *base;
+        if (i < F::NBK) {
+            base = pt.k + tb;
+            off = dma_src_offset(i, lane, D * F::ES, F::RK, hdb, nv);
+        } else if (i < F::NBK + F::NBT) {
+            base = wsc + W::kT;
+            off = 1024u * (i - F::NBK) + 16u * lane;
+        } else if (i < F::NBK + F::NBT + F::NBV) {
+            base = pt.v + tb;
+            off = dma_src_offset(i - F::NBK - F::NBT, lane, F::RW * F::ES, F::RV, hdb, nv);
+        } else {
+            base = wsc + W::kGates;
+            off = 16u * lane;
+        }
+        dma16(base, off, slot + 1024 * i);
     }
-#pragma unroll
-    for (int blk = 0; blk < F::NBT; ++blk) {
-        const uint32_t off = dma_src_offset(blk, lane, C * F::ES, F::RT, C * F::ES, C);
-        dma16(wsc + (part == 0 ? W::kT : W::kP), off, buf + (part == 0 ? F::kT : F::kP) + 1024 * blk);
-    }
-#pragma unroll
-    for (int blk = 0; blk < F::NBV; ++blk)
-        if ((blk & 1) == part)
-            dma16(vb, dma_src_offset(blk, lane, F::RW * F::ES, F::RV, hdb, nv), buf + F::kV + 1024 * blk);
-    if (part == (F::NBV & 1)) dma16(wsc + W::kGates, 16u * lane, buf + F::kG);
 }
 
-// Fragment loaders on the padded LDS layout.  A operand row `row`, k elements
-// k0 + {4g..4g+3} and k0 + 16 + {4g..4g+3}.
-template <bool BF16>
-__device__ __forceinline__ Frag<BF16> frag_rows(const unsigned char *base, int stride, int row,
-                                                int k0, int g)
+// Producer PART's blocks of chunk n's Q and P.
+template <int D, bool BF16, int VT, int PART>
+__device__ __forceinline__ void issue_qp(const ScanPtrs &pt, unsigned char *slot, int n, int nv,
+                                        int lane)
 {
-    Frag<BF16> f;
-    constexpr int ES = BF16 ? 2 : 4;
-    const unsigned char *p = base + row * stride + (k0 + 4 * g) * ES;
-    if constexpr (BF16) {
-        const uint2 lo = *reinterpret_cast<const uint2 *>(p);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(p + 32);
-        f.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    } else {
-        const float4 lo = *reinterpret_cast<const float4 *>(p);
-        const float4 hi = *reinterpret_cast<const float4 *>(p + 64);
-        f.v[0] = lo.x; f.v[1] = lo.y; f.v[2] = lo.z; f.v[3] = lo.w;
-        f.v[4] = hi.x; f.v[5] = hi.y; f.v[6] = hi.z; f.v[7] = hi.w;
+    using F = ScanCfg<D, BF16, VT>;
+    using W = WsLayout<BF16>;
+    const int64_t tb = int64_t(n) * C * pt.hd_bytes;
+    const uint32_t hdb = static_cast<uint32_t>(pt.hd_bytes);
+    const unsigned char *wsc = pt.ws + int64_t(n) * W::kBytes;
+#pragma unroll
+    for (int i = PART; i < F::NQP; i += kProducers) {
+        if (i < F::NBK)
+            dma16(pt.q + tb, dma_src_offset(i, lane, D * F::ES, F::RK, hdb, nv), slot + 1024 * i);
+        else
+            dma16(wsc + W::kP, 1024u * (i - F::NBK) + 16u * lane, slot + 1024 * i);
     }
-    return f;
+}
+
+// A operand from rows of a padded row-major LDS matrix: lane (g, r) gets row
+// row0 + r, k = k0 + 8g .. k0 + 8g + 7 (contiguous).
+template <bool BF16>
+__device__ __forceinline__ Frag<BF16> row_frag(const unsigned char *base, int stride, int row,
+                                               int k0, int g)
+{
+    return *reinterpret_cast<const Frag<BF16> *>(base + row * stride + (k0 + 8 * g) * (BF16 ? 2 : 4));
 }
 
 // Operand whose rows are columns c0 + (lane mod 16) of a row-major LDS matrix and
 // whose k values are rows t0 + {4g..4g+3}, t0 + 16 + {4g..4g+3} (eight rows of
-// one column).  bf16: two ds_read_b64_tr_b16 (see lds_frag_tr).
+// one column).  bf16: two ds_read_b64_tr_b16; inside each group of 16 lanes
+// this instruction hands lane i the (i mod 4)-th 16-bit value fetched by lane
+// 4j + i/4 as its element j, so lane p fetches row t0 + 4g + p/4 (then 16 rows
+// lower), columns c0 + 4 (p mod 4) .. +3.
 template <bool BF16>
 __device__ __forceinline__ Frag<BF16> frag_cols(const unsigned char *base, int stride, int t0,
                                                 int c0, int lane)
@@ -614,178 +740,350 @@ __device__ __forceinline__ floatx4 col4(const unsigned char *base, int stride, i
     return r;
 }
 
-// Chain wave, one chunk.  All LDS reads of the step (K rows, T, gates, V and the
-// transposed K for the update) are issued first; then X = K M^T, E = beta (V -
-// e^gam X), Delta = T E (published, then barrier B for the output wave) and the
-// state update M^T <- e^{gam_last} M^T + K^T diag(e^{gam_last - gam}) Delta,
-// whose new fragments are published for the next step.
+
+// ---- wave roles ---------------------------------------------------------------
+
+// X operands of one chunk.  The bf16 path holds the K and T fragments in
+// registers (read before barrier A); the fp32 path reads them when used.
+template <int D, bool BF16>
+struct XOps {
+    Frag<BF16> ak[4][D / 32];   // K rows: A operand of K M^T
+    Frag<BF16> at[6];           // T blocks
+    floatx4 bt[4], eg[4], edec[4];
+    floatx4 vv[4];              // the tile's V columns, accumulator layout
+};
+
 template <int D, bool BF16, int VT>
-__device__ __forceinline__ void chain_step(floatx4 (&Mt)[VT][D / 16], const unsigned char *buf,
-                                           Frag<BF16> *pub, int lane)
+__device__ __forceinline__ void x_load(XOps<D, BF16> &o, const unsigned char *kt, int vt, int lane)
 {
     using F = ScanCfg<D, BF16, VT>;
-    constexpr int KS = F::KS;
     const int gq = lane >> 4, cl = lane & 15;
-    const float *sG = reinterpret_cast<const float *>(buf + F::kG);
-    Frag<BF16> ak[4][KS];
+    if constexpr (F::PIPE) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) ak[tt][ks] = frag_rows<BF16>(buf + F::kK, F::RK, 16 * tt + cl, 32 * ks, gq);
-    Frag<BF16> at[6];
+            for (int ks = 0; ks < F::KS; ++ks)
+                o.ak[tt][ks] = row_frag<BF16>(kt + F::kK, F::RK, 16 * tt + cl, 32 * ks, gq);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        at[tt] = frag_rows<BF16>(buf + F::kT, F::RT, 16 * tt + cl, 0, gq);
-        if (tt >= 2) at[2 + tt] = frag_rows<BF16>(buf + F::kT, F::RT, 16 * tt + cl, 32, gq);
+        for (int b = 0; b < 6; ++b) o.at[b] = frag_blk<BF16>(kt + F::kT + b * F::BLK, lane);
     }
-    floatx4 bt[4], eg[4], edec[4];
+    const float *sG = reinterpret_cast<const float *>(kt + F::kG);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         const int t = 16 * tt + 4 * gq;
         const float4 b4 = *reinterpret_cast<const float4 *>(sG + t);
         const float4 e4 = *reinterpret_cast<const float4 *>(sG + C + t);
         const float4 d4 = *reinterpret_cast<const float4 *>(sG + 2 * C + t);
-        bt[tt] = floatx4{b4.x, b4.y, b4.z, b4.w};
-        eg[tt] = floatx4{e4.x, e4.y, e4.z, e4.w};
-        edec[tt] = floatx4{d4.x, d4.y, d4.z, d4.w};
-    }
-    const float eC = sG[3 * C];
-    floatx4 vv[VT][4];
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) vv[vt][tt] = col4<BF16>(buf + F::kV, F::RV, 16 * tt, 16 * vt, lane);
-    Frag<BF16> akt[D / 16][2];
-#pragma unroll
-    for (int kt = 0; kt < D / 16; ++kt) {
-        akt[kt][0] = frag_cols<BF16>(buf + F::kK, F::RK, 0, 16 * kt, lane);
-        akt[kt][1] = frag_cols<BF16>(buf + F::kK, F::RK, 32, 16 * kt, lane);
-    }
-
-    floatx4 dl[VT][4];
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt) {
-        Frag<BF16> bm[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bm[ks] = acc_frag<BF16>(Mt[vt][2 * ks], Mt[vt][2 * ks + 1]);
-        floatx4 xk[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) xk[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) xk[tt] = mma(ak[tt][ks], bm[ks], xk[tt]);
-        floatx4 e[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) e[tt][j] = bt[tt][j] * fmaf(-eg[tt][j], xk[tt][j], vv[vt][tt][j]);
-        const Frag<BF16> be0 = acc_frag<BF16>(e[0], e[1]);
-        const Frag<BF16> be1 = acc_frag<BF16>(e[2], e[3]);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) dl[vt][tt] = mma(at[tt], be0, floatx4{0.f, 0.f, 0.f, 0.f});
-        dl[vt][2] = mma(at[4], be1, dl[vt][2]);
-        dl[vt][3] = mma(at[5], be1, dl[vt][3]);
-        pub[(VT * KS + 2 * vt) * 64 + lane] = acc_frag<BF16>(dl[vt][0], dl[vt][1]);
-        pub[(VT * KS + 2 * vt + 1) * 64 + lane] = acc_frag<BF16>(dl[vt][2], dl[vt][3]);
-    }
-    lds_barrier();  // B: Delta_n is published
-    Frag<BF16> bs[VT][2];
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt) {
-        floatx4 ds[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) ds[tt] = edec[tt] * dl[vt][tt];
-        bs[vt][0] = acc_frag<BF16>(ds[0], ds[1]);
-        bs[vt][1] = acc_frag<BF16>(ds[2], ds[3]);
+        o.bt[tt] = floatx4{b4.x, b4.y, b4.z, b4.w};
+        o.eg[tt] = floatx4{e4.x, e4.y, e4.z, e4.w};
+        o.edec[tt] = floatx4{d4.x, d4.y, d4.z, d4.w};
     }
 #pragma unroll
-    for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-        for (int kt = 0; kt < D / 16; ++kt) Mt[vt][kt] = mma(akt[kt][0], bs[vt][0], Mt[vt][kt] * eC);
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-        for (int kt = 0; kt < D / 16; ++kt) Mt[vt][kt] = mma(akt[kt][1], bs[vt][1], Mt[vt][kt]);
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            pub[(vt * KS + ks) * 64 + lane] = acc_frag<BF16>(Mt[vt][2 * ks], Mt[vt][2 * ks + 1]);
+    for (int tt = 0; tt < 4; ++tt) o.vv[tt] = col4<BF16>(kt + F::kV, F::RV, 16 * tt, 16 * vt, lane);
 }
 
-// Output wave, one chunk: reads Q, P and gates, forms e^gam Q M^T from the
-// published M^T fragments, waits at barrier B for Delta, adds P Delta and stores
-// O / sqrt(d) for valid tokens.  orow points at out[(s, first token of the chunk,
-// h, first value row + lane%16)].
+// Lower-triangular block matrix (six fragment blocks) times the 64-row B operand
+// given as two k halves: rows tt of the product.
+template <bool BF16>
+__device__ __forceinline__ void tri_mul(const Frag<BF16> (&a)[6], const Frag<BF16> &b0,
+                                        const Frag<BF16> &b1, floatx4 (&acc)[4])
+{
+    acc[0] = mma(a[0], b0, acc[0]);
+    acc[1] = mma(a[1], b0, acc[1]);
+    acc[2] = mma(a[3], b1, mma(a[2], b0, acc[2]));
+    acc[3] = mma(a[5], b1, mma(a[4], b0, acc[3]));
+}
+
+// X_vt, one chunk (between barriers A and B): X = K M^T from the published M^T
+// blocks, E = beta (V - e^gam X), Delta = T E; publishes Delta and
+// diag(e^{gam_last - gam}) Delta.
 template <int D, bool BF16, int VT>
-__device__ __forceinline__ void output_step(const unsigned char *buf, const Frag<BF16> *pub,
-                                            int lane, typename Elem<BF16>::T *orow, int64_t hd,
-                                            int nv, float scale)
+__device__ __forceinline__ void x_step(const XOps<D, BF16> &o, const unsigned char *kt,
+                                       unsigned char *smem, int vt, int lane)
 {
     using F = ScanCfg<D, BF16, VT>;
-    using E = typename Elem<BF16>::T;
     constexpr int KS = F::KS;
     const int gq = lane >> 4, cl = lane & 15;
-    const float *sG = reinterpret_cast<const float *>(buf + F::kG);
-    Frag<BF16> aq[4][KS];
+    Frag<BF16> bm[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bm[ks] = frag_blk<BF16>(smem + F::kPubM + (vt * KS + ks) * F::BLK, lane);
+    floatx4 xk[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) xk[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            if constexpr (F::PIPE)
+                xk[tt] = mma(o.ak[tt][ks], bm[ks], xk[tt]);
+            else
+                xk[tt] = mma(row_frag<BF16>(kt + F::kK, F::RK, 16 * tt + cl, 32 * ks, gq), bm[ks],
+                             xk[tt]);
+        }
+    floatx4 e[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            aq[tt][ks] = frag_rows<BF16>(buf + F::kQ, F::RK, 16 * tt + cl, 32 * ks, gq);
-    Frag<BF16> ap[6];
+        for (int j = 0; j < 4; ++j) e[tt][j] = o.bt[tt][j] * fmaf(-o.eg[tt][j], xk[tt][j], o.vv[tt][j]);
+    const Frag<BF16> be0 = acc_frag<BF16>(e[0], e[1]);
+    const Frag<BF16> be1 = acc_frag<BF16>(e[2], e[3]);
+    Frag<BF16> at[6];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        ap[tt] = frag_rows<BF16>(buf + F::kP, F::RT, 16 * tt + cl, 0, gq);
-        if (tt >= 2) ap[2 + tt] = frag_rows<BF16>(buf + F::kP, F::RT, 16 * tt + cl, 32, gq);
+    for (int b = 0; b < 6; ++b) {
+        if constexpr (F::PIPE)
+            at[b] = o.at[b];
+        else
+            at[b] = frag_blk<BF16>(kt + F::kT + b * F::BLK, lane);
     }
+    floatx4 dl[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) dl[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    tri_mul<BF16>(at, be0, be1, dl);
+    floatx4 ds[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) ds[tt] = o.edec[tt] * dl[tt];
+    Frag<BF16> *pS = reinterpret_cast<Frag<BF16> *>(smem + F::kPubS) + 128 * vt;
+    Frag<BF16> *pD = reinterpret_cast<Frag<BF16> *>(smem + F::kPubD) + 128 * vt;
+    pS[lane] = acc_frag<BF16>(ds[0], ds[1]);
+    pS[64 + lane] = acc_frag<BF16>(ds[2], ds[3]);
+    pD[lane] = acc_frag<BF16>(dl[0], dl[1]);
+    pD[64 + lane] = acc_frag<BF16>(dl[2], dl[3]);
+}
+
+// U_vt: publishes its M^T tiles as fragment blocks with k (key) order 8g..8g+7:
+// tile t (keys 16t..16t+15) fills half of the units of block t/2.
+template <int D, bool BF16, int VT>
+__device__ __forceinline__ void publish_mt(const floatx4 (&Mt)[D / 16], unsigned char *smem, int vt,
+                                           int lane)
+{
+    using F = ScanCfg<D, BF16, VT>;
+    const int gq = lane >> 4, cl = lane & 15;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+        // lane (gq, cl) holds keys 16t + 4gq + 0..3: unit group 2 (t & 1) + gq / 2,
+        // elements 4 (gq & 1) .. +3
+        unsigned char *u = smem + F::kPubM + (vt * F::KS + (t >> 1)) * F::BLK +
+                           F::FB * blk_unit(cl, 2 * (t & 1) + (gq >> 1)) + 4 * F::ES * (gq & 1);
+        if constexpr (BF16)
+            *reinterpret_cast<uint2 *>(u) = make_uint2(pack2(Mt[t][0], Mt[t][1]), pack2(Mt[t][2], Mt[t][3]));
+        else
+            *reinterpret_cast<float4 *>(u) = make_float4(Mt[t][0], Mt[t][1], Mt[t][2], Mt[t][3]);
+    }
+}
+
+// U_vt operands of one chunk (read between barriers A and B): K^T fragments
+// (rows = key channels, k = tokens) and e^{gam_last}.
+template <int D, bool BF16, int VT>
+__device__ __forceinline__ void u_load(Frag<BF16> (&akt)[D / 16][2], float &eC,
+                                       const unsigned char *kt, int lane)
+{
+    using F = ScanCfg<D, BF16, VT>;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+        akt[t][0] = frag_cols<BF16>(kt + F::kK, F::RK, 0, 16 * t, lane);
+        akt[t][1] = frag_cols<BF16>(kt + F::kK, F::RK, 32, 16 * t, lane);
+    }
+    eC = reinterpret_cast<const float *>(kt + F::kG)[3 * C];
+}
+
+// U_vt, one chunk (after barrier B): M^T <- e^{gam_last} M^T + K^T Dscaled, then
+// publishes the new M^T.
+template <int D, bool BF16, int VT>
+__device__ __forceinline__ void u_step(floatx4 (&Mt)[D / 16], const Frag<BF16> (&akt)[D / 16][2],
+                                       float eC, unsigned char *smem, int vt, int lane)
+{
+    using F = ScanCfg<D, BF16, VT>;
+    const Frag<BF16> *pS = reinterpret_cast<const Frag<BF16> *>(smem + F::kPubS) + 128 * vt;
+    const Frag<BF16> bs0 = pS[lane];
+    const Frag<BF16> bs1 = pS[64 + lane];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) Mt[t] = mma(akt[t][0], bs0, Mt[t] * eC);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) Mt[t] = mma(akt[t][1], bs1, Mt[t]);
+    publish_mt<D, BF16, VT>(Mt, smem, vt, lane);
+}
+
+// O operands of one chunk.  The bf16 path holds the Q fragments in registers
+// (read before barrier A); the fp32 path reads them when used.  P and the gates
+// are always held: the slot may be refilled before they are used.
+template <int D, bool BF16>
+struct OOps {
+    Frag<BF16> aq[4][D / 32];
+    Frag<BF16> ap[6];
     floatx4 eg[4];
+};
+
+template <int D, bool BF16, int VT>
+__device__ __forceinline__ void o_load(OOps<D, BF16> &o, const unsigned char *kt,
+                                       const unsigned char *qp, int lane)
+{
+    using F = ScanCfg<D, BF16, VT>;
+    const int gq = lane >> 4, cl = lane & 15;
+    if constexpr (F::PIPE) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < F::KS; ++ks)
+                o.aq[tt][ks] = row_frag<BF16>(qp + F::kQ, F::RK, 16 * tt + cl, 32 * ks, gq);
+    }
+#pragma unroll
+    for (int b = 0; b < 6; ++b) o.ap[b] = frag_blk<BF16>(qp + F::kP + b * F::BLK, lane);
+    const float *sG = reinterpret_cast<const float *>(kt + F::kG);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         const float4 e4 = *reinterpret_cast<const float4 *>(sG + C + 16 * tt + 4 * gq);
-        eg[tt] = floatx4{e4.x, e4.y, e4.z, e4.w};
+        o.eg[tt] = floatx4{e4.x, e4.y, e4.z, e4.w};
     }
-    floatx4 o[VT][4];
+}
+
+// O_vt between barriers A and B: acc = e^gam (Q M^T).
+template <int D, bool BF16, int VT>
+__device__ __forceinline__ void o_xq(const OOps<D, BF16> &o, const unsigned char *qp,
+                                     const unsigned char *smem, int vt, int lane, floatx4 (&acc)[4])
+{
+    using F = ScanCfg<D, BF16, VT>;
+    constexpr int KS = F::KS;
+    const int gq = lane >> 4, cl = lane & 15;
+    Frag<BF16> bm[KS];
 #pragma unroll
-    for (int vt = 0; vt < VT; ++vt) {
-        Frag<BF16> bm[KS];
+    for (int ks = 0; ks < KS; ++ks) bm[ks] = frag_blk<BF16>(smem + F::kPubM + (vt * KS + ks) * F::BLK, lane);
+    floatx4 xq[4];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bm[ks] = pub[(vt * KS + ks) * 64 + lane];
-        floatx4 xq[4];
+    for (int tt = 0; tt < 4; ++tt) xq[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) xq[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) xq[tt] = mma(aq[tt][ks], bm[ks], xq[tt]);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) o[vt][tt] = eg[tt] * xq[tt];
-    }
-    lds_barrier();  // B: Delta_n is published
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt) {
-        const Frag<BF16> bd0 = pub[(VT * KS + 2 * vt) * 64 + lane];
-        const Frag<BF16> bd1 = pub[(VT * KS + 2 * vt + 1) * 64 + lane];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) o[vt][tt] = mma(ap[tt], bd0, o[vt][tt]);
-        o[vt][2] = mma(ap[4], bd1, o[vt][2]);
-        o[vt][3] = mma(ap[5], bd1, o[vt][3]);
-        E *ov = orow + 16 * vt;
-        if (nv == C) {
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) ov[(16 * tt + 4 * gq + j) * hd] = from_f<E>(scale * o[vt][tt][j]);
-        } else {
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * tt + 4 * gq + j;
-                    if (t < nv) ov[t * hd] = from_f<E>(scale * o[vt][tt][j]);
-                }
+        for (int tt = 0; tt < 4; ++tt) {
+            if constexpr (F::PIPE)
+                xq[tt] = mma(o.aq[tt][ks], bm[ks], xq[tt]);
+            else
+                xq[tt] = mma(row_frag<BF16>(qp + F::kQ, F::RK, 16 * tt + cl, 32 * ks, gq), bm[ks],
+                             xq[tt]);
         }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = o.eg[tt] * xq[tt];
+}
+
+// O_vt after barrier B: acc += P Delta, then out = acc / sqrt(d) for the valid
+// tokens.  The tile goes through LDS ([C][16] elements) so that each lane
+// stores whole 16-byte pieces of token rows.  obase points at
+// out[(s, first token of the chunk, h, first value row of the tile)].
+template <int D, bool BF16, int VT>
+__device__ __forceinline__ void o_finish(const OOps<D, BF16> &o, unsigned char *smem, int vt,
+                                         int lane, floatx4 (&acc)[4], typename Elem<BF16>::T *obase,
+                                         int64_t hd, int nv, float scale)
+{
+    using F = ScanCfg<D, BF16, VT>;
+    using E = typename Elem<BF16>::T;
+    const int gq = lane >> 4, cl = lane & 15;
+    const Frag<BF16> *pD = reinterpret_cast<const Frag<BF16> *>(smem + F::kPubD) + 128 * vt;
+    const Frag<BF16> bd0 = pD[lane];
+    const Frag<BF16> bd1 = pD[64 + lane];
+    tri_mul<BF16>(o.ap, bd0, bd1, acc);
+    E *sO = reinterpret_cast<E *>(smem + F::kOut) + vt * C * 16;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sO[(16 * tt + 4 * gq + j) * 16 + cl] = from_f<E>(scale * acc[tt][j]);
+    constexpr int UPR = 16 * F::ES / 16;  // 16-byte units per token row
+    constexpr int EPU = 16 / F::ES;       // elements per unit
+#pragma unroll
+    for (int i = 0; i < C * UPR / 64; ++i) {
+        const int u = lane + 64 * i, t = u / UPR, part = u - t * UPR;
+        const uint4 val = reinterpret_cast<const uint4 *>(sO)[u];
+        if (t < nv) *reinterpret_cast<uint4 *>(obase + t * hd + part * EPU) = val;
+    }
+}
+
+// Producer PART: moves every chunk's data into its ring slots and waits for it
+// before the barrier after which it is read.
+template <int D, bool BF16, int VT, int PART>
+__device__ __forceinline__ void producer_loop(const ScanPtrs &pt, unsigned char *smem, int nc,
+                                              int64_t n_tokens, int lane)
+{
+    using F = ScanCfg<D, BF16, VT>;
+    constexpr int SK = F::SK, SQ = F::SQ;
+    auto nv_of = [&](int m) { return static_cast<int>(min<int64_t>(C, n_tokens - int64_t(m) * C)); };
+    auto kt = [&](int m) {
+        if (m < nc)
+            issue_kt<D, BF16, VT, PART>(pt, smem + F::kRingKT + (m % SK) * F::kSlotKT, m, nv_of(m), lane);
+    };
+    auto qp = [&](int m) {
+        if (m < nc)
+            issue_qp<D, BF16, VT, PART>(pt, smem + F::kRingQP + (m % SQ) * F::kSlotQP, m, nv_of(m), lane);
+    };
+    if constexpr (F::PIPE) {
+        // prologue: the issues of times t < 0, oldest first
+#pragma unroll
+        for (int t = (2 - 2 * SQ < 1 - 2 * SK ? 2 - 2 * SQ : 1 - 2 * SK); t < 0; ++t) {
+            if (t % 2 == 0) {
+                if (F::qp_chunk(t) >= 0) qp(F::qp_chunk(t));
+            } else if (F::kt_chunk(t) >= 0) {
+                kt(F::kt_chunk(t));
+            }
+        }
+        constexpr int SM = SK > SQ ? SK : SQ;
+        if (nc >= SM)
+            wait_vmem_le<F::wait_prologue(PART)>();
+        else
+            wait_vmem_le<0>();
+        dma_barrier();  // B_{-1}: K/T of chunk 0 is in LDS
+        for (int n = 0; n < nc; ++n) {
+            // near the end some of the counted loads were never issued: wait for all
+            if (n + SM < nc)
+                wait_vmem_le<F::wait_a(PART)>();  // Q/P of chunk n landed
+            else
+                wait_vmem_le<0>();
+            dma_barrier();  // A_n: Q/P slot of chunk n-1 is free
+            qp(n + SQ - 1);
+            if (n + SM < nc)
+                wait_vmem_le<F::wait_b(PART)>();  // K/T of chunk n+1 landed
+            else
+                wait_vmem_le<0>();
+            dma_barrier();  // B_n: K/T slot of chunk n is free
+            kt(n + SK);
+        }
+    } else {
+        for (int n = 0; n < nc; ++n) {
+            kt(n);
+            qp(n);
+            wait_vmem_le<0>();
+            dma_barrier();  // L_n
+            dma_barrier();  // A_n
+            dma_barrier();  // B_n
+        }
+    }
+}
+
+enum { kRoleX = 0, kRoleU = 1, kRoleO = 2, kRoleProd = 3 };
+
+// Right after a barrier, the wave on the dependency chain reads a few published
+// fragments (M^T after A, scaled Delta after B) that it needs at once; the other
+// waves' bulk operand reads wait a little so that the LDS serves those first.
+#ifndef GDN_BULK_PAUSE
+#define GDN_BULK_PAUSE 2
+#endif
+__device__ __forceinline__ void bulk_pause()
+{
+    if constexpr (GDN_BULK_PAUSE > 0) __builtin_amdgcn_s_sleep(GDN_BULK_PAUSE);
+}
+
+// Wave order: X_0.., U_0.., then O and the producers arranged so that, with
+// waves dealt round-robin to the four SIMDs, no O wave shares a SIMD with an X
+// wave (both run their products between barriers A and B).
+template <int VT>
+__device__ __forceinline__ void wave_role(int wave, int &role, int &idx)
+{
+    if (wave < 2 * VT) {
+        role = wave / VT;
+        idx = wave % VT;
+    } else if constexpr (VT == 1) {
+        role = wave == 2 ? kRoleO : kRoleProd;  // 2: O; 3..6: producers
+        idx = wave == 2 ? 0 : wave - 3;
+    } else {
+        // 4, 5: producers 0, 1; 6, 7: O_0, O_1; 8, 9: producers 2, 3
+        role = (wave == 6 || wave == 7) ? kRoleO : kRoleProd;
+        idx = wave < 6 ? wave - 4 : wave - 6;
     }
 }
 
@@ -793,7 +1091,7 @@ __device__ __forceinline__ void output_step(const unsigned char *buf, const Frag
 // low three bits of the block id: consecutive ids go to different XCDs, so this
 // keeps a head's workgroups on one XCD, where its K, Q, T and P hit in L2.
 template <int D, bool BF16, int VT>
-__global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
+__global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *state_in, void *__restrict__ out, float *state_out,
     const unsigned char *__restrict__ ws, int64_t n_tokens, int64_t n_heads, int64_t n_sh,
@@ -803,7 +1101,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     using E = typename Elem<BF16>::T;
     using W = WsLayout<BF16>;
     constexpr int NRB = D / F::RW;  // row blocks per head
-    constexpr int S = F::kStages;
+    constexpr bool PIPE = F::PIPE;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int64_t b = blockIdx.x;
@@ -811,79 +1109,88 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const int rb = static_cast<int>((b >> 3) % NRB);
     if (sh >= n_sh) return;  // whole workgroup leaves before any barrier
     const int64_t s = sh / n_heads, h = sh - s * n_heads;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int v0 = rb * F::RW;                       // first value row of the workgroup
     const int64_t hd = n_heads * D;
     const int64_t tok0 = (s * n_tokens * n_heads + h) * D;
-    ScanPtrs pt;
-    pt.k = static_cast<const unsigned char *>(k) + tok0 * F::ES;
-    pt.q = static_cast<const unsigned char *>(q) + tok0 * F::ES;
-    pt.v = static_cast<const unsigned char *>(v) + (tok0 + v0) * F::ES;
-    pt.ws = ws + sh * n_chunks * W::kBytes;
-    pt.hd_bytes = hd * F::ES;
-    Frag<BF16> *pub = reinterpret_cast<Frag<BF16> *>(smem + F::kPub);
+    const int nc = n_chunks;
     auto nv_of = [&](int n) { return static_cast<int>(min<int64_t>(C, n_tokens - int64_t(n) * C)); };
+    auto kt_slot = [&](int n) { return smem + F::kRingKT + (n % F::SK) * F::kSlotKT; };
+    auto qp_slot = [&](int n) { return smem + F::kRingQP + (n % F::SQ) * F::kSlotQP; };
 
-    if (wave >= 2) {
-        // producers
-        const int part = wave - 2;
-        if constexpr (S == 2) scan_issue<D, BF16, VT>(pt, smem, 0, nv_of(0), part, lane);
-        for (int n = 0; n < n_chunks; ++n) {
-            if constexpr (S == 1) scan_issue<D, BF16, VT>(pt, smem, n, nv_of(n), part, lane);
-            wait_vmem();
-            lds_barrier();  // A: chunk n is in LDS
-            if constexpr (S == 2) {
-                if (n + 1 < n_chunks)
-                    scan_issue<D, BF16, VT>(pt, smem + ((n + 1) & 1) * F::kStage, n + 1,
-                                            nv_of(n + 1), part, lane);
-            }
-            lds_barrier();  // B
-            if constexpr (S == 1) lds_barrier();
+    int role, vt;
+    wave_role<VT>(wave, role, vt);
+    if (role == kRoleProd) {
+        ScanPtrs pt;
+        pt.k = static_cast<const unsigned char *>(k) + tok0 * F::ES;
+        pt.q = static_cast<const unsigned char *>(q) + tok0 * F::ES;
+        pt.v = static_cast<const unsigned char *>(v) + (tok0 + v0) * F::ES;
+        pt.ws = ws + sh * nc * W::kBytes;
+        pt.hd_bytes = hd * F::ES;
+        switch (vt) {
+        case 0: producer_loop<D, BF16, VT, 0>(pt, smem, nc, n_tokens, lane); break;
+        case 1: producer_loop<D, BF16, VT, 1>(pt, smem, nc, n_tokens, lane); break;
+        case 2: producer_loop<D, BF16, VT, 2>(pt, smem, nc, n_tokens, lane); break;
+        default: producer_loop<D, BF16, VT, 3>(pt, smem, nc, n_tokens, lane); break;
         }
         return;
     }
 
-    // M^T tiles in accumulator layout: Mt[vt][kt][j] = M[v0 + 16 vt + lane%16][16 kt + 4 g + j]
-    const int64_t st_off = sh * D * D + int64_t(v0 + (lane & 15)) * D + 4 * (lane >> 4);
-    if (wave == 0) {
-        floatx4 Mt[VT][D / 16];
+    if (role == kRoleX) {
+        XOps<D, BF16> ops;
+        if constexpr (PIPE) lds_barrier();  // B_{-1}
+        for (int n = 0; n < nc; ++n) {
+            if constexpr (!PIPE) lds_barrier();  // L_n
+            bulk_pause();
+            x_load<D, BF16, VT>(ops, kt_slot(n), vt, lane);
+            lds_barrier();  // A_n
+            x_step<D, BF16, VT>(ops, kt_slot(n), smem, vt, lane);
+            lds_barrier();  // B_n
+        }
+    } else if (role == kRoleU) {
+        // Mt[t][j] = M[v0 + 16 vt + lane%16][16 t + 4 (lane/16) + j]
+        const int64_t st_off = sh * D * D + int64_t(v0 + 16 * vt + (lane & 15)) * D + 4 * (lane >> 4);
+        floatx4 Mt[D / 16];
 #pragma unroll
-        for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-            for (int kt = 0; kt < D / 16; ++kt) {
-                if (state_in) {
-                    const float4 m = *reinterpret_cast<const float4 *>(state_in + st_off +
-                                                                       16 * vt * D + 16 * kt);
-                    Mt[vt][kt] = floatx4{m.x, m.y, m.z, m.w};
-                } else {
-                    Mt[vt][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-                }
+        for (int t = 0; t < D / 16; ++t) {
+            if (state_in) {
+                const float4 m = *reinterpret_cast<const float4 *>(state_in + st_off + 16 * t);
+                Mt[t] = floatx4{m.x, m.y, m.z, m.w};
+            } else {
+                Mt[t] = floatx4{0.f, 0.f, 0.f, 0.f};
             }
-#pragma unroll
-        for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-            for (int ks = 0; ks < F::KS; ++ks)
-                pub[(vt * F::KS + ks) * 64 + lane] = acc_frag<BF16>(Mt[vt][2 * ks], Mt[vt][2 * ks + 1]);
-        for (int n = 0; n < n_chunks; ++n) {
-            const unsigned char *buf = smem + (S == 2 ? (n & 1) : 0) * F::kStage;
-            lds_barrier();  // A: chunk n is in LDS; M^T_n is published
-            chain_step<D, BF16, VT>(Mt, buf, pub, lane);  // contains barrier B
-            if constexpr (S == 1) lds_barrier();
+        }
+        publish_mt<D, BF16, VT>(Mt, smem, vt, lane);
+        Frag<BF16> akt[D / 16][2];
+        float eC;
+        if constexpr (PIPE) lds_barrier();  // B_{-1}
+        for (int n = 0; n < nc; ++n) {
+            if constexpr (!PIPE) lds_barrier();  // L_n
+            lds_barrier();  // A_n
+            bulk_pause();
+            u_load<D, BF16, VT>(akt, eC, kt_slot(n), lane);
+            lds_barrier();  // B_n
+            u_step<D, BF16, VT>(Mt, akt, eC, smem, vt, lane);
         }
 #pragma unroll
-        for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-            for (int kt = 0; kt < D / 16; ++kt)
-                *reinterpret_cast<float4 *>(state_out + st_off + 16 * vt * D + 16 * kt) =
-                    make_float4(Mt[vt][kt][0], Mt[vt][kt][1], Mt[vt][kt][2], Mt[vt][kt][3]);
+        for (int t = 0; t < D / 16; ++t)
+            *reinterpret_cast<float4 *>(state_out + st_off + 16 * t) =
+                make_float4(Mt[t][0], Mt[t][1], Mt[t][2], Mt[t][3]);
     } else {
-        E *orow = static_cast<E *>(out) + tok0 + v0 + (lane & 15);
-        for (int n = 0; n < n_chunks; ++n) {
-            const unsigned char *buf = smem + (S == 2 ? (n & 1) : 0) * F::kStage;
-            lds_barrier();  // A
-            output_step<D, BF16, VT>(buf, pub, lane, orow + int64_t(n) * C * hd, hd, nv_of(n),
-                                     scale);  // contains barrier B
-            if constexpr (S == 1) lds_barrier();
+        E *obase = static_cast<E *>(out) + tok0 + v0 + 16 * vt;
+        OOps<D, BF16> ops;
+        floatx4 acc[4];
+        if constexpr (PIPE) lds_barrier();  // B_{-1}
+        for (int n = 0; n < nc; ++n) {
+            if constexpr (!PIPE) lds_barrier();  // L_n
+            lds_barrier();  // A_n
+            bulk_pause();
+            o_load<D, BF16, VT>(ops, kt_slot(n), qp_slot(n), lane);
+            o_xq<D, BF16, VT>(ops, qp_slot(n), smem, vt, lane, acc);
+            lds_barrier();  // B_n
+            bulk_pause();
+            o_finish<D, BF16, VT>(ops, smem, vt, lane, acc, obase + int64_t(n) * C * hd, hd,
+                                  nv_of(n), scale);
         }
     }
 }
@@ -922,7 +1229,7 @@ hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, 
     const int64_t n_sh = p.n_seqs * p.n_heads;
     const int64_t blocks = (n_sh + 7) / 8 * 8 * NRB;
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
-    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kScanThreads), F::kBytes,
+    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(64 * F::kWaves), F::kBytes,
                        stream, p.q, p.k, p.v, p.state_in, p.out, p.state_out, ws, p.n_tokens,
                        p.n_heads, n_sh, n_chunks, scale);
     return hipGetLastError();
