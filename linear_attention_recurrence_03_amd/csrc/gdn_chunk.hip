@@ -68,8 +68,6 @@ struct Elem<false> {
     using T = float;
 };
 
-__device__ __forceinline__ float to_f(uint16_t x) { return bf16_to_f32(x); }
-__device__ __forceinline__ float to_f(float x) { return x; }
 template <class T>
 __device__ __forceinline__ T from_f(float x);
 template <>
@@ -248,29 +246,190 @@ struct WsLayout {
     static constexpr int64_t kBytes = kGates + 4 * C * 4;
 };
 
+// A operand from rows of a padded row-major LDS matrix: lane (g, r) gets row
+// row0 + r, k = k0 + 8g .. k0 + 8g + 7 (contiguous).
+template <bool BF16>
+__device__ __forceinline__ Frag<BF16> row_frag(const unsigned char *base, int stride, int row,
+                                               int k0, int g)
+{
+    return *reinterpret_cast<const Frag<BF16> *>(base + row * stride + (k0 + 8 * g) * (BF16 ? 2 : 4));
+}
+
+// ---- LDS-DMA helpers ----------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
+
+// One 16-byte-per-lane LDS-DMA: lane l's 16 bytes (from base + off) land at
+// lds + 16 l.  base and lds are wave-uniform; off is a per-lane byte offset.
+__device__ __forceinline__ void dma16(const unsigned char *base, uint32_t off, void *lds)
+{
+    __builtin_amdgcn_global_load_lds((global_cvoid *)(base + off), (lds_void *)(lds), 16, 0, 0);
+}
+
+// Wait until at most N of this wave's global loads (LDS-DMA included) are
+// outstanding; they complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // s_waitcnt fields: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8]
+    // (15 = no wait), vmcnt[5:4] in bits 15:14
+    __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+
+// Byte offset, inside one chunk's data, of the 16 bytes lane `lane` loads for LDS
+// block `blk` of a padded region: rows of `rowb` valid bytes stored with stride
+// `stride`; pad slots read offset 0.  `gstride` is the source row stride; rows at
+// or past nv read row nv - 1.
+__device__ __forceinline__ uint32_t dma_src_offset(int blk, int lane, int rowb, int stride,
+                                                   uint32_t gstride, int nv)
+{
+    const int o = blk * 1024 + lane * 16;
+    const int r = o / stride, b = o - r * stride;
+    const uint32_t v = uint32_t(min(r, nv - 1)) * gstride + uint32_t(b);
+    return b < rowb ? v : 0u;
+}
+
 constexpr int kPrepThreads = 256;
 
+// LDS of the prep kernel (one workgroup per (seq, head, chunk)).  Region R holds
+// the chunk's K and Q rows (16-byte padded) while the products are formed; after
+// that it is reused for T, A (as MFMA input type) and the P staging image.
 template <int D, bool BF16>
 struct PrepSmem {
     using E = typename Elem<BF16>::T;
-    static constexpr int LDK = D + (BF16 ? 8 : 4);  // padded row, elements
-    static constexpr int LDA = C + 1;               // fp32 square matrices
-    static constexpr int kK = 0;
-    static constexpr int kQ = kK + C * LDK * sizeof(E);
-    static constexpr int kA = kQ + C * LDK * sizeof(E);
-    static constexpr int kT = kA + C * LDA * 4;
-    static constexpr int kG = kT + C * LDA * 4;
+    static constexpr int ES = sizeof(E);
+    static constexpr int RK = D * ES + 16;               // K, Q row stride (bytes)
+    static constexpr int LDT = C + 16 / ES;              // T and A rows (elements)
+    static constexpr int LDD = 16;                       // transposed diagonal blocks (floats)
+    static constexpr int kMat = C * LDT * ES;            // one C x C matrix of E
+    static constexpr int kK = 0, kQ = C * RK;            // during the products
+    static constexpr int kT = 0, kAe = kMat, kPst = 2 * kMat;  // afterwards
+    static constexpr int kR = (2 * C * RK > 2 * kMat + 6 * kBlkBytes<BF16>) ? 2 * C * RK
+                                                                             : 2 * kMat + 6 * kBlkBytes<BF16>;
+    static constexpr int kD = kR;                        // 4 x [16][LDD] fp32
+    static constexpr int kG = kD + 4 * 16 * LDD * 4;     // gates
     static constexpr int kBytes = kG + (4 * C + 4) * 4;
+    static constexpr int NBK = C * RK / 1024;            // DMA blocks per matrix
+    static_assert(C * RK % 1024 == 0 && kMat % 16 == 0 && kR % 16 == 0, "layout");
 };
 
-// Lower 16x16 tiles (tr >= tc) of a 4x4 tile grid, in a fixed order.
-__device__ __forceinline__ void lower_tile(int ix, int &tr, int &tc)
+// The products of one prep wave: the lower tiles of row tiles R0 and R1 of
+// K K^T (KK) or Q K^T, kept in registers across the barrier that frees the K/Q
+// rows.  K K^T tiles are already A = beta_r e^{gam_r - gam_s} (k_r . k_s) for
+// s < r (the diagonal tiles are also written, transposed and fp32, to sD for the
+// forward substitution); Q K^T tiles are P = e^{gam_r - gam_s} (q_r . k_s) for
+// s <= r.  Tile (i, tc) is acc[i ? R0 + 1 + tc : tc].
+template <int R0, int R1>
+struct PrepTiles {
+    static constexpr int N = R0 + 1 + R1 + 1;
+    floatx4 acc[N];
+};
+
+template <int D, bool BF16, bool KK, int R0, int R1>
+__device__ __forceinline__ void prep_products(PrepTiles<R0, R1> &pt, const unsigned char *smem,
+                                              const float *sG, float *sD, int lane)
 {
-    tr = (ix >= 6) ? 3 : (ix >= 3) ? 2 : (ix >= 1) ? 1 : 0;
-    tc = ix - tr * (tr + 1) / 2;
+    using L = PrepSmem<D, BF16>;
+    constexpr int KS = D / 32;
+    const int gq = lane >> 4, cl = lane & 15;
+    const unsigned char *sK = smem + L::kK;
+    const unsigned char *sA_rows = smem + (KK ? L::kK : L::kQ);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tr = i ? R1 : R0;
+        Frag<BF16> fa[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) fa[ks] = row_frag<BF16>(sA_rows, L::RK, 16 * tr + cl, 32 * ks, gq);
+#pragma unroll
+        for (int tc = 0; tc <= (i ? R1 : R0); ++tc) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                acc = mma(fa[ks], row_frag<BF16>(sK, L::RK, 16 * tc + cl, 32 * ks, gq), acc);
+            const int col = 16 * tc + cl;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * tr + 4 * gq + j;
+                const float e = __expf(sG[row] - sG[col]);
+                acc[j] = KK ? ((col < row) ? sG[C + row] * e * acc[j] : 0.f)
+                            : ((col <= row) ? e * acc[j] : 0.f);
+            }
+            if (KK && tc == tr)  // sD[tr][m][r] = A[16 tr + r][16 tr + m]
+                *reinterpret_cast<float4 *>(sD + (tr * 16 + cl) * L::LDD + 4 * gq) =
+                    make_float4(acc[0], acc[1], acc[2], acc[3]);
+            pt.acc[i ? R0 + 1 + tc : tc] = acc;
+        }
+    }
 }
 
+// Writes a wave's tiles into a C x C matrix of E (row stride LDT elements).
+template <bool BF16, int R0, int R1>
+__device__ __forceinline__ void store_tiles(const PrepTiles<R0, R1> &pt, typename Elem<BF16>::T *m,
+                                            int ld, int lane)
+{
+    using E = typename Elem<BF16>::T;
+    const int gq = lane >> 4, cl = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tr = i ? R1 : R0;
+#pragma unroll
+        for (int tc = 0; tc <= (i ? R1 : R0); ++tc)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                m[(16 * tr + 4 * gq + j) * ld + 16 * tc + cl] = from_f<E>(pt.acc[i ? R0 + 1 + tc : tc][j]);
+    }
+}
 
+// P staging: the wave owns every stored block of its row tiles, so it writes its
+// tiles (and the zero upper tile inside a stored block) into the block image and
+// copies those blocks to the workspace without waiting for other waves.
+template <bool BF16, int R0, int R1>
+__device__ __forceinline__ void emit_p(const PrepTiles<R0, R1> &pt, unsigned char *pst,
+                                       unsigned char *wp, int lane)
+{
+    using E = typename Elem<BF16>::T;
+    const int gq = lane >> 4, cl = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tr = i ? R1 : R0;
+#pragma unroll
+        for (int tc = 0; tc <= (i ? R1 : R0) + ((i ? R1 : R0) % 2 == 0 ? 1 : 0); ++tc)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * tr + 4 * gq + j, col = 16 * tc + cl;
+                const float v = tc <= tr ? pt.acc[i ? R0 + 1 + tc : tc][j] : 0.f;
+                *reinterpret_cast<E *>(pst + tri_offset<BF16>(row, col)) = from_f<E>(v);
+            }
+    }
+    constexpr int FB = kFragBytes<BF16>;
+    // blocks of row tile tt: tt < 2 -> block tt; tt >= 2 -> blocks 2 tt - 2, 2 tt - 1
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tr = i ? R1 : R0;
+        const int b0 = tr < 2 ? tr : 2 * tr - 2, nb = tr < 2 ? 1 : 2;
+        for (int u = lane; u < nb * 64 * FB / 16; u += 64) {
+            const int off = b0 * kBlkBytes<BF16> + 16 * u;
+            *reinterpret_cast<uint4 *>(wp + off) = *reinterpret_cast<const uint4 *>(pst + off);
+        }
+    }
+}
+
+// One workgroup per (seq, head, chunk): the state-independent part of the chunk.
+//   0. K and Q rows -> LDS by LDS-DMA (all waves); gate sums (wave 0)
+//   1. K K^T (waves 0, 1) and Q K^T (waves 2, 3) on MFMA, row tiles {0, 3} and
+//      {1, 2} per wave so that each does five tiles; results stay in registers
+//   2. the K/Q space is reused: waves 0, 1 store A; wave 0 then inverts the
+//      diagonal 16x16 blocks of I + A by forward substitution (lane = (block,
+//      column), right-looking over a transposed fp32 copy of the block); wave 1
+//      zeroes the blocks of T read before they are formed; waves 2, 3 emit P
+//   3. blocks (1,0), (3,2): T_ij = -T_ii (A_ij T_jj)                (waves 0, 1)
+//   4. blocks (2,0), (2,1), (3,0), (3,1): with the 32-row halves,
+//      T_hi,lo = -T_hi (A_hi,lo T_lo)                              (waves 0, 1)
+//   5. T to the workspace as six fragment blocks
+// The products of steps 3 and 4 run on MFMA with the k range padded to 32 by
+// blocks of T that are still zero; for bf16 inputs their operands are bf16.
 template <int D, bool BF16>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const float *__restrict__ g,
@@ -280,15 +439,15 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     using E = typename Elem<BF16>::T;
     using L = PrepSmem<D, BF16>;
     using W = WsLayout<BF16>;
-    constexpr int LDK = L::LDK, LDA = L::LDA;
+    constexpr int LDT = L::LDT;
     extern __shared__ __align__(16) unsigned char smem[];
-    E *sK = reinterpret_cast<E *>(smem + L::kK);
-    E *sQ = reinterpret_cast<E *>(smem + L::kQ);
-    float *sA = reinterpret_cast<float *>(smem + L::kA);
-    float *sT = reinterpret_cast<float *>(smem + L::kT);
+    E *sT = reinterpret_cast<E *>(smem + L::kT);
+    E *sAe = reinterpret_cast<E *>(smem + L::kAe);
+    float *sD = reinterpret_cast<float *>(smem + L::kD);
     float *sG = reinterpret_cast<float *>(smem + L::kG);  // gam, beta, e^gam, e^{last-gam}, e^last
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int gq = lane >> 4, cl = lane & 15;
     const int64_t chunk_id = blockIdx.x;
     const int64_t sh = chunk_id / n_chunks;
     const int n = static_cast<int>(chunk_id - sh * n_chunks);
@@ -296,23 +455,21 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const int64_t t0 = int64_t(n) * C;
     const int nv = static_cast<int>(min<int64_t>(C, n_tokens - t0));
     unsigned char *dst = ws + chunk_id * W::kBytes;
-    E *wP = reinterpret_cast<E *>(dst + W::kP);
 
-    // 1. K and Q rows of the chunk (zero past the end of the sequence)
-    constexpr int VE = 16 / sizeof(E);
-    constexpr int VPR = D / VE;
-    for (int i = tid; i < C * VPR; i += kPrepThreads) {
-        const int r = i / VPR, c = (i - r * VPR) * VE;
-        uint4 kv = make_uint4(0, 0, 0, 0), qv = kv;
-        if (r < nv) {
-            const int64_t off = ((s * n_tokens + t0 + r) * n_heads + h) * D + c;
-            kv = *reinterpret_cast<const uint4 *>(static_cast<const E *>(k) + off);
-            qv = *reinterpret_cast<const uint4 *>(static_cast<const E *>(q) + off);
+    // 0. K and Q rows (rows past the end repeat the last valid one: their A and
+    //    P entries are cleared by beta = 0 and never read); gates
+    {
+        const int64_t off = ((s * n_tokens + t0) * n_heads + h) * D * L::ES;
+        const unsigned char *kb = static_cast<const unsigned char *>(k) + off;
+        const unsigned char *qb = static_cast<const unsigned char *>(q) + off;
+        const uint32_t hdb = static_cast<uint32_t>(n_heads * D * L::ES);
+        for (int i = wave; i < 2 * L::NBK; i += kPrepThreads / 64) {
+            const bool isq = i >= L::NBK;
+            const int blk = isq ? i - L::NBK : i;
+            dma16(isq ? qb : kb, dma_src_offset(blk, lane, D * L::ES, L::RK, hdb, nv),
+                  smem + (isq ? L::kQ : L::kK) + 1024 * blk);
         }
-        *reinterpret_cast<uint4 *>(sK + r * LDK + c) = kv;
-        *reinterpret_cast<uint4 *>(sQ + r * LDK + c) = qv;
     }
-    // 2. gates: inclusive scan of g inside the chunk
     if (wave == 0) {
         float gv = 0.f, bv = 0.f;
         if (lane < nv) {
@@ -322,9 +479,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
         }
         float x = gv;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
         }
         const float glast = __shfl(x, nv - 1, 64);
         const bool ok = lane < nv;
@@ -334,104 +491,117 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
         sG[3 * C + lane] = ok ? expf(glast - x) : 0.f;
         if (lane == 0) sG[4 * C] = expf(glast);
     }
+    wait_vmem_le<0>();
     lds_barrier();
 
-    const int gq = lane >> 4, cl = lane & 15;
-    // 3. A = beta e^{gam_r - gam_s} K K^T (strictly lower), on the 10 lower tiles
-    for (int job = wave; job < 10; job += kPrepThreads / 64) {
-        int tr, tc;
-        lower_tile(job, tr, tc);
-        Frag<BF16> fa[D / 32], fb[D / 32];
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-            fa[ks] = lds_frag<BF16>(sK, LDK, 16 * tr + cl, 32 * ks, gq);
-            fb[ks] = lds_frag<BF16>(sK, LDK, 16 * tc + cl, 32 * ks, gq);
+    // 1-2. products, then the reuse of the K/Q space
+    if (wave < 2) {
+        if (wave == 0) {
+            PrepTiles<0, 3> pt;
+            prep_products<D, BF16, true, 0, 3>(pt, smem, sG, sD, lane);
+            lds_barrier();
+            store_tiles<BF16, 0, 3>(pt, sAe, LDT, lane);
+        } else {
+            PrepTiles<1, 2> pt;
+            prep_products<D, BF16, true, 1, 2>(pt, smem, sG, sD, lane);
+            lds_barrier();
+            store_tiles<BF16, 1, 2>(pt, sAe, LDT, lane);
         }
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) acc = mma(fa[ks], fb[ks], acc);
-        const int col = 16 * tc + cl;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * tr + 4 * gq + j;
-            sA[row * LDA + col] =
-                (col < row) ? sG[C + row] * __expf(sG[row] - sG[col]) * acc[j] : 0.f;
+    } else {
+        unsigned char *pst = smem + L::kPst;
+        if (wave == 2) {
+            PrepTiles<0, 3> pt;
+            prep_products<D, BF16, false, 0, 3>(pt, smem, sG, sD, lane);
+            lds_barrier();
+            emit_p<BF16, 0, 3>(pt, pst, dst + W::kP, lane);
+        } else {
+            PrepTiles<1, 2> pt;
+            prep_products<D, BF16, false, 1, 2>(pt, smem, sG, sD, lane);
+            lds_barrier();
+            emit_p<BF16, 1, 2>(pt, pst, dst + W::kP, lane);
+            float *wG = reinterpret_cast<float *>(dst + W::kGates);
+            wG[lane] = sG[C + lane];
+            wG[C + lane] = sG[2 * C + lane];
+            wG[2 * C + lane] = sG[3 * C + lane];
+            wG[3 * C + lane] = sG[4 * C];
         }
     }
-    lds_barrier();
-
     if (wave == 0) {
-        // 4a. 16x16 diagonal blocks of T = (I + A)^{-1}: lane = (block, column),
-        //     forward substitution down the column.
+        // diagonal blocks of T = (I + A)^{-1}: lane = (block b, column c); after
+        // x[m] is final it is eliminated from the rows below it
         const int b = lane >> 4, c = lane & 15;
-        const float *Ab = sA + (16 * b) * LDA + 16 * b;
+        const float *Ab = sD + b * 16 * L::LDD;  // Ab[m * LDD + r] = A[16b + r][16b + m]
         float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == c) ? 1.f : 0.f;
+        for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+        float4 cur[4], nxt[4];
 #pragma unroll
-            for (int m = 0; m < r; ++m) acc = fmaf(-Ab[r * LDA + m], x[m], acc);
-            x[r] = acc;
+        for (int v = 0; v < 4; ++v) cur[v] = *reinterpret_cast<const float4 *>(Ab + 4 * v);
+#pragma unroll
+        for (int m = 0; m < 15; ++m) {
+            if (m + 1 < 15) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    nxt[v] = *reinterpret_cast<const float4 *>(Ab + (m + 1) * L::LDD + 4 * v);
+            }
+            const float a[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y,
+                                 cur[1].z, cur[1].w, cur[2].x, cur[2].y, cur[2].z, cur[2].w,
+                                 cur[3].x, cur[3].y, cur[3].z, cur[3].w};
+            const float xm = x[m];
+#pragma unroll
+            for (int r = m + 1; r < 16; ++r) x[r] = fmaf(-a[r], xm, x[r]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) cur[v] = nxt[v];
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sT[(16 * b + r) * LDA + 16 * b + c] = x[r];
-    } else {
-        // 3b (other waves, meanwhile). P = e^{gam_r - gam_s} Q K^T (lower incl.
-        //    diagonal), written straight from the accumulators; upper tiles zero.
-        for (int job = wave - 1; job < 12; job += kPrepThreads / 64 - 1) {
-            int tr, tc;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (job < 10) {
-                lower_tile(job, tr, tc);
-                Frag<BF16> fa[D / 32], fb[D / 32];
+        for (int r = 0; r < 16; ++r) sT[(16 * b + r) * LDT + 16 * b + c] = from_f<E>(x[r]);
+    } else if (wave == 1) {
+        // blocks (1,0), (3,2), (0,1), (2,3) of T are read (as zeros) before they
+        // are formed or as the upper triangle: 16 rows x 16 elements each
+        const int blk = lane >> 4, r = lane & 15;
+        const int br = (blk == 0) ? 1 : (blk == 1) ? 3 : (blk == 2) ? 0 : 2;
+        const int bc = (blk == 0) ? 0 : (blk == 1) ? 2 : (blk == 2) ? 1 : 3;
+        E *row = sT + (16 * br + r) * LDT + 16 * bc;
 #pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks) {
-                    fa[ks] = lds_frag<BF16>(sQ, LDK, 16 * tr + cl, 32 * ks, gq);
-                    fb[ks] = lds_frag<BF16>(sK, LDK, 16 * tc + cl, 32 * ks, gq);
-                }
+        for (int c = 0; c < 16; ++c) row[c] = from_f<E>(0.f);
+    }
+    lds_barrier();
+
+    const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    // 3. T_10 and T_32 (wave 0: pair (1,0), wave 1: pair (3,2))
+    if (wave < 2) {
+        const int j = 2 * wave, i = j + 1;
+        // X = A[i rows][16j .. 16j+31] T[16j .. 16j+31][j cols]; rows 16i.. of that
+        // T range are T_ij, still zero, so X = A_ij T_jj
+        const Frag<BF16> a = lds_frag<BF16>(sAe, LDT, 16 * i + cl, 16 * j, gq);
+        const Frag<BF16> bt = lds_frag_tr<BF16>(sT, LDT, 16 * j, 16 * j, lane);
+        const floatx4 X = mma(a, bt, zero4);
+        // T_ij = -T[i rows][16j .. 16j+31] [0; X]  (= -T_ii X)
+        const Frag<BF16> ti = lds_frag<BF16>(sT, LDT, 16 * i + cl, 16 * j, gq);
+        const floatx4 Y = mma(ti, acc_frag<BF16>(zero4, X), zero4);
 #pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks) acc = mma(fa[ks], fb[ks], acc);
-            } else {
-                tr = job == 10 ? 0 : 2;  // upper tiles (0,1) and (2,3): zeros inside stored blocks
-                tc = tr + 1;
-            }
-            const int col = 16 * tc + cl;
+        for (int jj = 0; jj < 4; ++jj) sT[(16 * i + 4 * gq + jj) * LDT + 16 * j + cl] = from_f<E>(-Y[jj]);
+    }
+    lds_barrier();
+
+    // 4. column tile j = wave of the lower-left 32x32 block
+    if (wave < 2) {
+        const int j = wave;
+        const Frag<BF16> bt = lds_frag_tr<BF16>(sT, LDT, 0, 16 * j, lane);     // T[0..31][j cols]
+        const floatx4 X2 = mma(lds_frag<BF16>(sAe, LDT, 32 + cl, 0, gq), bt, zero4);
+        const floatx4 X3 = mma(lds_frag<BF16>(sAe, LDT, 48 + cl, 0, gq), bt, zero4);
+        const Frag<BF16> bx = acc_frag<BF16>(X2, X3);                          // rows 32..63
+        const floatx4 Y2 = mma(lds_frag<BF16>(sT, LDT, 32 + cl, 32, gq), bx, zero4);
+        const floatx4 Y3 = mma(lds_frag<BF16>(sT, LDT, 48 + cl, 32, gq), bx, zero4);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * tr + 4 * gq + j;
-                const float pv = (col <= row) ? __expf(sG[row] - sG[col]) * acc[j] : 0.f;
-                *reinterpret_cast<E *>(reinterpret_cast<unsigned char *>(wP) + tri_offset<BF16>(row, col)) =
-                    from_f<E>(pv);
-            }
+        for (int jj = 0; jj < 4; ++jj) {
+            sT[(32 + 4 * gq + jj) * LDT + 16 * j + cl] = from_f<E>(-Y2[jj]);
+            sT[(48 + 4 * gq + jj) * LDT + 16 * j + cl] = from_f<E>(-Y3[jj]);
         }
     }
     lds_barrier();
 
-    // 4b. off-diagonal blocks of T, one block diagonal at a time, on fp32 MFMA:
-    //     X = A[i rows][16j : 16i] T[16j : 16i][j cols] (inner length 16 (i-j)),
-    //     T_ij = -T_ii X.  X stays in accumulator registers: for the second
-    //     product, k step jj pairs lane group g with row 4g + jj of X.
-    for (int dd = 1; dd < 4; ++dd) {
-        if (wave < 4 - dd) {
-            const int j = wave, i = wave + dd;
-            floatx4 X = {0.f, 0.f, 0.f, 0.f};
-            for (int st = 0; st < 4 * dd; ++st) {
-                const int u = 16 * j + 4 * st + gq;
-                X = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * i + cl) * LDA + u],
-                                                         sT[u * LDA + 16 * j + cl], X, 0, 0, 0);
-            }
-            floatx4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                Y = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                    sT[(16 * i + cl) * LDA + 16 * i + 4 * gq + jj], X[jj], Y, 0, 0, 0);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) sT[(16 * i + 4 * gq + jj) * LDA + 16 * j + cl] = -Y[jj];
-        }
-        lds_barrier();
-    }
-
-    // 5. T as six fragment blocks (zeros above the diagonal), then the gates
+    // 5. T as six fragment blocks (zeros above the diagonal)
     constexpr int FB = kFragBytes<BF16>;
     for (int u = tid; u < 6 * 64; u += kPrepThreads) {
         const int b = u >> 6, p = u & 63;
@@ -442,20 +612,13 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int c = 32 * hh + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
-            vt[e] = from_f<E>(c <= r ? sT[r * LDA + c] : 0.f);
+            vt[e] = c <= r ? sT[r * LDT + c] : from_f<E>(0.f);
         }
         uint4 w[FB / 16];
         __builtin_memcpy(w, vt, FB);
         uint4 *ub = reinterpret_cast<uint4 *>(dst + W::kT + b * kBlkBytes<BF16> + FB * p);
 #pragma unroll
         for (int x = 0; x < FB / 16; ++x) ub[x] = w[x];
-    }
-    float *wG = reinterpret_cast<float *>(dst + W::kGates);
-    if (tid < C) {
-        wG[tid] = sG[C + tid];
-        wG[C + tid] = sG[2 * C + tid];
-        wG[2 * C + tid] = sG[3 * C + tid];
-        wG[3 * C + tid] = sG[4 * C];
     }
 }
 
@@ -576,40 +739,6 @@ struct ScanCfg {
     static constexpr int kWaves = 3 * VT + kProducers;  // also in chunk_scan_kernel's launch bounds
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void global_cvoid;
-
-// One 16-byte-per-lane LDS-DMA: lane l's 16 bytes (from base + off) land at
-// lds + 16 l.  base and lds are wave-uniform; off is a per-lane byte offset.
-__device__ __forceinline__ void dma16(const unsigned char *base, uint32_t off, void *lds)
-{
-    __builtin_amdgcn_global_load_lds((global_cvoid *)(base + off), (lds_void *)(lds), 16, 0, 0);
-}
-
-// Wait until at most N of this wave's global loads (LDS-DMA included) are
-// outstanding; they complete in issue order.
-template <int N>
-__device__ __forceinline__ void wait_vmem_le()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    // s_waitcnt fields: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8]
-    // (15 = no wait), vmcnt[5:4] in bits 15:14
-    __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
-}
-
-// Byte offset, inside one chunk's data, of the 16 bytes lane `lane` loads for LDS
-// block `blk` of a padded region: rows of `rowb` valid bytes stored with stride
-// `stride`; pad slots read offset 0.  `gstride` is the source row stride; rows at
-// or past nv read row nv - 1.
-__device__ __forceinline__ uint32_t dma_src_offset(int blk, int lane, int rowb, int stride,
-                                                   uint32_t gstride, int nv)
-{
-    const int o = blk * 1024 + lane * 16;
-    const int r = o / stride, b = o - r * stride;
-    const uint32_t v = uint32_t(min(r, nv - 1)) * gstride + uint32_t(b);
-    return b < rowb ? v : 0u;
-}
-
 // Workgroup barrier for the producer waves.  Their only LDS writes are the
 // LDS-DMA loads, and a release fence would wait for every one of them to land
 // (vmcnt 0), draining the prefetch pipeline at each barrier.  Instead each
@@ -674,14 +803,6 @@ __device__ __forceinline__ void issue_qp(const ScanPtrs &pt, unsigned char *slot
     }
 }
 
-// A operand from rows of a padded row-major LDS matrix: lane (g, r) gets row
-// row0 + r, k = k0 + 8g .. k0 + 8g + 7 (contiguous).
-template <bool BF16>
-__device__ __forceinline__ Frag<BF16> row_frag(const unsigned char *base, int stride, int row,
-                                               int k0, int g)
-{
-    return *reinterpret_cast<const Frag<BF16> *>(base + row * stride + (k0 + 8 * g) * (BF16 ? 2 : 4));
-}
 
 // Operand whose rows are columns c0 + (lane mod 16) of a row-major LDS matrix and
 // whose k values are rows t0 + {4g..4g+3}, t0 + 16 + {4g..4g+3} (eight rows of
