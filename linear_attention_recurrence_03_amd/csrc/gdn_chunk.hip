@@ -651,7 +651,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
 // one slot of each: a third barrier L_n per chunk marks the slot as loaded and
 // the phases of a chunk run back to back.
 //
-// K and Q rows are padded by 16 bytes, which makes both the 16-byte row reads
+// K and Q rows are padded by 32 bytes, which makes both the 16-byte row reads
 // (k order 8g..8g+7 per lane group, matched by the key order of the published
 // M^T blocks) and the transposing reads of K spread over the LDS banks.  T and
 // P arrive as fragment blocks.  Rows past the end of a partial chunk are loaded
@@ -670,7 +670,10 @@ struct ScanCfg {
     static constexpr int KS = D / 32;
     static constexpr int FB = kFragBytes<BF16>;
     static constexpr int BLK = kBlkBytes<BF16>;
-    static constexpr int RK = D * ES + 16;          // K, Q row stride (bytes)
+    // K, Q row stride (bytes): a multiple of 16 that is 2 mod 4 in 16-byte units, which
+    // keeps both the 16-byte row reads and the transposing reads free of bank conflicts
+    static constexpr int RK = D * ES + 32;
+    static_assert((RK / 16) % 4 == 2, "K/Q row stride");
     static constexpr int RV = RW * ES + 16;         // V row stride
     // K/T/V/gates slot
     static constexpr int kK = 0;
