@@ -685,9 +685,13 @@ struct ScanCfg {
     static constexpr int kQ = 0;
     static constexpr int kP = kQ + C * RK;
     static constexpr int kSlotQP = kP + 6 * BLK;
+    // output staging per value tile: bf16 [16 values][RO bytes] (value-major, read
+    // back transposed), fp32 [C][16]
+    static constexpr int RO = C * 2 + 16;
+    static constexpr int kOutTile = BF16 ? 16 * RO : C * 16 * ES;
     // published values: M^T blocks, Delta and scaled Delta (accumulator-pair
-    // fragments), output staging [C][16] per value tile
-    static constexpr int kPubBytes = VT * KS * BLK + 4 * VT * 64 * FB + VT * C * 16 * ES;
+    // fragments), output staging
+    static constexpr int kPubBytes = VT * KS * BLK + 4 * VT * 64 * FB + VT * kOutTile;
     static constexpr int kLds = 160 * 1024;
     static constexpr bool fits(int sk, int sq) { return sk * kSlotKT + sq * kSlotQP + kPubBytes <= kLds; }
     static constexpr int SK = !PIPE ? 1 : fits(3, 2) ? 3 : 2;
@@ -698,7 +702,7 @@ struct ScanCfg {
     static constexpr int kPubD = kPubM + VT * KS * BLK;
     static constexpr int kPubS = kPubD + 2 * VT * 64 * FB;
     static constexpr int kOut = kPubS + 2 * VT * 64 * FB;
-    static constexpr int kBytes = kOut + VT * C * 16 * ES;
+    static constexpr int kBytes = kOut + VT * kOutTile;
     static_assert(kBytes <= kLds, "LDS budget");
     // 1 KiB DMA blocks.  The regions of a slot are contiguous multiples of 1 KiB,
     // so block i of a slot's list lands at slot + 1024 i.
@@ -873,8 +877,8 @@ template <int D, bool BF16>
 struct XOps {
     Frag<BF16> ak[4][D / 32];   // K rows: A operand of K M^T
     Frag<BF16> at[6];           // T blocks
-    floatx4 bt[4], eg[4], edec[4];
-    floatx4 vv[4];              // the tile's V columns, accumulator layout
+    floatx4 be[4], edec[4];     // beta e^gam, e^{gam_last - gam}
+    floatx4 bv[4];              // beta V for the tile's columns, accumulator layout
 };
 
 template <int D, bool BF16, int VT>
@@ -898,12 +902,11 @@ __device__ __forceinline__ void x_load(XOps<D, BF16> &o, const unsigned char *kt
         const float4 b4 = *reinterpret_cast<const float4 *>(sG + t);
         const float4 e4 = *reinterpret_cast<const float4 *>(sG + C + t);
         const float4 d4 = *reinterpret_cast<const float4 *>(sG + 2 * C + t);
-        o.bt[tt] = floatx4{b4.x, b4.y, b4.z, b4.w};
-        o.eg[tt] = floatx4{e4.x, e4.y, e4.z, e4.w};
+        const floatx4 bt = floatx4{b4.x, b4.y, b4.z, b4.w};
+        o.be[tt] = bt * floatx4{e4.x, e4.y, e4.z, e4.w};
         o.edec[tt] = floatx4{d4.x, d4.y, d4.z, d4.w};
+        o.bv[tt] = bt * col4<BF16>(kt + F::kV, F::RV, 16 * tt, 16 * vt, lane);
     }
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) o.vv[tt] = col4<BF16>(kt + F::kV, F::RV, 16 * tt, 16 * vt, lane);
 }
 
 // Lower-triangular block matrix (six fragment blocks) times the 64-row B operand
@@ -948,7 +951,7 @@ __device__ __forceinline__ void x_step(const XOps<D, BF16> &o, const unsigned ch
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) e[tt][j] = o.bt[tt][j] * fmaf(-o.eg[tt][j], xk[tt][j], o.vv[tt][j]);
+        for (int j = 0; j < 4; ++j) e[tt][j] = fmaf(-o.be[tt][j], xk[tt][j], o.bv[tt][j]);
     const Frag<BF16> be0 = acc_frag<BF16>(e[0], e[1]);
     const Frag<BF16> be1 = acc_frag<BF16>(e[2], e[3]);
     Frag<BF16> at[6];
@@ -1010,18 +1013,18 @@ __device__ __forceinline__ void u_load(Frag<BF16> (&akt)[D / 16][2], float &eC,
     eC = reinterpret_cast<const float *>(kt + F::kG)[3 * C];
 }
 
-// U_vt, one chunk (after barrier B): M^T <- e^{gam_last} M^T + K^T Dscaled, then
-// publishes the new M^T.
+// U_vt, one chunk (after barrier B): M^T <- M^T + K^T Dscaled (M^T was already
+// multiplied by e^{gam_last} while waiting at barrier B), then publishes the new M^T.
 template <int D, bool BF16, int VT>
 __device__ __forceinline__ void u_step(floatx4 (&Mt)[D / 16], const Frag<BF16> (&akt)[D / 16][2],
-                                       float eC, unsigned char *smem, int vt, int lane)
+                                       unsigned char *smem, int vt, int lane)
 {
     using F = ScanCfg<D, BF16, VT>;
     const Frag<BF16> *pS = reinterpret_cast<const Frag<BF16> *>(smem + F::kPubS) + 128 * vt;
     const Frag<BF16> bs0 = pS[lane];
     const Frag<BF16> bs1 = pS[64 + lane];
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) Mt[t] = mma(akt[t][0], bs0, Mt[t] * eC);
+    for (int t = 0; t < D / 16; ++t) Mt[t] = mma(akt[t][0], bs0, Mt[t]);
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) Mt[t] = mma(akt[t][1], bs1, Mt[t]);
     publish_mt<D, BF16, VT>(Mt, smem, vt, lane);
@@ -1089,9 +1092,11 @@ __device__ __forceinline__ void o_xq(const OOps<D, BF16> &o, const unsigned char
 }
 
 // O_vt after barrier B: acc += P Delta, then out = acc / sqrt(d) for the valid
-// tokens.  The tile goes through LDS ([C][16] elements) so that each lane
-// stores whole 16-byte pieces of token rows.  obase points at
-// out[(s, first token of the chunk, h, first value row of the tile)].
+// tokens.  obase points at out[(s, first token of the chunk, h, first value row of
+// the tile)].  bf16: the tile goes through LDS value-major (one 8-byte write per
+// lane and row tile) and comes back with transposing reads, each lane then holding
+// four consecutive values of one token: lane i of group g in read r gets token
+// 16r + i, values 4g..4g+3.  fp32: token-major staging, 16-byte stores.
 template <int D, bool BF16, int VT>
 __device__ __forceinline__ void o_finish(const OOps<D, BF16> &o, unsigned char *smem, int vt,
                                          int lane, floatx4 (&acc)[4], typename Elem<BF16>::T *obase,
@@ -1104,18 +1109,34 @@ __device__ __forceinline__ void o_finish(const OOps<D, BF16> &o, unsigned char *
     const Frag<BF16> bd0 = pD[lane];
     const Frag<BF16> bd1 = pD[64 + lane];
     tri_mul<BF16>(o.ap, bd0, bd1, acc);
-    E *sO = reinterpret_cast<E *>(smem + F::kOut) + vt * C * 16;
+    unsigned char *sO = smem + F::kOut + vt * F::kOutTile;
+    if constexpr (BF16) {
+        // value cl, tokens 16tt + 4gq .. +3
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < 4; ++tt)
+            *reinterpret_cast<uint2 *>(sO + cl * F::RO + (16 * tt + 4 * gq) * 2) =
+                make_uint2(pack2(scale * acc[tt][0], scale * acc[tt][1]),
+                           pack2(scale * acc[tt][2], scale * acc[tt][3]));
+        typedef __attribute__((address_space(3))) short4_t lds_short4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sO[(16 * tt + 4 * gq + j) * 16 + cl] = from_f<E>(scale * acc[tt][j]);
-    constexpr int UPR = 16 * F::ES / 16;  // 16-byte units per token row
-    constexpr int EPU = 16 / F::ES;       // elements per unit
+        for (int r = 0; r < 4; ++r) {
+            const unsigned char *a = sO + (4 * gq + (cl >> 2)) * F::RO + (16 * r + 4 * (cl & 3)) * 2;
+            const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a));
+            const int t = 16 * r + cl;
+            if (t < nv) *reinterpret_cast<uint2 *>(obase + t * hd + 4 * gq) = __builtin_bit_cast(uint2, v);
+        }
+    } else {
+        E *so = reinterpret_cast<E *>(sO);
 #pragma unroll
-    for (int i = 0; i < C * UPR / 64; ++i) {
-        const int u = lane + 64 * i, t = u / UPR, part = u - t * UPR;
-        const uint4 val = reinterpret_cast<const uint4 *>(sO)[u];
-        if (t < nv) *reinterpret_cast<uint4 *>(obase + t * hd + part * EPU) = val;
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) so[(16 * tt + 4 * gq + j) * 16 + cl] = from_f<E>(scale * acc[tt][j]);
+#pragma unroll
+        for (int i = 0; i < C * 4 / 64; ++i) {
+            const int u = lane + 64 * i, t = u >> 2, part = u & 3;
+            const uint4 val = reinterpret_cast<const uint4 *>(so)[u];
+            if (t < nv) *reinterpret_cast<uint4 *>(obase + t * hd + part * 4) = val;
+        }
     }
 }
 
@@ -1293,8 +1314,10 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
             lds_barrier();  // A_n
             bulk_pause();
             u_load<D, BF16, VT>(akt, eC, kt_slot(n), lane);
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) Mt[t] *= eC;
             lds_barrier();  // B_n
-            u_step<D, BF16, VT>(Mt, akt, eC, smem, vt, lane);
+            u_step<D, BF16, VT>(Mt, akt, smem, vt, lane);
         }
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
