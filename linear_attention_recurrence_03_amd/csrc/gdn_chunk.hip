@@ -1382,8 +1382,9 @@ hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, 
     return hipGetLastError();
 }
 
-// Scan workgroups hold 16 value rows each while that still leaves at most one
-// workgroup per compute unit (few heads: more parallel chains), else 32.
+// bf16 scan workgroups hold 16 value rows each while that still leaves at most one
+// workgroup per compute unit (few heads: more parallel chains), else 32.  The fp32
+// scan (one slot per ring, no pipelining) always holds 16.
 template <int D, bool BF16>
 hipError_t launch_chunk_d(const Problem &p, unsigned char *ws, hipStream_t stream)
 {
@@ -1391,8 +1392,9 @@ hipError_t launch_chunk_d(const Problem &p, unsigned char *ws, hipStream_t strea
     hipError_t e = launch_prep<D, BF16>(p, ws, n_chunks, stream);
     if (e != hipSuccess) return e;
     const int64_t n_sh = p.n_seqs * p.n_heads;
-    if (n_sh * (D / 16) <= 256) return launch_scan<D, BF16, 1>(p, ws, n_chunks, stream);
-    return launch_scan<D, BF16, 2>(p, ws, n_chunks, stream);
+    if (!BF16 || n_sh * (D / 16) <= 256) return launch_scan<D, BF16, 1>(p, ws, n_chunks, stream);
+    if constexpr (BF16) return launch_scan<D, BF16, 2>(p, ws, n_chunks, stream);
+    return hipErrorInvalidValue;  // not reached
 }
 
 template <bool BF16>

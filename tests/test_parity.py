@@ -127,6 +127,15 @@ def test_decay_regimes(gdn, gate, algo):
     check(gdn, xf, "f32", algo, what="gate f32 " + gate)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_many_row_blocks(gdn, dtype):
+    """More (sequence, head, 16 value rows) blocks than compute units: the bf16 scan
+    then holds 32 value rows per workgroup, the fp32 scan runs more workgroups than
+    there are compute units."""
+    x = inputs.custom(2, 130, 20, 128, dtype=dtype, state="normal", seed=77)
+    check(gdn, x, dtype, "chunked", what="many row blocks")
+
+
 def test_zero_initial_state_pointer(gdn):
     x = inputs.custom(1, 70, 2, 64, dtype="f32", state="zeros", seed=1)
     check(gdn, x, "f32", "auto", state=False, what="state None")
