@@ -685,13 +685,9 @@ struct ScanCfg {
     static constexpr int kQ = 0;
     static constexpr int kP = kQ + C * RK;
     static constexpr int kSlotQP = kP + 6 * BLK;
-    // output staging per value tile: bf16 [16 values][RO bytes] (value-major, read
-    // back transposed), fp32 [C][16]
-    static constexpr int RO = C * 2 + 16;
-    static constexpr int kOutTile = BF16 ? 16 * RO : C * 16 * ES;
     // published values: M^T blocks, Delta and scaled Delta (accumulator-pair
     // fragments), output staging
-    static constexpr int kPubBytes = VT * KS * BLK + 4 * VT * 64 * FB + VT * kOutTile;
+    static constexpr int kPubBytes = VT * KS * BLK + 4 * VT * 64 * FB;
     static constexpr int kLds = 160 * 1024;
     static constexpr bool fits(int sk, int sq) { return sk * kSlotKT + sq * kSlotQP + kPubBytes <= kLds; }
     static constexpr int SK = !PIPE ? 1 : fits(3, 2) ? 3 : 2;
@@ -701,8 +697,7 @@ struct ScanCfg {
     static constexpr int kPubM = kRingQP + SQ * kSlotQP;
     static constexpr int kPubD = kPubM + VT * KS * BLK;
     static constexpr int kPubS = kPubD + 2 * VT * 64 * FB;
-    static constexpr int kOut = kPubS + 2 * VT * 64 * FB;
-    static constexpr int kBytes = kOut + VT * kOutTile;
+    static constexpr int kBytes = kPubS + 2 * VT * 64 * FB;
     static_assert(kBytes <= kLds, "LDS budget");
     // 1 KiB DMA blocks.  The regions of a slot are contiguous multiples of 1 KiB,
     // so block i of a slot's list lands at slot + 1024 i.
@@ -1037,7 +1032,7 @@ template <int D, bool BF16>
 struct OOps {
     Frag<BF16> aq[4][D / 32];
     Frag<BF16> ap[6];
-    floatx4 eg[4];
+    float eg[4];                // e^gam of token 16 tt + lane % 16
 };
 
 template <int D, bool BF16, int VT>
@@ -1057,13 +1052,16 @@ __device__ __forceinline__ void o_load(OOps<D, BF16> &o, const unsigned char *kt
     for (int b = 0; b < 6; ++b) o.ap[b] = frag_blk<BF16>(qp + F::kP + b * F::BLK, lane);
     const float *sG = reinterpret_cast<const float *>(kt + F::kG);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const float4 e4 = *reinterpret_cast<const float4 *>(sG + C + 16 * tt + 4 * gq);
-        o.eg[tt] = floatx4{e4.x, e4.y, e4.z, e4.w};
-    }
+    for (int tt = 0; tt < 4; ++tt) o.eg[tt] = sG[C + 16 * tt + cl];
 }
 
-// O_vt between barriers A and B: acc = e^gam (Q M^T).
+// O_vt works on the transposed output tile, O^T = M Q^T diag(e^gam) + Delta^T P^T:
+// an A operand and a B operand of the same matrix have the same register layout, so
+// the products are those of O with their operands swapped, and the accumulator of
+// row tile tt holds in lane (g, i) the values 4g .. 4g+3 of token 16 tt + i, which
+// is stored from registers as it stands.
+//
+// O_vt between barriers A and B: acc = (e^gam (Q M^T))^T.
 template <int D, bool BF16, int VT>
 __device__ __forceinline__ void o_xq(const OOps<D, BF16> &o, const unsigned char *qp,
                                      const unsigned char *smem, int vt, int lane, floatx4 (&acc)[4])
@@ -1082,60 +1080,44 @@ __device__ __forceinline__ void o_xq(const OOps<D, BF16> &o, const unsigned char
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             if constexpr (F::PIPE)
-                xq[tt] = mma(o.aq[tt][ks], bm[ks], xq[tt]);
+                xq[tt] = mma(bm[ks], o.aq[tt][ks], xq[tt]);
             else
-                xq[tt] = mma(row_frag<BF16>(qp + F::kQ, F::RK, 16 * tt + cl, 32 * ks, gq), bm[ks],
+                xq[tt] = mma(bm[ks], row_frag<BF16>(qp + F::kQ, F::RK, 16 * tt + cl, 32 * ks, gq),
                              xq[tt]);
         }
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[tt] = o.eg[tt] * xq[tt];
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = xq[tt] * o.eg[tt];
 }
 
-// O_vt after barrier B: acc += P Delta, then out = acc / sqrt(d) for the valid
-// tokens.  obase points at out[(s, first token of the chunk, h, first value row of
-// the tile)].  bf16: the tile goes through LDS value-major (one 8-byte write per
-// lane and row tile) and comes back with transposing reads, each lane then holding
-// four consecutive values of one token: lane i of group g in read r gets token
-// 16r + i, values 4g..4g+3.  fp32: token-major staging, 16-byte stores.
+// O_vt after barrier B: acc += (P Delta)^T, then out = acc / sqrt(d) for the valid
+// tokens, stored from registers (four consecutive values of one token per lane and
+// row tile).  obase points at out[(s, first token of the chunk, h, first value row
+// of the tile)].
 template <int D, bool BF16, int VT>
-__device__ __forceinline__ void o_finish(const OOps<D, BF16> &o, unsigned char *smem, int vt,
+__device__ __forceinline__ void o_finish(const OOps<D, BF16> &o, const unsigned char *smem, int vt,
                                          int lane, floatx4 (&acc)[4], typename Elem<BF16>::T *obase,
                                          int64_t hd, int nv, float scale)
 {
     using F = ScanCfg<D, BF16, VT>;
-    using E = typename Elem<BF16>::T;
     const int gq = lane >> 4, cl = lane & 15;
     const Frag<BF16> *pD = reinterpret_cast<const Frag<BF16> *>(smem + F::kPubD) + 128 * vt;
-    const Frag<BF16> bd0 = pD[lane];
-    const Frag<BF16> bd1 = pD[64 + lane];
-    tri_mul<BF16>(o.ap, bd0, bd1, acc);
-    unsigned char *sO = smem + F::kOut + vt * F::kOutTile;
-    if constexpr (BF16) {
-        // value cl, tokens 16tt + 4gq .. +3
+    const Frag<BF16> d0 = pD[lane];
+    const Frag<BF16> d1 = pD[64 + lane];
+    acc[0] = mma(d0, o.ap[0], acc[0]);
+    acc[1] = mma(d0, o.ap[1], acc[1]);
+    acc[2] = mma(d1, o.ap[3], mma(d0, o.ap[2], acc[2]));
+    acc[3] = mma(d1, o.ap[5], mma(d0, o.ap[4], acc[3]));
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-            *reinterpret_cast<uint2 *>(sO + cl * F::RO + (16 * tt + 4 * gq) * 2) =
-                make_uint2(pack2(scale * acc[tt][0], scale * acc[tt][1]),
-                           pack2(scale * acc[tt][2], scale * acc[tt][3]));
-        typedef __attribute__((address_space(3))) short4_t lds_short4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const unsigned char *a = sO + (4 * gq + (cl >> 2)) * F::RO + (16 * r + 4 * (cl & 3)) * 2;
-            const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a));
-            const int t = 16 * r + cl;
-            if (t < nv) *reinterpret_cast<uint2 *>(obase + t * hd + 4 * gq) = __builtin_bit_cast(uint2, v);
-        }
-    } else {
-        E *so = reinterpret_cast<E *>(sO);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) so[(16 * tt + 4 * gq + j) * 16 + cl] = from_f<E>(scale * acc[tt][j]);
-#pragma unroll
-        for (int i = 0; i < C * 4 / 64; ++i) {
-            const int u = lane + 64 * i, t = u >> 2, part = u & 3;
-            const uint4 val = reinterpret_cast<const uint4 *>(so)[u];
-            if (t < nv) *reinterpret_cast<uint4 *>(obase + t * hd + part * 4) = val;
+    for (int tt = 0; tt < 4; ++tt) {
+        const int t = 16 * tt + cl;
+        if (t < nv) {
+            typename Elem<BF16>::T *dst = obase + t * hd + 4 * gq;
+            if constexpr (BF16)
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2(scale * acc[tt][0], scale * acc[tt][1]),
+                                                             pack2(scale * acc[tt][2], scale * acc[tt][3]));
+            else
+                *reinterpret_cast<float4 *>(dst) = make_float4(scale * acc[tt][0], scale * acc[tt][1],
+                                                               scale * acc[tt][2], scale * acc[tt][3]);
         }
     }
 }
@@ -1335,7 +1317,6 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
             o_load<D, BF16, VT>(ops, kt_slot(n), qp_slot(n), lane);
             o_xq<D, BF16, VT>(ops, qp_slot(n), smem, vt, lane, acc);
             lds_barrier();  // B_n
-            bulk_pause();
             o_finish<D, BF16, VT>(ops, smem, vt, lane, acc, obase + int64_t(n) * C * hd, hd,
                                   nv_of(n), scale);
         }
