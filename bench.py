@@ -34,12 +34,14 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 CHUNK = 64
 
 
-def algorithmic_bytes(S, T, H, D, esz, state_read=True):
-    """Each input read once, each output written once, the state read+written once."""
+def algorithmic_bytes(S, T, H, D, esz, state_read=True, key_heads=None):
+    """Each input read once, each output written once, the state read+written once
+    (q and k hold key_heads heads when given)."""
     tok = S * T * H * D * esz
+    tok_kq = S * T * (H if key_heads is None else key_heads) * D * esz
     gate = S * T * H * 4
     st = S * H * D * D * 4
-    return 4 * tok + 2 * gate + st * (2 if state_read else 1)
+    return 2 * tok_kq + 2 * tok + 2 * gate + st * (2 if state_read else 1)
 
 
 def algorithmic_flops_chunked(S, T, H, D, C=CHUNK):
@@ -85,11 +87,11 @@ class Slot:
 
     def __init__(self, gdn, d, torch):
         self.d = d
-        q = d["q"]
-        S, T, H, D = q.shape
-        self.out = torch.empty_like(q)
+        v = d["v"]
+        S, T, H, D = v.shape
+        self.out = torch.empty_like(v)
         self.state_out = torch.empty((S, H, D, D), dtype=torch.float32, device="cuda")
-        need = gdn.workspace_size("bf16" if q.dtype == torch.bfloat16 else "f32", S, T, H, D)
+        need = gdn.workspace_size("bf16" if v.dtype == torch.bfloat16 else "f32", S, T, H, D)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def run(self, gdn):
@@ -338,6 +340,19 @@ def main():
             "hbm_frac": round(b5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "mfma_frac": round(f5 / (ms5 * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "workload": "4 seqs x 32768 tokens x 16 heads x d128 bf16, carried N(0,0.1) state"}
+        # prefill with 16 query/key heads tiled over 32 value heads (no expanded copy)
+        wlt = inputs.GQA_PREFILL
+        mst, slots = bench_prefill(gdn, torch, wlt, steps=100, warmup=10, nbuf=4)
+        del slots
+        torch.cuda.empty_cache()
+        St, Tt, Ht, Dt = wlt.shape()
+        bt = algorithmic_bytes(St, Tt, Ht, Dt, 2, key_heads=wlt.key_heads)
+        extras["prefill_tiled"] = {
+            "tokens_per_s": round(St * Tt / (mst * 1e-3), 1), "us_per_call": round(mst * 1e3, 2),
+            "bytes_per_call": bt,
+            "hbm_frac": round(bt / (mst * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "workload": "1 seq x 4096 tokens x 32 value heads (16 query/key heads, tiled) x "
+                        "d128 bf16, zero state, 4 rotating input copies"}
         line["extras"] = extras
 
     if not args.no_cpu_baseline:

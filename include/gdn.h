@@ -26,8 +26,9 @@
  *     q, k, v, out : (n_seqs, n_tokens, n_heads, head_dim)   dtype gdn_dtype
  *     g, beta      : (n_seqs, n_tokens, n_heads)             fp32
  *     state_in/out : (n_seqs, n_heads, head_dim, head_dim)   fp32, [value][key]
- * q and k carry one head per value head, already expanded (first contract
- * bullet): head h of q and k pairs with head h of v, in the caller's order.
+ * For gdn_forward, q and k carry one head per value head, already expanded
+ * (first contract bullet): head h of q and k pairs with head h of v, in the
+ * caller's order.  gdn_forward_tiled takes fewer key heads instead.
  * q and k are used as given (no normalisation inside the op).
  *
  * Ownership and streams.  Every data pointer is a DEVICE pointer owned by the
@@ -122,6 +123,28 @@ int gdn_forward(gdn_dtype dtype, const void *q, const void *k, const void *v,
                 void *out, float *state_out, int64_t n_seqs, int64_t n_tokens,
                 int64_t n_heads, int head_dim, void *workspace,
                 size_t workspace_bytes, gdn_algo algo, void *stream);
+
+/* gdn_forward for q and k that hold fewer heads than v: n_key_heads heads
+ * shared by the n_heads value heads in the tiled order, value head h reading
+ * key (and query) head h % n_key_heads.  That is the mapping the model card
+ * names as upstream's ("ggml attention kernels" model card, first bullet
+ * after the "Shapes, in torch order" table); with it the caller needs no
+ * expanded copy of q and k.
+ *
+ *   q, k         (n_seqs, n_tokens, n_key_heads, head_dim), device, read only
+ *   n_key_heads  >= 1 and a divisor of n_heads (else GDN_ERR_BAD_SHAPE); when
+ *                n_heads == 0 the call is a no-op and n_key_heads only has to
+ *                be >= 0
+ *
+ * Every other argument, the result, the workspace size (gdn_workspace_size
+ * with the value-head count n_heads), alignment, aliasing and error rules are
+ * those of gdn_forward; n_key_heads == n_heads is exactly gdn_forward. */
+int gdn_forward_tiled(gdn_dtype dtype, const void *q, const void *k, const void *v,
+                      const float *g, const float *beta, const float *state_in,
+                      void *out, float *state_out, int64_t n_seqs, int64_t n_tokens,
+                      int64_t n_heads, int64_t n_key_heads, int head_dim,
+                      void *workspace, size_t workspace_bytes, gdn_algo algo,
+                      void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *gdn_status_string(int status);

@@ -50,6 +50,10 @@ def _lib():
     lib.gdn_forward.restype = ctypes.c_int
     lib.gdn_forward.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
                                 ctypes.c_int, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    lib.gdn_forward_tiled.restype = ctypes.c_int
+    lib.gdn_forward_tiled.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
+                                      i64, i64, ctypes.c_int, vp, ctypes.c_size_t,
+                                      ctypes.c_int, vp]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_version.restype = ctypes.c_int
@@ -83,7 +87,10 @@ def forward(q, k, v, g, beta, state=None, algo: str = "auto", out=None, state_ou
     """Run the gated delta rule over all tokens.  Returns (out, final_state).
 
     q, k, v: (n_seqs, n_tokens, n_heads, head_dim) float32 or bfloat16 CUDA
-    tensors (same dtype); g, beta: (n_seqs, n_tokens, n_heads) float32; state:
+    tensors (same dtype).  q and k may instead hold n_key_heads heads, a
+    divisor of n_heads: value head h then reads key/query head h % n_key_heads
+    (the tiled order; ``gdn_forward_tiled``).  g, beta: (n_seqs, n_tokens,
+    n_heads) float32; state:
     (n_seqs, n_heads, head_dim, head_dim) float32 stored [value][key], or None
     for zeros.  ``state_out`` may be ``state`` itself for an in-place update.
     Work is enqueued on ``stream`` (default: torch's current stream); nothing
@@ -100,9 +107,12 @@ def forward(q, k, v, g, beta, state=None, algo: str = "auto", out=None, state_ou
     for name, t in (("k", k), ("v", v)):
         if t.dtype != q.dtype:
             raise TypeError("%s dtype %s differs from q dtype %s" % (name, t.dtype, q.dtype))
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must all be (n_seqs, n_tokens, n_heads, head_dim)")
-    S, T, H, D = q.shape
+    if q.dim() != 4 or v.dim() != 4 or k.shape != q.shape or \
+            q.shape[:2] != v.shape[:2] or q.shape[3] != v.shape[3]:
+        raise ValueError("q, k must be (n_seqs, n_tokens, n_key_heads, head_dim) and v "
+                         "(n_seqs, n_tokens, n_heads, head_dim)")
+    S, T, H, D = v.shape
+    HK = q.shape[2]
     if g.shape != (S, T, H) or beta.shape != (S, T, H):
         raise ValueError("g and beta must be (n_seqs, n_tokens, n_heads)")
     if g.dtype != torch.float32 or beta.dtype != torch.float32:
@@ -117,8 +127,16 @@ def forward(q, k, v, g, beta, state=None, algo: str = "auto", out=None, state_ou
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
     dev = q.device
+    if out is not None and (out.shape != v.shape or out.dtype != v.dtype or not out.is_cuda
+                            or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous GPU tensor shaped and typed like v")
+    if state_out is not None and (state_out.shape != (S, H, D, D) or not state_out.is_cuda
+                                  or state_out.dtype != torch.float32
+                                  or not state_out.is_contiguous()):
+        raise ValueError("state_out must be a contiguous float32 (n_seqs, n_heads, d, d) "
+                         "GPU tensor")
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(v)
     if state_out is None:
         state_out = torch.empty((S, H, D, D), dtype=torch.float32, device=dev)
     a = ALGOS[algo]
@@ -130,9 +148,14 @@ def forward(q, k, v, g, beta, state=None, algo: str = "auto", out=None, state_ou
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     handle = ctypes.c_void_p(stream.cuda_stream)
-    rc = lib.gdn_forward(_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                         _ptr(state), _ptr(out), _ptr(state_out), S, T, H, D,
-                         _ptr(workspace), ws_bytes, a, handle)
+    if HK == H:
+        rc = lib.gdn_forward(_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(state), _ptr(out), _ptr(state_out), S, T, H, D,
+                             _ptr(workspace), ws_bytes, a, handle)
+    else:
+        rc = lib.gdn_forward_tiled(_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                   _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out), S, T,
+                                   H, HK, D, _ptr(workspace), ws_bytes, a, handle)
     if rc != 0:
         raise GdnError(rc, status_string(rc))
     return out, state_out

@@ -75,6 +75,14 @@ int check_shape(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens, int64_t n_hea
     return GDN_OK;
 }
 
+// gdn_forward with n_key_heads query/key heads (value head h reads key head
+// h % n_key_heads); gdn_forward is the case n_key_heads == n_heads.
+int forward_impl(gdn_dtype dtype, const void *q, const void *k, const void *v, const float *g,
+                 const float *beta, const float *state_in, void *out, float *state_out,
+                 int64_t n_seqs, int64_t n_tokens, int64_t n_heads, int64_t n_key_heads,
+                 int head_dim, void *workspace, size_t workspace_bytes, gdn_algo algo,
+                 void *stream);
+
 }  // namespace
 
 extern "C" {
@@ -100,11 +108,62 @@ int gdn_forward(gdn_dtype dtype, const void *q, const void *k, const void *v, co
                 int64_t n_seqs, int64_t n_tokens, int64_t n_heads, int head_dim,
                 void *workspace, size_t workspace_bytes, gdn_algo algo, void *stream)
 {
+    return forward_impl(dtype, q, k, v, g, beta, state_in, out, state_out, n_seqs, n_tokens,
+                        n_heads, n_heads, head_dim, workspace, workspace_bytes, algo, stream);
+}
+
+int gdn_forward_tiled(gdn_dtype dtype, const void *q, const void *k, const void *v,
+                      const float *g, const float *beta, const float *state_in, void *out,
+                      float *state_out, int64_t n_seqs, int64_t n_tokens, int64_t n_heads,
+                      int64_t n_key_heads, int head_dim, void *workspace,
+                      size_t workspace_bytes, gdn_algo algo, void *stream)
+{
+    return forward_impl(dtype, q, k, v, g, beta, state_in, out, state_out, n_seqs, n_tokens,
+                        n_heads, n_key_heads, head_dim, workspace, workspace_bytes, algo,
+                        stream);
+}
+
+const char *gdn_status_string(int status)
+{
+    switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head_dim (need 32, 64, 96 or 128)";
+    case GDN_ERR_BAD_SHAPE: return "bad shape (negative or too large size)";
+    case GDN_ERR_NULL_POINTER: return "required pointer is NULL";
+    case GDN_ERR_BAD_DTYPE: return "bad dtype (need GDN_F32 or GDN_BF16)";
+    case GDN_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than gdn_workspace_size()";
+    case GDN_ERR_ALGO_UNAVAILABLE: return "algorithm value not recognised";
+    case GDN_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case GDN_ERR_ALIASING: return "output overlaps an input (only state_out == state_in is allowed)";
+    case GDN_ERR_HIP: return "HIP runtime refused a launch";
+    default: return "unknown status";
+    }
+}
+
+int gdn_version(void)
+{
+    return kVersion;
+}
+
+}  // extern "C"
+
+namespace {
+
+int forward_impl(gdn_dtype dtype, const void *q, const void *k, const void *v, const float *g,
+                 const float *beta, const float *state_in, void *out, float *state_out,
+                 int64_t n_seqs, int64_t n_tokens, int64_t n_heads, int64_t n_key_heads,
+                 int head_dim, void *workspace, size_t workspace_bytes, gdn_algo algo,
+                 void *stream)
+{
     int64_t tok_elems, gate_elems, state_elems;
     int rc = check_shape(dtype, n_seqs, n_tokens, n_heads, head_dim, algo, &tok_elems,
                          &gate_elems, &state_elems);
     if (rc != GDN_OK) return rc;
+    if (n_key_heads < 0) return GDN_ERR_BAD_SHAPE;
+    if (n_heads > 0 && (n_key_heads == 0 || n_heads % n_key_heads != 0)) return GDN_ERR_BAD_SHAPE;
     if (n_seqs == 0 || n_heads == 0) return GDN_OK;
+    // elements of q and k (n_key_heads heads; at most those of v)
+    const int64_t kq_elems = tok_elems / n_heads * n_key_heads;
 
     const int64_t esz = (dtype == GDN_BF16) ? 2 : 4;
     const bool have_tokens = n_tokens > 0;
@@ -121,7 +180,7 @@ int gdn_forward(gdn_dtype dtype, const void *q, const void *k, const void *v, co
         return GDN_ERR_ALIASING;
     if (have_tokens) {
         const Range r_out = range_of(out, tok_elems * esz);
-        const Range reads[] = {range_of(q, tok_elems * esz), range_of(k, tok_elems * esz),
+        const Range reads[] = {range_of(q, kq_elems * esz), range_of(k, kq_elems * esz),
                                range_of(v, tok_elems * esz), range_of(g, gate_elems * 4),
                                range_of(beta, gate_elems * 4)};
         for (const Range &r : reads)
@@ -137,7 +196,7 @@ int gdn_forward(gdn_dtype dtype, const void *q, const void *k, const void *v, co
         if (need > 0 && !workspace) return GDN_ERR_NULL_POINTER;
         if (need > 0) {
             const Range r_ws = range_of(workspace, static_cast<int64_t>(need));
-            const Range all[] = {range_of(q, tok_elems * esz), range_of(k, tok_elems * esz),
+            const Range all[] = {range_of(q, kq_elems * esz), range_of(k, kq_elems * esz),
                                  range_of(v, tok_elems * esz), range_of(g, gate_elems * 4),
                                  range_of(beta, gate_elems * 4), r_state_in, r_state_out,
                                  range_of(out, tok_elems * esz)};
@@ -167,6 +226,7 @@ int gdn_forward(gdn_dtype dtype, const void *q, const void *k, const void *v, co
     p.n_seqs = n_seqs;
     p.n_tokens = n_tokens;
     p.n_heads = n_heads;
+    p.n_k_heads = n_key_heads;
     p.head_dim = head_dim;
     if (chosen == GDN_ALGO_CHUNKED)
         err = gdn::launch_chunked(p, workspace, st);
@@ -175,26 +235,5 @@ int gdn_forward(gdn_dtype dtype, const void *q, const void *k, const void *v, co
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
-const char *gdn_status_string(int status)
-{
-    switch (status) {
-    case GDN_OK: return "ok";
-    case GDN_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head_dim (need 32, 64, 96 or 128)";
-    case GDN_ERR_BAD_SHAPE: return "bad shape (negative or too large size)";
-    case GDN_ERR_NULL_POINTER: return "required pointer is NULL";
-    case GDN_ERR_BAD_DTYPE: return "bad dtype (need GDN_F32 or GDN_BF16)";
-    case GDN_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than gdn_workspace_size()";
-    case GDN_ERR_ALGO_UNAVAILABLE: return "algorithm value not recognised";
-    case GDN_ERR_MISALIGNED: return "pointer not 16-byte aligned";
-    case GDN_ERR_ALIASING: return "output overlaps an input (only state_out == state_in is allowed)";
-    case GDN_ERR_HIP: return "HIP runtime refused a launch";
-    default: return "unknown status";
-    }
-}
+}  // namespace
 
-int gdn_version(void)
-{
-    return kVersion;
-}
-
-}  // extern "C"

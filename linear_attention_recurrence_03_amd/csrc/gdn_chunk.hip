@@ -434,7 +434,7 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, unsigned char *__restrict__ ws, int64_t n_tokens,
-    int64_t n_heads, int n_chunks)
+    int64_t n_heads, int64_t n_k_heads, int n_chunks)
 {
     using E = typename Elem<BF16>::T;
     using L = PrepSmem<D, BF16>;
@@ -456,13 +456,14 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const int nv = static_cast<int>(min<int64_t>(C, n_tokens - t0));
     unsigned char *dst = ws + chunk_id * W::kBytes;
 
-    // 0. K and Q rows (rows past the end repeat the last valid one: their A and
-    //    P entries are cleared by beta = 0 and never read); gates
+    // 0. K and Q rows of key head h % n_k_heads (rows past the end repeat the
+    //    last valid one: their A and P entries are cleared by beta = 0 and never
+    //    read); gates
     {
-        const int64_t off = ((s * n_tokens + t0) * n_heads + h) * D * L::ES;
+        const int64_t off = ((s * n_tokens + t0) * n_k_heads + h % n_k_heads) * D * L::ES;
         const unsigned char *kb = static_cast<const unsigned char *>(k) + off;
         const unsigned char *qb = static_cast<const unsigned char *>(q) + off;
-        const uint32_t hdb = static_cast<uint32_t>(n_heads * D * L::ES);
+        const uint32_t hdb = static_cast<uint32_t>(n_k_heads * D * L::ES);
         for (int i = wave; i < 2 * L::NBK; i += kPrepThreads / 64) {
             const bool isq = i >= L::NBK;
             const int blk = isq ? i - L::NBK : i;
@@ -752,7 +753,8 @@ __device__ __forceinline__ void dma_barrier() { __builtin_amdgcn_s_barrier(); }
 struct ScanPtrs {
     const unsigned char *k, *q, *v;   // token 0 of this (seq, head); v at the first value row
     const unsigned char *ws;          // this (seq, head)'s chunk 0 in the workspace
-    int64_t hd_bytes;                 // token stride in bytes (64 of them fit in 32 bits)
+    int64_t hd_bytes;                 // token stride of v in bytes (64 of them fit in 32 bits)
+    int64_t kq_bytes;                 // token stride of k and q in bytes
 };
 
 // Producer PART's blocks of chunk n's K, T, V and gates.
@@ -762,16 +764,16 @@ __device__ __forceinline__ void issue_kt(const ScanPtrs &pt, unsigned char *slot
 {
     using F = ScanCfg<D, BF16, VT>;
     using W = WsLayout<BF16>;
-    const int64_t tb = int64_t(n) * C * pt.hd_bytes;
-    const uint32_t hdb = static_cast<uint32_t>(pt.hd_bytes);
+    const int64_t tb = int64_t(n) * C * pt.hd_bytes, tbk = int64_t(n) * C * pt.kq_bytes;
+    const uint32_t hdb = static_cast<uint32_t>(pt.hd_bytes), kqb = static_cast<uint32_t>(pt.kq_bytes);
     const unsigned char *wsc = pt.ws + int64_t(n) * W::kBytes;
 #pragma unroll
     for (int i = PART; i < F::NKT; i += kProducers) {
         uint32_t off;
         const unsigned char *base;
         if (i < F::NBK) {
-            base = pt.k + tb;
-            off = dma_src_offset(i, lane, D * F::ES, F::RK, hdb, nv);
+            base = pt.k + tbk;
+            off = dma_src_offset(i, lane, D * F::ES, F::RK, kqb, nv);
         } else if (i < F::NBK + F::NBT) {
             base = wsc + W::kT;
             off = 1024u * (i - F::NBK) + 16u * lane;
@@ -793,13 +795,13 @@ __device__ __forceinline__ void issue_qp(const ScanPtrs &pt, unsigned char *slot
 {
     using F = ScanCfg<D, BF16, VT>;
     using W = WsLayout<BF16>;
-    const int64_t tb = int64_t(n) * C * pt.hd_bytes;
-    const uint32_t hdb = static_cast<uint32_t>(pt.hd_bytes);
+    const int64_t tbk = int64_t(n) * C * pt.kq_bytes;
+    const uint32_t kqb = static_cast<uint32_t>(pt.kq_bytes);
     const unsigned char *wsc = pt.ws + int64_t(n) * W::kBytes;
 #pragma unroll
     for (int i = PART; i < F::NQP; i += kProducers) {
         if (i < F::NBK)
-            dma16(pt.q + tb, dma_src_offset(i, lane, D * F::ES, F::RK, hdb, nv), slot + 1024 * i);
+            dma16(pt.q + tbk, dma_src_offset(i, lane, D * F::ES, F::RK, kqb, nv), slot + 1024 * i);
         else
             dma16(wsc + W::kP, 1024u * (i - F::NBK) + 16u * lane, slot + 1024 * i);
     }
@@ -1221,8 +1223,8 @@ template <int D, bool BF16, int VT>
 __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *state_in, void *__restrict__ out, float *state_out,
-    const unsigned char *__restrict__ ws, int64_t n_tokens, int64_t n_heads, int64_t n_sh,
-    int n_chunks, float scale)
+    const unsigned char *__restrict__ ws, int64_t n_tokens, int64_t n_heads, int64_t n_k_heads,
+    int64_t n_sh, int n_chunks, float scale)
 {
     using F = ScanCfg<D, BF16, VT>;
     using E = typename Elem<BF16>::T;
@@ -1239,7 +1241,8 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int v0 = rb * F::RW;                       // first value row of the workgroup
     const int64_t hd = n_heads * D;
-    const int64_t tok0 = (s * n_tokens * n_heads + h) * D;
+    const int64_t tok0 = (s * n_tokens * n_heads + h) * D;                        // v, out
+    const int64_t ktok0 = (s * n_tokens * n_k_heads + h % n_k_heads) * D;         // k, q
     const int nc = n_chunks;
     auto nv_of = [&](int n) { return static_cast<int>(min<int64_t>(C, n_tokens - int64_t(n) * C)); };
     auto kt_slot = [&](int n) { return smem + F::kRingKT + (n % F::SK) * F::kSlotKT; };
@@ -1249,11 +1252,12 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
     wave_role<VT>(wave, role, vt);
     if (role == kRoleProd) {
         ScanPtrs pt;
-        pt.k = static_cast<const unsigned char *>(k) + tok0 * F::ES;
-        pt.q = static_cast<const unsigned char *>(q) + tok0 * F::ES;
+        pt.k = static_cast<const unsigned char *>(k) + ktok0 * F::ES;
+        pt.q = static_cast<const unsigned char *>(q) + ktok0 * F::ES;
         pt.v = static_cast<const unsigned char *>(v) + (tok0 + v0) * F::ES;
         pt.ws = ws + sh * nc * W::kBytes;
         pt.hd_bytes = hd * F::ES;
+        pt.kq_bytes = n_k_heads * D * F::ES;
         switch (vt) {
         case 0: producer_loop<D, BF16, VT, 0>(pt, smem, nc, n_tokens, lane); break;
         case 1: producer_loop<D, BF16, VT, 1>(pt, smem, nc, n_tokens, lane); break;
@@ -1337,7 +1341,8 @@ hipError_t launch_prep(const Problem &p, unsigned char *ws, int n_chunks, hipStr
     }
     const int64_t blocks = p.n_seqs * p.n_heads * n_chunks;
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kPrepThreads), L::kBytes,
-                       stream, p.q, p.k, p.g, p.beta, ws, p.n_tokens, p.n_heads, n_chunks);
+                       stream, p.q, p.k, p.g, p.beta, ws, p.n_tokens, p.n_heads, p.n_k_heads,
+                       n_chunks);
     return hipGetLastError();
 }
 
@@ -1359,7 +1364,7 @@ hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, 
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(64 * F::kWaves), F::kBytes,
                        stream, p.q, p.k, p.v, p.state_in, p.out, p.state_out, ws, p.n_tokens,
-                       p.n_heads, n_sh, n_chunks, scale);
+                       p.n_heads, p.n_k_heads, n_sh, n_chunks, scale);
     return hipGetLastError();
 }
 

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
     const void *__restrict__ q, const void *__restrict__ k,
     const void *__restrict__ v, const float *__restrict__ g,
     const float *__restrict__ beta, const float *state_in, void *__restrict__ out,
-    float *state_out, int64_t n_tokens, int64_t n_heads, float scale)
+    float *state_out, int64_t n_tokens, int64_t n_heads, int64_t n_k_heads, float scale)
 {
     constexpr int NV = D / 32;
     constexpr int kRowsPerWave = 2 * NP;
@@ -144,10 +144,12 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
         }
     }
 
-    // token t of (s, h): vectors at ((s*T + t)*H + h)*D, gates at (s*T + t)*H + h
+    // token t of (s, h): v and out at ((s*T + t)*H + h)*D, gates at (s*T + t)*H + h,
+    // q and k at ((s*T + t)*Hk + h % Hk)*D
     int64_t gi = s * n_tokens * n_heads + h;
-    Vec<NV> kv = load_in<NV, BF16>(k, gi * D + col);
-    Vec<NV> qv = load_in<NV, BF16>(q, gi * D + col);
+    int64_t ki = s * n_tokens * n_k_heads + h % n_k_heads;
+    Vec<NV> kv = load_in<NV, BF16>(k, ki * D + col);
+    Vec<NV> qv = load_in<NV, BF16>(q, ki * D + col);
     float vr[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) vr[p] = load_scalar_in<BF16>(v, gi * D + row0 + 2 * p);
@@ -155,13 +157,13 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
 
     for (int64_t t = 0; t < n_tokens; ++t) {
         // prefetch the next token's inputs while this one is computed
-        const int64_t gn = gi + n_heads;
+        const int64_t gn = gi + n_heads, kn_i = ki + n_k_heads;
         const bool more = (t + 1 < n_tokens);
         Vec<NV> kn, qn;
         float vn[NP], gnext = 0.f, bnext = 0.f;
         if (more) {
-            kn = load_in<NV, BF16>(k, gn * D + col);
-            qn = load_in<NV, BF16>(q, gn * D + col);
+            kn = load_in<NV, BF16>(k, kn_i * D + col);
+            qn = load_in<NV, BF16>(q, kn_i * D + col);
 #pragma unroll
             for (int p = 0; p < NP; ++p) vn[p] = load_scalar_in<BF16>(v, gn * D + row0 + 2 * p);
             gnext = g[gn];
@@ -207,6 +209,7 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
             bt = bnext;
         }
         gi = gn;
+        ki = kn_i;
     }
 
 #pragma unroll
@@ -224,7 +227,7 @@ hipError_t launch_rec(const Problem &p, hipStream_t stream)
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
     hipLaunchKernelGGL((recurrent_kernel<D, NP, BF16>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kWaves * 64), 0, stream, p.q, p.k, p.v, p.g, p.beta,
-                       p.state_in, p.out, p.state_out, p.n_tokens, p.n_heads, scale);
+                       p.state_in, p.out, p.state_out, p.n_tokens, p.n_heads, p.n_k_heads, scale);
     return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@ struct Problem {
     void *out;
     float *state_out;
     int64_t n_seqs, n_tokens, n_heads;
+    int64_t n_k_heads;      // heads of q and k; value head h reads head h % n_k_heads
     int head_dim;
 };
 

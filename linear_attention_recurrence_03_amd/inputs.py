@@ -61,9 +61,13 @@ class Workload:
     beta_std: float = 1.0      # beta = sigmoid(N(0, beta_std))
     seed: int = 0
     per_seq_seeds: bool = False  # spawn one child seed per sequence
+    key_heads: Optional[int] = None  # heads of q and k (None: n_heads)
 
     def shape(self):
         return (self.n_seqs, self.n_tokens, self.n_heads, self.head_dim)
+
+    def n_key_heads(self):
+        return self.n_heads if self.key_heads is None else self.key_heads
 
 
 # The five workloads.  Seeds follow 1000 * workload number (+ layer index for the
@@ -79,11 +83,17 @@ WORKLOADS = {
                 beta_std=2.0, seed=5000, per_seq_seeds=True),
 }
 
+# 32 value heads sharing 16 query/key heads (tiled order), otherwise the prefill
+# workload above: the key-head count of a GQA-style GDN layer.
+GQA_PREFILL = Workload("prefill_tiled_bf16", 1, 4096, 32, 128, "bf16", "zeros", "standard",
+                       seed=6000, key_heads=16)
 
-def _draw(rng, shape, dtype, state_kind, gate, beta_std, head_dim):
+
+def _draw(rng, shape, dtype, state_kind, gate, beta_std, head_dim, key_heads=None):
     S, T, H, d = shape
-    q = rng.standard_normal((S, T, H, d), dtype=np.float32)
-    k = rng.standard_normal((S, T, H, d), dtype=np.float32)
+    HK = H if key_heads is None else key_heads
+    q = rng.standard_normal((S, T, HK, d), dtype=np.float32)
+    k = rng.standard_normal((S, T, HK, d), dtype=np.float32)
     v = rng.standard_normal((S, T, H, d), dtype=np.float32)
     zg = rng.standard_normal((S, T, H), dtype=np.float32)
     if gate == "mixed":
@@ -131,7 +141,7 @@ def make(workload: Workload, layer: int = 0, seq: Optional[int] = None):
             rng = np.random.default_rng(children[s])
             parts.append(_draw(rng, (1,) + shape[1:], workload.dtype,
                                workload.state, workload.gate, workload.beta_std,
-                               workload.head_dim))
+                               workload.head_dim, workload.key_heads))
         if len(parts) == 1:
             return parts[0]
         return {key: np.concatenate([p[key] for p in parts], axis=0)
@@ -140,12 +150,12 @@ def make(workload: Workload, layer: int = 0, seq: Optional[int] = None):
         raise ValueError("this workload draws all sequences from one seed")
     rng = np.random.default_rng(base)
     return _draw(rng, shape, workload.dtype, workload.state, workload.gate,
-                 workload.beta_std, workload.head_dim)
+                 workload.beta_std, workload.head_dim, workload.key_heads)
 
 
 def custom(n_seqs, n_tokens, n_heads, head_dim, dtype="f32", state="normal",
-           gate="standard", beta_std=1.0, seed=0):
+           gate="standard", beta_std=1.0, seed=0, key_heads=None):
     """Inputs of any shape with one of the recipes above (for edge cases)."""
     wl = Workload("custom", n_seqs, n_tokens, n_heads, head_dim, dtype, state,
-                  gate, beta_std=beta_std, seed=seed)
+                  gate, beta_std=beta_std, seed=seed, key_heads=key_heads)
     return make(wl)

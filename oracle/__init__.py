@@ -59,14 +59,30 @@ def max_threads() -> int:
     return int(_lib().oracle_max_threads())
 
 
+def tile_key_heads(x, n_heads: int):
+    """Expand q or k of n_key_heads heads to n_heads value heads in the tiled
+    order: value head h takes key head h mod n_key_heads ("ggml attention
+    kernels" model card, first bullet after the "Shapes, in torch order"
+    table).  n_key_heads must divide n_heads."""
+    x = np.asarray(x)
+    hk = x.shape[2]
+    if hk < 1 or n_heads % hk != 0:
+        raise ValueError("n_key_heads must divide n_heads")
+    return x[:, :, [h % hk for h in range(n_heads)]]
+
+
 def _prep(q, k, v, g, beta, state):
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    if np.ndim(q) == 4 and np.ndim(v) == 4 and np.shape(q)[2] != v.shape[2]:
+        q = tile_key_heads(q, v.shape[2])
+        k = tile_key_heads(k, v.shape[2])
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)
-    v = np.ascontiguousarray(v, dtype=np.float32)
     g = np.ascontiguousarray(g, dtype=np.float32)
     beta = np.ascontiguousarray(beta, dtype=np.float32)
     if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share shape (n_seqs, n_tokens, n_heads, d)")
+        raise ValueError("q, k, v must share shape (n_seqs, n_tokens, n_heads, d), or q "
+                         "and k hold a divisor of n_heads key heads")
     S, T, H, d = q.shape
     if g.shape != (S, T, H) or beta.shape != (S, T, H):
         raise ValueError("g and beta must be (n_seqs, n_tokens, n_heads)")
@@ -86,8 +102,9 @@ def gdn_recurrent(q, k, v, g, beta, state=None, threads: int = 0):
 
     q, k, v: (n_seqs, n_tokens, n_heads, d); g, beta: (n_seqs, n_tokens,
     n_heads); state: (n_seqs, n_heads, d, d) stored [value][key] or None for
-    zeros.  Values are taken as given (bf16 inputs should be passed already
-    rounded); all arithmetic is fp64.
+    zeros.  q and k may hold fewer (key) heads, tiled over the value heads as
+    ``tile_key_heads`` states.  Values are taken as given (bf16 inputs should
+    be passed already rounded); all arithmetic is fp64.
     """
     q, k, v, g, beta, state, (S, T, H, d) = _prep(q, k, v, g, beta, state)
     out = np.empty((S, T, H, d), dtype=np.float64)

@@ -152,3 +152,44 @@ def test_forward_noops_without_gpu(lib):
     # n_tokens == 0 with state_out == state_in: nothing to launch
     assert c(lib, T=0, q=None, k=None, v=None, g=None, beta=None, out=None,
              state_out=c.p["state_in"]) == OK
+
+
+def _tiled(lib, c, HK, **over):
+    """gdn_forward_tiled with the pointers of _Call c (q, k sized for H heads, so
+    any HK <= H fits).  Every call here must fail validation or be a no-op."""
+    a = dict(c.p)
+    a.update(over)
+    return lib.gdn_forward_tiled(c.dtype, a["q"], a["k"], a["v"], a["g"], a["beta"],
+                                 a["state_in"], a["out"], a["state_out"], over.get("S", c.S),
+                                 over.get("T", c.T), over.get("H", c.H), HK, c.D, a["ws"],
+                                 over.get("ws_bytes", c.ws_bytes), over.get("algo", c.algo),
+                                 None)
+
+
+def test_forward_tiled_rejects_before_launch(lib):
+    c = _Call(H=6)
+    assert _tiled(lib, c, 0) == E_SHAPE          # no key heads
+    assert _tiled(lib, c, -2) == E_SHAPE
+    assert _tiled(lib, c, 4) == E_SHAPE          # 4 does not divide 6
+    assert _tiled(lib, c, 7) == E_SHAPE          # more key heads than value heads
+    assert _tiled(lib, c, 3, q=None) == E_NULL
+    assert _tiled(lib, c, 3, k=c.p["k"] + 4) == E_ALIGN
+    assert _tiled(lib, c, 3, out=c.p["q"]) == E_ALIAS
+    assert _tiled(lib, c, 2, state_out=c.p["k"]) == E_ALIAS
+    # n_heads == 0 is a no-op whatever the (non-negative) key-head count
+    assert _tiled(lib, c, 0, H=0) == OK
+    assert _tiled(lib, c, 5, S=0) == E_SHAPE     # not a divisor of 6, even with no sequences
+    assert _tiled(lib, c, -1, H=0) == E_SHAPE
+
+
+def test_forward_tiled_q_extent_uses_key_heads(lib):
+    """q and k span n_key_heads heads: an output placed right after a one-head q
+    passes the aliasing checks (the call then stops at the workspace check, the
+    last one before a launch), one that starts inside it does not."""
+    c = _Call(H=4, T=64, D=32)
+    one_head_q = 1 * 64 * 1 * 32 * 4
+    q = c.p["ws"]  # q in the free region, so that only q can meet out
+    chunked = dict(algo=CHUNK, ws_bytes=0, q=q)
+    assert _tiled(lib, c, 1, out=q + one_head_q, **chunked) == E_WS
+    assert _tiled(lib, c, 1, out=q + one_head_q - 16, **chunked) == E_ALIAS
+    assert _tiled(lib, c, 4, out=q + one_head_q, **chunked) == E_ALIAS

@@ -280,3 +280,57 @@ def test_threads_do_not_change_results():
     o1, f1 = oracle.gdn_recurrent(q, k, v, g, beta, st, threads=1)
     o2, f2 = oracle.gdn_recurrent(q, k, v, g, beta, st, threads=4)
     assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+
+
+# ---- tiled key heads: value head h reads query/key head h mod n_key_heads -------
+
+@pytest.mark.parametrize("H,HK", [(6, 2), (6, 3), (4, 1)])
+def test_tiled_key_heads_beta_zero_closed_form(H, HK):
+    """With beta = 0, out_t(h) = exp(G_t(h)) M0(h) q_t(h mod HK) / sqrt(d): the
+    tiled order of the model card's first contract bullet, in closed form.  For
+    (6, 2) and (6, 3) the grouped order h // (H / HK) reads other heads, so it
+    would fail here."""
+    S, T, d = 2, 23, 8
+    _, _, v, g, beta, st = _problem(S, T, H, d, seed=11 * H + HK)
+    rng = np.random.default_rng(HK)
+    q = _unit(rng.standard_normal((S, T, HK, d)))
+    k = _unit(rng.standard_normal((S, T, HK, d)))
+    beta = np.zeros_like(beta)
+    out, fin = oracle.gdn_recurrent(q, k, v, g, beta, st)
+    G = np.exp(np.cumsum(g.astype(np.float64), axis=1))
+    M0 = st.astype(np.float64)
+    for h in range(H):
+        qh = q[:, :, h % HK, :].astype(np.float64)
+        expect = np.einsum("st,sij,stj->sti", G[:, :, h], M0[:, h], qh) / np.sqrt(d)
+        np.testing.assert_allclose(out[:, :, h, :], expect, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(fin, G[:, -1, :][:, :, None, None] * M0, rtol=1e-12, atol=1e-14)
+    if HK > 1:
+        grouped = [h // (H // HK) for h in range(H)]
+        assert grouped != [h % HK for h in range(H)]
+
+
+@pytest.mark.parametrize("algo", ["recurrent", "chunked"])
+def test_tiled_key_heads_per_head(algo):
+    """Full recurrence: value head h of a tiled call equals a one-head call on
+    q, k of key head h mod HK and v, g, beta, state of head h."""
+    S, T, H, HK, d = 1, 70, 6, 3, 16
+    _, _, v, g, beta, st = _problem(S, T, H, d, seed=5)
+    rng = np.random.default_rng(6)
+    q = _unit(rng.standard_normal((S, T, HK, d)))
+    k = _unit(rng.standard_normal((S, T, HK, d)))
+    run = oracle.gdn_recurrent if algo == "recurrent" else oracle.gdn_chunked
+    out, fin = run(q, k, v, g, beta, st)
+    for h in range(H):
+        j = h % HK
+        o1, f1 = oracle.gdn_recurrent(q[:, :, j:j + 1], k[:, :, j:j + 1], v[:, :, h:h + 1],
+                                      g[:, :, h:h + 1], beta[:, :, h:h + 1], st[:, h:h + 1])
+        np.testing.assert_allclose(out[:, :, h:h + 1], o1, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(fin[:, h:h + 1], f1, rtol=1e-11, atol=1e-12)
+
+
+def test_tiled_key_heads_rejects_non_divisor():
+    q = np.zeros((1, 3, 4, 8), np.float32)
+    v = np.zeros((1, 3, 6, 8), np.float32)
+    g = np.zeros((1, 3, 6), np.float32)
+    with pytest.raises(ValueError):
+        oracle.gdn_recurrent(q, q, v, g, g)

@@ -136,6 +136,37 @@ def test_many_row_blocks(gdn, dtype):
     check(gdn, x, dtype, "chunked", what="many row blocks")
 
 
+# ---- q and k with fewer (key) heads, tiled over the value heads ---------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("HK", [1, 2, 3])
+@pytest.mark.parametrize("T,algo", [(1, "recurrent"), (7, "recurrent"), (63, "chunked"),
+                                    (130, "chunked")])
+def test_tiled_key_heads(gdn, dtype, HK, T, algo):
+    x = inputs.custom(2, T, 6, 64, dtype=dtype, state="normal", seed=900 + 10 * HK + T,
+                      key_heads=HK)
+    assert x["q"].shape[2] == HK and x["v"].shape[2] == 6
+    check(gdn, x, dtype, algo, what="tiled key heads HK=%d T=%d" % (HK, T))
+
+
+@pytest.mark.parametrize("algo", ["recurrent", "chunked"])
+def test_tiled_equals_expanded_copy(gdn, algo):
+    """The tiled call reads the same values as a call on q, k expanded to one head
+    per value head (h -> h mod HK), so the results are identical bit for bit."""
+    x = inputs.custom(1, 200, 8, 128, dtype="bf16", state="normal", seed=31, key_heads=2)
+    a = run_gpu(gdn, x, "bf16", algo)
+    y = dict(x)
+    idx = [h % 2 for h in range(8)]
+    y["q"], y["k"] = x["q"][:, :, idx], x["k"][:, :, idx]
+    b = run_gpu(gdn, y, "bf16", algo)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_tiled_prefill_workload(gdn):
+    """The full 4096-token prefill with 32 value heads over 16 query/key heads."""
+    check(gdn, inputs.make(inputs.GQA_PREFILL), "bf16", "auto", what="tiled prefill 4096")
+
+
 def test_zero_initial_state_pointer(gdn):
     x = inputs.custom(1, 70, 2, 64, dtype="f32", state="zeros", seed=1)
     check(gdn, x, "f32", "auto", state=False, what="state None")
@@ -222,3 +253,8 @@ def test_rejects_bad_arguments(gdn):
     g = torch.zeros((1, 4, 2), device="cuda")
     with pytest.raises(gdn.GdnError):
         gdn.forward(q48, q48, q48, g, g, None)
+    q3 = torch.zeros((1, 4, 3, 64), device="cuda")
+    v2 = torch.zeros((1, 4, 2, 64), device="cuda")
+    g2 = torch.zeros((1, 4, 2), device="cuda")
+    with pytest.raises(gdn.GdnError):
+        gdn.forward(q3, q3, v2, g2, g2, None)   # 3 key heads do not tile 2 value heads
