@@ -62,6 +62,7 @@ class Workload:
     seed: int = 0
     per_seq_seeds: bool = False  # spawn one child seed per sequence
     key_heads: Optional[int] = None  # heads of q and k (None: n_heads)
+    raw: bool = False  # leave q, k unnormalised and g, beta as pre-activations
 
     def shape(self):
         return (self.n_seqs, self.n_tokens, self.n_heads, self.head_dim)
@@ -89,13 +90,15 @@ GQA_PREFILL = Workload("prefill_tiled_bf16", 1, 4096, 32, 128, "bf16", "zeros", 
                        seed=6000, key_heads=16)
 
 
-def _draw(rng, shape, dtype, state_kind, gate, beta_std, head_dim, key_heads=None):
+def _draw(rng, shape, dtype, state_kind, gate, beta_std, head_dim, key_heads=None, raw=False):
     S, T, H, d = shape
     HK = H if key_heads is None else key_heads
     q = rng.standard_normal((S, T, HK, d), dtype=np.float32)
     k = rng.standard_normal((S, T, HK, d), dtype=np.float32)
     v = rng.standard_normal((S, T, H, d), dtype=np.float32)
     zg = rng.standard_normal((S, T, H), dtype=np.float32)
+    if raw and gate != "standard":
+        raise ValueError("raw inputs use the standard gate recipe")
     if gate == "mixed":
         zs = rng.standard_normal((S, T, H), dtype=np.float32) + np.float32(4.0)
         sel = rng.random((S, T, H), dtype=np.float32) < np.float32(0.1)
@@ -115,8 +118,13 @@ def _draw(rng, shape, dtype, state_kind, gate, beta_std, head_dim, key_heads=Non
         st = np.zeros((S, H, d, d), dtype=np.float32)
     else:
         raise ValueError("unknown state recipe %r" % state_kind)
-    q = _l2norm(q)
-    k = _l2norm(k)
+    if raw:
+        # the pre-activations and unnormalised rows that the transforms above
+        # would turn into g, beta, q and k
+        g, beta = zg, zb
+    else:
+        q = _l2norm(q)
+        k = _l2norm(k)
     if dtype == "bf16":
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     elif dtype != "f32":
@@ -141,7 +149,7 @@ def make(workload: Workload, layer: int = 0, seq: Optional[int] = None):
             rng = np.random.default_rng(children[s])
             parts.append(_draw(rng, (1,) + shape[1:], workload.dtype,
                                workload.state, workload.gate, workload.beta_std,
-                               workload.head_dim, workload.key_heads))
+                               workload.head_dim, workload.key_heads, workload.raw))
         if len(parts) == 1:
             return parts[0]
         return {key: np.concatenate([p[key] for p in parts], axis=0)
@@ -150,12 +158,12 @@ def make(workload: Workload, layer: int = 0, seq: Optional[int] = None):
         raise ValueError("this workload draws all sequences from one seed")
     rng = np.random.default_rng(base)
     return _draw(rng, shape, workload.dtype, workload.state, workload.gate,
-                 workload.beta_std, workload.head_dim, workload.key_heads)
+                 workload.beta_std, workload.head_dim, workload.key_heads, workload.raw)
 
 
 def custom(n_seqs, n_tokens, n_heads, head_dim, dtype="f32", state="normal",
-           gate="standard", beta_std=1.0, seed=0, key_heads=None):
+           gate="standard", beta_std=1.0, seed=0, key_heads=None, raw=False):
     """Inputs of any shape with one of the recipes above (for edge cases)."""
     wl = Workload("custom", n_seqs, n_tokens, n_heads, head_dim, dtype, state,
-                  gate, beta_std=beta_std, seed=seed, key_heads=key_heads)
+                  gate, beta_std=beta_std, seed=seed, key_heads=key_heads, raw=raw)
     return make(wl)

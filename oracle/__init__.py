@@ -42,7 +42,7 @@ def _lib():
     lib.oracle_gdn_recurrent.restype = ctypes.c_int
     lib.oracle_gdn_recurrent.argtypes = [
         _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_void_p, _f64p, _f64p,
-        _L, _L, _L, _L, ctypes.c_int]
+        _L, _L, _L, _L, ctypes.c_int, ctypes.c_int]
     lib.oracle_gdn_chunked.restype = ctypes.c_int
     lib.oracle_gdn_chunked.argtypes = [
         _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_void_p, _f64p, _f64p,
@@ -97,20 +97,29 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def gdn_recurrent(q, k, v, g, beta, state=None, threads: int = 0):
+# Input transforms the C oracle can apply first (see gdn_oracle.c)
+L2NORM_QK = 1
+RAW_GATES = 2
+
+
+def gdn_recurrent(q, k, v, g, beta, state=None, threads: int = 0, l2norm_qk: bool = False,
+                  raw_gates: bool = False):
     """Token-sequential fp64 recurrence.  Returns (out, final_state) as float64.
 
     q, k, v: (n_seqs, n_tokens, n_heads, d); g, beta: (n_seqs, n_tokens,
     n_heads); state: (n_seqs, n_heads, d, d) stored [value][key] or None for
     zeros.  q and k may hold fewer (key) heads, tiled over the value heads as
     ``tile_key_heads`` states.  Values are taken as given (bf16 inputs should
-    be passed already rounded); all arithmetic is fp64.
+    be passed already rounded); all arithmetic is fp64.  ``l2norm_qk`` divides
+    each q and k row by sqrt(|row|^2 + 1e-6) first; ``raw_gates`` takes g and
+    beta as pre-activations, g <- -softplus(g) and beta <- sigmoid(beta).
     """
     q, k, v, g, beta, state, (S, T, H, d) = _prep(q, k, v, g, beta, state)
     out = np.empty((S, T, H, d), dtype=np.float64)
     fin = np.empty((S, H, d, d), dtype=np.float64)
+    flags = (L2NORM_QK if l2norm_qk else 0) | (RAW_GATES if raw_gates else 0)
     rc = _lib().oracle_gdn_recurrent(q, k, v, g, beta, _ptr(state), out, fin,
-                                     S, T, H, d, int(threads))
+                                     S, T, H, d, flags, int(threads))
     if rc != 0:
         raise MemoryError("oracle_gdn_recurrent failed (%d)" % rc)
     return out, fin

@@ -73,38 +73,77 @@ static long idx_state(long s, long h, long i, long j, long H, long d)
     return ((s * H + h) * d + i) * d + j;
 }
 
-/* Token-sequential recurrence for one (seq, head).  M is d*d doubles, u is d
+/* Optional transforms of raw inputs, applied in fp64 before the step (the
+ * steps that precede the op in a model layer, done inside it on request):
+ *   ORACLE_L2NORM_QK  q_t <- q_t / sqrt(|q_t|^2 + ORACLE_L2_EPS), same for k_t
+ *   ORACLE_RAW_GATES  g_t <- -softplus(g_t) = -log(1 + exp(g_t)),
+ *                     beta_t <- sigmoid(beta_t) = 1 / (1 + exp(-beta_t))
+ * The epsilon keeps an all-zero row at zero instead of dividing by zero. */
+#define ORACLE_L2NORM_QK 1
+#define ORACLE_RAW_GATES 2
+#define ORACLE_L2_EPS 1e-6
+
+/* x <- x / sqrt(|x|^2 + eps) */
+static void l2_normalize(double *x, long d)
+{
+    double ss = 0.0;
+    for (long j = 0; j < d; ++j)
+        ss += x[j] * x[j];
+    const double r = 1.0 / sqrt(ss + ORACLE_L2_EPS);
+    for (long j = 0; j < d; ++j)
+        x[j] *= r;
+}
+
+/* log(1 + exp(x)) without overflow: max(x, 0) + log1p(exp(-|x|)) */
+static double softplus(double x)
+{
+    return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+}
+
+/* Token-sequential recurrence for one (seq, head).  M is d*d doubles, u is 3*d
  * doubles of scratch. */
 static void recur_one(const float *q, const float *k, const float *v,
                       const float *g, const float *beta, double *out,
                       double *M, double *u, long s, long h, long T, long H,
-                      long d)
+                      long d, int flags)
 {
     const double scale = 1.0 / sqrt((double)d);
+    double *kt = u + d, *qt = u + 2 * d;
     for (long t = 0; t < T; ++t) {
-        const float *kt = k + idx_tok(s, t, h, 0, T, H, d);
-        const float *qt = q + idx_tok(s, t, h, 0, T, H, d);
+        for (long j = 0; j < d; ++j) {
+            kt[j] = (double)k[idx_tok(s, t, h, j, T, H, d)];
+            qt[j] = (double)q[idx_tok(s, t, h, j, T, H, d)];
+        }
         const float *vt = v + idx_tok(s, t, h, 0, T, H, d);
-        const double alpha = exp((double)g[idx_gate(s, t, h, T, H)]);
-        const double b = (double)beta[idx_gate(s, t, h, T, H)];
+        double gt = (double)g[idx_gate(s, t, h, T, H)];
+        double b = (double)beta[idx_gate(s, t, h, T, H)];
+        if (flags & ORACLE_L2NORM_QK) {
+            l2_normalize(kt, d);
+            l2_normalize(qt, d);
+        }
+        if (flags & ORACLE_RAW_GATES) {
+            gt = -softplus(gt);
+            b = 1.0 / (1.0 + exp(-b));
+        }
+        const double alpha = exp(gt);
 
         for (long i = 0; i < d * d; ++i)
             M[i] *= alpha;
         for (long i = 0; i < d; ++i) {
             double acc = 0.0;
             for (long j = 0; j < d; ++j)
-                acc += M[i * d + j] * (double)kt[j];
+                acc += M[i * d + j] * kt[j];
             u[i] = acc;
         }
         for (long i = 0; i < d; ++i) {
             const double delta = b * ((double)vt[i] - u[i]);
             for (long j = 0; j < d; ++j)
-                M[i * d + j] += delta * (double)kt[j];
+                M[i * d + j] += delta * kt[j];
         }
         for (long i = 0; i < d; ++i) {
             double acc = 0.0;
             for (long j = 0; j < d; ++j)
-                acc += M[i * d + j] * (double)qt[j];
+                acc += M[i * d + j] * qt[j];
             out[idx_tok(s, t, h, i, T, H, d)] = scale * acc;
         }
     }
@@ -130,20 +169,23 @@ int oracle_max_threads(void)
 }
 
 /* out: (S, T, H, d) fp64.  state_out: (S, H, d, d) fp64.  state_in may be NULL
- * for a zero initial state.  Returns 0, or -1 on allocation failure. */
+ * for a zero initial state.  flags: ORACLE_L2NORM_QK | ORACLE_RAW_GATES or 0.
+ * Returns 0, or -1 on allocation failure or unknown flags. */
 int oracle_gdn_recurrent(const float *q, const float *k, const float *v,
                          const float *g, const float *beta,
                          const double *state_in, double *out,
                          double *state_out, long S, long T, long H, long d,
-                         int n_threads)
+                         int flags, int n_threads)
 {
+    if (flags & ~(ORACLE_L2NORM_QK | ORACLE_RAW_GATES))
+        return -1;
     int failed = 0;
     set_threads(n_threads);
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
     for (long sh = 0; sh < S * H; ++sh) {
         const long s = sh / H, h = sh % H;
         double *M = state_out + idx_state(s, h, 0, 0, H, d);
-        double *u = (double *)malloc(sizeof(double) * (size_t)d);
+        double *u = (double *)malloc(sizeof(double) * (size_t)(3 * d));
         if (!u) {
             failed = 1;
             continue;
@@ -153,7 +195,7 @@ int oracle_gdn_recurrent(const float *q, const float *k, const float *v,
                    sizeof(double) * (size_t)(d * d));
         else
             memset(M, 0, sizeof(double) * (size_t)(d * d));
-        recur_one(q, k, v, g, beta, out, M, u, s, h, T, H, d);
+        recur_one(q, k, v, g, beta, out, M, u, s, h, T, H, d, flags);
         free(u);
     }
     return failed ? -1 : 0;

@@ -334,3 +334,84 @@ def test_tiled_key_heads_rejects_non_divisor():
     g = np.zeros((1, 3, 6), np.float32)
     with pytest.raises(ValueError):
         oracle.gdn_recurrent(q, q, v, g, g)
+
+
+# ---- input transforms applied inside the op (raw gates, L2-normalised q/k) -------
+
+def test_raw_gates_closed_forms():
+    """Raw gates: g = -softplus(a), beta = sigmoid(b).  With a = ln 3 every token
+    decays the state by exactly 1/4 (softplus(ln 3) = ln 4; the mirrored
+    softplus(-a) would give 3/4), and with b = -60 the write is negligible, so
+    out_t = 4^-(t+1) M0 q_t / sqrt(d).  With M0 = 0 and b = ln 3, one token
+    writes beta = 3/4 (sigmoid(-b) would give 1/4): out = (3/4) (k.q) v / sqrt(d)."""
+    S, T, H, d = 1, 9, 2, 8
+    q, k, v, g, beta, st = _problem(S, T, H, d, seed=77)
+    a = np.full_like(g, np.log(3.0))
+    out, fin = oracle.gdn_recurrent(q, k, v, a, np.full_like(beta, -60.0), st, raw_gates=True)
+    decay = 0.25 ** np.arange(1, T + 1)
+    expect = np.einsum("t,shij,sthj->sthi", decay, st.astype(np.float64),
+                       q.astype(np.float64)) / np.sqrt(d)
+    # ln 3 is stored in fp32 (relative error ~3e-8), hence rtol 1e-6 below: far
+    # tighter than the 3x gap between softplus(a) and softplus(-a)
+    np.testing.assert_allclose(out, expect, rtol=1e-6, atol=1e-14)
+    np.testing.assert_allclose(fin, 0.25 ** T * st.astype(np.float64), rtol=1e-6, atol=1e-14)
+    o1, f1 = oracle.gdn_recurrent(q[:, :1], k[:, :1], v[:, :1], g[:, :1],
+                                  np.full_like(beta[:, :1], np.log(3.0)), None, raw_gates=True)
+    kq = np.sum(k[:, 0].astype(np.float64) * q[:, 0], axis=-1)          # (S, H)
+    np.testing.assert_allclose(o1[:, 0], 0.75 * kq[..., None] * v[:, 0] / np.sqrt(d),
+                               rtol=1e-6, atol=1e-14)
+    np.testing.assert_allclose(f1, 0.75 * np.einsum("shi,shj->shij", v[:, 0].astype(np.float64),
+                                                    k[:, 0].astype(np.float64)),
+                               rtol=1e-6, atol=1e-14)
+
+
+def test_l2norm_scale_invariance_and_unit_rows():
+    """L2-normalised q and k: scaling raw q or k rows by positive factors leaves
+    the result unchanged (up to the 1e-6 epsilon), and unit rows give the plain
+    result (up to the same epsilon).  Without the flag scaling k changes it."""
+    S, T, H, d = 2, 40, 3, 16
+    q, k, v, g, beta, st = _problem(S, T, H, d, seed=78)
+    rng = np.random.default_rng(79)
+    cq = rng.uniform(0.5, 20.0, (S, T, H, 1)).astype(np.float32)
+    ck = rng.uniform(0.5, 20.0, (S, T, H, 1)).astype(np.float32)
+    o_unit, f_unit = oracle.gdn_recurrent(q, k, v, g, beta, st, l2norm_qk=True)
+    o_plain, f_plain = oracle.gdn_recurrent(q, k, v, g, beta, st)
+    o_sc, f_sc = oracle.gdn_recurrent(q * cq, k * ck, v, g, beta, st, l2norm_qk=True)
+    np.testing.assert_allclose(o_unit, o_plain, rtol=0, atol=1e-5)
+    np.testing.assert_allclose(f_unit, f_plain, rtol=0, atol=1e-5)
+    np.testing.assert_allclose(o_sc, o_unit, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(f_sc, f_unit, rtol=0, atol=1e-6)
+    o_raw, _ = oracle.gdn_recurrent(q, k * ck, v, g, beta, st)
+    assert np.max(np.abs(o_raw - o_plain)) > 1e-2
+
+
+def test_l2norm_zero_rows_stay_finite():
+    """An all-zero key row writes nothing and an all-zero query row reads zero."""
+    S, T, H, d = 1, 6, 1, 8
+    q, k, v, g, beta, st = _problem(S, T, H, d, seed=80)
+    k[0, 2] = 0.0
+    q[0, 4] = 0.0
+    out, fin = oracle.gdn_recurrent(q, k, v, g, beta, st, l2norm_qk=True)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(fin))
+    assert np.all(out[0, 4] == 0.0)
+    # token 2 only decays the state
+    o2, f2 = oracle.gdn_recurrent(q[:, :2], k[:, :2], v[:, :2], g[:, :2], beta[:, :2], st,
+                                  l2norm_qk=True)
+    o3, f3 = oracle.gdn_recurrent(q[:, :3], k[:, :3], v[:, :3], g[:, :3], beta[:, :3], st,
+                                  l2norm_qk=True)
+    np.testing.assert_allclose(f3, np.exp(np.float64(g[0, 2, 0])) * f2, rtol=1e-13, atol=1e-15)
+
+
+def test_raw_inputs_match_transformed_inputs():
+    """The raw recipe of the input generator holds the pre-activations and the
+    unnormalised rows of the standard recipe: transforming them inside the
+    oracle reproduces the result on the generator's transformed inputs (up to
+    those inputs' fp32 rounding and the 1e-6 epsilon)."""
+    raw = inputs.custom(1, 50, 3, 16, dtype="f32", state="normal", seed=81, raw=True)
+    std = inputs.custom(1, 50, 3, 16, dtype="f32", state="normal", seed=81)
+    o1, f1 = oracle.gdn_recurrent(raw["q"], raw["k"], raw["v"], raw["g"], raw["beta"],
+                                  raw["state"], l2norm_qk=True, raw_gates=True)
+    o2, f2 = oracle.gdn_recurrent(std["q"], std["k"], std["v"], std["g"], std["beta"],
+                                  std["state"])
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-5)
+    np.testing.assert_allclose(f1, f2, rtol=0, atol=1e-5)
