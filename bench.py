@@ -17,6 +17,7 @@ call reads inputs the cache no longer holds.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -85,8 +86,9 @@ def to_dev(x, dtype, torch):
 class Slot:
     """One resident copy of a workload's inputs plus its output buffers."""
 
-    def __init__(self, gdn, d, torch):
+    def __init__(self, gdn, d, torch, pre=None):
         self.d = d
+        self.pre = pre or {}
         v = d["v"]
         S, T, H, D = v.shape
         self.out = torch.empty_like(v)
@@ -97,7 +99,7 @@ class Slot:
     def run(self, gdn):
         d = self.d
         gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], out=self.out,
-                    state_out=self.state_out, workspace=self.ws)
+                    state_out=self.state_out, workspace=self.ws, **self.pre)
 
 
 def clone_dev(d):
@@ -117,11 +119,11 @@ def time_loop(torch, fn, n):
     return a.elapsed_time(b) / n
 
 
-def bench_prefill(gdn, torch, wl, steps, warmup, nbuf):
+def bench_prefill(gdn, torch, wl, steps, warmup, nbuf, pre=None):
     from linear_attention_recurrence_03_amd import inputs
     x = inputs.make(wl)
     base = to_dev(x, wl.dtype, torch)
-    slots = [Slot(gdn, base if i == 0 else clone_dev(base), torch) for i in range(nbuf)]
+    slots = [Slot(gdn, base if i == 0 else clone_dev(base), torch, pre) for i in range(nbuf)]
     del x
     for i in range(warmup):
         slots[i % nbuf].run(gdn)
@@ -353,6 +355,18 @@ def main():
             "hbm_frac": round(bt / (mst * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "workload": "1 seq x 4096 tokens x 32 value heads (16 query/key heads, tiled) x "
                         "d128 bf16, zero state, 4 rotating input copies"}
+        # the same with raw inputs: q/k rows normalised and gates activated inside the op
+        wlr = dataclasses.replace(wlt, raw=True)
+        msr, slots = bench_prefill(gdn, torch, wlr, steps=100, warmup=10, nbuf=4,
+                                   pre={"l2norm_qk": True, "raw_gates": True})
+        del slots
+        torch.cuda.empty_cache()
+        extras["prefill_tiled_raw"] = {
+            "tokens_per_s": round(St * Tt / (msr * 1e-3), 1), "us_per_call": round(msr * 1e3, 2),
+            "bytes_per_call": bt,
+            "hbm_frac": round(bt / (msr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "workload": "as prefill_tiled, with unnormalised q/k rows and raw gate "
+                        "pre-activations transformed inside the op"}
         line["extras"] = extras
 
     if not args.no_cpu_baseline:

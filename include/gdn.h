@@ -80,7 +80,24 @@ enum {
     GDN_ERR_MISALIGNED = -7,           /* a pointer is not 16-byte aligned    */
     GDN_ERR_ALIASING = -8,             /* out overlaps an input, or state_out
                                           overlaps state_in without being equal */
-    GDN_ERR_HIP = -9                   /* the HIP runtime refused a launch     */
+    GDN_ERR_HIP = -9,                  /* the HIP runtime refused a launch     */
+    GDN_ERR_BAD_FLAGS = -10            /* unknown bits in gdn_forward_ex flags */
+};
+
+/* Input transforms gdn_forward_ex can apply inside the op (bit mask).  They are
+ * the steps that come just before the recurrence in a model layer (the pages
+ * count eager torch's version of a layer at ~200 ops: model card, section
+ * "Ops", the sentence under the op list):
+ *   GDN_PRE_L2NORM_QK  each q and k row (head_dim values) is divided by
+ *                      sqrt(sum of its squares + 1e-6), in fp32, before use;
+ *                      the epsilon keeps an all-zero row at zero
+ *   GDN_PRE_RAW_GATES  g and beta are pre-activations: the op uses
+ *                      g := -softplus(g) = -log(1 + exp(g)) as the log-domain
+ *                      gate and beta := sigmoid(beta) = 1 / (1 + exp(-beta)) */
+enum {
+    GDN_PRE_NONE = 0,
+    GDN_PRE_L2NORM_QK = 1,
+    GDN_PRE_RAW_GATES = 2
 };
 
 /* 1 if head_dim is supported, else 0.  Supported widths are the multiples of 32
@@ -145,6 +162,23 @@ int gdn_forward_tiled(gdn_dtype dtype, const void *q, const void *k, const void 
                       int64_t n_heads, int64_t n_key_heads, int head_dim,
                       void *workspace, size_t workspace_bytes, gdn_algo algo,
                       void *stream);
+
+/* The general form: gdn_forward_tiled plus input transforms.
+ *
+ *   n_key_heads  as in gdn_forward_tiled (n_heads for one key head per value
+ *                head)
+ *   flags        GDN_PRE_NONE or an OR of GDN_PRE_L2NORM_QK and
+ *                GDN_PRE_RAW_GATES; other bits return GDN_ERR_BAD_FLAGS.  With
+ *                GDN_PRE_RAW_GATES, g may hold any finite value.
+ *
+ * Everything else is as in gdn_forward; flags == GDN_PRE_NONE with
+ * n_key_heads == n_heads is exactly gdn_forward. */
+int gdn_forward_ex(gdn_dtype dtype, const void *q, const void *k, const void *v,
+                   const float *g, const float *beta, const float *state_in,
+                   void *out, float *state_out, int64_t n_seqs, int64_t n_tokens,
+                   int64_t n_heads, int64_t n_key_heads, int head_dim,
+                   unsigned int flags, void *workspace, size_t workspace_bytes,
+                   gdn_algo algo, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *gdn_status_string(int status);

@@ -17,6 +17,9 @@ __all__ = ["forward", "supports", "workspace_size", "status_string", "library_pa
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
+# input transforms (gdn.h GDN_PRE_*)
+PRE_L2NORM_QK = 1
+PRE_RAW_GATES = 2
 _DTYPES = {"f32": 0, "bf16": 1}
 _LIB = None
 
@@ -54,6 +57,10 @@ def _lib():
     lib.gdn_forward_tiled.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
                                       i64, i64, ctypes.c_int, vp, ctypes.c_size_t,
                                       ctypes.c_int, vp]
+    lib.gdn_forward_ex.restype = ctypes.c_int
+    lib.gdn_forward_ex.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
+                                   i64, i64, ctypes.c_int, ctypes.c_uint, vp, ctypes.c_size_t,
+                                   ctypes.c_int, vp]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_version.restype = ctypes.c_int
@@ -83,7 +90,7 @@ def _ptr(t):
 
 
 def forward(q, k, v, g, beta, state=None, algo: str = "auto", out=None, state_out=None,
-            workspace=None, stream=None):
+            workspace=None, stream=None, l2norm_qk: bool = False, raw_gates: bool = False):
     """Run the gated delta rule over all tokens.  Returns (out, final_state).
 
     q, k, v: (n_seqs, n_tokens, n_heads, head_dim) float32 or bfloat16 CUDA
@@ -93,6 +100,8 @@ def forward(q, k, v, g, beta, state=None, algo: str = "auto", out=None, state_ou
     n_heads) float32; state:
     (n_seqs, n_heads, head_dim, head_dim) float32 stored [value][key], or None
     for zeros.  ``state_out`` may be ``state`` itself for an in-place update.
+    ``l2norm_qk`` normalises each q and k row inside the op; ``raw_gates`` takes
+    g and beta as pre-activations (g := -softplus(g), beta := sigmoid(beta)).
     Work is enqueued on ``stream`` (default: torch's current stream); nothing
     is synchronised.
     """
@@ -148,7 +157,12 @@ def forward(q, k, v, g, beta, state=None, algo: str = "auto", out=None, state_ou
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     handle = ctypes.c_void_p(stream.cuda_stream)
-    if HK == H:
+    flags = (PRE_L2NORM_QK if l2norm_qk else 0) | (PRE_RAW_GATES if raw_gates else 0)
+    if flags:
+        rc = lib.gdn_forward_ex(_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(state), _ptr(out), _ptr(state_out), S, T, H, HK, D, flags,
+                                _ptr(workspace), ws_bytes, a, handle)
+    elif HK == H:
         rc = lib.gdn_forward(_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                              _ptr(state), _ptr(out), _ptr(state_out), S, T, H, D,
                              _ptr(workspace), ws_bytes, a, handle)

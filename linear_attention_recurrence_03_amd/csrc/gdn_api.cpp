@@ -80,8 +80,8 @@ int check_shape(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens, int64_t n_hea
 int forward_impl(gdn_dtype dtype, const void *q, const void *k, const void *v, const float *g,
                  const float *beta, const float *state_in, void *out, float *state_out,
                  int64_t n_seqs, int64_t n_tokens, int64_t n_heads, int64_t n_key_heads,
-                 int head_dim, void *workspace, size_t workspace_bytes, gdn_algo algo,
-                 void *stream);
+                 int head_dim, unsigned flags, void *workspace, size_t workspace_bytes,
+                 gdn_algo algo, void *stream);
 
 }  // namespace
 
@@ -109,7 +109,8 @@ int gdn_forward(gdn_dtype dtype, const void *q, const void *k, const void *v, co
                 void *workspace, size_t workspace_bytes, gdn_algo algo, void *stream)
 {
     return forward_impl(dtype, q, k, v, g, beta, state_in, out, state_out, n_seqs, n_tokens,
-                        n_heads, n_heads, head_dim, workspace, workspace_bytes, algo, stream);
+                        n_heads, n_heads, head_dim, GDN_PRE_NONE, workspace, workspace_bytes,
+                        algo, stream);
 }
 
 int gdn_forward_tiled(gdn_dtype dtype, const void *q, const void *k, const void *v,
@@ -119,7 +120,18 @@ int gdn_forward_tiled(gdn_dtype dtype, const void *q, const void *k, const void 
                       size_t workspace_bytes, gdn_algo algo, void *stream)
 {
     return forward_impl(dtype, q, k, v, g, beta, state_in, out, state_out, n_seqs, n_tokens,
-                        n_heads, n_key_heads, head_dim, workspace, workspace_bytes, algo,
+                        n_heads, n_key_heads, head_dim, GDN_PRE_NONE, workspace,
+                        workspace_bytes, algo, stream);
+}
+
+int gdn_forward_ex(gdn_dtype dtype, const void *q, const void *k, const void *v, const float *g,
+                   const float *beta, const float *state_in, void *out, float *state_out,
+                   int64_t n_seqs, int64_t n_tokens, int64_t n_heads, int64_t n_key_heads,
+                   int head_dim, unsigned int flags, void *workspace, size_t workspace_bytes,
+                   gdn_algo algo, void *stream)
+{
+    return forward_impl(dtype, q, k, v, g, beta, state_in, out, state_out, n_seqs, n_tokens,
+                        n_heads, n_key_heads, head_dim, flags, workspace, workspace_bytes, algo,
                         stream);
 }
 
@@ -136,6 +148,7 @@ const char *gdn_status_string(int status)
     case GDN_ERR_MISALIGNED: return "pointer not 16-byte aligned";
     case GDN_ERR_ALIASING: return "output overlaps an input (only state_out == state_in is allowed)";
     case GDN_ERR_HIP: return "HIP runtime refused a launch";
+    case GDN_ERR_BAD_FLAGS: return "unknown bits in the input-transform flags";
     default: return "unknown status";
     }
 }
@@ -152,13 +165,14 @@ namespace {
 int forward_impl(gdn_dtype dtype, const void *q, const void *k, const void *v, const float *g,
                  const float *beta, const float *state_in, void *out, float *state_out,
                  int64_t n_seqs, int64_t n_tokens, int64_t n_heads, int64_t n_key_heads,
-                 int head_dim, void *workspace, size_t workspace_bytes, gdn_algo algo,
-                 void *stream)
+                 int head_dim, unsigned flags, void *workspace, size_t workspace_bytes,
+                 gdn_algo algo, void *stream)
 {
     int64_t tok_elems, gate_elems, state_elems;
     int rc = check_shape(dtype, n_seqs, n_tokens, n_heads, head_dim, algo, &tok_elems,
                          &gate_elems, &state_elems);
     if (rc != GDN_OK) return rc;
+    if (flags & ~unsigned(GDN_PRE_L2NORM_QK | GDN_PRE_RAW_GATES)) return GDN_ERR_BAD_FLAGS;
     if (n_key_heads < 0) return GDN_ERR_BAD_SHAPE;
     if (n_heads > 0 && (n_key_heads == 0 || n_heads % n_key_heads != 0)) return GDN_ERR_BAD_SHAPE;
     if (n_seqs == 0 || n_heads == 0) return GDN_OK;
@@ -227,6 +241,8 @@ int forward_impl(gdn_dtype dtype, const void *q, const void *k, const void *v, c
     p.n_tokens = n_tokens;
     p.n_heads = n_heads;
     p.n_k_heads = n_key_heads;
+    p.l2norm_qk = (flags & GDN_PRE_L2NORM_QK) ? 1 : 0;
+    p.raw_gates = (flags & GDN_PRE_RAW_GATES) ? 1 : 0;
     p.head_dim = head_dim;
     if (chosen == GDN_ALGO_CHUNKED)
         err = gdn::launch_chunked(p, workspace, st);

@@ -243,7 +243,8 @@ struct WsLayout {
     static constexpr int64_t kT = 0;
     static constexpr int64_t kP = 6 * kBlkBytes<BF16>;
     static constexpr int64_t kGates = 2 * kP;
-    static constexpr int64_t kBytes = kGates + 4 * C * 4;
+    // gates: rows of C floats, then room up to 2 KiB
+    static constexpr int64_t kBytes = kGates + 8 * C * 4;
 };
 
 // A operand from rows of a padded row-major LDS matrix: lane (g, r) gets row
@@ -310,7 +311,8 @@ struct PrepSmem {
                                                                              : 2 * kMat + 6 * kBlkBytes<BF16>;
     static constexpr int kD = kR;                        // 4 x [16][LDD] fp32
     static constexpr int kG = kD + 4 * 16 * LDD * 4;     // gates
-    static constexpr int kBytes = kG + (4 * C + 4) * 4;
+    static constexpr int kN = kG + (4 * C + 4) * 4;      // 1/|k_r|, 1/|q_r| (normalised rows)
+    static constexpr int kBytes = kN + 2 * C * 4;
     static constexpr int NBK = C * RK / 1024;            // DMA blocks per matrix
     static_assert(C * RK % 1024 == 0 && kMat % 16 == 0 && kR % 16 == 0, "layout");
 };
@@ -329,7 +331,8 @@ struct PrepTiles {
 
 template <int D, bool BF16, bool KK, int R0, int R1>
 __device__ __forceinline__ void prep_products(PrepTiles<R0, R1> &pt, const unsigned char *smem,
-                                              const float *sG, float *sD, int lane)
+                                              const float *sG, float *sD, const float *sN,
+                                              int lane)
 {
     using L = PrepSmem<D, BF16>;
     constexpr int KS = D / 32;
@@ -349,6 +352,11 @@ __device__ __forceinline__ void prep_products(PrepTiles<R0, R1> &pt, const unsig
             for (int ks = 0; ks < KS; ++ks)
                 acc = mma(fa[ks], row_frag<BF16>(sK, L::RK, 16 * tc + cl, 32 * ks, gq), acc);
             const int col = 16 * tc + cl;
+            if (sN) {  // normalised rows: (x_r / |x_r|) . (k_s / |k_s|)
+                const float rc = sN[col];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] *= sN[(KK ? 0 : C) + 16 * tr + 4 * gq + j] * rc;
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * tr + 4 * gq + j;
@@ -434,7 +442,7 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, unsigned char *__restrict__ ws, int64_t n_tokens,
-    int64_t n_heads, int64_t n_k_heads, int n_chunks)
+    int64_t n_heads, int64_t n_k_heads, int n_chunks, int l2norm_qk, int raw_gates)
 {
     using E = typename Elem<BF16>::T;
     using L = PrepSmem<D, BF16>;
@@ -477,6 +485,10 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
             const int64_t gi = (s * n_tokens + t0 + lane) * n_heads + h;
             gv = g[gi];
             bv = beta[gi];
+            if (raw_gates) {
+                gv = neg_softplus(gv);
+                bv = sigmoid(bv);
+            }
         }
         float x = gv;
 #pragma unroll
@@ -495,16 +507,47 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     wait_vmem_le<0>();
     lds_barrier();
 
+    // 0b. normalised rows: 1 / sqrt(|x_r|^2 + eps) for the K rows (waves 0, 2) and
+    //     the Q rows (waves 1, 3), 32 rows per wave, two lanes per row
+    float *sN = nullptr;
+    if (l2norm_qk) {
+        sN = reinterpret_cast<float *>(smem + L::kN);
+        const int r = 32 * (wave >> 1) + (lane & 31), half = lane >> 5;
+        constexpr int HB = D * L::ES / 2;  // bytes of half a row
+        const unsigned char *row = smem + ((wave & 1) ? L::kQ : L::kK) + r * L::RK + half * HB;
+        float acc = 0.f;
+#pragma unroll
+        for (int o = 0; o < HB; o += 16) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(row + o);
+            if constexpr (BF16) {
+                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xffff0000u);
+                    acc = fmaf(lo, lo, fmaf(hi, hi, acc));
+                }
+            } else {
+                const float f[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                                    __uint_as_float(u.w)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = fmaf(f[e], f[e], acc);
+            }
+        }
+        acc += __shfl_xor(acc, 32, 64);
+        if (half == 0) sN[((wave & 1) ? C : 0) + r] = 1.f / sqrtf(acc + kL2Eps);
+        lds_barrier();
+    }
+
     // 1-2. products, then the reuse of the K/Q space
     if (wave < 2) {
         if (wave == 0) {
             PrepTiles<0, 3> pt;
-            prep_products<D, BF16, true, 0, 3>(pt, smem, sG, sD, lane);
+            prep_products<D, BF16, true, 0, 3>(pt, smem, sG, sD, sN, lane);
             lds_barrier();
             store_tiles<BF16, 0, 3>(pt, sAe, LDT, lane);
         } else {
             PrepTiles<1, 2> pt;
-            prep_products<D, BF16, true, 1, 2>(pt, smem, sG, sD, lane);
+            prep_products<D, BF16, true, 1, 2>(pt, smem, sG, sD, sN, lane);
             lds_barrier();
             store_tiles<BF16, 1, 2>(pt, sAe, LDT, lane);
         }
@@ -512,19 +555,23 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
         unsigned char *pst = smem + L::kPst;
         if (wave == 2) {
             PrepTiles<0, 3> pt;
-            prep_products<D, BF16, false, 0, 3>(pt, smem, sG, sD, lane);
+            prep_products<D, BF16, false, 0, 3>(pt, smem, sG, sD, sN, lane);
             lds_barrier();
             emit_p<BF16, 0, 3>(pt, pst, dst + W::kP, lane);
         } else {
             PrepTiles<1, 2> pt;
-            prep_products<D, BF16, false, 1, 2>(pt, smem, sG, sD, lane);
+            prep_products<D, BF16, false, 1, 2>(pt, smem, sG, sD, sN, lane);
             lds_barrier();
             emit_p<BF16, 1, 2>(pt, pst, dst + W::kP, lane);
+            // beta, e^gam, e^{last-gam}, e^last; with normalised rows the second and
+            // third carry 1/|k| and a fifth row holds e^gam / |q|
             float *wG = reinterpret_cast<float *>(dst + W::kGates);
+            const float rk = sN ? sN[lane] : 1.f;
             wG[lane] = sG[C + lane];
-            wG[C + lane] = sG[2 * C + lane];
-            wG[2 * C + lane] = sG[3 * C + lane];
+            wG[C + lane] = sG[2 * C + lane] * rk;
+            wG[2 * C + lane] = sG[3 * C + lane] * rk;
             wG[3 * C + lane] = sG[4 * C];
+            if (sN) wG[4 * C + lane] = sG[2 * C + lane] * sN[C + lane];
         }
     }
     if (wave == 0) {
@@ -681,7 +728,7 @@ struct ScanCfg {
     static constexpr int kT = kK + C * RK;
     static constexpr int kV = kT + 6 * BLK;
     static constexpr int kG = kV + C * RV;
-    static constexpr int kSlotKT = kG + 1024;
+    static constexpr int kSlotKT = kG + 2048;  // gates: one or two 1 KiB blocks
     // Q/P slot
     static constexpr int kQ = 0;
     static constexpr int kP = kQ + C * RK;
@@ -706,10 +753,11 @@ struct ScanCfg {
     static constexpr int NBT = 6 * BLK / 1024;
     static constexpr int NBV = C * RV / 1024;
     static_assert(C * RK % 1024 == 0 && C * RV % 1024 == 0, "blocks");
-    static constexpr int NKT = NBK + NBT + NBV + 1;  // K, T, V, gates
+    static constexpr int NKT = NBK + NBT + NBV + 1;  // K, T, V, gates (+1 gates block, NG)
     static constexpr int NQP = NBK + NBT;            // Q, P
-    // producer p takes blocks p, p + 4, ...: its instruction counts
-    static constexpr int nkt(int p) { return (NKT + kProducers - 1 - p) / kProducers; }
+    // producer p takes blocks p, p + 4, ...: its instruction counts; ng = 1 when
+    // the second gates block (rows of normalised q/k) is loaded too
+    static constexpr int nkt(int p, int ng) { return (NKT + ng + kProducers - 1 - p) / kProducers; }
     static constexpr int nqp(int p) { return (NQP + kProducers - 1 - p) / kProducers; }
     // Issue times (barrier A_j = time 2j, B_j = 2j + 1): right after A_j the
     // producers issue Q/P of chunk j + SQ - 1, right after B_j K/T of chunk j + SK;
@@ -718,14 +766,14 @@ struct ScanCfg {
     static constexpr int kt_chunk(int t) { return (t - 1) / 2 + SK; }        // t odd
     // Number of a producer's load instructions issued at times in (lo, hi] for
     // chunks >= 0 (assuming every such chunk < n_chunks).
-    static constexpr int issued(int lo, int hi, int p)
+    static constexpr int issued(int lo, int hi, int p, int ng)
     {
         int c = 0;
         for (int t = lo + 1; t <= hi; ++t) {
             if (t % 2 == 0)
                 c += qp_chunk(t) >= 0 ? nqp(p) : 0;
             else
-                c += kt_chunk(t) >= 0 ? nkt(p) : 0;
+                c += kt_chunk(t) >= 0 ? nkt(p, ng) : 0;
         }
         return c;
     }
@@ -734,10 +782,11 @@ struct ScanCfg {
     //   before B_{-1}: K/T of chunk 0 (issued at time 1 - 2 SK) has landed;
     //   before A_n:    Q/P of chunk n (issued at 2n + 2 - 2 SQ) has landed;
     //   before B_n:    K/T of chunk n+1 (issued at 2n + 3 - 2 SK) has landed.
-    static constexpr int wait_prologue(int p) { return issued(1 - 2 * SK, -1, p); }
-    static constexpr int wait_a(int p) { return issued(2 - 2 * SQ, -1, p); }
-    static constexpr int wait_b(int p) { return issued(3 - 2 * SK, 0, p); }
-    static_assert(wait_prologue(0) < 64 && wait_a(0) < 64 && wait_b(0) < 64, "vmcnt range");
+    static constexpr int wait_prologue(int p, int ng) { return issued(1 - 2 * SK, -1, p, ng); }
+    static constexpr int wait_a(int p, int ng) { return issued(2 - 2 * SQ, -1, p, ng); }
+    static constexpr int wait_b(int p, int ng) { return issued(3 - 2 * SK, 0, p, ng); }
+    static_assert(wait_prologue(0, 1) < 64 && wait_a(0, 1) < 64 && wait_b(0, 1) < 64,
+                  "vmcnt range");
     static_assert(qp_chunk(2 - 2 * SQ) == 0 && kt_chunk(1 - 2 * SK) == 0, "issue times");
     static constexpr int kWaves = 3 * VT + kProducers;  // also in chunk_scan_kernel's launch bounds
 };
@@ -760,7 +809,7 @@ struct ScanPtrs {
 // Producer PART's blocks of chunk n's K, T, V and gates.
 template <int D, bool BF16, int VT, int PART>
 __device__ __forceinline__ void issue_kt(const ScanPtrs &pt, unsigned char *slot, int n, int nv,
-                                        int lane)
+                                        int ng, int lane)
 {
     using F = ScanCfg<D, BF16, VT>;
     using W = WsLayout<BF16>;
@@ -768,7 +817,8 @@ __device__ __forceinline__ void issue_kt(const ScanPtrs &pt, unsigned char *slot
     const uint32_t hdb = static_cast<uint32_t>(pt.hd_bytes), kqb = static_cast<uint32_t>(pt.kq_bytes);
     const unsigned char *wsc = pt.ws + int64_t(n) * W::kBytes;
 #pragma unroll
-    for (int i = PART; i < F::NKT; i += kProducers) {
+    for (int i = PART; i < F::NKT + 1; i += kProducers) {
+        if (i == F::NKT && !ng) break;
         uint32_t off;
         const unsigned char *base;
         if (i < F::NBK) {
@@ -782,7 +832,7 @@ __device__ __forceinline__ void issue_kt(const ScanPtrs &pt, unsigned char *slot
             off = dma_src_offset(i - F::NBK - F::NBT, lane, F::RW * F::ES, F::RV, hdb, nv);
         } else {
             base = wsc + W::kGates;
-            off = 16u * lane;
+            off = 1024u * (i - F::NBK - F::NBT - F::NBV) + 16u * lane;
         }
         dma16(base, off, slot + 1024 * i);
     }
@@ -1039,7 +1089,7 @@ struct OOps {
 
 template <int D, bool BF16, int VT>
 __device__ __forceinline__ void o_load(OOps<D, BF16> &o, const unsigned char *kt,
-                                       const unsigned char *qp, int lane)
+                                       const unsigned char *qp, int eg_row, int lane)
 {
     using F = ScanCfg<D, BF16, VT>;
     const int gq = lane >> 4, cl = lane & 15;
@@ -1054,7 +1104,7 @@ __device__ __forceinline__ void o_load(OOps<D, BF16> &o, const unsigned char *kt
     for (int b = 0; b < 6; ++b) o.ap[b] = frag_blk<BF16>(qp + F::kP + b * F::BLK, lane);
     const float *sG = reinterpret_cast<const float *>(kt + F::kG);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) o.eg[tt] = sG[C + 16 * tt + cl];
+    for (int tt = 0; tt < 4; ++tt) o.eg[tt] = sG[eg_row * C + 16 * tt + cl];
 }
 
 // O_vt works on the transposed output tile, O^T = M Q^T diag(e^gam) + Delta^T P^T:
@@ -1126,7 +1176,7 @@ __device__ __forceinline__ void o_finish(const OOps<D, BF16> &o, const unsigned 
 
 // Producer PART: moves every chunk's data into its ring slots and waits for it
 // before the barrier after which it is read.
-template <int D, bool BF16, int VT, int PART>
+template <int D, bool BF16, int VT, int PART, int NG>
 __device__ __forceinline__ void producer_loop(const ScanPtrs &pt, unsigned char *smem, int nc,
                                               int64_t n_tokens, int lane)
 {
@@ -1135,7 +1185,8 @@ __device__ __forceinline__ void producer_loop(const ScanPtrs &pt, unsigned char 
     auto nv_of = [&](int m) { return static_cast<int>(min<int64_t>(C, n_tokens - int64_t(m) * C)); };
     auto kt = [&](int m) {
         if (m < nc)
-            issue_kt<D, BF16, VT, PART>(pt, smem + F::kRingKT + (m % SK) * F::kSlotKT, m, nv_of(m), lane);
+            issue_kt<D, BF16, VT, PART>(pt, smem + F::kRingKT + (m % SK) * F::kSlotKT, m, nv_of(m),
+                                        NG, lane);
     };
     auto qp = [&](int m) {
         if (m < nc)
@@ -1153,20 +1204,20 @@ __device__ __forceinline__ void producer_loop(const ScanPtrs &pt, unsigned char 
         }
         constexpr int SM = SK > SQ ? SK : SQ;
         if (nc >= SM)
-            wait_vmem_le<F::wait_prologue(PART)>();
+            wait_vmem_le<F::wait_prologue(PART, NG)>();
         else
             wait_vmem_le<0>();
         dma_barrier();  // B_{-1}: K/T of chunk 0 is in LDS
         for (int n = 0; n < nc; ++n) {
             // near the end some of the counted loads were never issued: wait for all
             if (n + SM < nc)
-                wait_vmem_le<F::wait_a(PART)>();  // Q/P of chunk n landed
+                wait_vmem_le<F::wait_a(PART, NG)>();  // Q/P of chunk n landed
             else
                 wait_vmem_le<0>();
             dma_barrier();  // A_n: Q/P slot of chunk n-1 is free
             qp(n + SQ - 1);
             if (n + SM < nc)
-                wait_vmem_le<F::wait_b(PART)>();  // K/T of chunk n+1 landed
+                wait_vmem_le<F::wait_b(PART, NG)>();  // K/T of chunk n+1 landed
             else
                 wait_vmem_le<0>();
             dma_barrier();  // B_n: K/T slot of chunk n is free
@@ -1224,7 +1275,7 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *state_in, void *__restrict__ out, float *state_out,
     const unsigned char *__restrict__ ws, int64_t n_tokens, int64_t n_heads, int64_t n_k_heads,
-    int64_t n_sh, int n_chunks, float scale)
+    int64_t n_sh, int n_chunks, float scale, int l2norm_qk)
 {
     using F = ScanCfg<D, BF16, VT>;
     using E = typename Elem<BF16>::T;
@@ -1258,11 +1309,21 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
         pt.ws = ws + sh * nc * W::kBytes;
         pt.hd_bytes = hd * F::ES;
         pt.kq_bytes = n_k_heads * D * F::ES;
-        switch (vt) {
-        case 0: producer_loop<D, BF16, VT, 0>(pt, smem, nc, n_tokens, lane); break;
-        case 1: producer_loop<D, BF16, VT, 1>(pt, smem, nc, n_tokens, lane); break;
-        case 2: producer_loop<D, BF16, VT, 2>(pt, smem, nc, n_tokens, lane); break;
-        default: producer_loop<D, BF16, VT, 3>(pt, smem, nc, n_tokens, lane); break;
+        // the second gates block (e^gam / |q|) is loaded only for normalised rows
+        if (l2norm_qk) {
+            switch (vt) {
+            case 0: producer_loop<D, BF16, VT, 0, 1>(pt, smem, nc, n_tokens, lane); break;
+            case 1: producer_loop<D, BF16, VT, 1, 1>(pt, smem, nc, n_tokens, lane); break;
+            case 2: producer_loop<D, BF16, VT, 2, 1>(pt, smem, nc, n_tokens, lane); break;
+            default: producer_loop<D, BF16, VT, 3, 1>(pt, smem, nc, n_tokens, lane); break;
+            }
+        } else {
+            switch (vt) {
+            case 0: producer_loop<D, BF16, VT, 0, 0>(pt, smem, nc, n_tokens, lane); break;
+            case 1: producer_loop<D, BF16, VT, 1, 0>(pt, smem, nc, n_tokens, lane); break;
+            case 2: producer_loop<D, BF16, VT, 2, 0>(pt, smem, nc, n_tokens, lane); break;
+            default: producer_loop<D, BF16, VT, 3, 0>(pt, smem, nc, n_tokens, lane); break;
+            }
         }
         return;
     }
@@ -1311,6 +1372,7 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
                 make_float4(Mt[t][0], Mt[t][1], Mt[t][2], Mt[t][3]);
     } else {
         E *obase = static_cast<E *>(out) + tok0 + v0 + 16 * vt;
+        const int eg_row = l2norm_qk ? 4 : 1;  // e^gam, or e^gam / |q| for normalised rows
         OOps<D, BF16> ops;
         floatx4 acc[4];
         if constexpr (PIPE) lds_barrier();  // B_{-1}
@@ -1318,7 +1380,7 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
             if constexpr (!PIPE) lds_barrier();  // L_n
             lds_barrier();  // A_n
             bulk_pause();
-            o_load<D, BF16, VT>(ops, kt_slot(n), qp_slot(n), lane);
+            o_load<D, BF16, VT>(ops, kt_slot(n), qp_slot(n), eg_row, lane);
             o_xq<D, BF16, VT>(ops, qp_slot(n), smem, vt, lane, acc);
             lds_barrier();  // B_n
             o_finish<D, BF16, VT>(ops, smem, vt, lane, acc, obase + int64_t(n) * C * hd, hd,
@@ -1342,7 +1404,7 @@ hipError_t launch_prep(const Problem &p, unsigned char *ws, int n_chunks, hipStr
     const int64_t blocks = p.n_seqs * p.n_heads * n_chunks;
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kPrepThreads), L::kBytes,
                        stream, p.q, p.k, p.g, p.beta, ws, p.n_tokens, p.n_heads, p.n_k_heads,
-                       n_chunks);
+                       n_chunks, p.l2norm_qk, p.raw_gates);
     return hipGetLastError();
 }
 
@@ -1364,7 +1426,7 @@ hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, 
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(64 * F::kWaves), F::kBytes,
                        stream, p.q, p.k, p.v, p.state_in, p.out, p.state_out, ws, p.n_tokens,
-                       p.n_heads, p.n_k_heads, n_sh, n_chunks, scale);
+                       p.n_heads, p.n_k_heads, n_sh, n_chunks, scale, p.l2norm_qk);
     return hipGetLastError();
 }
 

@@ -44,4 +44,21 @@ __device__ __forceinline__ float sum32(float x)
     return x;
 }
 
+// Input transforms applied inside the op on request (fp32).
+// Epsilon inside the root of the q/k row normalisation: an all-zero row stays zero.
+constexpr float kL2Eps = 1e-6f;
+
+// g := -softplus(x) = -log(1 + e^x), written as -(max(x, 0) + log1p(e^-|x|)) so
+// that neither branch overflows.
+__device__ __forceinline__ float neg_softplus(float x)
+{
+    return -(fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))));
+}
+
+// beta := sigmoid(x) = 1 / (1 + e^-x)
+__device__ __forceinline__ float sigmoid(float x)
+{
+    return 1.f / (1.f + expf(-x));
+}
+
 }  // namespace gdn

@@ -115,7 +115,8 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
     const void *__restrict__ q, const void *__restrict__ k,
     const void *__restrict__ v, const float *__restrict__ g,
     const float *__restrict__ beta, const float *state_in, void *__restrict__ out,
-    float *state_out, int64_t n_tokens, int64_t n_heads, int64_t n_k_heads, float scale)
+    float *state_out, int64_t n_tokens, int64_t n_heads, int64_t n_k_heads, float scale,
+    int l2norm_qk, int raw_gates)
 {
     constexpr int NV = D / 32;
     constexpr int kRowsPerWave = 2 * NP;
@@ -170,6 +171,26 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
             bnext = beta[gn];
         }
 
+        if (l2norm_qk) {
+            // both 32-lane halves hold the whole rows: one reduction each
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                sk = fmaf(kv.x[i], kv.x[i], sk);
+                sq = fmaf(qv.x[i], qv.x[i], sq);
+            }
+            const float rk = 1.f / sqrtf(sum32(sk) + kL2Eps);
+            const float rq = 1.f / sqrtf(sum32(sq) + kL2Eps);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                kv.x[i] *= rk;
+                qv.x[i] *= rq;
+            }
+        }
+        if (raw_gates) {
+            gt = neg_softplus(gt);
+            bt = sigmoid(bt);
+        }
         const float alpha = expf(gt);
         float a[NP], b[NP], kq = 0.f;
 #pragma unroll
@@ -227,7 +248,8 @@ hipError_t launch_rec(const Problem &p, hipStream_t stream)
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
     hipLaunchKernelGGL((recurrent_kernel<D, NP, BF16>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kWaves * 64), 0, stream, p.q, p.k, p.v, p.g, p.beta,
-                       p.state_in, p.out, p.state_out, p.n_tokens, p.n_heads, p.n_k_heads, scale);
+                       p.state_in, p.out, p.state_out, p.n_tokens, p.n_heads, p.n_k_heads, scale,
+                       p.l2norm_qk, p.raw_gates);
     return hipGetLastError();
 }
 

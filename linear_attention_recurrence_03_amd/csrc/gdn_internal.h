@@ -21,6 +21,8 @@ struct Problem {
     int64_t n_seqs, n_tokens, n_heads;
     int64_t n_k_heads;      // heads of q and k; value head h reads head h % n_k_heads
     int head_dim;
+    int l2norm_qk;          // 1: q and k rows are divided by sqrt(|row|^2 + 1e-6)
+    int raw_gates;          // 1: g <- -softplus(g), beta <- sigmoid(beta)
 };
 
 // Token recurrence, any n_tokens >= 1.

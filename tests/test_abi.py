@@ -193,3 +193,25 @@ def test_forward_tiled_q_extent_uses_key_heads(lib):
     assert _tiled(lib, c, 1, out=q + one_head_q, **chunked) == E_WS
     assert _tiled(lib, c, 1, out=q + one_head_q - 16, **chunked) == E_ALIAS
     assert _tiled(lib, c, 4, out=q + one_head_q, **chunked) == E_ALIAS
+
+
+def test_forward_ex_flags(lib):
+    """gdn_forward_ex: unknown transform bits are rejected; known ones pass the
+    flag check and the call stops at the next failing check (no launch)."""
+    c = _Call(H=4)
+    a = c.p
+
+    def ex(flags, HK=4, **over):
+        b = dict(a)
+        b.update(over)
+        return lib.gdn_forward_ex(c.dtype, b["q"], b["k"], b["v"], b["g"], b["beta"],
+                                  b["state_in"], b["out"], b["state_out"], c.S, c.T, c.H, HK,
+                                  c.D, flags, b["ws"], 0, c.algo, None)
+    E_FLAGS = -10
+    for bad in (4, 8, 1 << 31, 0xFFFFFFFF):
+        assert ex(bad) == E_FLAGS
+    for ok in (0, 1, 2, 3):
+        assert ex(ok, q=None) == E_NULL
+        assert ex(ok, out=a["q"]) == E_ALIAS
+        assert ex(ok, HK=3) == E_SHAPE
+    assert "flag" in gdn.status_string(E_FLAGS)

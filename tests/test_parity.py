@@ -37,10 +37,10 @@ def to_dev(x, dtype):
     return d
 
 
-def run_gpu(gdn, x, dtype, algo="auto", state=True):
+def run_gpu(gdn, x, dtype, algo="auto", state=True, **pre):
     d = to_dev(x, dtype)
     out, fin = gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"],
-                           d["state"] if state else None, algo=algo)
+                           d["state"] if state else None, algo=algo, **pre)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), fin.cpu().numpy().astype(np.float64)
 
@@ -51,11 +51,11 @@ def rel_err(a, b):
     return num / den if den > 0 else num
 
 
-def check(gdn, x, dtype, algo, state=True, what=""):
-    print("case:", what, dtype, algo, x["q"].shape, flush=True)
-    out, fin = run_gpu(gdn, x, dtype, algo, state)
+def check(gdn, x, dtype, algo, state=True, what="", **pre):
+    print("case:", what, dtype, algo, x["q"].shape, pre, flush=True)
+    out, fin = run_gpu(gdn, x, dtype, algo, state, **pre)
     ro, rf = oracle.gdn_recurrent(x["q"], x["k"], x["v"], x["g"], x["beta"],
-                                  x["state"] if state else None)
+                                  x["state"] if state else None, **pre)
     eo, ef = rel_err(out, ro), rel_err(fin, rf)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(fin))
     assert eo <= TOL[dtype], "out err %.3e > %.1e (%s)" % (eo, TOL[dtype], what)
@@ -165,6 +165,50 @@ def test_tiled_equals_expanded_copy(gdn, algo):
 def test_tiled_prefill_workload(gdn):
     """The full 4096-token prefill with 32 value heads over 16 query/key heads."""
     check(gdn, inputs.make(inputs.GQA_PREFILL), "bf16", "auto", what="tiled prefill 4096")
+
+
+# ---- input transforms inside the op (unnormalised q/k rows, raw gates) ------------
+
+def _mixed_raw(n_seqs, n_tokens, n_heads, head_dim, dtype, seed, l2, gates, key_heads=None):
+    """Raw q/k rows and/or raw gate pre-activations, the rest from the standard
+    recipe of the same draw."""
+    raw = inputs.custom(n_seqs, n_tokens, n_heads, head_dim, dtype=dtype, state="normal",
+                        seed=seed, raw=True, key_heads=key_heads)
+    std = inputs.custom(n_seqs, n_tokens, n_heads, head_dim, dtype=dtype, state="normal",
+                        seed=seed, key_heads=key_heads)
+    x = dict(std)
+    if l2:
+        x["q"], x["k"] = raw["q"], raw["k"]
+    if gates:
+        x["g"], x["beta"] = raw["g"], raw["beta"]
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("l2,gates", [(True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("D", [32, 128])
+@pytest.mark.parametrize("T,algo", [(1, "recurrent"), (9, "recurrent"), (65, "chunked"),
+                                    (130, "chunked")])
+def test_input_transforms(gdn, dtype, l2, gates, D, T, algo):
+    x = _mixed_raw(2, T, 3, D, dtype, seed=700 + T + D, l2=l2, gates=gates)
+    check(gdn, x, dtype, algo, what="transforms D=%d T=%d" % (D, T), l2norm_qk=l2,
+          raw_gates=gates)
+
+
+def test_input_transforms_tiled_prefill(gdn):
+    """Both transforms with 16 query/key heads over 32 value heads, 4096 tokens."""
+    x = _mixed_raw(1, 4096, 32, 128, "bf16", seed=6100, l2=True, gates=True, key_heads=16)
+    check(gdn, x, "bf16", "auto", what="transforms, tiled prefill 4096", l2norm_qk=True,
+          raw_gates=True)
+
+
+def test_input_transforms_zero_rows(gdn):
+    """All-zero q or k rows stay finite with normalisation (epsilon in the root)."""
+    x = _mixed_raw(1, 130, 2, 64, "bf16", seed=7, l2=True, gates=False)
+    x["k"][0, 5] = 0.0
+    x["q"][0, 70] = 0.0
+    for algo in ("recurrent", "chunked"):
+        check(gdn, x, "bf16", algo, what="zero rows", l2norm_qk=True)
 
 
 def test_zero_initial_state_pointer(gdn):
