@@ -243,8 +243,11 @@ struct WsLayout {
     static constexpr int64_t kT = 0;
     static constexpr int64_t kP = 6 * kBlkBytes<BF16>;
     static constexpr int64_t kGates = 2 * kP;
-    // gates: rows of C floats, then room up to 2 KiB
-    static constexpr int64_t kBytes = kGates + 8 * C * 4;
+    // gates: four rows of C floats (1 KiB); five with normalised q/k rows, which
+    // then take a 2 KiB area
+    static constexpr int64_t kBytes = kGates + 4 * C * 4;
+    static constexpr int64_t kBytesNorm = kGates + 8 * C * 4;
+    static constexpr int64_t stride(int l2norm_qk) { return l2norm_qk ? kBytesNorm : kBytes; }
 };
 
 // A operand from rows of a padded row-major LDS matrix: lane (g, r) gets row
@@ -462,7 +465,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const int64_t s = sh / n_heads, h = sh - s * n_heads;
     const int64_t t0 = int64_t(n) * C;
     const int nv = static_cast<int>(min<int64_t>(C, n_tokens - t0));
-    unsigned char *dst = ws + chunk_id * W::kBytes;
+    unsigned char *dst = ws + chunk_id * W::stride(l2norm_qk);
 
     // 0. K and Q rows of key head h % n_k_heads (rows past the end repeat the
     //    last valid one: their A and P entries are cleared by beta = 0 and never
@@ -804,6 +807,7 @@ struct ScanPtrs {
     const unsigned char *ws;          // this (seq, head)'s chunk 0 in the workspace
     int64_t hd_bytes;                 // token stride of v in bytes (64 of them fit in 32 bits)
     int64_t kq_bytes;                 // token stride of k and q in bytes
+    int64_t ws_stride;                // workspace bytes per chunk
 };
 
 // Producer PART's blocks of chunk n's K, T, V and gates.
@@ -815,7 +819,7 @@ __device__ __forceinline__ void issue_kt(const ScanPtrs &pt, unsigned char *slot
     using W = WsLayout<BF16>;
     const int64_t tb = int64_t(n) * C * pt.hd_bytes, tbk = int64_t(n) * C * pt.kq_bytes;
     const uint32_t hdb = static_cast<uint32_t>(pt.hd_bytes), kqb = static_cast<uint32_t>(pt.kq_bytes);
-    const unsigned char *wsc = pt.ws + int64_t(n) * W::kBytes;
+    const unsigned char *wsc = pt.ws + int64_t(n) * pt.ws_stride;
 #pragma unroll
     for (int i = PART; i < F::NKT + 1; i += kProducers) {
         if (i == F::NKT && !ng) break;
@@ -847,7 +851,7 @@ __device__ __forceinline__ void issue_qp(const ScanPtrs &pt, unsigned char *slot
     using W = WsLayout<BF16>;
     const int64_t tbk = int64_t(n) * C * pt.kq_bytes;
     const uint32_t kqb = static_cast<uint32_t>(pt.kq_bytes);
-    const unsigned char *wsc = pt.ws + int64_t(n) * W::kBytes;
+    const unsigned char *wsc = pt.ws + int64_t(n) * pt.ws_stride;
 #pragma unroll
     for (int i = PART; i < F::NQP; i += kProducers) {
         if (i < F::NBK)
@@ -1306,7 +1310,8 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
         pt.k = static_cast<const unsigned char *>(k) + ktok0 * F::ES;
         pt.q = static_cast<const unsigned char *>(q) + ktok0 * F::ES;
         pt.v = static_cast<const unsigned char *>(v) + (tok0 + v0) * F::ES;
-        pt.ws = ws + sh * nc * W::kBytes;
+        pt.ws_stride = W::stride(l2norm_qk);
+        pt.ws = ws + sh * nc * pt.ws_stride;
         pt.hd_bytes = hd * F::ES;
         pt.kq_bytes = n_k_heads * D * F::ES;
         // the second gates block (e^gam / |q|) is loaded only for normalised rows
@@ -1462,7 +1467,8 @@ hipError_t launch_chunk_t(const Problem &p, unsigned char *ws, hipStream_t strea
 size_t chunk_workspace_bytes(int bf16, int64_t n_seqs, int64_t n_tokens, int64_t n_heads, int)
 {
     const int64_t n_chunks = (n_tokens + C - 1) / C;
-    const int64_t per = bf16 ? WsLayout<true>::kBytes : WsLayout<false>::kBytes;
+    // sized for the larger (normalised q/k) layout, so one workspace serves both
+    const int64_t per = bf16 ? WsLayout<true>::kBytesNorm : WsLayout<false>::kBytesNorm;
     return static_cast<size_t>(n_seqs * n_heads * n_chunks * per);
 }
 

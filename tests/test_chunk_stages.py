@@ -4,9 +4,9 @@ The chunked algorithm first computes, for every (sequence, head, chunk), the
 state-independent matrices T = (I + A)^{-1} and the decay-masked P, plus the
 per-token gate factors, into the caller's workspace.  This test decodes that
 workspace (its layout is internal to the library and mirrored here: per chunk
-T and then P as six "fragment blocks" each, then a 2 KiB gates area whose first
-four fp32 rows of 64 are beta, e^gam, e^(gam_last - gam) and e^gam_last repeated;
-a fifth row is written only when the op normalises q and k) and compares it with the
+T and then P as six "fragment blocks" each, then four fp32 rows of 64: beta,
+e^gam, e^(gam_last - gam) and e^gam_last repeated; when the op normalises q and
+k the gates take 2 KiB with a fifth row) and compares it with the
 oracle's stage values, so that a parity failure can be attributed to the first
 or the second half of the path.
 
@@ -46,7 +46,7 @@ def _block_index_map():
 def _decode_ws(ws, dtype, n_units):
     esz = 2 if dtype == "bf16" else 4
     nel = 6 * 64 * 8                      # elements in six blocks
-    per = 2 * nel * esz + 8 * C * 4      # gates: 2 KiB, the first four rows used here
+    per = 2 * nel * esz + 4 * C * 4      # gates: four rows (1 KiB) without normalisation
     raw = ws[: n_units * per].cpu().numpy().reshape(n_units, per)
     mats = raw[:, : 2 * nel * esz]
     if dtype == "bf16":
