@@ -441,11 +441,11 @@ __device__ __forceinline__ void emit_p(const PrepTiles<R0, R1> &pt, unsigned cha
 //   5. T to the workspace as six fragment blocks
 // The products of steps 3 and 4 run on MFMA with the k range padded to 32 by
 // blocks of T that are still zero; for bf16 inputs their operands are bf16.
-template <int D, bool BF16>
+template <int D, bool BF16, bool NORM>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, unsigned char *__restrict__ ws, int64_t n_tokens,
-    int64_t n_heads, int64_t n_k_heads, int n_chunks, int l2norm_qk, int raw_gates)
+    int64_t n_heads, int64_t n_k_heads, int n_chunks, int raw_gates)
 {
     using E = typename Elem<BF16>::T;
     using L = PrepSmem<D, BF16>;
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const int64_t s = sh / n_heads, h = sh - s * n_heads;
     const int64_t t0 = int64_t(n) * C;
     const int nv = static_cast<int>(min<int64_t>(C, n_tokens - t0));
-    unsigned char *dst = ws + chunk_id * W::stride(l2norm_qk);
+    unsigned char *dst = ws + chunk_id * W::stride(NORM);
 
     // 0. K and Q rows of key head h % n_k_heads (rows past the end repeat the
     //    last valid one: their A and P entries are cleared by beta = 0 and never
@@ -513,7 +513,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     // 0b. normalised rows: 1 / sqrt(|x_r|^2 + eps) for the K rows (waves 0, 2) and
     //     the Q rows (waves 1, 3), 32 rows per wave, two lanes per row
     float *sN = nullptr;
-    if (l2norm_qk) {
+    if constexpr (NORM) {
         sN = reinterpret_cast<float *>(smem + L::kN);
         const int r = 32 * (wave >> 1) + (lane & 31), half = lane >> 5;
         constexpr int HB = D * L::ES / 2;  // bytes of half a row
@@ -1274,12 +1274,12 @@ __device__ __forceinline__ void wave_role(int wave, int &role, int &idx)
 // Workgroups are numbered so that the row blocks of one (seq, head) share the
 // low three bits of the block id: consecutive ids go to different XCDs, so this
 // keeps a head's workgroups on one XCD, where its K, Q, T and P hit in L2.
-template <int D, bool BF16, int VT>
+template <int D, bool BF16, int VT, bool NORM>
 __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *state_in, void *__restrict__ out, float *state_out,
     const unsigned char *__restrict__ ws, int64_t n_tokens, int64_t n_heads, int64_t n_k_heads,
-    int64_t n_sh, int n_chunks, float scale, int l2norm_qk)
+    int64_t n_sh, int n_chunks, float scale)
 {
     using F = ScanCfg<D, BF16, VT>;
     using E = typename Elem<BF16>::T;
@@ -1310,12 +1310,12 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
         pt.k = static_cast<const unsigned char *>(k) + ktok0 * F::ES;
         pt.q = static_cast<const unsigned char *>(q) + ktok0 * F::ES;
         pt.v = static_cast<const unsigned char *>(v) + (tok0 + v0) * F::ES;
-        pt.ws_stride = W::stride(l2norm_qk);
+        pt.ws_stride = W::stride(NORM);
         pt.ws = ws + sh * nc * pt.ws_stride;
         pt.hd_bytes = hd * F::ES;
         pt.kq_bytes = n_k_heads * D * F::ES;
         // the second gates block (e^gam / |q|) is loaded only for normalised rows
-        if (l2norm_qk) {
+        if constexpr (NORM) {
             switch (vt) {
             case 0: producer_loop<D, BF16, VT, 0, 1>(pt, smem, nc, n_tokens, lane); break;
             case 1: producer_loop<D, BF16, VT, 1, 1>(pt, smem, nc, n_tokens, lane); break;
@@ -1377,7 +1377,7 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
                 make_float4(Mt[t][0], Mt[t][1], Mt[t][2], Mt[t][3]);
     } else {
         E *obase = static_cast<E *>(out) + tok0 + v0 + 16 * vt;
-        const int eg_row = l2norm_qk ? 4 : 1;  // e^gam, or e^gam / |q| for normalised rows
+        constexpr int eg_row = NORM ? 4 : 1;  // e^gam, or e^gam / |q| for normalised rows
         OOps<D, BF16> ops;
         floatx4 acc[4];
         if constexpr (PIPE) lds_barrier();  // B_{-1}
@@ -1394,11 +1394,11 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
     }
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool NORM>
 hipError_t launch_prep(const Problem &p, unsigned char *ws, int n_chunks, hipStream_t stream)
 {
     using L = PrepSmem<D, BF16>;
-    auto kern = chunk_prep_kernel<D, BF16>;
+    auto kern = chunk_prep_kernel<D, BF16, NORM>;
     static bool attr_set = false;  // one-time attribute; same value every time
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -1409,15 +1409,15 @@ hipError_t launch_prep(const Problem &p, unsigned char *ws, int n_chunks, hipStr
     const int64_t blocks = p.n_seqs * p.n_heads * n_chunks;
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kPrepThreads), L::kBytes,
                        stream, p.q, p.k, p.g, p.beta, ws, p.n_tokens, p.n_heads, p.n_k_heads,
-                       n_chunks, p.l2norm_qk, p.raw_gates);
+                       n_chunks, p.raw_gates);
     return hipGetLastError();
 }
 
-template <int D, bool BF16, int VT>
+template <int D, bool BF16, int VT, bool NORM>
 hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, hipStream_t stream)
 {
     using F = ScanCfg<D, BF16, VT>;
-    auto kern = chunk_scan_kernel<D, BF16, VT>;
+    auto kern = chunk_scan_kernel<D, BF16, VT, NORM>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -1431,23 +1431,33 @@ hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, 
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(64 * F::kWaves), F::kBytes,
                        stream, p.q, p.k, p.v, p.state_in, p.out, p.state_out, ws, p.n_tokens,
-                       p.n_heads, p.n_k_heads, n_sh, n_chunks, scale, p.l2norm_qk);
+                       p.n_heads, p.n_k_heads, n_sh, n_chunks, scale);
     return hipGetLastError();
 }
 
 // bf16 scan workgroups hold 16 value rows each while that still leaves at most one
 // workgroup per compute unit (few heads: more parallel chains), else 32.  The fp32
 // scan (one slot per ring, no pipelining) always holds 16.
+// Normalised q/k rows are a kernel variant of their own (NORM), so that the plain
+// kernels carry none of that mode's code.
+template <int D, bool BF16, bool NORM>
+hipError_t launch_chunk_dn(const Problem &p, unsigned char *ws, hipStream_t stream)
+{
+    const int n_chunks = static_cast<int>((p.n_tokens + C - 1) / C);
+    hipError_t e = launch_prep<D, BF16, NORM>(p, ws, n_chunks, stream);
+    if (e != hipSuccess) return e;
+    const int64_t n_sh = p.n_seqs * p.n_heads;
+    if (!BF16 || n_sh * (D / 16) <= 256)
+        return launch_scan<D, BF16, 1, NORM>(p, ws, n_chunks, stream);
+    if constexpr (BF16) return launch_scan<D, BF16, 2, NORM>(p, ws, n_chunks, stream);
+    return hipErrorInvalidValue;  // not reached
+}
+
 template <int D, bool BF16>
 hipError_t launch_chunk_d(const Problem &p, unsigned char *ws, hipStream_t stream)
 {
-    const int n_chunks = static_cast<int>((p.n_tokens + C - 1) / C);
-    hipError_t e = launch_prep<D, BF16>(p, ws, n_chunks, stream);
-    if (e != hipSuccess) return e;
-    const int64_t n_sh = p.n_seqs * p.n_heads;
-    if (!BF16 || n_sh * (D / 16) <= 256) return launch_scan<D, BF16, 1>(p, ws, n_chunks, stream);
-    if constexpr (BF16) return launch_scan<D, BF16, 2>(p, ws, n_chunks, stream);
-    return hipErrorInvalidValue;  // not reached
+    return p.l2norm_qk ? launch_chunk_dn<D, BF16, true>(p, ws, stream)
+                       : launch_chunk_dn<D, BF16, false>(p, ws, stream);
 }
 
 template <bool BF16>
