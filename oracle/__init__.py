@@ -161,3 +161,51 @@ def chunk_stages(q, k, v, g, beta, state=None):
         raise MemoryError("oracle_gdn_chunk_stages failed (%d)" % rc)
     res["state"] = M
     return res
+
+
+# ---- decode flash attention (the model card's second op, vector variant) -------
+
+def flash_attn(q, k, v, mask=None, scale=None):
+    """Softmax attention of a few queries over a key/value cache, fp64.
+
+    Follows the "ggml attention kernels" model card, section "flash_attn":
+    q (n_seqs, n_heads, n_q, d); k, v (n_seqs, n_heads_kv, n_kv, d) with query
+    head h reading key/value head h // (n_heads / n_heads_kv) (grouped-query
+    attention without an expanded copy; the card measures against repeat_kv,
+    whose copies of key/value head j serve query heads j*g .. j*g + g - 1);
+    mask (n_seqs, 1, n_q, n_kv) additive, cast to f16 first as the card says the
+    kernel does, or None.  Returns (n_seqs, n_q, n_heads, d): tokens before
+    heads.  scale defaults to 1 / sqrt(d).  A query row whose scores are all
+    -inf (or an empty cache) gives zeros.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    S, H, NQ, D = q.shape
+    _, HKV, NKV, DV = v.shape
+    if k.shape != (S, HKV, NKV, D) or v.shape[:3] != (S, HKV, NKV):
+        raise ValueError("k, v must be (n_seqs, n_heads_kv, n_kv, d)")
+    if HKV < 1 or H % HKV != 0:
+        raise ValueError("n_heads_kv must divide n_heads")
+    g = H // HKV
+    sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    m16 = None
+    if mask is not None:
+        m16 = np.asarray(mask, dtype=np.float32).astype(np.float16).astype(np.float64)
+        if m16.shape != (S, 1, NQ, NKV):
+            raise ValueError("mask must be (n_seqs, 1, n_q, n_kv)")
+    out = np.zeros((S, NQ, H, DV))
+    for s in range(S):
+        for h in range(H):
+            j = h // g
+            scores = sc * (q[s, h] @ k[s, j].T)               # (n_q, n_kv)
+            if m16 is not None:
+                scores = scores + m16[s, 0]
+            for i in range(NQ):
+                row = scores[i]
+                top = np.max(row) if NKV else -np.inf
+                if not np.isfinite(top):
+                    continue                                  # nothing to attend to
+                w = np.exp(row - top)
+                out[s, i, h] = (w @ v[s, j]) / np.sum(w)
+    return out

@@ -415,3 +415,82 @@ def test_raw_inputs_match_transformed_inputs():
                                   std["state"])
     np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-5)
     np.testing.assert_allclose(f1, f2, rtol=0, atol=1e-5)
+
+
+# ---- decode flash attention --------------------------------------------------------
+
+def _attn_problem(S, H, HKV, NQ, NKV, D, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((S, H, NQ, D)).astype(np.float32)
+    k = rng.standard_normal((S, HKV, NKV, D)).astype(np.float32)
+    v = rng.standard_normal((S, HKV, NKV, D)).astype(np.float32)
+    return q, k, v
+
+
+def test_attn_uniform_scores_give_mean():
+    """scale = 0 (all scores equal): every query returns the mean value row."""
+    q, k, v = _attn_problem(2, 4, 2, 3, 37, 16, seed=1)
+    out = oracle.flash_attn(q, k, v, None, scale=0.0)
+    for h in range(4):
+        np.testing.assert_allclose(out[:, :, h], np.broadcast_to(
+            v[:, h // 2].astype(np.float64).mean(axis=1)[:, None], out[:, :, h].shape),
+            rtol=1e-13, atol=1e-14)
+
+
+def test_attn_one_hot_mask_selects_a_row():
+    """A mask that is 0 at token j and -inf elsewhere returns value row j exactly."""
+    q, k, v = _attn_problem(1, 2, 1, 2, 20, 8, seed=2)
+    mask = np.full((1, 1, 2, 20), -np.inf, np.float32)
+    mask[0, 0, 0, 7] = 0.0
+    mask[0, 0, 1, 13] = 0.0
+    out = oracle.flash_attn(q, k, v, mask)
+    np.testing.assert_array_equal(out[0, 0, :], np.broadcast_to(v[0, 0, 7], (2, 8)))
+    np.testing.assert_array_equal(out[0, 1, :], np.broadcast_to(v[0, 0, 13], (2, 8)))
+
+
+def test_attn_matches_torch_sdpa_fp64():
+    """Against torch's scaled_dot_product_attention (CPU, float64) on the
+    explicitly expanded keys/values (repeat_interleave: the grouped order)."""
+    torch = pytest.importorskip("torch")
+    q, k, v = _attn_problem(2, 8, 2, 5, 61, 32, seed=3)
+    mask = np.random.default_rng(4).normal(0, 2, (2, 1, 5, 61)).astype(np.float32)
+    out = oracle.flash_attn(q, k, v, mask, scale=0.3)
+    tq = torch.from_numpy(q).double()
+    tk = torch.from_numpy(k).double().repeat_interleave(4, dim=1)
+    tv = torch.from_numpy(v).double().repeat_interleave(4, dim=1)
+    tm = torch.from_numpy(mask.astype(np.float16).astype(np.float64))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=tm, scale=0.3)
+    np.testing.assert_allclose(out, ref.transpose(1, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_attn_mask_is_rounded_to_f16():
+    """Two tokens, equal scores, mask (0, 0.1): the weights follow the f16 value
+    of 0.1 (0.0999755859375), not the f32 one."""
+    q = np.zeros((1, 1, 1, 4), np.float32)
+    k = np.ones((1, 1, 2, 4), np.float32)
+    v = np.array([[[[1, 0, 0, 0], [0, 1, 0, 0]]]], np.float32)
+    mask = np.array([[[[0.0, 0.1]]]], np.float32)
+    out = oracle.flash_attn(q, k, v, mask)
+    m = 0.0999755859375
+    w1 = np.exp(m) / (1 + np.exp(m))
+    np.testing.assert_allclose(out[0, 0, 0, :2], [1 - w1, w1], rtol=0, atol=1e-15)
+    w1_f32 = np.exp(np.float64(np.float32(0.1))) / (1 + np.exp(np.float64(np.float32(0.1))))
+    assert abs(w1 - w1_f32) > 1e-6
+
+
+def test_attn_grouped_head_order_and_empty_rows():
+    """Query head h reads key/value head h // (H / HKV); a fully masked row and an
+    empty cache give zeros."""
+    q, k, v = _attn_problem(1, 6, 2, 2, 9, 8, seed=5)
+    out = oracle.flash_attn(q, k, v, None)
+    for h in range(6):
+        j = h // 3
+        one = oracle.flash_attn(q[:, h:h + 1], k[:, j:j + 1], v[:, j:j + 1], None)
+        np.testing.assert_array_equal(out[:, :, h:h + 1], one)
+    assert not np.allclose(out[:, :, 1], oracle.flash_attn(q[:, 1:2], k[:, 1:2], v[:, 1:2])[:, :, 0])
+    mask = np.zeros((1, 1, 2, 9), np.float32)
+    mask[0, 0, 1, :] = -np.inf
+    out = oracle.flash_attn(q, k, v, mask)
+    assert np.all(out[0, 1] == 0.0) and np.any(out[0, 0] != 0.0)
+    empty = oracle.flash_attn(q, k[:, :, :0], v[:, :, :0], None)
+    assert empty.shape == (1, 2, 6, 8) and np.all(empty == 0.0)
