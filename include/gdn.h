@@ -180,6 +180,49 @@ int gdn_forward_ex(gdn_dtype dtype, const void *q, const void *k, const void *v,
                    unsigned int flags, void *workspace, size_t workspace_bytes,
                    gdn_algo algo, void *stream);
 
+/* ---- decode flash attention ("ggml attention kernels" model card, section
+ * "flash_attn": the vector variant, a few queries against a key/value cache) ----
+ *
+ * For sequence s, query head h and query i, with key/value head
+ * j = h / (n_heads / n_heads_kv) (grouped-query attention, keys and values read
+ * in place with no expanded copy; the card's second bullet under that section):
+ *     score_t = scale * (q[s][h][i] . k[s][j][t]) + f16(mask[s][0][i][t])
+ *     out[s][i][h] = sum_t softmax_t(score) v[s][j][t]
+ * The additive mask is rounded to f16 before use, as the card says its kernel
+ * does; all other arithmetic is fp32 (the card's kernel accumulates in f16).
+ * A query row with no finite score (fully masked, or n_kv == 0) gives zeros.
+ */
+
+/* 1 if the decode attention runs these sizes: 1 <= n_q < 20 (the card's vector
+ * variant; a caller falls back to its own attention otherwise) and
+ * head_dim_k == head_dim_v in {64, 128, 256}. */
+int gdn_flash_attn_supports(int n_q, int head_dim_k, int head_dim_v);
+
+/* Bytes of device workspace gdn_flash_attn needs (0 when the cache is not split
+ * across workgroups); 0 for sizes gdn_flash_attn would reject. */
+size_t gdn_flash_attn_workspace_size(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv,
+                                     int64_t n_q, int64_t n_kv, int head_dim);
+
+/*   dtype        storage dtype of q, k, v, out
+ *   q            (n_seqs, n_heads, n_q, head_dim), device, read only
+ *   k, v         (n_seqs, n_heads_kv, n_kv, head_dim), device, read only
+ *   mask         (n_seqs, 1, n_q, n_kv) fp32 additive, device, read only, or NULL
+ *   out          (n_seqs, n_q, n_heads, head_dim): tokens before heads (the
+ *                card's return layout), device, written
+ *   n_heads_kv   >= 1 and a divisor of n_heads
+ *   scale        multiplies q . k (callers usually pass 1/sqrt(head_dim))
+ *   workspace    device scratch of at least gdn_flash_attn_workspace_size(...)
+ *   stream       a hipStream_t (NULL = the default stream)
+ * Rejects (nothing launched): unsupported sizes (GDN_ERR_UNSUPPORTED_HEAD_DIM
+ * for the width, GDN_ERR_BAD_SHAPE for n_q, negative sizes or a non-dividing
+ * n_heads_kv), a non-finite scale (GDN_ERR_BAD_SHAPE), null or misaligned
+ * pointers, out overlapping an input, a too small workspace.  n_seqs == 0 or
+ * n_heads == 0 is a no-op; n_kv == 0 writes zeros. */
+int gdn_flash_attn(gdn_dtype dtype, const void *q, const void *k, const void *v,
+                   const float *mask, void *out, int64_t n_seqs, int64_t n_heads,
+                   int64_t n_heads_kv, int64_t n_q, int64_t n_kv, int head_dim, float scale,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *gdn_status_string(int status);
 

@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = ["forward", "supports", "workspace_size", "status_string", "library_path",
-           "GdnError", "ALGOS"]
+           "GdnError", "ALGOS", "flash_attn", "supports_flash_attn"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
@@ -61,6 +61,13 @@ def _lib():
     lib.gdn_forward_ex.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
                                    i64, i64, ctypes.c_int, ctypes.c_uint, vp, ctypes.c_size_t,
                                    ctypes.c_int, vp]
+    lib.gdn_flash_attn_supports.restype = ctypes.c_int
+    lib.gdn_flash_attn_supports.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.gdn_flash_attn_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_flash_attn_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int]
+    lib.gdn_flash_attn.restype = ctypes.c_int
+    lib.gdn_flash_attn.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                   ctypes.c_int, ctypes.c_float, vp, ctypes.c_size_t, vp]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_version.restype = ctypes.c_int
@@ -173,3 +180,62 @@ def forward(q, k, v, g, beta, state=None, algo: str = "auto", out=None, state_ou
     if rc != 0:
         raise GdnError(rc, status_string(rc))
     return out, state_out
+
+
+def supports_flash_attn(n_q: int, head_dim_k: int, head_dim_v: int) -> bool:
+    """True iff the decode attention runs these sizes (1 <= n_q < 20, equal key and
+    value widths of 64, 128 or 256)."""
+    return bool(_lib().gdn_flash_attn_supports(int(n_q), int(head_dim_k), int(head_dim_v)))
+
+
+def flash_attn(q, k, v, mask=None, scale=None, out=None, workspace=None, stream=None):
+    """Decode attention of a few queries over a key/value cache ("ggml attention
+    kernels" model card, section "flash_attn").  Returns out.
+
+    q: (n_seqs, n_heads, n_q, d); k, v: (n_seqs, n_heads_kv, n_kv, d), float32 or
+    bfloat16 CUDA tensors of one dtype, n_heads_kv dividing n_heads (query head h
+    reads key/value head h // (n_heads / n_heads_kv)); mask: (n_seqs, 1, n_q,
+    n_kv) additive (converted to float32 here; the op rounds it to f16) or None;
+    scale defaults to 1/sqrt(d).  out: (n_seqs, n_q, n_heads, d), like q.
+    """
+    import torch
+    if q.dtype == torch.float32:
+        dt = "f32"
+    elif q.dtype == torch.bfloat16:
+        dt = "bf16"
+    else:
+        raise TypeError("q/k/v must be float32 or bfloat16, got %s" % q.dtype)
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s dtype %s differs from q dtype %s" % (name, t.dtype, q.dtype))
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k.shape[0] != q.shape[0] or \
+            k.shape[3] != q.shape[3]:
+        raise ValueError("q must be (n_seqs, n_heads, n_q, d) and k, v (n_seqs, n_heads_kv, "
+                         "n_kv, d)")
+    S, H, NQ, D = q.shape
+    HKV, NKV = k.shape[1], k.shape[2]
+    if mask is not None:
+        if mask.shape != (S, 1, NQ, NKV):
+            raise ValueError("mask must be (n_seqs, 1, n_q, n_kv)")
+        mask = mask.to(torch.float32).contiguous()
+    for t in (q, k, v) + ((mask,) if mask is not None else ()):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous GPU tensors")
+    if out is None:
+        out = torch.empty((S, NQ, H, D), dtype=q.dtype, device=q.device)
+    elif out.shape != (S, NQ, H, D) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (n_seqs, n_q, n_heads, d) tensor like q")
+    sc = (1.0 / D ** 0.5) if scale is None else float(scale)
+    lib = _lib()
+    need = int(lib.gdn_flash_attn_workspace_size(S, H, HKV, NQ, NKV, D))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = lib.gdn_flash_attn(_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(out),
+                            S, H, HKV, NQ, NKV, D, sc, _ptr(workspace), ws_bytes,
+                            ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise GdnError(rc, status_string(rc))
+    return out

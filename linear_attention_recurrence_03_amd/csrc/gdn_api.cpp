@@ -8,6 +8,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "gdn_internal.h"
 
 namespace {
@@ -75,6 +77,38 @@ int check_shape(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens, int64_t n_hea
     return GDN_OK;
 }
 
+// Element counts of the decode-attention tensors.
+struct AttnSizes {
+    int64_t q_elems, kv_elems, mask_elems, out_elems;
+};
+
+// Shape checks of the decode attention (sizes may be null).
+int attn_check(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_t n_q, int64_t n_kv,
+               int head_dim, float scale, AttnSizes *sizes)
+{
+    if (!(head_dim == 64 || head_dim == 128 || head_dim == 256)) return GDN_ERR_UNSUPPORTED_HEAD_DIM;
+    if (n_seqs < 0 || n_heads < 0 || n_heads_kv < 0 || n_kv < 0) return GDN_ERR_BAD_SHAPE;
+    if (n_q < 1 || n_q >= 20) return GDN_ERR_BAD_SHAPE;
+    if (!std::isfinite(scale)) return GDN_ERR_BAD_SHAPE;
+    if (n_heads > 0 && (n_heads_kv == 0 || n_heads % n_heads_kv != 0)) return GDN_ERR_BAD_SHAPE;
+    int64_t a, b, c, d;
+    if (!mul_ok(n_seqs, n_heads, &a) || !mul_ok(a, n_q, &b) || !mul_ok(b, head_dim, &c))
+        return GDN_ERR_BAD_SHAPE;
+    if (!mul_ok(n_seqs, n_heads_kv, &a) || !mul_ok(a, n_kv, &b) || !mul_ok(b, head_dim, &d))
+        return GDN_ERR_BAD_SHAPE;
+    int64_t m;
+    if (!mul_ok(n_seqs, n_q, &a) || !mul_ok(a, n_kv, &m)) return GDN_ERR_BAD_SHAPE;
+    // grid: (seq, key/value head, row group, token range) with 32-bit block ids
+    if (n_seqs * n_heads * n_q > (int64_t(1) << 24)) return GDN_ERR_BAD_SHAPE;
+    if (sizes) {
+        sizes->q_elems = c;
+        sizes->out_elems = c;
+        sizes->kv_elems = d;
+        sizes->mask_elems = m;
+    }
+    return GDN_OK;
+}
+
 // gdn_forward with n_key_heads query/key heads (value head h reads key head
 // h % n_key_heads); gdn_forward is the case n_key_heads == n_heads.
 int forward_impl(gdn_dtype dtype, const void *q, const void *k, const void *v, const float *g,
@@ -133,6 +167,74 @@ int gdn_forward_ex(gdn_dtype dtype, const void *q, const void *k, const void *v,
     return forward_impl(dtype, q, k, v, g, beta, state_in, out, state_out, n_seqs, n_tokens,
                         n_heads, n_key_heads, head_dim, flags, workspace, workspace_bytes, algo,
                         stream);
+}
+
+int gdn_flash_attn_supports(int n_q, int head_dim_k, int head_dim_v)
+{
+    const bool width = head_dim_k == head_dim_v &&
+                       (head_dim_k == 64 || head_dim_k == 128 || head_dim_k == 256);
+    return (n_q >= 1 && n_q < 20 && width) ? 1 : 0;
+}
+
+size_t gdn_flash_attn_workspace_size(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv,
+                                     int64_t n_q, int64_t n_kv, int head_dim)
+{
+    if (attn_check(n_seqs, n_heads, n_heads_kv, n_q, n_kv, head_dim, 1.f, nullptr) != GDN_OK)
+        return 0;
+    if (n_seqs == 0 || n_heads == 0) return 0;
+    return gdn::attn_workspace_bytes(n_seqs, n_heads, n_heads_kv, n_q, n_kv, head_dim);
+}
+
+int gdn_flash_attn(gdn_dtype dtype, const void *q, const void *k, const void *v,
+                   const float *mask, void *out, int64_t n_seqs, int64_t n_heads,
+                   int64_t n_heads_kv, int64_t n_q, int64_t n_kv, int head_dim, float scale,
+                   void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+    AttnSizes z;
+    int rc = attn_check(n_seqs, n_heads, n_heads_kv, n_q, n_kv, head_dim, scale, &z);
+    if (rc != GDN_OK) return rc;
+    if (n_seqs == 0 || n_heads == 0) return GDN_OK;
+    const int64_t esz = (dtype == GDN_BF16) ? 2 : 4;
+    if (!q || !out) return GDN_ERR_NULL_POINTER;
+    if (n_kv > 0 && (!k || !v)) return GDN_ERR_NULL_POINTER;
+    const void *ptrs[] = {q, k, v, mask, out, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_MISALIGNED;
+    const Range r_out = range_of(out, z.out_elems * esz);
+    const Range reads[] = {range_of(q, z.q_elems * esz), range_of(k, z.kv_elems * esz),
+                           range_of(v, z.kv_elems * esz),
+                           mask ? range_of(mask, z.mask_elems * 4) : Range{0, 0}};
+    for (const Range &r : reads)
+        if (overlap(r_out, r)) return GDN_ERR_ALIASING;
+    const size_t need = gdn::attn_workspace_bytes(n_seqs, n_heads, n_heads_kv, n_q, n_kv,
+                                                  head_dim);
+    if (workspace_bytes < need) return GDN_ERR_WORKSPACE_TOO_SMALL;
+    if (need > 0) {
+        if (!workspace) return GDN_ERR_NULL_POINTER;
+        const Range r_ws = range_of(workspace, static_cast<int64_t>(need));
+        for (const Range &r : reads)
+            if (overlap(r_ws, r)) return GDN_ERR_ALIASING;
+        if (overlap(r_ws, r_out)) return GDN_ERR_ALIASING;
+    }
+
+    // ---- validated: from here on only launches ----
+    gdn::AttnProblem p;
+    p.bf16 = (dtype == GDN_BF16);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.mask = mask;
+    p.out = out;
+    p.scale = scale;
+    p.n_seqs = n_seqs;
+    p.n_heads = n_heads;
+    p.n_heads_kv = n_heads_kv;
+    p.n_q = n_q;
+    p.n_kv = n_kv;
+    p.head_dim = head_dim;
+    const hipError_t err = gdn::launch_attn(p, workspace, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 const char *gdn_status_string(int status)

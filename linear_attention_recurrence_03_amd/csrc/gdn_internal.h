@@ -37,4 +37,27 @@ hipError_t launch_chunked(const Problem &p, void *workspace, hipStream_t stream)
 hipError_t launch_state_copy(const float *state_in, float *state_out,
                              int64_t count, hipStream_t stream);
 
+// ---- decode flash attention ----------------------------------------------------
+
+struct AttnProblem {
+    int bf16;               // 1: q, k, v, out are bf16; 0: fp32
+    const void *q, *k, *v;  // q (S, H, n_q, D); k, v (S, Hkv, n_kv, D)
+    const float *mask;      // (S, 1, n_q, n_kv) additive, or null
+    void *out;              // (S, n_q, H, D)
+    float scale;
+    int64_t n_seqs, n_heads, n_heads_kv, n_q, n_kv;
+    int head_dim;           // 64, 128 or 256
+};
+
+// How the cache is cut: rows of one (seq, key/value head) in groups of four, and
+// n_split token ranges of split_len tokens.
+struct AttnSplit {
+    int groups, n_split, split_len;
+};
+AttnSplit attn_split(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_t n_q,
+                     int64_t n_kv);
+size_t attn_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_t n_q,
+                            int64_t n_kv, int head_dim);
+hipError_t launch_attn(const AttnProblem &p, void *workspace, hipStream_t stream);
+
 }  // namespace gdn

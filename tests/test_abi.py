@@ -215,3 +215,43 @@ def test_forward_ex_flags(lib):
         assert ex(ok, out=a["q"]) == E_ALIAS
         assert ex(ok, HK=3) == E_SHAPE
     assert "flag" in gdn.status_string(E_FLAGS)
+
+
+def test_flash_attn_host_checks(lib):
+    """Decode attention: supports table, workspace query and rejections before any
+    launch (fake pointers; every call fails validation or is a no-op)."""
+    assert lib.gdn_flash_attn_supports(1, 256, 256) == 1
+    assert lib.gdn_flash_attn_supports(19, 64, 64) == 1
+    assert lib.gdn_flash_attn_supports(20, 64, 64) == 0
+    assert lib.gdn_flash_attn_supports(0, 64, 64) == 0
+    assert lib.gdn_flash_attn_supports(1, 128, 64) == 0
+    assert lib.gdn_flash_attn_supports(1, 96, 96) == 0
+    assert lib.gdn_flash_attn_workspace_size(1, 16, 4, 1, 512, 256) > 0
+    assert lib.gdn_flash_attn_workspace_size(1, 16, 3, 1, 512, 256) == 0   # bad ratio
+    assert lib.gdn_flash_attn_workspace_size(1, 16, 4, 1, 512, 96) == 0    # bad width
+    base = 1 << 32
+    q, k, v, m, o = (base + i * (1 << 24) for i in range(5))
+    ws = base + 6 * (1 << 24)
+
+    def fa(dtype=F32, q=q, k=k, v=v, m=m, o=o, S=1, H=4, HKV=2, NQ=2, NKV=100, D=64,
+           scale=0.125, ws=ws, ws_bytes=0):
+        return lib.gdn_flash_attn(dtype, q, k, v, m, o, S, H, HKV, NQ, NKV, D,
+                                  ctypes.c_float(scale), ws, ws_bytes, None)
+    assert fa(D=96) == E_HD
+    assert fa(dtype=3) == E_DTYPE
+    assert fa(NQ=20) == E_SHAPE
+    assert fa(NQ=0) == E_SHAPE
+    assert fa(HKV=3) == E_SHAPE
+    assert fa(NKV=-1) == E_SHAPE
+    assert fa(scale=float("nan")) == E_SHAPE
+    assert fa(q=None) == E_NULL
+    assert fa(k=None) == E_NULL
+    assert fa(q=q + 4) == E_ALIGN
+    assert fa(o=q) == E_ALIAS
+    assert fa(o=m + 16) == E_ALIAS
+    need = lib.gdn_flash_attn_workspace_size(1, 4, 2, 2, 100, 64)
+    if need > 0:
+        assert fa(ws_bytes=need - 1) == E_WS
+        assert fa(ws_bytes=need, ws=None) == E_NULL
+    assert fa(S=0, q=None, k=None, v=None, m=None, o=None) == OK
+    assert fa(H=0, HKV=0) == OK
