@@ -173,6 +173,69 @@ def bench_decode_layers(gdn, torch, wl, reps, n_layers=24):
     return statistics.median(dev_us), min(dev_us), max(dev_us), statistics.median(host_us)
 
 
+def bench_attn(gdn, torch, n_calls=40, reps=7):
+    """Decode attention, one query per head: the card's shape (16 query heads over 4
+    key/value heads, head_dim 256, 141 and 512 cached positions; warm, as a decode
+    loop re-reads its cache) and 32 sequences x 32 query heads over 8 key/value heads
+    x d128 x 4096 positions (0.5 GB of cache, 4 rotating copies: HBM-bound).  Device
+    time from replaying n_calls calls captured in one HIP graph (median of reps);
+    host time from eager calls."""
+    res = {}
+    for (S, H, HKV, NKV, D, nbuf) in ((1, 16, 4, 141, 256, 1), (1, 16, 4, 512, 256, 1),
+                                      (32, 32, 8, 4096, 128, 4)):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(S * 100000 + NKV)
+        sets = []
+        for _ in range(nbuf):
+            q = torch.randn((S, H, 1, D), device="cuda", generator=g).to(torch.bfloat16)
+            k = torch.randn((S, HKV, NKV, D), device="cuda", generator=g).to(torch.bfloat16)
+            v = torch.randn((S, HKV, NKV, D), device="cuda", generator=g).to(torch.bfloat16)
+            out = torch.empty((S, 1, H, D), dtype=torch.bfloat16, device="cuda")
+            sets.append((q, k, v, out))
+        ws = torch.empty(max(gdn.workspace_size_flash_attn(S, H, HKV, 1, NKV, D), 1),
+                         dtype=torch.uint8, device="cuda")
+
+        def call(i):
+            q, k, v, out = sets[i % nbuf]
+            gdn.flash_attn(q, k, v, None, out=out, workspace=ws)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):       # warm up outside capture
+            for i in range(2 * nbuf):
+                call(i)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n_calls):
+                call(i)
+        dev = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            graph.replay()
+            b.record()
+            torch.cuda.synchronize()
+            dev.append(a.elapsed_time(b) * 1e3 / n_calls)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n_calls):
+            call(i)
+        torch.cuda.synchronize()
+        host = (time.perf_counter() - t0) * 1e6 / n_calls
+        us = statistics.median(dev)
+        nbytes = 2 * S * HKV * NKV * D * 2 + 2 * S * H * D * 2
+        res["S%d_H%d_Hkv%d_nkv%d_d%d" % (S, H, HKV, NKV, D)] = {
+            "us_per_call_device": round(us, 2), "us_per_call_host_eager": round(host, 2),
+            "bytes_per_call": nbytes,
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "inputs": "bf16, warm" if nbuf == 1 else "bf16, %d rotating copies" % nbuf}
+        del sets, ws, graph
+        torch.cuda.empty_cache()
+    return res
+
+
 def profile_pass(gdn, torch, wl, launches=10):
     """Short run for hardware-counter passes: an elementwise multiply by one over
     512 MiB (known bytes: reads 512 MiB, writes 512 MiB; it calibrates FETCH_SIZE
@@ -367,6 +430,8 @@ def main():
             "hbm_frac": round(bt / (msr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "workload": "as prefill_tiled, with unnormalised q/k rows and raw gate "
                         "pre-activations transformed inside the op"}
+        # decode flash attention: the card's measured shape, and a bandwidth-sized cache
+        extras["flash_attn_decode"] = bench_attn(gdn, torch)
         line["extras"] = extras
 
     if not args.no_cpu_baseline:

@@ -13,7 +13,8 @@ import ctypes
 import os
 
 __all__ = ["forward", "supports", "workspace_size", "status_string", "library_path",
-           "GdnError", "ALGOS", "flash_attn", "supports_flash_attn"]
+           "GdnError", "ALGOS", "flash_attn", "supports_flash_attn",
+           "workspace_size_flash_attn"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
@@ -186,6 +187,13 @@ def supports_flash_attn(n_q: int, head_dim_k: int, head_dim_v: int) -> bool:
     """True iff the decode attention runs these sizes (1 <= n_q < 20, equal key and
     value widths of 64, 128 or 256)."""
     return bool(_lib().gdn_flash_attn_supports(int(n_q), int(head_dim_k), int(head_dim_v)))
+
+
+def workspace_size_flash_attn(n_seqs: int, n_heads: int, n_heads_kv: int, n_q: int,
+                              n_kv: int, head_dim: int) -> int:
+    """Device workspace bytes gdn_flash_attn needs for these sizes (0: none)."""
+    return int(_lib().gdn_flash_attn_workspace_size(n_seqs, n_heads, n_heads_kv, n_q, n_kv,
+                                                    head_dim))
 
 
 def flash_attn(q, k, v, mask=None, scale=None, out=None, workspace=None, stream=None):

@@ -13,12 +13,13 @@
 // Work split (memory-bound: every key/value byte is read once per row group):
 //   attn_split_kernel   one workgroup per (seq, key/value head, group of up to four
 //                       (query head, query) rows, range of cache tokens).  Per tile of
-//                       256 tokens: each thread scores one token against the rows
-//                       (its key row read with 16-byte loads), one wave per row
-//                       updates the running max / sum and turns scores into weights,
-//                       then the waves accumulate weights x value rows with lanes
-//                       owning 8 consecutive columns (whole value rows per load
-//                       instruction).  The partial (max, sum, weighted values) of the
+//                       64 tokens: four threads score one token against the rows
+//                       (a quarter of its key row each, 16-byte loads all issued
+//                       before the products), one wave per row updates the running
+//                       max / sum and turns scores into weights, then the waves
+//                       accumulate weights x value rows with lanes owning 8
+//                       consecutive columns (whole value rows per load instruction,
+//                       a wave's loads of the tile in flight together).  The partial (max, sum, weighted values) of the
 //                       token range goes to the workspace, or straight to the output
 //                       when the cache is not split.
 //   attn_combine_kernel merges the token ranges of each row.
@@ -34,10 +35,10 @@ namespace gdn {
 namespace {
 
 constexpr int kAttnThreads = 256;  // four waves
-constexpr int kAttnTile = 256;     // cache tokens per tile (one per thread when scoring)
+constexpr int kAttnTile = 64;      // cache tokens per tile (four threads each when scoring)
 constexpr int kAttnRows = 4;       // (query head, query) rows per workgroup
 constexpr int kAttnSplitUnit = 64; // token ranges are multiples of this
-constexpr int kAttnTargetBlocks = 512;
+constexpr int kAttnTargetBlocks = 2048;  // workgroups to aim for (about 8 per CU)
 
 template <bool BF16>
 struct AttnElem;
@@ -98,10 +99,13 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
 {
     using E = typename AttnElem<BF16>::T;
+    constexpr int QW = D / 4;            // key elements per scoring thread
     constexpr int LPR = D / 8;           // lanes covering one value row
     constexpr int SPW = 64 / LPR;        // value rows per wave instruction
     constexpr int STREAMS = 4 * SPW;     // partial accumulators per column
+    constexpr int TPW = kAttnTile / 4;   // tile tokens per wave in the value pass
     static_assert(D % 64 == 0 && D <= 256, "head width");
+    static_assert(kAttnTile == 64 && TPW % SPW == 0, "tile");
 
     __shared__ __align__(16) float sQ[kAttnRows][D];
     __shared__ float sS[kAttnRows][kAttnTile];
@@ -150,6 +154,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
 
     float m_run = -INFINITY, l_run = 0.f;   // wave r's row statistics (row r = wave)
     const int stream = wave * SPW + lane / LPR, col = (lane % LPR) * 8;
+    const int tok = tid >> 2, qtr = tid & 3;  // scoring: four threads per token
     float acc[kAttnRows][8];
 #pragma unroll
     for (int r = 0; r < kAttnRows; ++r)
@@ -158,61 +163,75 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
     __syncthreads();
 
     for (int64_t t0 = t_begin; t0 < t_end; t0 += kAttnTile) {
-        // 1. scores of token t0 + tid against the rows
+        const int last = static_cast<int>(t_end - t0 < kAttnTile ? t_end - t0 : kAttnTile) - 1;
+        // the value rows of the tile do not depend on the scores: their loads go out
+        // with the key loads, so a tile costs one memory round trip.  Wave w takes
+        // tile tokens TPW w .. TPW w + TPW - 1; tokens past the end read the last
+        // valid row and get weight 0.
+        const int tl0 = TPW * wave + lane / LPR;
+        uint4 vraw[TPW / SPW][BF16 ? 1 : 2];
+#pragma unroll
+        for (int it = 0; it < TPW / SPW; ++it) {
+            const int tl = tl0 + it * SPW;
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                vbase + (t0 + (tl < last ? tl : last)) * D + col);
+#pragma unroll
+            for (int h = 0; h < (BF16 ? 1 : 2); ++h) vraw[it][h] = src[h];
+        }
+        // 1. scores: thread (tok, qtr) takes a quarter of key row t0 + tok (rows past
+        //    the end read the last valid one and are masked below); all its loads are
+        //    issued before the first product
         {
-            const int64_t t = t0 + tid;
+            const E *kr = kbase + (t0 + (tok < last ? tok : last)) * D + qtr * QW;
+            float kx[QW];
+#pragma unroll
+            for (int c = 0; c < QW; c += 8) {
+                float x8[8];
+                load8<BF16>(kr + c, x8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kx[c + e] = x8[e];
+            }
             float sc[kAttnRows];
-            if (t < t_end) {
 #pragma unroll
-                for (int r = 0; r < kAttnRows; ++r) sc[r] = 0.f;
-                const E *kr = kbase + t * D;
-#pragma unroll 4
-                for (int c = 0; c < D; c += 8) {
-                    float kx[8];
-                    load8<BF16>(kr + c, kx);
+            for (int r = 0; r < kAttnRows; ++r) {
+                float acc_r = 0.f;
 #pragma unroll
-                    for (int r = 0; r < kAttnRows; ++r) {
-                        const float4 q0 = *reinterpret_cast<const float4 *>(&sQ[r][c]);
-                        const float4 q1 = *reinterpret_cast<const float4 *>(&sQ[r][c + 4]);
-                        sc[r] = fmaf(q0.x, kx[0], fmaf(q0.y, kx[1], fmaf(q0.z, kx[2], fmaf(q0.w, kx[3], sc[r]))));
-                        sc[r] = fmaf(q1.x, kx[4], fmaf(q1.y, kx[5], fmaf(q1.z, kx[6], fmaf(q1.w, kx[7], sc[r]))));
-                    }
+                for (int c = 0; c < QW; c += 4) {
+                    const float4 qv = *reinterpret_cast<const float4 *>(&sQ[r][qtr * QW + c]);
+                    acc_r = fmaf(qv.x, kx[c], fmaf(qv.y, kx[c + 1], fmaf(qv.z, kx[c + 2],
+                                 fmaf(qv.w, kx[c + 3], acc_r))));
                 }
+                acc_r += __shfl_xor(acc_r, 1, 64);
+                acc_r += __shfl_xor(acc_r, 2, 64);
+                sc[r] = acc_r;
+            }
+            if (qtr == 0) {
+                const int64_t t = t0 + tok;
 #pragma unroll
                 for (int r = 0; r < kAttnRows; ++r) {
-                    if (a.mask && rv[r]) sc[r] += mask_f16(a.mask[(s * a.n_q + ri[r]) * a.n_kv + t]);
-                    if (!rv[r]) sc[r] = -INFINITY;
+                    float v = sc[r];
+                    if (!rv[r] || tok > last)
+                        v = -INFINITY;
+                    else if (a.mask)
+                        v += mask_f16(a.mask[(s * a.n_q + ri[r]) * a.n_kv + t]);
+                    sS[r][tok] = v;
                 }
-            } else {
-#pragma unroll
-                for (int r = 0; r < kAttnRows; ++r) sc[r] = -INFINITY;
             }
-#pragma unroll
-            for (int r = 0; r < kAttnRows; ++r) sS[r][tid] = sc[r];
         }
         __syncthreads();
 
         // 2. wave r: running max and sum of row r; scores become weights
         {
             const int r = wave;
-            float x[kAttnTile / 64];
-            float mt = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < kAttnTile / 64; ++e) {
-                x[e] = sS[r][lane + 64 * e];
-                mt = fmaxf(mt, x[e]);
-            }
+            const float x = sS[r][lane];
+            float mt = x;
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 64));
             const float m_new = fmaxf(m_run, mt);
             const float corr = exp_diff(m_run, m_new);
-            float ps = 0.f;
-#pragma unroll
-            for (int e = 0; e < kAttnTile / 64; ++e) {
-                const float p = (x[e] == -INFINITY) ? 0.f : __expf(x[e] - m_new);
-                sS[r][lane + 64 * e] = p;
-                ps += p;
-            }
+            const float p = (x == -INFINITY) ? 0.f : __expf(x - m_new);
+            sS[r][lane] = p;
+            float ps = p;
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 64);
             l_run = l_run * corr + ps;
@@ -221,20 +240,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
         }
         __syncthreads();
 
-        // 3. weighted value rows: wave w takes tokens 64w .. 64w + 63 of the tile
+        // 3. weighted value rows (loaded above)
         {
-            float cr[kAttnRows];
 #pragma unroll
             for (int r = 0; r < kAttnRows; ++r) {
-                cr[r] = sCorr[r];
+                const float cr = sCorr[r];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[r][e] *= cr[r];
+                for (int e = 0; e < 8; ++e) acc[r][e] *= cr;
             }
-            const int tl0 = 64 * wave + lane / LPR;
-            const int64_t n_here = t_end - t0;
-            for (int tl = tl0; tl < 64 * wave + 64 && tl < n_here; tl += SPW) {
+#pragma unroll
+            for (int it = 0; it < TPW / SPW; ++it) {
+                const int tl = tl0 + it * SPW;
                 float vx[8];
-                load8<BF16>(vbase + (t0 + tl) * D + col, vx);
+                load8<BF16>(reinterpret_cast<const E *>(&vraw[it][0]), vx);
 #pragma unroll
                 for (int r = 0; r < kAttnRows; ++r) {
                     const float p = sS[r][tl];
@@ -281,28 +299,56 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
     }
 }
 
-// One workgroup of 64 threads per (seq, query, head) row: merges its token ranges.
+// One wave per (seq, query, head) row: merges its token ranges.  Lanes load the
+// ranges' maxima and sums in parallel (64 ranges per pass), then each lane adds the
+// weighted partial sums of its D/64 columns with the weights taken from the lanes
+// that hold them.
 template <int D, bool BF16>
 __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a)
 {
     const int64_t row = blockIdx.x;
-    const float *pp = a.part + row * a.n_split * (D + 2);
+    const int lane = threadIdx.x;
+    const int ns = a.n_split;
+    const float *pp = a.part + row * ns * (D + 2);
     float M = -INFINITY;
-    for (int i = 0; i < a.n_split; ++i) M = fmaxf(M, pp[i * (D + 2) + D]);
+    for (int i0 = 0; i0 < ns; i0 += 64)
+        if (i0 + lane < ns) M = fmaxf(M, pp[(i0 + lane) * (D + 2) + D]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     float den = 0.f, num[D / 64];
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) num[e] = 0.f;
-    for (int i = 0; i < a.n_split; ++i) {
-        const float *pi = pp + i * (D + 2);
-        const float w = (pi[D] == -INFINITY) ? 0.f : __expf(pi[D] - M);
-        den = fmaf(w, pi[D + 1], den);
+    for (int i0 = 0; i0 < ns; i0 += 64) {
+        float w = 0.f;
+        if (i0 + lane < ns) {
+            const float *pi = pp + (i0 + lane) * (D + 2);
+            const float m = pi[D];
+            w = (m == -INFINITY) ? 0.f : __expf(m - M);
+            den = fmaf(w, pi[D + 1], den);
+        }
+        const int cnt = ns - i0 < 64 ? ns - i0 : 64;
+        for (int i = 0; i < cnt; i += 8) {
+            float x[8][D / 64], wi[8];
 #pragma unroll
-        for (int e = 0; e < D / 64; ++e) num[e] = fmaf(w, pi[threadIdx.x + 64 * e], num[e]);
+            for (int q = 0; q < 8; ++q) {
+                const int ii = i + q < cnt ? i + q : cnt - 1;
+                wi[q] = __shfl(w, ii, 64);
+                if (i + q >= cnt) wi[q] = 0.f;
+#pragma unroll
+                for (int e = 0; e < D / 64; ++e) x[q][e] = pp[(i0 + ii) * (D + 2) + lane + 64 * e];
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+#pragma unroll
+                for (int e = 0; e < D / 64; ++e) num[e] = fmaf(wi[q], x[q][e], num[e]);
+        }
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) {
         const float o = (den > 0.f) ? num[e] / den : 0.f;
-        const int64_t idx = row * D + threadIdx.x + 64 * e;
+        const int64_t idx = row * D + lane + 64 * e;
         if constexpr (BF16)
             static_cast<uint16_t *>(a.out)[idx] = f32_to_bf16(o);
         else
