@@ -70,7 +70,10 @@ def test_status_strings(lib):
 
 def test_workspace_size(lib):
     assert gdn.workspace_size("f32", 1, 1, 32, 128, "auto") == 0       # recurrence
-    assert gdn.workspace_size("f32", 64, 63, 32, 128, "auto") == 0
+    assert gdn.workspace_size("f32", 64, 39, 32, 128, "auto") == 0     # AUTO: fp32 from 40
+    assert gdn.workspace_size("f32", 64, 40, 32, 128, "auto") > 0
+    assert gdn.workspace_size("bf16", 2, 15, 32, 128, "auto") == 0     # bf16 from 16
+    assert gdn.workspace_size("bf16", 2, 16, 32, 128, "auto") > 0
     assert gdn.workspace_size("bf16", 1, 4096, 32, 128, "recurrent") == 0
     assert gdn.workspace_size("bf16", 0, 4096, 32, 128, "chunked") == 0
     assert gdn.workspace_size("bf16", 1, 4096, 32, 48, "chunked") == 0  # unsupported
