@@ -46,6 +46,8 @@
 // j of group g stands for row 4g+j (j < 4) or 16+4g+j-4 (j >= 4) of the 32; every
 // A operand here is loaded with that same k order, so no data moves between
 // lanes when a product feeds the next one.
+#include <atomic>
+
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
@@ -1394,18 +1396,30 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
     }
 }
 
+// Raises the dynamic-LDS limit of `kern` to `bytes`, once per device (bit d of
+// `done` records device d; concurrent first calls may both set it, harmlessly).
+template <typename K>
+hipError_t ensure_lds_limit(K kern, int bytes, std::atomic<uint64_t> &done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
 template <int D, bool BF16, bool NORM>
 hipError_t launch_prep(const Problem &p, unsigned char *ws, int n_chunks, hipStream_t stream)
 {
     using L = PrepSmem<D, BF16>;
     auto kern = chunk_prep_kernel<D, BF16, NORM>;
-    static bool attr_set = false;  // one-time attribute; same value every time
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::kBytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = ensure_lds_limit(kern, L::kBytes, lds_set);
+    if (e != hipSuccess) return e;
     const int64_t blocks = p.n_seqs * p.n_heads * n_chunks;
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kPrepThreads), L::kBytes,
                        stream, p.q, p.k, p.g, p.beta, ws, p.n_tokens, p.n_heads, p.n_k_heads,
@@ -1418,13 +1432,9 @@ hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, 
 {
     using F = ScanCfg<D, BF16, VT>;
     auto kern = chunk_scan_kernel<D, BF16, VT, NORM>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, F::kBytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = ensure_lds_limit(kern, F::kBytes, lds_set);
+    if (e != hipSuccess) return e;
     constexpr int NRB = D / F::RW;
     const int64_t n_sh = p.n_seqs * p.n_heads;
     const int64_t blocks = (n_sh + 7) / 8 * 8 * NRB;
