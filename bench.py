@@ -73,6 +73,19 @@ def load_traffic(workload_key):
     return rec.get("bytes_per_launch")
 
 
+def load_mfma(workload_key):
+    """Matrix-core busy share per prefill kernel from the committed counter run, if it
+    was taken on the current kernel sources (else None)."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "mfma.json")) as f:
+            rec = json.load(f).get(workload_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return {k: round(v["mfma_busy_frac"], 4) for k, v in rec["kernels"].items()}
+
+
 def to_dev(x, dtype, torch):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     d = {}
@@ -287,6 +300,44 @@ def summarize_pmc(fetch_dir, write_dir):
     print(json.dumps(rec, indent=1))
 
 
+def summarize_mfma(pmc_dir):
+    """Matrix-core counters of one rocprofv3 --pmc run of --profile-pass
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE) per
+    launch of each prefill kernel: bf16 MFMA FLOP (MOPS x 512, the counter's unit);
+    the share of SIMD cycles with the matrix core busy while the kernel ran (busy
+    cycles summed over SIMDs, over active cycles x SIMDs; GRBM_GUI_ACTIVE comes summed
+    over the XCDs, so it is divided by their count from the agent table); and the
+    MFMA rate over the dispatch's own duration against the dense bf16 peak.  Writes
+    profiles/mfma.json."""
+    import csv
+    agent = next(r for r in csv.DictReader(open(os.path.join(pmc_dir, "run_agent_info.csv")))
+                 if r.get("Agent_Type", "").upper().endswith("GPU") or r.get("Name") == "gfx950")
+    n_xcc, n_simd = int(agent["Num_Xcc"]), int(agent["Simd_Count"])
+    vals, dur = {}, {}
+    for r in csv.DictReader(open(os.path.join(pmc_dir, "run_counter_collection.csv"))):
+        name = r["Kernel_Name"]
+        key = ("chunk_scan" if "chunk_scan" in name else
+               "chunk_prep" if "chunk_prep" in name else None)
+        if key:
+            vals.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+            dur.setdefault(key, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) -
+                                                         int(r["Start_Timestamp"])) * 1e-9
+    rec = {"source_hash": kernel_source_hash(), "xcds": n_xcc, "simds": n_simd, "kernels": {}}
+    for k in ("chunk_prep", "chunk_scan"):
+        flop = statistics.median(vals[(k, "SQ_INSTS_VALU_MFMA_MOPS_BF16")]) * 512
+        busy = statistics.median(vals[(k, "SQ_VALU_MFMA_BUSY_CYCLES")])
+        gui = statistics.median(vals[(k, "GRBM_GUI_ACTIVE")]) / n_xcc
+        t = statistics.median(dur[k].values())
+        rec["kernels"][k] = {"mfma_flop_bf16": flop, "mfma_busy_cycles": busy,
+                             "active_cycles": gui, "mfma_busy_frac": busy / (gui * n_simd),
+                             "seconds_under_counters": t,
+                             "mfma_frac_of_bf16_peak": flop / t / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    out = os.path.join(ROOT, "profiles", "mfma.json")
+    with open(out, "w") as fh:
+        json.dump({"prefill_bf16": rec}, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def cpu_baseline(wl, min_seconds=10.0):
     """The fp64 oracle on this host's cores over the whole prefill workload, repeated
     until about min_seconds of CPU time have been spent (one pass takes well under a
@@ -321,9 +372,15 @@ def main():
                     help="short run for rocprofv3 --pmc passes (copy calibration + 10 launches)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two --pmc runs of --profile-pass")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="write profiles/mfma.json from a --pmc run of --profile-pass with "
+                         "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -373,6 +430,7 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes,
                      "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "mfma_busy_counters": load_mfma("prefill_bf16"),
                      "scope": "one gdn_forward call (all kernels of the chunked path)"},
     }
 
