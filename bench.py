@@ -73,6 +73,25 @@ def load_traffic(workload_key):
     return rec.get("bytes_per_launch")
 
 
+def run_env(torch):
+    """Where the numbers were taken: GPU, its compute units, HIP and torch builds,
+    host CPU model and the cores this process may use."""
+    props = torch.cuda.get_device_properties(0)
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"gpu": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hip": torch.version.hip,
+            "torch": torch.__version__, "host_cpu": cpu,
+            "host_cores": len(os.sched_getaffinity(0))}
+
+
 def load_mfma(workload_key):
     """Matrix-core busy share per prefill kernel from the committed counter run, if it
     was taken on the current kernel sources (else None)."""
@@ -498,6 +517,7 @@ def main():
         extras["flash_attn_decode"] = bench_attn(gdn, torch)
         line["extras"] = extras
 
+    line["env"] = run_env(torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)
