@@ -9,7 +9,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "gdn_oracle.c")
-LIB = os.path.join(HERE, "libgdn_oracle.so")
+# GDN_ORACLE_PATH points the tests at another build of the same source
+LIB = os.environ.get("GDN_ORACLE_PATH", os.path.join(HERE, "libgdn_oracle.so"))
 
 
 def build(verbose: bool = False) -> str:
