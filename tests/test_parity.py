@@ -202,6 +202,15 @@ def test_input_transforms_tiled_prefill(gdn):
           raw_gates=True)
 
 
+@pytest.mark.parametrize("T,algo", [(1, "recurrent"), (5, "recurrent"), (130, "chunked")])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_input_transforms_tiled(gdn, T, algo, dtype):
+    """Both transforms with q/k of 2 heads tiled over 6 value heads (decode and prefill)."""
+    x = _mixed_raw(2, T, 6, 64, dtype, seed=800 + T, l2=True, gates=True, key_heads=2)
+    check(gdn, x, dtype, algo, what="transforms tiled T=%d" % T, l2norm_qk=True,
+          raw_gates=True)
+
+
 def test_input_transforms_zero_rows(gdn):
     """All-zero q or k rows stay finite with normalisation (epsilon in the root)."""
     x = _mixed_raw(1, 130, 2, 64, "bf16", seed=7, l2=True, gates=False)
