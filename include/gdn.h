@@ -135,7 +135,13 @@ size_t gdn_workspace_size(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens,
  * n_seqs == 0 or n_heads == 0 is a no-op.  n_tokens == 0 copies state_in to
  * state_out (or zero-fills it when state_in is NULL) and writes no output.
  * Every pointer must be 16-byte aligned.  Returns GDN_OK or a negative status;
- * on error nothing is launched. */
+ * on error nothing is launched.
+ *
+ * Size limits (a dispatch counts the work-items of its grid in 32 bits): at most
+ * 2^27 state rows, n_seqs * n_heads * head_dim (a 64 GiB state at head_dim 128),
+ * and, when the chunked form runs, fewer than 2^24 chunks,
+ * n_seqs * n_heads * ceil(n_tokens / 64).  Larger calls return GDN_ERR_BAD_SHAPE;
+ * split the batch or the sequence over several calls (the state carries over). */
 int gdn_forward(gdn_dtype dtype, const void *q, const void *k, const void *v,
                 const float *g, const float *beta, const float *state_in,
                 void *out, float *state_out, int64_t n_seqs, int64_t n_tokens,
@@ -218,7 +224,9 @@ size_t gdn_flash_attn_workspace_size(int64_t n_seqs, int64_t n_heads, int64_t n_
  * for the width, GDN_ERR_BAD_SHAPE for n_q, negative sizes or a non-dividing
  * n_heads_kv), a non-finite scale (GDN_ERR_BAD_SHAPE), null or misaligned
  * pointers, out overlapping an input, a too small workspace.  n_seqs == 0 or
- * n_heads == 0 is a no-op; n_kv == 0 writes zeros. */
+ * n_heads == 0 is a no-op; n_kv == 0 writes zeros.  Size limits: at most 2^24
+ * query rows (n_seqs * n_heads * n_q), and grids that fit one dispatch each
+ * (their work-items are counted in 32 bits); else GDN_ERR_BAD_SHAPE. */
 int gdn_flash_attn(gdn_dtype dtype, const void *q, const void *k, const void *v,
                    const float *mask, void *out, int64_t n_seqs, int64_t n_heads,
                    int64_t n_heads_kv, int64_t n_q, int64_t n_kv, int head_dim, float scale,

@@ -20,6 +20,14 @@ constexpr int kVersion = 100;  // 0.1.0
 // small enough that every byte offset fits comfortably in int64.
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
+// A dispatch counts the work-items of its grid in 32 bits, so one call is bounded
+// by the grids it launches: state rows (n_seqs * n_heads * head_dim; the token
+// recurrence runs 8 work-items per row, the chunked scan at most 28) and, for the
+// chunked form, chunks (n_seqs * n_heads * ceil(n_tokens / 64); 256 work-items
+// each).  Both bounds lie beyond what fits in device memory at head_dim 128.
+constexpr int64_t kMaxStateRows = int64_t(1) << 27;
+constexpr int64_t kMaxChunks = (int64_t(1) << 24) - 1;
+
 bool mul_ok(int64_t a, int64_t b, int64_t *r)
 {
     if (a < 0 || b < 0) return false;
@@ -77,8 +85,10 @@ int check_shape(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens, int64_t n_hea
         return GDN_ERR_BAD_SHAPE;
     if (!mul_ok(n_seqs, n_heads, &b) || !mul_ok(b, int64_t(head_dim) * head_dim, state_elems))
         return GDN_ERR_BAD_SHAPE;
-    // launch grids index (seq, head, row block) with 32-bit block ids
-    if (b > (int64_t(1) << 24)) return GDN_ERR_BAD_SHAPE;
+    if (b * head_dim > kMaxStateRows) return GDN_ERR_BAD_SHAPE;
+    if (b > 0 && n_tokens > 0 && pick_algo(algo, n_tokens, dtype) == GDN_ALGO_CHUNKED &&
+        (n_tokens + 63) / 64 > kMaxChunks / b)
+        return GDN_ERR_BAD_SHAPE;
     return GDN_OK;
 }
 
@@ -103,8 +113,12 @@ int attn_check(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_t n_q,
         return GDN_ERR_BAD_SHAPE;
     int64_t m;
     if (!mul_ok(n_seqs, n_q, &a) || !mul_ok(a, n_kv, &m)) return GDN_ERR_BAD_SHAPE;
-    // grid: (seq, key/value head, row group, token range) with 32-bit block ids
+    // grids: (seq, key/value head, row group, token range) workgroups of 256
+    // work-items, then one wave per (seq, query, head) row to merge the ranges; a
+    // dispatch counts work-items in 32 bits
     if (n_seqs * n_heads * n_q > (int64_t(1) << 24)) return GDN_ERR_BAD_SHAPE;
+    if (n_seqs > 0 && n_heads > 0 && !gdn::attn_grid_fits(n_seqs, n_heads, n_heads_kv, n_q, n_kv))
+        return GDN_ERR_BAD_SHAPE;
     if (sizes) {
         sizes->q_elems = c;
         sizes->out_elems = c;

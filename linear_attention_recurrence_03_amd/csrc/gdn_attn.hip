@@ -376,11 +376,11 @@ hipError_t launch_attn_d(const AttnProblem &p, void *ws, hipStream_t stream)
     a.n_split = sp.n_split;
     a.split_len = sp.split_len;
     const int64_t blocks = p.n_seqs * p.n_heads_kv * sp.groups * int64_t(sp.n_split);
-    if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const int64_t rows = p.n_seqs * p.n_q * p.n_heads;
+    if (!grid_fits(blocks, kAttnThreads) || !grid_fits(rows, 64)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((attn_split_kernel<D, BF16>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kAttnThreads), 0, stream, a);
     if (sp.n_split > 1) {
-        const int64_t rows = p.n_seqs * p.n_q * p.n_heads;
         hipLaunchKernelGGL((attn_combine_kernel<D, BF16>), dim3(static_cast<uint32_t>(rows)),
                            dim3(64), 0, stream, a);
     }
@@ -400,12 +400,18 @@ hipError_t launch_attn_t(const AttnProblem &p, void *ws, hipStream_t stream)
 
 }  // namespace
 
-AttnSplit attn_split(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_t n_q,
-                     int64_t n_kv)
+namespace {
+
+struct SplitSizes {
+    int64_t groups, n_split, split_len;
+};
+
+SplitSizes split_sizes(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_t n_q,
+                       int64_t n_kv)
 {
-    AttnSplit sp;
+    SplitSizes sp;
     const int64_t hg = n_heads / n_heads_kv;
-    sp.groups = static_cast<int>((hg * n_q + kAttnRows - 1) / kAttnRows);
+    sp.groups = (hg * n_q + kAttnRows - 1) / kAttnRows;
     const int64_t units = n_seqs * n_heads_kv * sp.groups;
     const int64_t max_split = (n_kv + kAttnSplitUnit - 1) / kAttnSplitUnit;
     int64_t ns = (kAttnTargetBlocks + units - 1) / units;
@@ -417,9 +423,32 @@ AttnSplit attn_split(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_
     if (len < kAttnSplitUnit) len = kAttnSplitUnit;
     ns = (n_kv + len - 1) / len;
     if (ns < 1) ns = 1;
-    sp.n_split = static_cast<int>(ns);
-    sp.split_len = static_cast<int>(len);
+    sp.n_split = ns;
+    sp.split_len = len;
     return sp;
+}
+
+}  // namespace
+
+AttnSplit attn_split(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_t n_q,
+                     int64_t n_kv)
+{
+    const SplitSizes z = split_sizes(n_seqs, n_heads, n_heads_kv, n_q, n_kv);
+    AttnSplit sp;
+    sp.groups = static_cast<int>(z.groups);
+    sp.n_split = static_cast<int>(z.n_split);
+    sp.split_len = static_cast<int>(z.split_len);
+    return sp;
+}
+
+bool attn_grid_fits(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_t n_q,
+                    int64_t n_kv)
+{
+    const SplitSizes z = split_sizes(n_seqs, n_heads, n_heads_kv, n_q, n_kv);
+    if (z.groups > INT32_MAX || z.n_split > INT32_MAX || z.split_len > INT32_MAX) return false;
+    const int64_t units = n_seqs * n_heads_kv * z.groups;
+    return grid_fits(units, kAttnThreads) && units <= INT64_MAX / z.n_split &&
+           grid_fits(units * z.n_split, kAttnThreads) && grid_fits(n_seqs * n_q * n_heads, 64);
 }
 
 size_t attn_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_t n_q,

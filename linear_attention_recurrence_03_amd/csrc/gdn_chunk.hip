@@ -1427,6 +1427,14 @@ hipError_t launch_prep(const Problem &p, unsigned char *ws, int n_chunks, hipStr
     return hipGetLastError();
 }
 
+// Scan workgroups: the row blocks of every (seq, head), heads padded to a multiple
+// of eight (one XCD per head).
+template <int D, bool BF16, int VT>
+int64_t scan_blocks(int64_t n_sh)
+{
+    return (n_sh + 7) / 8 * 8 * (D / ScanCfg<D, BF16, VT>::RW);
+}
+
 template <int D, bool BF16, int VT, bool NORM>
 hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, hipStream_t stream)
 {
@@ -1435,9 +1443,8 @@ hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, 
     static std::atomic<uint64_t> lds_set{0};
     const hipError_t e = ensure_lds_limit(kern, F::kBytes, lds_set);
     if (e != hipSuccess) return e;
-    constexpr int NRB = D / F::RW;
     const int64_t n_sh = p.n_seqs * p.n_heads;
-    const int64_t blocks = (n_sh + 7) / 8 * 8 * NRB;
+    const int64_t blocks = scan_blocks<D, BF16, VT>(n_sh);
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(64 * F::kWaves), F::kBytes,
                        stream, p.q, p.k, p.v, p.state_in, p.out, p.state_out, ws, p.n_tokens,
@@ -1453,11 +1460,19 @@ hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, 
 template <int D, bool BF16, bool NORM>
 hipError_t launch_chunk_dn(const Problem &p, unsigned char *ws, hipStream_t stream)
 {
-    const int n_chunks = static_cast<int>((p.n_tokens + C - 1) / C);
+    const int64_t n_chunks64 = (p.n_tokens + C - 1) / C;
+    const int64_t n_sh = p.n_seqs * p.n_heads;
+    const bool vt1 = !BF16 || n_sh * (D / 16) <= 256;
+    // both grids are checked before either kernel is launched
+    const bool scan_fits =
+        vt1 ? grid_fits(scan_blocks<D, BF16, 1>(n_sh), 64 * ScanCfg<D, BF16, 1>::kWaves)
+            : grid_fits(scan_blocks<D, BF16, 2>(n_sh), 64 * ScanCfg<D, BF16, 2>::kWaves);
+    if (n_chunks64 > INT32_MAX || !grid_fits(n_sh * n_chunks64, kPrepThreads) || !scan_fits)
+        return hipErrorInvalidConfiguration;
+    const int n_chunks = static_cast<int>(n_chunks64);
     hipError_t e = launch_prep<D, BF16, NORM>(p, ws, n_chunks, stream);
     if (e != hipSuccess) return e;
-    const int64_t n_sh = p.n_seqs * p.n_heads;
-    if (!BF16 || n_sh * (D / 16) <= 256)
+    if (vt1)
         return launch_scan<D, BF16, 1, NORM>(p, ws, n_chunks, stream);
     if constexpr (BF16) return launch_scan<D, BF16, 2, NORM>(p, ws, n_chunks, stream);
     return hipErrorInvalidValue;  // not reached

@@ -244,7 +244,7 @@ hipError_t launch_rec(const Problem &p, hipStream_t stream)
     constexpr int kRowsPerBlock = kWaves * 2 * NP;
     static_assert(D % kRowsPerBlock == 0, "rows per block must divide head_dim");
     const int64_t blocks = p.n_seqs * p.n_heads * (D / kRowsPerBlock);
-    if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (!grid_fits(blocks, kWaves * 64)) return hipErrorInvalidConfiguration;
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
     hipLaunchKernelGGL((recurrent_kernel<D, NP, BF16>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kWaves * 64), 0, stream, p.q, p.k, p.v, p.g, p.beta,

@@ -11,6 +11,12 @@ namespace gdn {
 // Chunk length of the chunked algorithm (tokens per block of the sequence).
 constexpr int kChunk = 64;
 
+// A dispatch counts the work-items of its grid in 32 bits.
+inline bool grid_fits(int64_t blocks, int64_t threads)
+{
+    return blocks > 0 && threads > 0 && blocks <= int64_t(0xffffffffLL) / threads;
+}
+
 struct Problem {
     int bf16;               // 1: q, k, v, out are bf16; 0: fp32
     const void *q, *k, *v;
@@ -58,6 +64,10 @@ AttnSplit attn_split(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_
                      int64_t n_kv);
 size_t attn_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_t n_q,
                             int64_t n_kv, int head_dim);
+// Whether both attention grids fit one dispatch each (n_seqs, n_heads >= 1 and
+// n_heads_kv a divisor of n_heads).
+bool attn_grid_fits(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_t n_q,
+                    int64_t n_kv);
 hipError_t launch_attn(const AttnProblem &p, void *workspace, hipStream_t stream);
 
 }  // namespace gdn

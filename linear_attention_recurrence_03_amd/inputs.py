@@ -167,3 +167,43 @@ def custom(n_seqs, n_tokens, n_heads, head_dim, dtype="f32", state="normal",
     wl = Workload("custom", n_seqs, n_tokens, n_heads, head_dim, dtype, state,
                   gate, beta_std=beta_std, seed=seed, key_heads=key_heads, raw=raw)
     return make(wl)
+
+
+def make_device(n_seqs, n_tokens, n_heads, head_dim, dtype="bf16", state="zeros",
+                gate_offset=0.0, seed=0, device="cuda"):
+    """The standard recipe drawn on a GPU with torch's seeded generator, for sizes
+    whose host-side draw would take minutes; the tensors stay on ``device``.
+
+    q, k: N(0,1) rows L2-normalised in fp32; v: N(0,1); g = -softplus(N(0,1)) -
+    gate_offset; beta = sigmoid(N(0,1)); state: zeros or N(0, 0.1) fp32
+    [value][key].  q, k, v are then stored as ``dtype`` (bf16 rounds to nearest
+    even); g, beta and the state are fp32.  Draw order: q, k, v, gate normals,
+    beta normals, state.  Returns a dict of torch tensors like ``make``.
+    """
+    import torch
+
+    gen = torch.Generator(device=device).manual_seed(int(seed))
+    S, T, H, d = n_seqs, n_tokens, n_heads, head_dim
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+
+    def rows(shape, normalise):
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        if normalise:
+            x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True).clamp_min_(1e-30)
+        return x.to(tdt)
+
+    q = rows((S, T, H, d), True)
+    k = rows((S, T, H, d), True)
+    v = rows((S, T, H, d), False)
+    zg = torch.randn((S, T, H), generator=gen, device=device, dtype=torch.float32)
+    g = -torch.nn.functional.softplus(zg) - float(gate_offset)
+    zb = torch.randn((S, T, H), generator=gen, device=device, dtype=torch.float32)
+    beta = torch.sigmoid(zb)
+    if state == "normal":
+        st = torch.randn((S, H, d, d), generator=gen, device=device, dtype=torch.float32)
+        st *= 0.1
+    elif state == "zeros":
+        st = torch.zeros((S, H, d, d), device=device, dtype=torch.float32)
+    else:
+        raise ValueError("unknown state recipe %r" % state)
+    return {"q": q, "k": k, "v": v, "g": g, "beta": beta, "state": st}

@@ -258,3 +258,37 @@ def test_flash_attn_host_checks(lib):
         assert fa(ws_bytes=need, ws=None) == E_NULL
     assert fa(S=0, q=None, k=None, v=None, m=None, o=None) == OK
     assert fa(H=0, HKV=0) == OK
+
+
+def test_size_limits(lib):
+    """Calls whose grids would not fit one dispatch (work-items counted in 32 bits)
+    are rejected up front: at most 2^27 state rows, fewer than 2^24 chunks for the
+    chunked form, and decode-attention grids that fit.  Accepted shapes reach the
+    pointer checks (null q: GDN_ERR_NULL_POINTER), so nothing is launched either way."""
+    rows = 1 << 27
+    c = _Call(T=1, H=1, D=128)
+    assert c(lib, S=rows // 128, q=None) == E_NULL
+    assert c(lib, S=rows // 128 + 1, q=None) == E_SHAPE
+    c32 = _Call(T=1, H=4, D=32)
+    assert c32(lib, S=rows // 128, q=None) == E_NULL
+    assert c32(lib, S=rows // 128 + 1, q=None) == E_SHAPE
+    # chunks: n_seqs * n_heads * ceil(n_tokens / 64) < 2^24 when the chunked form runs
+    nmax = (1 << 24) - 1
+    assert gdn.workspace_size("bf16", 1, nmax * 64, 1, 32, "chunked") > 0
+    assert gdn.workspace_size("bf16", 1, nmax * 64 + 1, 1, 32, "chunked") == 0
+    assert gdn.workspace_size("bf16", 2, (nmax // 2) * 64, 1, 32, "auto") > 0
+    assert gdn.workspace_size("bf16", 2, (nmax // 2 + 1) * 64, 1, 32, "auto") == 0
+    cl = _Call(S=1, H=1, D=32, dtype=BF16)
+    assert cl(lib, T=nmax * 64 + 1, algo=CHUNK, q=None) == E_SHAPE
+    assert cl(lib, T=nmax * 64 + 1, algo=REC, q=None) == E_NULL   # the recurrence has no chunks
+    # decode attention: 2^24 single-row (seq, head) units of 256 work-items overflow
+    base = 1 << 32
+
+    def fa(S, H=1, HKV=1, NQ=1, NKV=64, q=base):
+        return lib.gdn_flash_attn(F32, q, base + (1 << 40), base + (2 << 40), None,
+                                  base + (3 << 40), S, H, HKV, NQ, NKV, 64,
+                                  ctypes.c_float(0.125), None, 0, None)
+    assert fa(S=(1 << 24) - 1, q=None) == E_NULL
+    assert fa(S=1 << 24, q=None) == E_SHAPE
+    assert fa(S=1 << 22, H=4, HKV=1, NQ=1, q=None) == E_NULL     # four rows per workgroup
+    assert fa(S=(1 << 24) + 1, q=None) == E_SHAPE
