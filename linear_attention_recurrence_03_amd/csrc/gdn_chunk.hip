@@ -223,16 +223,6 @@ __device__ __forceinline__ Frag<BF16> frag_blk(const unsigned char *blk, int lan
     return *reinterpret_cast<const Frag<BF16> *>(blk + kFragBytes<BF16> * blk_unit(lane & 15, lane >> 4));
 }
 
-// Byte offset of element (r, c), c < 32 (r / 32 + 1), in a triangular block image.
-template <bool BF16>
-__device__ __forceinline__ int tri_offset(int r, int c)
-{
-    const int tt = r >> 4, i = r & 15, h = c >> 5, kk = c & 31;
-    const int b = tt < 2 ? tt : 2 * tt - 2 + h;
-    const int g = (kk & 15) >> 2, j = (kk & 3) + ((kk >> 4) << 2);
-    return b * kBlkBytes<BF16> + kFragBytes<BF16> * blk_unit(i, g) + j * (BF16 ? 2 : 4);
-}
-
 // ---- workspace layout, per (seq, head, chunk) ----------------------------------
 //   T     six fragment blocks (elements like q/k/v: fp32 or bf16)
 //   P     six fragment blocks
@@ -301,7 +291,7 @@ constexpr int kPrepThreads = 256;
 
 // LDS of the prep kernel (one workgroup per (seq, head, chunk)).  Region R holds
 // the chunk's K and Q rows (16-byte padded) while the products are formed; after
-// that it is reused for T, A (as MFMA input type) and the P staging image.
+// that it is reused for T and A (as MFMA input type).
 template <int D, bool BF16>
 struct PrepSmem {
     using E = typename Elem<BF16>::T;
@@ -311,9 +301,8 @@ struct PrepSmem {
     static constexpr int LDD = 16;                       // transposed diagonal blocks (floats)
     static constexpr int kMat = C * LDT * ES;            // one C x C matrix of E
     static constexpr int kK = 0, kQ = C * RK;            // during the products
-    static constexpr int kT = 0, kAe = kMat, kPst = 2 * kMat;  // afterwards
-    static constexpr int kR = (2 * C * RK > 2 * kMat + 6 * kBlkBytes<BF16>) ? 2 * C * RK
-                                                                             : 2 * kMat + 6 * kBlkBytes<BF16>;
+    static constexpr int kT = 0, kAe = kMat;             // afterwards
+    static constexpr int kR = (2 * C * RK > 2 * kMat) ? 2 * C * RK : 2 * kMat;
     static constexpr int kD = kR;                        // 4 x [16][LDD] fp32
     static constexpr int kG = kD + 4 * 16 * LDD * 4;     // gates
     static constexpr int kN = kG + (4 * C + 4) * 4;      // 1/|k_r|, 1/|q_r| (normalised rows)
@@ -324,10 +313,14 @@ struct PrepSmem {
 
 // The products of one prep wave: the lower tiles of row tiles R0 and R1 of
 // K K^T (KK) or Q K^T, kept in registers across the barrier that frees the K/Q
-// rows.  K K^T tiles are already A = beta_r e^{gam_r - gam_s} (k_r . k_s) for
-// s < r (the diagonal tiles are also written, transposed and fp32, to sD for the
-// forward substitution); Q K^T tiles are P = e^{gam_r - gam_s} (q_r . k_s) for
-// s <= r.  Tile (i, tc) is acc[i ? R0 + 1 + tc : tc].
+// rows.  Each tile is formed transposed (K rows as the MFMA's A operand), so that
+// lane (g, i) holds entries (16 tr + i, 16 tc + 4g + j), j = 0..3: four
+// consecutive columns of one row.  K K^T tiles are already
+// A = beta_r e^{gam_r - gam_s} (k_r . k_s) for s < r; Q K^T tiles are
+// P = e^{gam_r - gam_s} (q_r . k_s) for s <= r.  A diagonal tile of K K^T is
+// symmetric before the scaling, so it also gives the lane the diagonal block's
+// entries (16 tr + 4g + j, 16 tr + i): those go, as the transposed fp32 block
+// the forward substitution reads, to sD.  Tile (i, tc) is acc[i ? R0 + 1 + tc : tc].
 template <int R0, int R1>
 struct PrepTiles {
     static constexpr int N = R0 + 1 + R1 + 1;
@@ -350,81 +343,93 @@ __device__ __forceinline__ void prep_products(PrepTiles<R0, R1> &pt, const unsig
         Frag<BF16> fa[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) fa[ks] = row_frag<BF16>(sA_rows, L::RK, 16 * tr + cl, 32 * ks, gq);
+        const int row = 16 * tr + cl;
+        const float g_row = sG[row];
 #pragma unroll
         for (int tc = 0; tc <= (i ? R1 : R0); ++tc) {
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                acc = mma(fa[ks], row_frag<BF16>(sK, L::RK, 16 * tc + cl, 32 * ks, gq), acc);
-            const int col = 16 * tc + cl;
+                acc = mma(row_frag<BF16>(sK, L::RK, 16 * tc + cl, 32 * ks, gq), fa[ks], acc);
+            const int col0 = 16 * tc + 4 * gq;
             if (sN) {  // normalised rows: (x_r / |x_r|) . (k_s / |k_s|)
-                const float rc = sN[col];
+                const float rr = sN[(KK ? 0 : C) + row];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] *= sN[(KK ? 0 : C) + 16 * tr + 4 * gq + j] * rc;
+                for (int j = 0; j < 4; ++j) acc[j] *= rr * sN[col0 + j];
+            }
+            if (KK && tc == tr) {
+                // sD[tr][m][r] = A[16 tr + r][16 tr + m]: entry (col0 + j, row) of the
+                // symmetric tile, scaled as row col0 + j of A
+                float d[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r2 = col0 + j;
+                    const float e2 = __expf(sG[r2] - g_row);
+                    d[j] = (row < r2) ? sG[C + r2] * e2 * acc[j] : 0.f;
+                }
+                *reinterpret_cast<float4 *>(sD + (tr * 16 + cl) * L::LDD + 4 * gq) =
+                    make_float4(d[0], d[1], d[2], d[3]);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int row = 16 * tr + 4 * gq + j;
-                const float e = __expf(sG[row] - sG[col]);
+                const int col = col0 + j;
+                const float e = __expf(g_row - sG[col]);
                 acc[j] = KK ? ((col < row) ? sG[C + row] * e * acc[j] : 0.f)
                             : ((col <= row) ? e * acc[j] : 0.f);
             }
-            if (KK && tc == tr)  // sD[tr][m][r] = A[16 tr + r][16 tr + m]
-                *reinterpret_cast<float4 *>(sD + (tr * 16 + cl) * L::LDD + 4 * gq) =
-                    make_float4(acc[0], acc[1], acc[2], acc[3]);
             pt.acc[i ? R0 + 1 + tc : tc] = acc;
         }
     }
 }
 
-// Writes a wave's tiles into a C x C matrix of E (row stride LDT elements).
+// Writes a wave's A tiles into a C x C matrix of E (row stride ld elements): four
+// consecutive columns of one row per lane and tile.
 template <bool BF16, int R0, int R1>
 __device__ __forceinline__ void store_tiles(const PrepTiles<R0, R1> &pt, typename Elem<BF16>::T *m,
                                             int ld, int lane)
 {
-    using E = typename Elem<BF16>::T;
     const int gq = lane >> 4, cl = lane & 15;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int tr = i ? R1 : R0;
 #pragma unroll
-        for (int tc = 0; tc <= (i ? R1 : R0); ++tc)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                m[(16 * tr + 4 * gq + j) * ld + 16 * tc + cl] = from_f<E>(pt.acc[i ? R0 + 1 + tc : tc][j]);
+        for (int tc = 0; tc <= (i ? R1 : R0); ++tc) {
+            const floatx4 &a = pt.acc[i ? R0 + 1 + tc : tc];
+            typename Elem<BF16>::T *dst = m + (16 * tr + cl) * ld + 16 * tc + 4 * gq;
+            if constexpr (BF16)
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2(a[0], a[1]), pack2(a[2], a[3]));
+            else
+                *reinterpret_cast<float4 *>(dst) = make_float4(a[0], a[1], a[2], a[3]);
+        }
     }
 }
 
-// P staging: the wave owns every stored block of its row tiles, so it writes its
-// tiles (and the zero upper tile inside a stored block) into the block image and
-// copies those blocks to the workspace without waiting for other waves.
+// P straight to the workspace: the fragment unit of block (row tile tt, k half h)
+// that lane (g, i) owns holds row 16 tt + i, columns 32 h + 4g + j and
+// 32 h + 16 + 4g + j, i.e. tiles (tt, 2h) and (tt, 2h + 1) of this lane (zero
+// above the diagonal).  The wave owns every block of its two row tiles.
 template <bool BF16, int R0, int R1>
-__device__ __forceinline__ void emit_p(const PrepTiles<R0, R1> &pt, unsigned char *pst,
-                                       unsigned char *wp, int lane)
+__device__ __forceinline__ void emit_p(const PrepTiles<R0, R1> &pt, unsigned char *wp, int lane)
 {
-    using E = typename Elem<BF16>::T;
-    const int gq = lane >> 4, cl = lane & 15;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int tr = i ? R1 : R0;
-#pragma unroll
-        for (int tc = 0; tc <= (i ? R1 : R0) + ((i ? R1 : R0) % 2 == 0 ? 1 : 0); ++tc)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * tr + 4 * gq + j, col = 16 * tc + cl;
-                const float v = tc <= tr ? pt.acc[i ? R0 + 1 + tc : tc][j] : 0.f;
-                *reinterpret_cast<E *>(pst + tri_offset<BF16>(row, col)) = from_f<E>(v);
-            }
-    }
     constexpr int FB = kFragBytes<BF16>;
-    // blocks of row tile tt: tt < 2 -> block tt; tt >= 2 -> blocks 2 tt - 2, 2 tt - 1
+    const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    unsigned char *unit = wp + FB * blk_unit(lane & 15, lane >> 4);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int tr = i ? R1 : R0;
-        const int b0 = tr < 2 ? tr : 2 * tr - 2, nb = tr < 2 ? 1 : 2;
-        for (int u = lane; u < nb * 64 * FB / 16; u += 64) {
-            const int off = b0 * kBlkBytes<BF16> + 16 * u;
-            *reinterpret_cast<uint4 *>(wp + off) = *reinterpret_cast<const uint4 *>(pst + off);
+        const int tt = i ? R1 : R0;
+        const int base = i ? R0 + 1 : 0;
+#pragma unroll
+        for (int h = 0; 32 * h <= 16 * tt + 15; ++h) {
+            const int b = tt < 2 ? tt : 2 * tt - 2 + h;
+            const floatx4 &c0 = pt.acc[base + 2 * h];
+            const int i1 = base + 2 * h + 1 < PrepTiles<R0, R1>::N ? base + 2 * h + 1 : 0;
+            const floatx4 &c1 = (2 * h + 1 <= tt) ? pt.acc[i1] : zero4;
+            const Frag<BF16> f = acc_frag<BF16>(c0, c1);
+            uint4 w[FB / 16];
+            __builtin_memcpy(w, &f, FB);
+#pragma unroll
+            for (int x = 0; x < FB / 16; ++x)
+                reinterpret_cast<uint4 *>(unit + b * kBlkBytes<BF16>)[x] = w[x];
         }
     }
 }
@@ -432,11 +437,12 @@ __device__ __forceinline__ void emit_p(const PrepTiles<R0, R1> &pt, unsigned cha
 // One workgroup per (seq, head, chunk): the state-independent part of the chunk.
 //   0. K and Q rows -> LDS by LDS-DMA (all waves); gate sums (wave 0)
 //   1. K K^T (waves 0, 1) and Q K^T (waves 2, 3) on MFMA, row tiles {0, 3} and
-//      {1, 2} per wave so that each does five tiles; results stay in registers
+//      {1, 2} per wave so that each does five tiles; results stay in registers,
+//      and waves 2, 3 write P to the workspace from them
 //   2. the K/Q space is reused: waves 0, 1 store A; wave 0 then inverts the
 //      diagonal 16x16 blocks of I + A by forward substitution (lane = (block,
 //      column), right-looking over a transposed fp32 copy of the block); wave 1
-//      zeroes the blocks of T read before they are formed; waves 2, 3 emit P
+//      zeroes the blocks of T read before they are formed
 //   3. blocks (1,0), (3,2): T_ij = -T_ii (A_ij T_jj)                (waves 0, 1)
 //   4. blocks (2,0), (2,1), (3,0), (3,1): with the 32-row halves,
 //      T_hi,lo = -T_hi (A_hi,lo T_lo)                              (waves 0, 1)
@@ -557,17 +563,16 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
             store_tiles<BF16, 1, 2>(pt, sAe, LDT, lane);
         }
     } else {
-        unsigned char *pst = smem + L::kPst;
         if (wave == 2) {
             PrepTiles<0, 3> pt;
             prep_products<D, BF16, false, 0, 3>(pt, smem, sG, sD, sN, lane);
+            emit_p<BF16, 0, 3>(pt, dst + W::kP, lane);
             lds_barrier();
-            emit_p<BF16, 0, 3>(pt, pst, dst + W::kP, lane);
         } else {
             PrepTiles<1, 2> pt;
             prep_products<D, BF16, false, 1, 2>(pt, smem, sG, sD, sN, lane);
+            emit_p<BF16, 1, 2>(pt, dst + W::kP, lane);
             lds_barrier();
-            emit_p<BF16, 1, 2>(pt, pst, dst + W::kP, lane);
             // beta, e^gam, e^{last-gam}, e^last; with normalised rows the second and
             // third carry 1/|k| and a fifth row holds e^gam / |q|
             float *wG = reinterpret_cast<float *>(dst + W::kGates);
@@ -654,21 +659,17 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     }
     lds_barrier();
 
-    // 5. T as six fragment blocks (zeros above the diagonal)
+    // 5. T as six fragment blocks.  Every entry of sT above the diagonal that a
+    //    block covers is zero: the diagonal blocks' upper triangles come out of
+    //    the substitution as zeros and blocks (0,1), (2,3) were cleared.
     constexpr int FB = kFragBytes<BF16>;
     for (int u = tid; u < 6 * 64; u += kPrepThreads) {
         const int b = u >> 6, p = u & 63;
         const int tt = b < 2 ? b : 2 + ((b - 2) >> 1), hh = b < 2 ? 0 : (b - 2) & 1;
         const int i = p >> 2, gg = (p & 3) ^ (i >> 2);
-        const int r = 16 * tt + i;
-        E vt[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = 32 * hh + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
-            vt[e] = c <= r ? sT[r * LDT + c] : from_f<E>(0.f);
-        }
+        const Frag<BF16> f = lds_frag<BF16>(sT, LDT, 16 * tt + i, 32 * hh, gg);
         uint4 w[FB / 16];
-        __builtin_memcpy(w, vt, FB);
+        __builtin_memcpy(w, &f, FB);
         uint4 *ub = reinterpret_cast<uint4 *>(dst + W::kT + b * kBlkBytes<BF16> + FB * p);
 #pragma unroll
         for (int x = 0; x < FB / 16; ++x) ub[x] = w[x];
