@@ -813,55 +813,83 @@ struct ScanPtrs {
     int64_t ws_stride;                // workspace bytes per chunk
 };
 
+// Producer PART's per-lane source offsets inside one chunk's data, for its K, T,
+// V, gates blocks (kt) and its Q, P blocks (qp).  They depend on the chunk only
+// through its number of valid rows, so they are formed once for full chunks and
+// again for a partial last chunk, keeping that arithmetic out of the chunk loop
+// (the producers share SIMDs with the waves on the dependency chain).
+template <int D, bool BF16, int VT, int PART>
+struct ProdOffsets {
+    using F = ScanCfg<D, BF16, VT>;
+    static constexpr int NK = (F::NKT + 1 - PART + kProducers - 1) / kProducers;
+    static constexpr int NQ = (F::NQP - PART + kProducers - 1) / kProducers;
+    uint32_t kt[NK], qp[NQ];
+
+    __device__ __forceinline__ void set_kt(const ScanPtrs &pt, int nv, int lane)
+    {
+        const uint32_t hdb = static_cast<uint32_t>(pt.hd_bytes), kqb = static_cast<uint32_t>(pt.kq_bytes);
+#pragma unroll
+        for (int m = 0; m < NK; ++m) {
+            const int i = PART + kProducers * m;
+            if (i < F::NBK)
+                kt[m] = dma_src_offset(i, lane, D * F::ES, F::RK, kqb, nv);
+            else if (i < F::NBK + F::NBT)
+                kt[m] = 1024u * (i - F::NBK) + 16u * lane;
+            else if (i < F::NBK + F::NBT + F::NBV)
+                kt[m] = dma_src_offset(i - F::NBK - F::NBT, lane, F::RW * F::ES, F::RV, hdb, nv);
+            else
+                kt[m] = 1024u * (i - F::NBK - F::NBT - F::NBV) + 16u * lane;
+        }
+    }
+    __device__ __forceinline__ void set_qp(const ScanPtrs &pt, int nv, int lane)
+    {
+        const uint32_t kqb = static_cast<uint32_t>(pt.kq_bytes);
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+            const int i = PART + kProducers * m;
+            qp[m] = i < F::NBK ? dma_src_offset(i, lane, D * F::ES, F::RK, kqb, nv)
+                               : 1024u * (i - F::NBK) + 16u * lane;
+        }
+    }
+};
+
 // Producer PART's blocks of chunk n's K, T, V and gates.
 template <int D, bool BF16, int VT, int PART>
-__device__ __forceinline__ void issue_kt(const ScanPtrs &pt, unsigned char *slot, int n, int nv,
-                                        int ng, int lane)
+__device__ __forceinline__ void issue_kt(const ScanPtrs &pt, unsigned char *slot, int n, int ng,
+                                        const ProdOffsets<D, BF16, VT, PART> &po)
 {
     using F = ScanCfg<D, BF16, VT>;
     using W = WsLayout<BF16>;
     const int64_t tb = int64_t(n) * C * pt.hd_bytes, tbk = int64_t(n) * C * pt.kq_bytes;
-    const uint32_t hdb = static_cast<uint32_t>(pt.hd_bytes), kqb = static_cast<uint32_t>(pt.kq_bytes);
     const unsigned char *wsc = pt.ws + int64_t(n) * pt.ws_stride;
 #pragma unroll
     for (int i = PART; i < F::NKT + 1; i += kProducers) {
         if (i == F::NKT && !ng) break;
-        uint32_t off;
         const unsigned char *base;
-        if (i < F::NBK) {
+        if (i < F::NBK)
             base = pt.k + tbk;
-            off = dma_src_offset(i, lane, D * F::ES, F::RK, kqb, nv);
-        } else if (i < F::NBK + F::NBT) {
+        else if (i < F::NBK + F::NBT)
             base = wsc + W::kT;
-            off = 1024u * (i - F::NBK) + 16u * lane;
-        } else if (i < F::NBK + F::NBT + F::NBV) {
+        else if (i < F::NBK + F::NBT + F::NBV)
             base = pt.v + tb;
-            off = dma_src_offset(i - F::NBK - F::NBT, lane, F::RW * F::ES, F::RV, hdb, nv);
-        } else {
+        else
             base = wsc + W::kGates;
-            off = 1024u * (i - F::NBK - F::NBT - F::NBV) + 16u * lane;
-        }
-        dma16(base, off, slot + 1024 * i);
+        dma16(base, po.kt[(i - PART) / kProducers], slot + 1024 * i);
     }
 }
 
 // Producer PART's blocks of chunk n's Q and P.
 template <int D, bool BF16, int VT, int PART>
-__device__ __forceinline__ void issue_qp(const ScanPtrs &pt, unsigned char *slot, int n, int nv,
-                                        int lane)
+__device__ __forceinline__ void issue_qp(const ScanPtrs &pt, unsigned char *slot, int n,
+                                        const ProdOffsets<D, BF16, VT, PART> &po)
 {
     using F = ScanCfg<D, BF16, VT>;
     using W = WsLayout<BF16>;
     const int64_t tbk = int64_t(n) * C * pt.kq_bytes;
-    const uint32_t kqb = static_cast<uint32_t>(pt.kq_bytes);
     const unsigned char *wsc = pt.ws + int64_t(n) * pt.ws_stride;
 #pragma unroll
-    for (int i = PART; i < F::NQP; i += kProducers) {
-        if (i < F::NBK)
-            dma16(pt.q + tbk, dma_src_offset(i, lane, D * F::ES, F::RK, kqb, nv), slot + 1024 * i);
-        else
-            dma16(wsc + W::kP, 1024u * (i - F::NBK) + 16u * lane, slot + 1024 * i);
-    }
+    for (int i = PART; i < F::NQP; i += kProducers)
+        dma16(i < F::NBK ? pt.q + tbk : wsc + W::kP, po.qp[(i - PART) / kProducers], slot + 1024 * i);
 }
 
 
@@ -1190,14 +1218,21 @@ __device__ __forceinline__ void producer_loop(const ScanPtrs &pt, unsigned char 
     using F = ScanCfg<D, BF16, VT>;
     constexpr int SK = F::SK, SQ = F::SQ;
     auto nv_of = [&](int m) { return static_cast<int>(min<int64_t>(C, n_tokens - int64_t(m) * C)); };
+    // offsets for full chunks; a partial chunk is the last one of each kind issued
+    ProdOffsets<D, BF16, VT, PART> po;
+    po.set_kt(pt, C, lane);
+    po.set_qp(pt, C, lane);
     auto kt = [&](int m) {
-        if (m < nc)
-            issue_kt<D, BF16, VT, PART>(pt, smem + F::kRingKT + (m % SK) * F::kSlotKT, m, nv_of(m),
-                                        NG, lane);
+        if (m < nc) {
+            if (nv_of(m) < C) po.set_kt(pt, nv_of(m), lane);
+            issue_kt<D, BF16, VT, PART>(pt, smem + F::kRingKT + (m % SK) * F::kSlotKT, m, NG, po);
+        }
     };
     auto qp = [&](int m) {
-        if (m < nc)
-            issue_qp<D, BF16, VT, PART>(pt, smem + F::kRingQP + (m % SQ) * F::kSlotQP, m, nv_of(m), lane);
+        if (m < nc) {
+            if (nv_of(m) < C) po.set_qp(pt, nv_of(m), lane);
+            issue_qp<D, BF16, VT, PART>(pt, smem + F::kRingQP + (m % SQ) * F::kSlotQP, m, po);
+        }
     };
     if constexpr (F::PIPE) {
         // prologue: the issues of times t < 0, oldest first
