@@ -225,7 +225,7 @@ __device__ __forceinline__ Frag<BF16> frag_blk(const unsigned char *blk, int lan
 
 // ---- workspace layout, per (seq, head, chunk) ----------------------------------
 //   T     six fragment blocks (elements like q/k/v: fp32 or bf16)
-//   P     six fragment blocks
+//   P     six fragment blocks, holding P / sqrt(d)
 //   gates [4][C] fp32: beta_r, e^{gam_r}, e^{gam_last - gam_r}, then e^{gam_last}
 //                      repeated C times
 // Rows past the end of a partial last chunk carry beta = e^gam = 0, so they add
@@ -311,13 +311,19 @@ struct PrepSmem {
     static_assert(C * RK % 1024 == 0 && kMat % 16 == 0 && kR % 16 == 0, "layout");
 };
 
+// The output's factor 1/sqrt(d), applied where P is formed (and by the scan's
+// output wave to e^gam), so that the output needs no scaling of its own.
+template <int D>
+constexpr float kOutScale = D == 32 ? 0.17677669529663687f : D == 64 ? 0.125f
+                          : D == 96 ? 0.10206207261596575f : 0.08838834764831845f;
+
 // The products of one prep wave: the lower tiles of row tiles R0 and R1 of
 // K K^T (KK) or Q K^T, kept in registers across the barrier that frees the K/Q
 // rows.  Each tile is formed transposed (K rows as the MFMA's A operand), so that
 // lane (g, i) holds entries (16 tr + i, 16 tc + 4g + j), j = 0..3: four
 // consecutive columns of one row.  K K^T tiles are already
 // A = beta_r e^{gam_r - gam_s} (k_r . k_s) for s < r; Q K^T tiles are
-// P = e^{gam_r - gam_s} (q_r . k_s) for s <= r.  A diagonal tile of K K^T is
+// P = e^{gam_r - gam_s} (q_r . k_s) / sqrt(d) for s <= r.  A diagonal tile of K K^T is
 // symmetric before the scaling, so it also gives the lane the diagonal block's
 // entries (16 tr + 4g + j, 16 tr + i): those go, as the transposed fp32 block
 // the forward substitution reads, to sD.  Tile (i, tc) is acc[i ? R0 + 1 + tc : tc].
@@ -375,7 +381,7 @@ __device__ __forceinline__ void prep_products(PrepTiles<R0, R1> &pt, const unsig
                 const int col = col0 + j;
                 const float e = __expf(g_row - sG[col]);
                 acc[j] = KK ? ((col < row) ? sG[C + row] * e * acc[j] : 0.f)
-                            : ((col <= row) ? e * acc[j] : 0.f);
+                            : ((col <= row) ? kOutScale<D> * e * acc[j] : 0.f);
             }
             pt.acc[i ? R0 + 1 + tc : tc] = acc;
         }
@@ -685,8 +691,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
 //   U_vt  holds its rows of M^T in fp32 and applies
 //         M^T <- e^{gam_last} M^T + K^T (scaled Delta), publishing the new M^T
 //         as B-operand fragment blocks;
-//   O_vt  e^gam Q M_n^T, then + P Delta, staged through LDS and stored as
-//         O / sqrt(d) with 16-byte stores;
+//   O_vt  e^gam Q M_n^T / sqrt(d), then + (P / sqrt(d)) Delta: the output,
+//         stored from registers;
 // and four producer waves move the chunk data global -> LDS with
 // global_load_lds (16 bytes per lane; a compute unit ingests faster the more
 // waves keep such loads in flight).
@@ -1119,7 +1125,7 @@ template <int D, bool BF16>
 struct OOps {
     Frag<BF16> aq[4][D / 32];
     Frag<BF16> ap[6];
-    float eg[4];                // e^gam of token 16 tt + lane % 16
+    float eg[4];                // e^gam / sqrt(d) of token 16 tt + lane % 16
 };
 
 template <int D, bool BF16, int VT>
@@ -1139,10 +1145,11 @@ __device__ __forceinline__ void o_load(OOps<D, BF16> &o, const unsigned char *kt
     for (int b = 0; b < 6; ++b) o.ap[b] = frag_blk<BF16>(qp + F::kP + b * F::BLK, lane);
     const float *sG = reinterpret_cast<const float *>(kt + F::kG);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) o.eg[tt] = sG[eg_row * C + 16 * tt + cl];
+    for (int tt = 0; tt < 4; ++tt) o.eg[tt] = kOutScale<D> * sG[eg_row * C + 16 * tt + cl];
 }
 
-// O_vt works on the transposed output tile, O^T = M Q^T diag(e^gam) + Delta^T P^T:
+// O_vt works on the transposed output tile, O^T = M Q^T diag(e^gam) + Delta^T P^T
+// (1/sqrt(d) already in e^gam and P):
 // an A operand and a B operand of the same matrix have the same register layout, so
 // the products are those of O with their operands swapped, and the accumulator of
 // row tile tt holds in lane (g, i) the values 4g .. 4g+3 of token 16 tt + i, which
@@ -1176,14 +1183,14 @@ __device__ __forceinline__ void o_xq(const OOps<D, BF16> &o, const unsigned char
     for (int tt = 0; tt < 4; ++tt) acc[tt] = xq[tt] * o.eg[tt];
 }
 
-// O_vt after barrier B: acc += (P Delta)^T, then out = acc / sqrt(d) for the valid
+// O_vt after barrier B: acc += (P Delta)^T, which is the output of the valid
 // tokens, stored from registers (four consecutive values of one token per lane and
-// row tile).  obase points at out[(s, first token of the chunk, h, first value row
-// of the tile)].
+// row tile; no per-token test for a full chunk).  obase points at out[(s, first
+// token of the chunk, h, first value row of the tile)].
 template <int D, bool BF16, int VT>
 __device__ __forceinline__ void o_finish(const OOps<D, BF16> &o, const unsigned char *smem, int vt,
                                          int lane, floatx4 (&acc)[4], typename Elem<BF16>::T *obase,
-                                         int64_t hd, int nv, float scale)
+                                         int64_t hd, int nv)
 {
     using F = ScanCfg<D, BF16, VT>;
     const int gq = lane >> 4, cl = lane & 15;
@@ -1194,18 +1201,22 @@ __device__ __forceinline__ void o_finish(const OOps<D, BF16> &o, const unsigned 
     acc[1] = mma(d0, o.ap[1], acc[1]);
     acc[2] = mma(d1, o.ap[3], mma(d0, o.ap[2], acc[2]));
     acc[3] = mma(d1, o.ap[5], mma(d0, o.ap[4], acc[3]));
+    auto store = [&](int tt) {
+        typename Elem<BF16>::T *dst = obase + (16 * tt + cl) * hd + 4 * gq;
+        if constexpr (BF16)
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2(acc[tt][0], acc[tt][1]),
+                                                         pack2(acc[tt][2], acc[tt][3]));
+        else
+            *reinterpret_cast<float4 *>(dst) = make_float4(acc[tt][0], acc[tt][1], acc[tt][2],
+                                                           acc[tt][3]);
+    };
+    if (nv == C) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const int t = 16 * tt + cl;
-        if (t < nv) {
-            typename Elem<BF16>::T *dst = obase + t * hd + 4 * gq;
-            if constexpr (BF16)
-                *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2(scale * acc[tt][0], scale * acc[tt][1]),
-                                                             pack2(scale * acc[tt][2], scale * acc[tt][3]));
-            else
-                *reinterpret_cast<float4 *>(dst) = make_float4(scale * acc[tt][0], scale * acc[tt][1],
-                                                               scale * acc[tt][2], scale * acc[tt][3]);
-        }
+        for (int tt = 0; tt < 4; ++tt) store(tt);
+    } else {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+            if (16 * tt + cl < nv) store(tt);
     }
 }
 
@@ -1317,7 +1328,7 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *state_in, void *__restrict__ out, float *state_out,
     const unsigned char *__restrict__ ws, int64_t n_tokens, int64_t n_heads, int64_t n_k_heads,
-    int64_t n_sh, int n_chunks, float scale)
+    int64_t n_sh, int n_chunks)
 {
     using F = ScanCfg<D, BF16, VT>;
     using E = typename Elem<BF16>::T;
@@ -1427,7 +1438,7 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
             o_xq<D, BF16, VT>(ops, qp_slot(n), smem, vt, lane, acc);
             lds_barrier();  // B_n
             o_finish<D, BF16, VT>(ops, smem, vt, lane, acc, obase + int64_t(n) * C * hd, hd,
-                                  nv_of(n), scale);
+                                  nv_of(n));
         }
     }
 }
@@ -1481,10 +1492,9 @@ hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, 
     if (e != hipSuccess) return e;
     const int64_t n_sh = p.n_seqs * p.n_heads;
     const int64_t blocks = scan_blocks<D, BF16, VT>(n_sh);
-    const float scale = 1.0f / sqrtf(static_cast<float>(D));
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(64 * F::kWaves), F::kBytes,
                        stream, p.q, p.k, p.v, p.state_in, p.out, p.state_out, ws, p.n_tokens,
-                       p.n_heads, p.n_k_heads, n_sh, n_chunks, scale);
+                       p.n_heads, p.n_k_heads, n_sh, n_chunks);
     return hipGetLastError();
 }
 

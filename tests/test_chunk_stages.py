@@ -4,7 +4,8 @@ The chunked algorithm first computes, for every (sequence, head, chunk), the
 state-independent matrices T = (I + A)^{-1} and the decay-masked P, plus the
 per-token gate factors, into the caller's workspace.  This test decodes that
 workspace (its layout is internal to the library and mirrored here: per chunk
-T and then P as six "fragment blocks" each, then four fp32 rows of 64: beta,
+T and then P / sqrt(head_dim) (the output's factor, applied where P is formed)
+as six "fragment blocks" each, then four fp32 rows of 64: beta,
 e^gam, e^(gam_last - gam) and e^gam_last repeated; when the op normalises q and
 k the gates take 2 KiB with a fifth row) and compares it with the
 oracle's stage values, so that a parity failure can be attributed to the first
@@ -103,6 +104,6 @@ def test_workspace_matches_oracle_stages(dtype, T):
             np.testing.assert_allclose(G[u, 0, 3], np.exp(r["gam"][-1]), rtol=1e-4, err_msg=what)
             assert np.all(G[u, nv:, :3] == 0), what
             eT = np.max(np.abs(Tm[u, :nv, :nv] - r["T"])) / np.max(np.abs(r["T"]))
-            eP = np.max(np.abs(Pm[u, :nv, :nv] - r["P"])) / np.max(np.abs(r["P"]))
+            eP = np.max(np.abs(Pm[u, :nv, :nv] * np.sqrt(D) - r["P"])) / np.max(np.abs(r["P"]))
             assert eT < tol and eP < tol, (what, eT, eP)
             assert np.all(np.triu(Tm[u], 1) == 0) and np.all(np.triu(Pm[u], 1) == 0), what
