@@ -1290,17 +1290,6 @@ __device__ __forceinline__ void producer_loop(const ScanPtrs &pt, unsigned char 
 
 enum { kRoleX = 0, kRoleU = 1, kRoleO = 2, kRoleProd = 3 };
 
-// Right after a barrier, the wave on the dependency chain reads a few published
-// fragments (M^T after A, scaled Delta after B) that it needs at once; the other
-// waves' bulk operand reads wait a little so that the LDS serves those first.
-#ifndef GDN_BULK_PAUSE
-#define GDN_BULK_PAUSE 2
-#endif
-__device__ __forceinline__ void bulk_pause()
-{
-    if constexpr (GDN_BULK_PAUSE > 0) __builtin_amdgcn_s_sleep(GDN_BULK_PAUSE);
-}
-
 // Wave order: X_0.., U_0.., then O and the producers arranged so that, with
 // waves dealt round-robin to the four SIMDs, no O wave shares a SIMD with an X
 // wave (both run their products between barriers A and B).
@@ -1387,7 +1376,6 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
         if constexpr (PIPE) lds_barrier();  // B_{-1}
         for (int n = 0; n < nc; ++n) {
             if constexpr (!PIPE) lds_barrier();  // L_n
-            bulk_pause();
             x_load<D, BF16, VT>(ops, kt_slot(n), vt, lane);
             lds_barrier();  // A_n
             x_step<D, BF16, VT>(ops, kt_slot(n), smem, vt, lane);
@@ -1413,7 +1401,6 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
         for (int n = 0; n < nc; ++n) {
             if constexpr (!PIPE) lds_barrier();  // L_n
             lds_barrier();  // A_n
-            bulk_pause();
             u_load<D, BF16, VT>(akt, eC, kt_slot(n), lane);
 #pragma unroll
             for (int t = 0; t < D / 16; ++t) Mt[t] *= eC;
@@ -1433,7 +1420,6 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
         for (int n = 0; n < nc; ++n) {
             if constexpr (!PIPE) lds_barrier();  // L_n
             lds_barrier();  // A_n
-            bulk_pause();
             o_load<D, BF16, VT>(ops, kt_slot(n), qp_slot(n), eg_row, lane);
             o_xq<D, BF16, VT>(ops, qp_slot(n), smem, vt, lane, acc);
             lds_barrier();  // B_n
