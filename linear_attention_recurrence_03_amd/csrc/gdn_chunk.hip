@@ -745,8 +745,8 @@ struct ScanCfg {
     static constexpr int kQ = 0;
     static constexpr int kP = kQ + C * RK;
     static constexpr int kSlotQP = kP + 6 * BLK;
-    // published values: M^T blocks, Delta and scaled Delta (accumulator-pair
-    // fragments), output staging
+    // published values: M^T blocks, then Delta and scaled Delta as accumulator-pair
+    // fragments
     static constexpr int kPubBytes = VT * KS * BLK + 4 * VT * 64 * FB;
     static constexpr int kLds = 160 * 1024;
     static constexpr bool fits(int sk, int sq) { return sk * kSlotKT + sq * kSlotQP + kPubBytes <= kLds; }
@@ -1101,8 +1101,10 @@ __device__ __forceinline__ void u_load(Frag<BF16> (&akt)[D / 16][2], float &eC,
     eC = reinterpret_cast<const float *>(kt + F::kG)[3 * C];
 }
 
-// U_vt, one chunk (after barrier B): M^T <- M^T + K^T Dscaled (M^T was already
-// multiplied by e^{gam_last} while waiting at barrier B), then publishes the new M^T.
+// U_vt, one chunk (after barrier B): M^T <- M^T + K^T Dscaled, then publishes the
+// new M^T.  The multiplication of M^T by e^{gam_last} is written before barrier B;
+// the compiler interleaves it with these products, which measured faster than
+// keeping it in the wait before the barrier.
 template <int D, bool BF16, int VT>
 __device__ __forceinline__ void u_step(floatx4 (&Mt)[D / 16], const Frag<BF16> (&akt)[D / 16][2],
                                        unsigned char *smem, int vt, int lane)
