@@ -50,12 +50,45 @@ def algorithmic_flops_chunked(S, T, H, D, C=CHUNK):
     return S * T * H * (5 * C * D + 6 * D * D + C * C / 3.0)
 
 
-def kernel_source_hash():
-    h = hashlib.sha256()
+def _code_tokens(text):
+    """C/C++/HIP source with comments removed and whitespace runs collapsed, so that
+    the fingerprint below changes with the code only."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                        # string or character literal
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def kernel_source_hash(read=None):
+    """Fingerprint of the kernel sources (code only: comments and layout do not
+    count), which the committed counter summaries record."""
     csrc = os.path.join(ROOT, "linear_attention_recurrence_03_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+    if read is None:
+        def read(name):
+            with open(os.path.join(csrc, name), "rb") as f:
+                return f.read()
+        names = sorted(os.listdir(csrc))
+    else:
+        names = sorted(read(None))
+    h = hashlib.sha256()
+    for name in names:
+        h.update(name.encode() + _code_tokens(read(name).decode("utf-8")).encode())
     return h.hexdigest()[:16]
 
 
