@@ -183,27 +183,31 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
         //    issued before the first product
         {
             const E *kr = kbase + (t0 + (tok < last ? tok : last)) * D + qtr * QW;
-            float kx[QW];
+            constexpr int KU = BF16 ? 1 : 2;          // 16-byte units per 8 elements
+            uint4 kraw[QW / 8][KU];
 #pragma unroll
-            for (int c = 0; c < QW; c += 8) {
-                float x8[8];
-                load8<BF16>(kr + c, x8);
+            for (int c = 0; c < QW / 8; ++c)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kx[c + e] = x8[e];
-            }
+                for (int h = 0; h < KU; ++h) kraw[c][h] = reinterpret_cast<const uint4 *>(kr + 8 * c)[h];
             float sc[kAttnRows];
 #pragma unroll
-            for (int r = 0; r < kAttnRows; ++r) {
-                float acc_r = 0.f;
+            for (int r = 0; r < kAttnRows; ++r) sc[r] = 0.f;
 #pragma unroll
-                for (int c = 0; c < QW; c += 4) {
-                    const float4 qv = *reinterpret_cast<const float4 *>(&sQ[r][qtr * QW + c]);
-                    acc_r = fmaf(qv.x, kx[c], fmaf(qv.y, kx[c + 1], fmaf(qv.z, kx[c + 2],
-                                 fmaf(qv.w, kx[c + 3], acc_r))));
+            for (int c = 0; c < QW / 8; ++c) {
+                float x8[8];
+                load8<BF16>(reinterpret_cast<const E *>(&kraw[c][0]), x8);
+#pragma unroll
+                for (int r = 0; r < kAttnRows; ++r) {
+                    const float4 q0 = *reinterpret_cast<const float4 *>(&sQ[r][qtr * QW + 8 * c]);
+                    const float4 q1 = *reinterpret_cast<const float4 *>(&sQ[r][qtr * QW + 8 * c + 4]);
+                    sc[r] = fmaf(q0.x, x8[0], fmaf(q0.y, x8[1], fmaf(q0.z, x8[2], fmaf(q0.w, x8[3], sc[r]))));
+                    sc[r] = fmaf(q1.x, x8[4], fmaf(q1.y, x8[5], fmaf(q1.z, x8[6], fmaf(q1.w, x8[7], sc[r]))));
                 }
-                acc_r += __shfl_xor(acc_r, 1, 64);
-                acc_r += __shfl_xor(acc_r, 2, 64);
-                sc[r] = acc_r;
+            }
+#pragma unroll
+            for (int r = 0; r < kAttnRows; ++r) {
+                sc[r] += __shfl_xor(sc[r], 1, 64);
+                sc[r] += __shfl_xor(sc[r], 2, 64);
             }
             if (qtr == 0) {
                 const int64_t t = t0 + tok;
