@@ -92,8 +92,8 @@ def kernel_source_hash(read=None):
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload_key):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+def load_traffic_record(workload_key):
+    """The committed counter record of a workload (profiles/traffic.json), if it was
     taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -103,7 +103,14 @@ def load_traffic(workload_key):
         return None
     if not rec or rec.get("source_hash") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def load_traffic(workload_key):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources (else None)."""
+    rec = load_traffic_record(workload_key)
+    return rec.get("bytes_per_launch") if rec else None
 
 
 def run_env(torch):
@@ -304,48 +311,78 @@ def bench_attn(gdn, torch, n_calls=40, reps=7):
 def profile_pass(gdn, torch, wl, launches=10):
     """Short run for hardware-counter passes: an elementwise multiply by one over
     512 MiB (known bytes: reads 512 MiB, writes 512 MiB; it calibrates FETCH_SIZE
-    and WRITE_SIZE) and a few launches of the headline workload."""
+    and WRITE_SIZE), a few launches of the headline workload, then of the batched
+    decode (rotating input copies) and of the single-token decode (24 layers, each
+    with its own inputs and state)."""
+    from linear_attention_recurrence_03_amd import inputs
     src = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.mul(src, 1.0, out=dst)          # the calibration kernel: 512 MiB in, 512 MiB out
     torch.cuda.synchronize()
     _, slots = bench_prefill(gdn, torch, wl, steps=launches, warmup=0, nbuf=4)
+    del slots
+    _, slots = bench_prefill(gdn, torch, inputs.WORKLOADS[3], steps=launches, warmup=0, nbuf=3)
+    del slots
+    wl2 = inputs.WORKLOADS[2]
+    for layer in range(24):
+        Slot(gdn, to_dev(inputs.make(wl2, layer=layer), wl2.dtype, torch), torch).run(gdn)
     torch.cuda.synchronize()
     print("profile pass done: copy %d bytes, %d launches" % (src.numel() * 4, launches), flush=True)
 
 
 def summarize_pmc(fetch_dir, write_dir):
     """Turn two rocprofv3 --pmc runs of --profile-pass (FETCH_SIZE, WRITE_SIZE, in
-    KiB per dispatch) into HBM bytes per launch of each libgdn kernel, scaled by
-    what the same counters read for the 512 MiB copy; writes profiles/traffic.json."""
+    KiB per dispatch) into HBM bytes per launch of each libgdn kernel.  Each counter
+    is scaled by what it reads for the 512 MiB elementwise kernel, whose reads and
+    writes are known (512 MiB each); writes profiles/traffic.json."""
     import csv
-    copy_bytes = 2 * 512 * 1024 * 1024   # read + write of the calibration copy
+    copy_bytes = 512 * 1024 * 1024       # read, and written, by the calibration kernel
 
-    def per_kernel(d, counter):
+    def kernel_key(name):
+        return ("copy" if "MulFunctor" in name else
+                "chunk_scan" if "chunk_scan" in name else
+                "chunk_prep" if "chunk_prep" in name else
+                "decode_batched" if "recurrent_kernel<128, 4" in name else
+                "decode_1tok" if "recurrent_kernel<128, 1" in name else None)
+
+    def per_kernel(d, counter, dur):
         vals = {}
         path = os.path.join(d, "run_counter_collection.csv")
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
-            name = r["Kernel_Name"]
-            key = ("copy" if "MulFunctor" in name else
-                   "chunk_scan" if "chunk_scan" in name else
-                   "chunk_prep" if "chunk_prep" in name else
-                   "recurrent" if "recurrent_kernel" in name else None)
+            key = kernel_key(r["Kernel_Name"])
             if key:
                 vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+                dur.setdefault(key, {})[(d, r["Dispatch_Id"])] = (
+                    int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
         return {k: statistics.median(v) for k, v in vals.items()}
 
-    f = per_kernel(fetch_dir, "FETCH_SIZE")
-    w = per_kernel(write_dir, "WRITE_SIZE")
-    scale = copy_bytes / (f["copy"] + w["copy"])
-    kernels = {k: {"fetch_bytes": f.get(k, 0) * scale, "write_bytes": w.get(k, 0) * scale}
+    dur = {}
+    f = per_kernel(fetch_dir, "FETCH_SIZE", dur)
+    w = per_kernel(write_dir, "WRITE_SIZE", dur)
+    fs, ws = copy_bytes / f["copy"], copy_bytes / w["copy"]
+    kernels = {k: {"fetch_bytes": f.get(k, 0) * fs, "write_bytes": w.get(k, 0) * ws}
                for k in ("chunk_prep", "chunk_scan")}
     total = sum(v["fetch_bytes"] + v["write_bytes"] for v in kernels.values())
+    note = ("FETCH_SIZE and WRITE_SIZE per dispatch (medians), each scaled by the factor that "
+            "maps its reading for the 512 MiB elementwise kernel to the kernel's known 512 MiB "
+            "of reads or writes")
+    factors = {"fetch": fs, "write": ws}
     rec = {"prefill_bf16": {"source_hash": kernel_source_hash(), "bytes_per_launch": round(total),
-                            "kernels": kernels, "copy_calibration_factor": scale,
-                            "note": "FETCH_SIZE + WRITE_SIZE per dispatch, scaled by the factor "
-                                    "that maps the 512 MiB copy's counters to its 1 GiB of traffic"}}
+                            "kernels": kernels, "calibration_factors": factors, "note": note}}
+    # decode: one kernel per call; counted bytes over the dispatch's own duration
+    for key, shape in (("decode_batched", (64, 1, 32, 128)), ("decode_1tok", (1, 1, 32, 128))):
+        if key not in f or key not in w:
+            continue
+        nb = f[key] * fs + w[key] * ws
+        t = statistics.median(dur[key].values())
+        rec[key] = {"source_hash": kernel_source_hash(), "bytes_per_launch": round(nb),
+                    "fetch_bytes": round(f[key] * fs), "write_bytes": round(w[key] * ws),
+                    "algorithmic_bytes": algorithmic_bytes(*shape, 4),
+                    "seconds_under_counters": t, "counted_GBs": round(nb / t / 1e9, 1),
+                    "counted_hbm_frac": round(nb / t / 1e9 / HBM_PEAK_GBS, 4),
+                    "calibration_factors": factors, "note": note}
     out = os.path.join(ROOT, "profiles", "traffic.json")
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
@@ -496,6 +533,7 @@ def main():
             "us_per_layer_device": round(med, 3), "us_min": round(lo, 3), "us_max": round(hi, 3),
             "us_per_layer_host": round(host, 3), "bytes_per_call": b2,
             "hbm_frac": round(b2 / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "counters": load_traffic_record("decode_1tok"),
             "workload": "1 seq x 1 token x 32 heads x d128 fp32, 24 sequential layer calls "
                         "replayed from one HIP graph, 1 GiB scrub before each replay"}
         # batched decode
@@ -506,6 +544,7 @@ def main():
             "us_per_call": round(ms3 * 1e3, 3), "bytes_per_call": b3,
             "achieved_GBs": round(b3 / (ms3 * 1e-3) / 1e9, 1),
             "hbm_frac": round(b3 / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "counters": load_traffic_record("decode_batched"),
             "workload": "64 seqs x 1 token x 32 heads x d128 fp32, 3 rotating input copies"}
         torch.cuda.empty_cache()
         # long prefill
