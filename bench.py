@@ -330,11 +330,11 @@ def profile_pass(gdn, torch, wl, launches=10):
     print("profile pass done: copy %d bytes, %d launches" % (src.numel() * 4, launches), flush=True)
 
 
-def summarize_pmc(fetch_dir, write_dir):
+def traffic_records(fetch_dir, write_dir):
     """Turn two rocprofv3 --pmc runs of --profile-pass (FETCH_SIZE, WRITE_SIZE, in
     KiB per dispatch) into HBM bytes per launch of each libgdn kernel.  Each counter
     is scaled by what it reads for the 512 MiB elementwise kernel, whose reads and
-    writes are known (512 MiB each); writes profiles/traffic.json."""
+    writes are known (512 MiB each)."""
     import csv
     copy_bytes = 512 * 1024 * 1024       # read, and written, by the calibration kernel
 
@@ -383,6 +383,12 @@ def summarize_pmc(fetch_dir, write_dir):
                     "seconds_under_counters": t, "counted_GBs": round(nb / t / 1e9, 1),
                     "counted_hbm_frac": round(nb / t / 1e9 / HBM_PEAK_GBS, 4),
                     "calibration_factors": factors, "note": note}
+    return rec
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """traffic_records of two counter runs, written to profiles/traffic.json."""
+    rec = traffic_records(fetch_dir, write_dir)
     out = os.path.join(ROOT, "profiles", "traffic.json")
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)

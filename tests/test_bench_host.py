@@ -46,3 +46,46 @@ def test_code_fingerprint_ignores_comments_and_layout():
 def test_fingerprint_of_the_tree_is_stable():
     h = bench.kernel_source_hash()
     assert len(h) == 16 and h == bench.kernel_source_hash()
+
+
+def _counter_csv(path, counter, rows):
+    import csv
+    import os
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                    "Start_Timestamp", "End_Timestamp"])
+        for i, (name, kib, ns) in enumerate(rows):
+            w.writerow([i, name, counter, kib, 1000, 1000 + ns])
+
+
+def test_traffic_records_calibrate_each_counter(tmp_path):
+    """Synthetic counter files: the elementwise kernel's FETCH_SIZE reads half of its
+    512 MiB of reads and WRITE_SIZE all of its writes, so fetch values scale by 2 and
+    write values by 1; decode records take bytes over the dispatch's own duration."""
+    mib = 1024  # KiB per MiB
+    copy = "void at::native::vectorized_elementwise_kernel<4, at::native::MulFunctor<float>>"
+    scan = "void gdn::chunk_scan_kernel<128, true, 1, false>(...)"
+    prep = "void gdn::chunk_prep_kernel<128, true, false>(...)"
+    dec = "void gdn::recurrent_kernel<128, 4, false>(...)"
+    _counter_csv(tmp_path / "f", "FETCH_SIZE",
+                 [(copy, 256 * mib, 10), (prep, 10 * mib, 10), (scan, 20 * mib, 10),
+                  (scan, 22 * mib, 10), (scan, 21 * mib, 10), (dec, 60 * mib, 50_000)])
+    _counter_csv(tmp_path / "w", "WRITE_SIZE",
+                 [(copy, 512 * mib, 10), (prep, 5 * mib, 10), (scan, 7 * mib, 10),
+                  (dec, 130 * mib, 50_000)])
+    rec = bench.traffic_records(str(tmp_path / "f"), str(tmp_path / "w"))
+    mb = 1024 * 1024
+    p = rec["prefill_bf16"]
+    assert abs(p["calibration_factors"]["fetch"] - 2.0) < 1e-12
+    assert abs(p["calibration_factors"]["write"] - 1.0) < 1e-12
+    assert abs(p["kernels"]["chunk_prep"]["fetch_bytes"] - 20 * mb) < 1
+    assert abs(p["kernels"]["chunk_scan"]["fetch_bytes"] - 42 * mb) < 1   # median of 20, 22, 21
+    assert abs(p["kernels"]["chunk_scan"]["write_bytes"] - 7 * mb) < 1
+    assert p["bytes_per_launch"] == round((20 + 5 + 42 + 7) * mb)
+    d = rec["decode_batched"]
+    assert d["bytes_per_launch"] == round((120 + 130) * mb)
+    assert abs(d["seconds_under_counters"] - 50e-6) < 1e-12
+    assert abs(d["counted_GBs"] - round(250 * mb / 50e-6 / 1e9, 1)) < 0.06
+    assert "decode_1tok" not in rec
