@@ -464,7 +464,8 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the decode and long-prefill extras")
     ap.add_argument("--profile-pass", action="store_true",
-                    help="short run for rocprofv3 --pmc passes (copy calibration + 10 launches)")
+                    help="short run for rocprofv3 --pmc passes (copy calibration, 10 prefill and "
+                         "10 batched-decode launches, 24 single-token decode calls)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two --pmc runs of --profile-pass")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR",

@@ -89,3 +89,18 @@ def test_traffic_records_calibrate_each_counter(tmp_path):
     assert abs(d["seconds_under_counters"] - 50e-6) < 1e-12
     assert abs(d["counted_GBs"] - round(250 * mb / 50e-6 / 1e9, 1)) < 0.06
     assert "decode_1tok" not in rec
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py --gpus N > 1 (or a multi-rank launch) exits with a message before
+    touching any GPU."""
+    import os
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    for args, world in ((["--gpus", "2"], "1"), ([], "2")):
+        env["WORLD_SIZE"] = world
+        r = subprocess.run([sys.executable, bench.__file__] + args, env=env,
+                           capture_output=True, text=True, timeout=120)
+        assert r.returncode == 2, r.stderr
+        assert "exactly one GPU" in r.stderr
