@@ -34,6 +34,9 @@
 namespace gdn {
 namespace {
 
+typedef __bf16 attn_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float attn_floatx4 __attribute__((ext_vector_type(4)));
+
 constexpr int kAttnThreads = 256;  // four waves
 constexpr int kAttnTile = 64;      // cache tokens per tile (four threads each when scoring)
 constexpr int kAttnRows = 4;       // (query head, query) rows per workgroup
@@ -147,6 +150,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
         sQ[r][c] = val * a.scale;
     }
 
+    // bf16: the query rows as the A operand of the scoring product (row m = lane % 16
+    // of the group, dimensions 32 ks + 8 (lane / 16) .. +7; rows past the group's
+    // four, or unused, are zero); the scale is applied to the fp32 scores
+    uint4 aq[D / 32];
+    if constexpr (BF16) {
+        const int m = lane & 15, g = lane >> 4;
+        const int64_t R = int64_t(grp) * kAttnRows + m;
+        const bool ok = m < kAttnRows && R < rows_here;
+        const int64_t off = ok ? ((s * a.n_heads + j * hg + R / a.n_q) * a.n_q + R % a.n_q) * D : 0;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            aq[ks] = ok ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + off +
+                                                           32 * ks + 8 * g)
+                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+
     const int64_t t_begin = int64_t(split) * a.split_len;
     const int64_t t_end = t_begin + a.split_len < a.n_kv ? t_begin + a.split_len : a.n_kv;
     const E *kbase = static_cast<const E *>(a.k) + (s * a.n_heads_kv + j) * a.n_kv * D;
@@ -178,10 +197,37 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
 #pragma unroll
             for (int h = 0; h < (BF16 ? 1 : 2); ++h) vraw[it][h] = src[h];
         }
-        // 1. scores: thread (tok, qtr) takes a quarter of key row t0 + tok (rows past
-        //    the end read the last valid one and are masked below); all its loads are
-        //    issued before the first product
-        {
+        // 1. scores.  bf16: wave w scores tile tokens 16 w .. 16 w + 15 against the
+        //    group's rows on MFMA (A: the query rows, B: lane (g, n) holds key row
+        //    16 w + n, dimensions 32 ks + 8 g .. +7); lane n of the first 16 holds the
+        //    four rows' scores of token 16 w + n.  fp32: thread (tok, qtr) takes a
+        //    quarter of key row t0 + tok.  Rows past the end read the last valid one
+        //    and are masked below; all loads are issued before the first product.
+        if constexpr (BF16) {
+            const int n = lane & 15, g = lane >> 4, tokl = 16 * wave + n;
+            const E *kr = kbase + (t0 + (tokl < last ? tokl : last)) * D + 8 * g;
+            uint4 bk[D / 32];
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) bk[ks] = *reinterpret_cast<const uint4 *>(kr + 32 * ks);
+            attn_floatx4 sc4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
+                sc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(attn_bf16x8_t, aq[ks]),
+                                                              __builtin_bit_cast(attn_bf16x8_t, bk[ks]),
+                                                              sc4, 0, 0, 0);
+            if (g == 0) {
+                const int64_t t = t0 + tokl;
+#pragma unroll
+                for (int r = 0; r < kAttnRows; ++r) {
+                    float v = sc4[r] * a.scale;
+                    if (!rv[r] || tokl > last)
+                        v = -INFINITY;
+                    else if (a.mask)
+                        v += mask_f16(a.mask[(s * a.n_q + ri[r]) * a.n_kv + t]);
+                    sS[r][tokl] = v;
+                }
+            }
+        } else {
             const E *kr = kbase + (t0 + (tok < last ? tok : last)) * D + qtr * QW;
             constexpr int KU = BF16 ? 1 : 2;          // 16-byte units per 8 elements
             uint4 kraw[QW / 8][KU];
