@@ -7,22 +7,27 @@
 //     score_t = scale (q_i . k_t) + f16(mask[s][i][t])        t < n_kv
 //     out_i   = sum_t softmax(score)_t v_t
 // The card's kernel casts the additive mask to f16 and accumulates in f16; here the
-// mask is rounded to f16 the same way and everything else runs in fp32.  A row with
-// no finite score (fully masked, or an empty cache) gives zeros.
+// mask is rounded to f16 the same way and everything else runs in fp32, except
+// that the bf16 kernel multiplies bf16 operands on MFMA (the query and key rows as
+// given, and the softmax weights rounded to bf16 for the weighted sum of value
+// rows), accumulating in fp32.  A row with no finite score (fully masked, or an
+// empty cache) gives zeros.
 //
-// Work split (memory-bound: every key/value byte is read once per row group):
-//   attn_split_kernel   one workgroup per (seq, key/value head, group of up to four
-//                       (query head, query) rows, range of cache tokens).  Per tile of
-//                       64 tokens: four threads score one token against the rows
-//                       (a quarter of its key row each, 16-byte loads all issued
-//                       before the products), one wave per row updates the running
-//                       max / sum and turns scores into weights, then the waves
-//                       accumulate weights x value rows with lanes owning 8
-//                       consecutive columns (whole value rows per load instruction,
-//                       a wave's loads of the tile in flight together).  The partial (max, sum, weighted values) of the
-//                       token range goes to the workspace, or straight to the output
-//                       when the cache is not split.
-//   attn_combine_kernel merges the token ranges of each row.
+// Work split (memory-bound: every key/value byte is read once per row group): one
+// workgroup per (seq, key/value head, group of up to four (query head, query) rows,
+// range of cache tokens), ranges sized for about 2,048 workgroups.  Per tile of 64
+// tokens, one wave per row updates the running max / sum and turns scores into
+// weights; the products differ by type:
+//   attn_split_mma_kernel  (bf16) each wave scores its 16 tokens on MFMA and owns a
+//                          quarter of the output columns, accumulating V^T P^T on
+//                          MFMA from the tile's value rows staged in LDS by LDS-DMA
+//                          (read back with transposing reads);
+//   attn_split_kernel      (fp32) four threads score one token (a quarter of its key
+//                          row each), and the waves accumulate weights x value rows
+//                          with lanes owning 8 consecutive columns, merged at the end.
+// The partial (max, sum, weighted values) of each token range goes to the
+// workspace, or straight to the output when the cache is not split;
+// attn_combine_kernel merges the token ranges of each row.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -150,22 +155,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
         sQ[r][c] = val * a.scale;
     }
 
-    // bf16: the query rows as the A operand of the scoring product (row m = lane % 16
-    // of the group, dimensions 32 ks + 8 (lane / 16) .. +7; rows past the group's
-    // four, or unused, are zero); the scale is applied to the fp32 scores
-    uint4 aq[D / 32];
-    if constexpr (BF16) {
-        const int m = lane & 15, g = lane >> 4;
-        const int64_t R = int64_t(grp) * kAttnRows + m;
-        const bool ok = m < kAttnRows && R < rows_here;
-        const int64_t off = ok ? ((s * a.n_heads + j * hg + R / a.n_q) * a.n_q + R % a.n_q) * D : 0;
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-            aq[ks] = ok ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + off +
-                                                           32 * ks + 8 * g)
-                        : make_uint4(0u, 0u, 0u, 0u);
-    }
-
     const int64_t t_begin = int64_t(split) * a.split_len;
     const int64_t t_end = t_begin + a.split_len < a.n_kv ? t_begin + a.split_len : a.n_kv;
     const E *kbase = static_cast<const E *>(a.k) + (s * a.n_heads_kv + j) * a.n_kv * D;
@@ -197,37 +186,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
 #pragma unroll
             for (int h = 0; h < (BF16 ? 1 : 2); ++h) vraw[it][h] = src[h];
         }
-        // 1. scores.  bf16: wave w scores tile tokens 16 w .. 16 w + 15 against the
-        //    group's rows on MFMA (A: the query rows, B: lane (g, n) holds key row
-        //    16 w + n, dimensions 32 ks + 8 g .. +7); lane n of the first 16 holds the
-        //    four rows' scores of token 16 w + n.  fp32: thread (tok, qtr) takes a
-        //    quarter of key row t0 + tok.  Rows past the end read the last valid one
-        //    and are masked below; all loads are issued before the first product.
-        if constexpr (BF16) {
-            const int n = lane & 15, g = lane >> 4, tokl = 16 * wave + n;
-            const E *kr = kbase + (t0 + (tokl < last ? tokl : last)) * D + 8 * g;
-            uint4 bk[D / 32];
-#pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) bk[ks] = *reinterpret_cast<const uint4 *>(kr + 32 * ks);
-            attn_floatx4 sc4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks)
-                sc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(attn_bf16x8_t, aq[ks]),
-                                                              __builtin_bit_cast(attn_bf16x8_t, bk[ks]),
-                                                              sc4, 0, 0, 0);
-            if (g == 0) {
-                const int64_t t = t0 + tokl;
-#pragma unroll
-                for (int r = 0; r < kAttnRows; ++r) {
-                    float v = sc4[r] * a.scale;
-                    if (!rv[r] || tokl > last)
-                        v = -INFINITY;
-                    else if (a.mask)
-                        v += mask_f16(a.mask[(s * a.n_q + ri[r]) * a.n_kv + t]);
-                    sS[r][tokl] = v;
-                }
-            }
-        } else {
+        // 1. scores: thread (tok, qtr) takes a quarter of key row t0 + tok (rows past
+        //    the end read the last valid one and are masked below); all its loads are
+        //    issued before the first product
+        {
             const E *kr = kbase + (t0 + (tok < last ? tok : last)) * D + qtr * QW;
             constexpr int KU = BF16 ? 1 : 2;          // 16-byte units per 8 elements
             uint4 kraw[QW / 8][KU];
@@ -349,6 +311,223 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
     }
 }
 
+// bf16 decode attention with both products on MFMA.  Same work split as
+// attn_split_kernel; per tile of 64 cache tokens:
+//   1. each wave loads the key rows of its 16 tokens into registers and issues the
+//      LDS-DMA of its share of the tile's value rows (rows padded to 2 (mod 4)
+//      16-byte units, which keeps the transposing reads below free of bank
+//      conflicts); scores on MFMA as in attn_split_kernel;
+//   2. wave r: running max and sum of row r; scores become weights (fp32);
+//   3. O^T += V^T P^T on MFMA: wave w owns D/4 output columns; the A operand (V^T:
+//      rows = columns of V, k = tokens) comes from transposing LDS reads of the
+//      staged tile, the B operand (P^T) from the weights rounded to bf16, zero for
+//      rows past the group's four.  Each lane's accumulator holds one row, so the
+//      running correction factor is one multiply per lane.
+// A wave's output columns are its own: no merge between waves.
+template <int D>
+struct AttnMmaCfg {
+    static constexpr int RS = D * 2 + 32;            // staged value row stride (bytes)
+    static constexpr int NB = kAttnTile * RS / 1024; // LDS-DMA blocks per tile
+    static constexpr int CW = D / 4;                 // output columns per wave
+    static constexpr int MT = CW / 16;               // their 16-column MFMA tiles
+    static_assert((RS / 16) % 4 == 2 && kAttnTile * RS % 1024 == 0 && CW % 16 == 0, "layout");
+};
+
+// A operand whose rows are columns c0 + (lane mod 16) of the staged tile and whose k
+// values are tokens t0 + {4g .. 4g+3}, t0 + 16 + {4g .. 4g+3} (g = lane / 16): two
+// ds_read_b64_tr_b16, inside each group of 16 lanes lane p fetching token
+// t0 + 4g + p/4 (then 16 tokens later), columns c0 + 4 (p mod 4) .. +3.
+__device__ __forceinline__ uint4 attn_vt_frag(const unsigned char *base, int stride, int t0, int c0,
+                                              int lane)
+{
+    typedef short short4v __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) short4v lds_short4v;
+    const int g = lane >> 4, p = lane & 15;
+    const unsigned char *a1 = base + (t0 + 4 * g + (p >> 2)) * stride + (c0 + 4 * (p & 3)) * 2;
+    const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(a1));
+    const short4v r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(a1 + 16 * stride));
+    const uint2 u1 = __builtin_bit_cast(uint2, r1), u2 = __builtin_bit_cast(uint2, r2);
+    return make_uint4(u1.x, u1.y, u2.x, u2.y);
+}
+
+__device__ __forceinline__ uint32_t attn_pack_bf16(float a, float b)
+{
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    typedef float float2v __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{a, b}, bf16x2v));
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void attn_split_mma_kernel(AttnArgs a)
+{
+    using F = AttnMmaCfg<D>;
+    __shared__ __align__(16) unsigned char sV[kAttnTile * F::RS];
+    __shared__ __align__(16) float sS[kAttnRows][kAttnTile];
+    __shared__ float sCorr[kAttnRows];
+    __shared__ float sML[kAttnRows][2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int64_t b = blockIdx.x;
+    const int split = static_cast<int>(b % a.n_split);
+    const int64_t u = b / a.n_split;
+    const int grp = static_cast<int>(u % a.groups);
+    const int64_t sj = u / a.groups;                  // s * n_heads_kv + j
+    const int64_t s = sj / a.n_heads_kv, j = sj - s * a.n_heads_kv;
+    const int64_t hg = a.n_heads / a.n_heads_kv;
+    const int64_t rows_here = hg * a.n_q;
+
+    bool rv[kAttnRows];
+    int64_t ri[kAttnRows];
+#pragma unroll
+    for (int r = 0; r < kAttnRows; ++r) {
+        const int64_t R = int64_t(grp) * kAttnRows + r;
+        rv[r] = R < rows_here;
+        ri[r] = rv[r] ? R % a.n_q : 0;
+    }
+
+    // query rows as the A operand of the scores (lane row n of the group)
+    uint4 aq[D / 32];
+    {
+        const int64_t R = int64_t(grp) * kAttnRows + n;
+        const bool ok = n < kAttnRows && R < rows_here;
+        const int64_t off = ok ? ((s * a.n_heads + j * hg + R / a.n_q) * a.n_q + R % a.n_q) * D : 0;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            aq[ks] = ok ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + off +
+                                                           32 * ks + 8 * g)
+                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    const int64_t t_begin = int64_t(split) * a.split_len;
+    const int64_t t_end = t_begin + a.split_len < a.n_kv ? t_begin + a.split_len : a.n_kv;
+    const uint16_t *kbase = static_cast<const uint16_t *>(a.k) + (s * a.n_heads_kv + j) * a.n_kv * D;
+    const unsigned char *vbase = reinterpret_cast<const unsigned char *>(
+        static_cast<const uint16_t *>(a.v) + (s * a.n_heads_kv + j) * a.n_kv * D);
+
+    float m_run = -INFINITY, l_run = 0.f;   // wave r's row statistics (row r = wave)
+    attn_floatx4 acc[F::MT];
+#pragma unroll
+    for (int mt = 0; mt < F::MT; ++mt) acc[mt] = attn_floatx4{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += kAttnTile) {
+        const int last = static_cast<int>(t_end - t0 < kAttnTile ? t_end - t0 : kAttnTile) - 1;
+        // 1. key rows of this wave's tokens, then the value rows' LDS-DMA; tokens
+        //    past the end read the last valid row and get weight 0
+        const int tokl = 16 * wave + n;
+        const uint16_t *kr = kbase + (t0 + (tokl < last ? tokl : last)) * D + 8 * g;
+        uint4 bk[D / 32];
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) bk[ks] = *reinterpret_cast<const uint4 *>(kr + 32 * ks);
+        const unsigned char *vt = vbase + t0 * (D * 2);
+        for (int i = wave; i < F::NB; i += kAttnThreads / 64)
+            dma16(vt, dma_src_offset(i, lane, D * 2, F::RS, D * 2, last + 1), sV + 1024 * i);
+        attn_floatx4 sc4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            sc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(attn_bf16x8_t, aq[ks]),
+                                                          __builtin_bit_cast(attn_bf16x8_t, bk[ks]),
+                                                          sc4, 0, 0, 0);
+        if (g == 0) {
+            const int64_t t = t0 + tokl;
+#pragma unroll
+            for (int r = 0; r < kAttnRows; ++r) {
+                float v = sc4[r] * a.scale;
+                if (!rv[r] || tokl > last)
+                    v = -INFINITY;
+                else if (a.mask)
+                    v += mask_f16(a.mask[(s * a.n_q + ri[r]) * a.n_kv + t]);
+                sS[r][tokl] = v;
+            }
+        }
+        wait_vmem_le<0>();
+        __syncthreads();
+
+        // 2. wave r: running max and sum of row r; scores become weights
+        {
+            const int r = wave;
+            const float x = sS[r][lane];
+            float mx = x;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+            const float m_new = fmaxf(m_run, mx);
+            const float corr = exp_diff(m_run, m_new);
+            const float p = (x == -INFINITY) ? 0.f : __expf(x - m_new);
+            sS[r][lane] = p;
+            float ps = p;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 64);
+            l_run = l_run * corr + ps;
+            m_run = m_new;
+            if (lane == 0) sCorr[r] = corr;
+        }
+        __syncthreads();
+
+        // 3. O^T += V^T P^T for this wave's columns
+        {
+            const float cr = n < kAttnRows ? sCorr[n < kAttnRows ? n : 0] : 0.f;
+#pragma unroll
+            for (int mt = 0; mt < F::MT; ++mt) acc[mt] *= cr;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                uint4 pb = make_uint4(0u, 0u, 0u, 0u);
+                if (n < kAttnRows) {
+                    const float4 p0 = *reinterpret_cast<const float4 *>(&sS[n][32 * kk + 4 * g]);
+                    const float4 p1 = *reinterpret_cast<const float4 *>(&sS[n][32 * kk + 16 + 4 * g]);
+                    pb = make_uint4(attn_pack_bf16(p0.x, p0.y), attn_pack_bf16(p0.z, p0.w),
+                                    attn_pack_bf16(p1.x, p1.y), attn_pack_bf16(p1.z, p1.w));
+                }
+#pragma unroll
+                for (int mt = 0; mt < F::MT; ++mt) {
+                    const uint4 va = attn_vt_frag(sV, F::RS, 32 * kk, wave * F::CW + 16 * mt, lane);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(attn_bf16x8_t, va), __builtin_bit_cast(attn_bf16x8_t, pb),
+                        acc[mt], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // 4. lane (g, n < 4) holds row n's columns wave * CW + 16 mt + 4 g .. +3
+    if (lane == 0) {
+        sML[wave][0] = m_run;
+        sML[wave][1] = l_run;
+    }
+    __syncthreads();
+    if (n < kAttnRows) {
+        bool ok = false;
+        int64_t row = 0;
+#pragma unroll
+        for (int r = 0; r < kAttnRows; ++r)
+            if (r == n) {
+                ok = rv[r];
+                row = (s * a.n_q + ri[r]) * a.n_heads + j * hg + (int64_t(grp) * kAttnRows + r) / a.n_q;
+            }
+        if (ok) {
+            const float m = sML[n][0], l = sML[n][1];
+#pragma unroll
+            for (int mt = 0; mt < F::MT; ++mt) {
+                const int c = wave * F::CW + 16 * mt + 4 * g;
+                if (a.n_split == 1) {
+                    const float inv = l > 0.f ? 1.f / l : 0.f;
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * D + c) =
+                        make_uint2(attn_pack_bf16(acc[mt][0] * inv, acc[mt][1] * inv),
+                                   attn_pack_bf16(acc[mt][2] * inv, acc[mt][3] * inv));
+                } else {
+                    float *pp = a.part + (row * a.n_split + split) * (D + 2);   // 8-byte aligned
+                    *reinterpret_cast<float2 *>(pp + c) = make_float2(acc[mt][0], acc[mt][1]);
+                    *reinterpret_cast<float2 *>(pp + c + 2) = make_float2(acc[mt][2], acc[mt][3]);
+                    if (c == 0) {
+                        pp[D] = m;
+                        pp[D + 1] = l;
+                    }
+                }
+            }
+        }
+    }
+}
+
 // One wave per (seq, query, head) row: merges its token ranges.  Lanes load the
 // ranges' maxima and sums in parallel (64 ranges per pass), then each lane adds the
 // weighted partial sums of its D/64 columns with the weights taken from the lanes
@@ -428,8 +607,12 @@ hipError_t launch_attn_d(const AttnProblem &p, void *ws, hipStream_t stream)
     const int64_t blocks = p.n_seqs * p.n_heads_kv * sp.groups * int64_t(sp.n_split);
     const int64_t rows = p.n_seqs * p.n_q * p.n_heads;
     if (!grid_fits(blocks, kAttnThreads) || !grid_fits(rows, 64)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_split_kernel<D, BF16>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kAttnThreads), 0, stream, a);
+    if constexpr (BF16)
+        hipLaunchKernelGGL((attn_split_mma_kernel<D>), dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kAttnThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((attn_split_kernel<D, false>), dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kAttnThreads), 0, stream, a);
     if (sp.n_split > 1) {
         hipLaunchKernelGGL((attn_combine_kernel<D, BF16>), dim3(static_cast<uint32_t>(rows)),
                            dim3(64), 0, stream, a);

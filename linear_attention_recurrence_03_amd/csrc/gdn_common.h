@@ -44,6 +44,42 @@ __device__ __forceinline__ float sum32(float x)
     return x;
 }
 
+// ---- LDS-DMA helpers ----------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
+
+// One 16-byte-per-lane LDS-DMA: lane l's 16 bytes (from base + off) land at
+// lds + 16 l.  base and lds are wave-uniform; off is a per-lane byte offset.
+__device__ __forceinline__ void dma16(const unsigned char *base, uint32_t off, void *lds)
+{
+    __builtin_amdgcn_global_load_lds((global_cvoid *)(base + off), (lds_void *)(lds), 16, 0, 0);
+}
+
+// Wait until at most N of this wave's global loads (LDS-DMA included) are
+// outstanding; they complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // s_waitcnt fields: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8]
+    // (15 = no wait), vmcnt[5:4] in bits 15:14
+    __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+
+// Byte offset, inside one chunk's data, of the 16 bytes lane `lane` loads for LDS
+// block `blk` of a padded region: rows of `rowb` valid bytes stored with stride
+// `stride`; pad slots read offset 0.  `gstride` is the source row stride; rows at
+// or past nv read row nv - 1.
+__device__ __forceinline__ uint32_t dma_src_offset(int blk, int lane, int rowb, int stride,
+                                                   uint32_t gstride, int nv)
+{
+    const int o = blk * 1024 + lane * 16;
+    const int r = o / stride, b = o - r * stride;
+    const uint32_t v = uint32_t(min(r, nv - 1)) * gstride + uint32_t(b);
+    return b < rowb ? v : 0u;
+}
+
 // Input transforms applied inside the op on request (fp32).
 // Epsilon inside the root of the q/k row normalisation: an all-zero row stays zero.
 constexpr float kL2Eps = 1e-6f;
