@@ -254,8 +254,10 @@ __device__ __forceinline__ Frag<BF16> row_frag(const unsigned char *base, int st
 constexpr int kPrepThreads = 256;
 
 // LDS of the prep kernel (one workgroup per (seq, head, chunk)).  Region R holds
-// the chunk's K and Q rows (16-byte padded) while the products are formed; after
-// that it is reused for T and A (as MFMA input type).
+// the chunk's K rows (16-byte padded) while the products are formed; after that
+// it is reused for T and A (as MFMA input type).  Q rows never pass through LDS:
+// the two waves that form Q K^T load their row tiles straight into MFMA operand
+// registers.
 template <int D, bool BF16>
 struct PrepSmem {
     using E = typename Elem<BF16>::T;
@@ -264,15 +266,18 @@ struct PrepSmem {
     static constexpr int LDT = C + 16 / ES;              // T and A rows (elements)
     static constexpr int LDD = 16;                       // transposed diagonal blocks (floats)
     static constexpr int kMat = C * LDT * ES;            // one C x C matrix of E
-    static constexpr int kK = 0, kQ = C * RK;            // during the products
+    static constexpr int kK = 0;                         // during the products
     static constexpr int kT = 0, kAe = kMat;             // afterwards
-    static constexpr int kR = (2 * C * RK > 2 * kMat) ? 2 * C * RK : 2 * kMat;
+    static constexpr int kR = (C * RK > 2 * kMat) ? C * RK : 2 * kMat;
     static constexpr int kD = kR;                        // 4 x [16][LDD] fp32
     static constexpr int kG = kD + 4 * 16 * LDD * 4;     // gates
     static constexpr int kN = kG + (4 * C + 4) * 4;      // 1/|k_r|, 1/|q_r| (normalised rows)
     static constexpr int kBytes = kN + 2 * C * 4;
-    static constexpr int NBK = C * RK / 1024;            // DMA blocks per matrix
-    static_assert(C * RK % 1024 == 0 && kMat % 16 == 0 && kR % 16 == 0, "layout");
+    static constexpr int NBK = C * RK / 1024;            // DMA blocks of the K rows
+    // Workgroups per CU that 160 KiB of LDS allows, at most five; the kernel's
+    // register budget is set for that many (one wave per SIMD each).
+    static constexpr int kPerCU = (160 * 1024 / kBytes < 5) ? 160 * 1024 / kBytes : 5;
+    static_assert(C * RK % 1024 == 0 && kMat % 16 == 0 && kR % 16 == 0 && kPerCU >= 1, "layout");
 };
 
 // The output's factor 1/sqrt(d), applied where P is formed (and by the scan's
@@ -282,8 +287,9 @@ constexpr float kOutScale = D == 32 ? 0.17677669529663687f : D == 64 ? 0.125f
                           : D == 96 ? 0.10206207261596575f : 0.08838834764831845f;
 
 // The products of one prep wave: the lower tiles of row tiles R0 and R1 of
-// K K^T (KK) or Q K^T, kept in registers across the barrier that frees the K/Q
-// rows.  Each tile is formed transposed (K rows as the MFMA's A operand), so that
+// K K^T (KK) or Q K^T, kept in registers across the barrier that frees the K
+// rows.  K rows come from LDS; Q rows from `fq` (row tile R0's D / 32 operand
+// fragments, then R1's).  Each tile is formed transposed (K rows as the MFMA's A operand), so that
 // lane (g, i) holds entries (16 tr + i, 16 tc + 4g + j), j = 0..3: four
 // consecutive columns of one row.  K K^T tiles are already
 // A = beta_r e^{gam_r - gam_s} (k_r . k_s) for s < r; Q K^T tiles are
@@ -300,19 +306,21 @@ struct PrepTiles {
 template <int D, bool BF16, bool KK, int R0, int R1>
 __device__ __forceinline__ void prep_products(PrepTiles<R0, R1> &pt, const unsigned char *smem,
                                               const float *sG, float *sD, const float *sN,
-                                              int lane)
+                                              int lane, const Frag<BF16> *fq)
 {
     using L = PrepSmem<D, BF16>;
     constexpr int KS = D / 32;
     const int gq = lane >> 4, cl = lane & 15;
     const unsigned char *sK = smem + L::kK;
-    const unsigned char *sA_rows = smem + (KK ? L::kK : L::kQ);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int tr = i ? R1 : R0;
         Frag<BF16> fa[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) fa[ks] = row_frag<BF16>(sA_rows, L::RK, 16 * tr + cl, 32 * ks, gq);
+        for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (KK) fa[ks] = row_frag<BF16>(sK, L::RK, 16 * tr + cl, 32 * ks, gq);
+            else fa[ks] = fq[i * KS + ks];   // Q rows, already in registers
+        }
         const int row = 16 * tr + cl;
         const float g_row = sG[row];
 #pragma unroll
@@ -405,11 +413,12 @@ __device__ __forceinline__ void emit_p(const PrepTiles<R0, R1> &pt, unsigned cha
 }
 
 // One workgroup per (seq, head, chunk): the state-independent part of the chunk.
-//   0. K and Q rows -> LDS by LDS-DMA (all waves); gate sums (wave 0)
+//   0. K rows -> LDS by LDS-DMA (all waves); Q rows -> operand registers
+//      (waves 2, 3); gate sums (wave 0)
 //   1. K K^T (waves 0, 1) and Q K^T (waves 2, 3) on MFMA, row tiles {0, 3} and
 //      {1, 2} per wave so that each does five tiles; results stay in registers,
 //      and waves 2, 3 write P to the workspace from them
-//   2. the K/Q space is reused: waves 0, 1 store A; wave 0 then inverts the
+//   2. the K space is reused: waves 0, 1 store A; wave 0 then inverts the
 //      diagonal 16x16 blocks of I + A by forward substitution (lane = (block,
 //      column), right-looking over a transposed fp32 copy of the block); wave 1
 //      zeroes the blocks of T read before they are formed
@@ -419,8 +428,35 @@ __device__ __forceinline__ void emit_p(const PrepTiles<R0, R1> &pt, unsigned cha
 //   5. T to the workspace as six fragment blocks
 // The products of steps 3 and 4 run on MFMA with the k range padded to 32 by
 // blocks of T that are still zero; for bf16 inputs their operands are bf16.
+// Register budget of the prep kernel, as workgroups per CU: what the LDS allows,
+// except that fp32 rows of 128 with normalisation need more than 128 registers.
 template <int D, bool BF16, bool NORM>
-__global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
+constexpr int prep_per_cu()
+{
+    return (!BF16 && NORM && D >= 128 && PrepSmem<D, BF16>::kPerCU > 3) ? 3 : PrepSmem<D, BF16>::kPerCU;
+}
+
+// Sum of squares of the elements in 16 bytes (eight bf16 or four fp32), added to acc.
+template <bool BF16>
+__device__ __forceinline__ float sumsq16(const uint4 &u, float acc)
+{
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (BF16) {
+            const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xffff0000u);
+            acc = fmaf(lo, lo, fmaf(hi, hi, acc));
+        } else {
+            const float f = __uint_as_float(w[e]);
+            acc = fmaf(f, f, acc);
+        }
+    }
+    return acc;
+}
+
+template <int D, bool BF16, bool NORM>
+__global__ __launch_bounds__(kPrepThreads)
+__attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM>()))) void chunk_prep_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, unsigned char *__restrict__ ws, int64_t n_tokens,
     int64_t n_heads, int64_t n_k_heads, int n_chunks, int raw_gates)
@@ -445,19 +481,30 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const int nv = static_cast<int>(min<int64_t>(C, n_tokens - t0));
     unsigned char *dst = ws + chunk_id * W::stride(NORM);
 
-    // 0. K and Q rows of key head h % n_k_heads (rows past the end repeat the
-    //    last valid one: their A and P entries are cleared by beta = 0 and never
-    //    read); gates
+    // 0. K rows of key head h % n_k_heads into LDS; waves 2 and 3 load the Q rows
+    //    of their row tiles ({0, 3} and {1, 2}) as MFMA operands (lane (g, i): row
+    //    16 tr + i, k = 8g .. 8g + 7 of each 32-wide k step).  Rows past the end
+    //    repeat the last valid one: their A and P entries are cleared by beta = 0
+    //    and never read.  Then the gates.
+    constexpr int KS = D / 32;
+    Frag<BF16> fq[2 * KS];
     {
         const int64_t off = ((s * n_tokens + t0) * n_k_heads + h % n_k_heads) * D * L::ES;
         const unsigned char *kb = static_cast<const unsigned char *>(k) + off;
         const unsigned char *qb = static_cast<const unsigned char *>(q) + off;
         const uint32_t hdb = static_cast<uint32_t>(n_k_heads * D * L::ES);
-        for (int i = wave; i < 2 * L::NBK; i += kPrepThreads / 64) {
-            const bool isq = i >= L::NBK;
-            const int blk = isq ? i - L::NBK : i;
-            dma16(isq ? qb : kb, dma_src_offset(blk, lane, D * L::ES, L::RK, hdb, nv),
-                  smem + (isq ? L::kQ : L::kK) + 1024 * blk);
+        for (int i = wave; i < L::NBK; i += kPrepThreads / 64)
+            dma16(kb, dma_src_offset(i, lane, D * L::ES, L::RK, hdb, nv), smem + L::kK + 1024 * i);
+        if (wave >= 2) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int tr = (wave == 2) ? (i ? 3 : 0) : (i ? 2 : 1);
+                const unsigned char *src =
+                    qb + int64_t(min(16 * tr + cl, nv - 1)) * hdb + 8 * gq * L::ES;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    fq[i * KS + ks] = *reinterpret_cast<const Frag<BF16> *>(src + 32 * ks * L::ES);
+            }
         }
     }
     if (wave == 0) {
@@ -488,59 +535,63 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     wait_vmem_le<0>();
     lds_barrier();
 
-    // 0b. normalised rows: 1 / sqrt(|x_r|^2 + eps) for the K rows (waves 0, 2) and
-    //     the Q rows (waves 1, 3), 32 rows per wave, two lanes per row
+    // 0b. normalised rows: 1 / sqrt(|x_r|^2 + eps) for the K rows (waves 0, 1: 32
+    //     rows each, two lanes per row, from LDS) and the Q rows (waves 2, 3: their
+    //     row tiles, from the operand registers, four lanes per row)
     float *sN = nullptr;
     if constexpr (NORM) {
         sN = reinterpret_cast<float *>(smem + L::kN);
-        const int r = 32 * (wave >> 1) + (lane & 31), half = lane >> 5;
-        constexpr int HB = D * L::ES / 2;  // bytes of half a row
-        const unsigned char *row = smem + ((wave & 1) ? L::kQ : L::kK) + r * L::RK + half * HB;
-        float acc = 0.f;
+        if (wave < 2) {
+            const int r = 32 * wave + (lane & 31), half = lane >> 5;
+            constexpr int HB = D * L::ES / 2;  // bytes of half a row
+            const unsigned char *row = smem + L::kK + r * L::RK + half * HB;
+            float acc = 0.f;
 #pragma unroll
-        for (int o = 0; o < HB; o += 16) {
-            const uint4 u = *reinterpret_cast<const uint4 *>(row + o);
-            if constexpr (BF16) {
-                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+            for (int o = 0; o < HB; o += 16) acc = sumsq16<BF16>(*reinterpret_cast<const uint4 *>(row + o), acc);
+            acc += __shfl_xor(acc, 32, 64);
+            if (half == 0) sN[r] = 1.f / sqrtf(acc + kL2Eps);
+        } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xffff0000u);
-                    acc = fmaf(lo, lo, fmaf(hi, hi, acc));
+            for (int i = 0; i < 2; ++i) {
+                const int tr = (wave == 2) ? (i ? 3 : 0) : (i ? 2 : 1);
+                float acc = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    uint4 w[sizeof(Frag<BF16>) / 16];
+                    __builtin_memcpy(w, &fq[i * KS + ks], sizeof(w));
+#pragma unroll
+                    for (int x = 0; x < int(sizeof(w) / 16); ++x) acc = sumsq16<BF16>(w[x], acc);
                 }
-            } else {
-                const float f[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
-                                    __uint_as_float(u.w)};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc = fmaf(f[e], f[e], acc);
+                acc += __shfl_xor(acc, 16, 64);
+                acc += __shfl_xor(acc, 32, 64);
+                if (gq == 0) sN[C + 16 * tr + cl] = 1.f / sqrtf(acc + kL2Eps);
             }
         }
-        acc += __shfl_xor(acc, 32, 64);
-        if (half == 0) sN[((wave & 1) ? C : 0) + r] = 1.f / sqrtf(acc + kL2Eps);
         lds_barrier();
     }
 
-    // 1-2. products, then the reuse of the K/Q space
+    // 1-2. products, then the reuse of the K space
     if (wave < 2) {
         if (wave == 0) {
             PrepTiles<0, 3> pt;
-            prep_products<D, BF16, true, 0, 3>(pt, smem, sG, sD, sN, lane);
+            prep_products<D, BF16, true, 0, 3>(pt, smem, sG, sD, sN, lane, nullptr);
             lds_barrier();
             store_tiles<BF16, 0, 3>(pt, sAe, LDT, lane);
         } else {
             PrepTiles<1, 2> pt;
-            prep_products<D, BF16, true, 1, 2>(pt, smem, sG, sD, sN, lane);
+            prep_products<D, BF16, true, 1, 2>(pt, smem, sG, sD, sN, lane, nullptr);
             lds_barrier();
             store_tiles<BF16, 1, 2>(pt, sAe, LDT, lane);
         }
     } else {
         if (wave == 2) {
             PrepTiles<0, 3> pt;
-            prep_products<D, BF16, false, 0, 3>(pt, smem, sG, sD, sN, lane);
+            prep_products<D, BF16, false, 0, 3>(pt, smem, sG, sD, sN, lane, fq);
             emit_p<BF16, 0, 3>(pt, dst + W::kP, lane);
             lds_barrier();
         } else {
             PrepTiles<1, 2> pt;
-            prep_products<D, BF16, false, 1, 2>(pt, smem, sG, sD, sN, lane);
+            prep_products<D, BF16, false, 1, 2>(pt, smem, sG, sD, sN, lane, fq);
             emit_p<BF16, 1, 2>(pt, dst + W::kP, lane);
             lds_barrier();
             // beta, e^gam, e^{last-gam}, e^last; with normalised rows the second and
