@@ -21,7 +21,8 @@
 //   attn_split_mma_kernel  (bf16) each wave scores its 16 tokens on MFMA and owns a
 //                          quarter of the output columns, accumulating V^T P^T on
 //                          MFMA from the tile's value rows staged in LDS by LDS-DMA
-//                          (read back with transposing reads);
+//                          (read back with transposing reads); the next tile's key
+//                          rows are loaded while the current tile is reduced;
 //   attn_split_kernel      (fp32) four threads score one token (a quarter of its key
 //                          row each), and the waves accumulate weights x value rows
 //                          with lanes owning 8 consecutive columns, merged at the end.
@@ -410,15 +411,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_mma_kernel(AttnArgs a
 #pragma unroll
     for (int mt = 0; mt < F::MT; ++mt) acc[mt] = attn_floatx4{0.f, 0.f, 0.f, 0.f};
 
+    // key rows of this wave's 16 tokens of the tile at tt (B operand of the scores);
+    // tokens past the end read the last valid row
+    const int tokl = 16 * wave + n;
+    uint4 bk[D / 32];
+    auto load_k = [&](int64_t tt, uint4 (&dstk)[D / 32]) {
+        const int lst = static_cast<int>(t_end - tt < kAttnTile ? t_end - tt : kAttnTile) - 1;
+        const uint16_t *kr = kbase + (tt + (tokl < lst ? tokl : lst)) * D + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) dstk[ks] = *reinterpret_cast<const uint4 *>(kr + 32 * ks);
+    };
+    if (t_begin < t_end) load_k(t_begin, bk);
     for (int64_t t0 = t_begin; t0 < t_end; t0 += kAttnTile) {
         const int last = static_cast<int>(t_end - t0 < kAttnTile ? t_end - t0 : kAttnTile) - 1;
-        // 1. key rows of this wave's tokens, then the value rows' LDS-DMA; tokens
-        //    past the end read the last valid row and get weight 0
-        const int tokl = 16 * wave + n;
-        const uint16_t *kr = kbase + (t0 + (tokl < last ? tokl : last)) * D + 8 * g;
-        uint4 bk[D / 32];
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) bk[ks] = *reinterpret_cast<const uint4 *>(kr + 32 * ks);
+        // 1. value rows' LDS-DMA; the key rows of this wave's tokens were loaded
+        //    one tile ahead; tokens past the end read the last valid row and get weight 0
         const unsigned char *vt = vbase + t0 * (D * 2);
         for (int i = wave; i < F::NB; i += kAttnThreads / 64)
             dma16(vt, dma_src_offset(i, lane, D * 2, F::RS, D * 2, last + 1), sV + 1024 * i);
@@ -440,7 +447,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_mma_kernel(AttnArgs a
                 sS[r][tokl] = v;
             }
         }
-        wait_vmem_le<0>();
+        const bool more = t0 + kAttnTile < t_end;
+        uint4 bkn[D / 32];
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) bkn[ks] = bk[ks];
+        if (more) {
+            load_k(t0 + kAttnTile, bkn);
+            wait_vmem_le<D / 32>();  // the value rows have landed; the next keys may not
+        } else {
+            wait_vmem_le<0>();
+        }
         __syncthreads();
 
         // 2. wave r: running max and sum of row r; scores become weights
@@ -487,6 +503,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_mma_kernel(AttnArgs a
             }
         }
         __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) bk[ks] = bkn[ks];
     }
 
     // 4. lane (g, n < 4) holds row n's columns wave * CW + 16 mt + 4 g .. +3
