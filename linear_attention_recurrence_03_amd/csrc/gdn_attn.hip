@@ -15,7 +15,7 @@
 //
 // Work split (memory-bound: every key/value byte is read once per row group): one
 // workgroup per (seq, key/value head, group of up to four (query head, query) rows,
-// range of cache tokens), ranges sized for about 1,280 workgroups.  Per tile of 64
+// range of cache tokens), ranges sized for about 1,024 workgroups.  Per tile of 64
 // tokens, one wave per row updates the running max / sum and turns scores into
 // weights; the products differ by type:
 //   attn_split_mma_kernel  (bf16) each wave scores its 16 tokens on MFMA and owns a
@@ -47,7 +47,7 @@ constexpr int kAttnThreads = 256;  // four waves
 constexpr int kAttnTile = 64;      // cache tokens per tile (four threads each when scoring)
 constexpr int kAttnRows = 4;       // (query head, query) rows per workgroup
 constexpr int kAttnSplitUnit = 64; // token ranges are multiples of this
-constexpr int kAttnTargetBlocks = 1280;  // workgroups to aim for: one round of the bf16 kernel (5 per CU)
+constexpr int kAttnTargetBlocks = 1024;  // workgroups to aim for: one round of the bf16 kernel (4 per CU)
 
 template <bool BF16>
 struct AttnElem;

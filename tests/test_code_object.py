@@ -1,7 +1,7 @@
 """The built gfx950 code objects (no GPU): read the kernel metadata of libgdn.so
 and check that no kernel spills registers to scratch memory and that the prep
-kernel of the headline shape keeps the register budget of five workgroups per
-compute unit.  Uses ROCm's LLVM tools on this library's own build."""
+kernel of the headline shape and the bf16 attention kernel keep the register
+budgets their launch sizes assume.  Uses ROCm's LLVM tools on this library's own build."""
 import os
 import re
 import subprocess
@@ -78,6 +78,14 @@ def _waves_per_simd(m):
     total = (m["vgpr_count"] + 3) // 4 * 4 + m.get("agpr_count", 0)
     total = (total + 7) // 8 * 8
     return min(8, 512 // total)
+
+
+def test_attention_register_budget(kernels):
+    """The bf16 decode attention kernel at d=128 keeps four workgroups per CU (the
+    cache ranges are sized for one round of them)."""
+    att = [m for n, m in kernels.items() if "attn_split_mma_kernelILi128E" in n]
+    assert len(att) == 1, sorted(kernels)
+    assert _waves_per_simd(att[0]) >= 4, att[0]
 
 
 def test_prep_register_budget(kernels):
