@@ -473,9 +473,14 @@ __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM>()))) void chunk_pr
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int gq = lane >> 4, cl = lane & 15;
-    const int64_t chunk_id = blockIdx.x;
-    const int64_t sh = chunk_id / n_chunks;
-    const int n = static_cast<int>(chunk_id - sh * n_chunks);
+    // Blocks are numbered chunk-major (every (seq, head) of chunk n, then chunk n+1;
+    // the grid is exactly n_sh * n_chunks): all heads of a token are contiguous in q
+    // and k, so each round of workgroups reads whole token rows.  The workspace stays
+    // (seq, head)-major.
+    const int64_t n_sh = gridDim.x / n_chunks;
+    const int n = static_cast<int>(blockIdx.x / n_sh);
+    const int64_t sh = blockIdx.x - int64_t(n) * n_sh;
+    const int64_t chunk_id = sh * n_chunks + n;
     const int64_t s = sh / n_heads, h = sh - s * n_heads;
     const int64_t t0 = int64_t(n) * C;
     const int nv = static_cast<int>(min<int64_t>(C, n_tokens - t0));
