@@ -167,11 +167,15 @@ class Slot:
         self.state_out = torch.empty((S, H, D, D), dtype=torch.float32, device="cuda")
         need = gdn.workspace_size("bf16" if v.dtype == torch.bfloat16 else "f32", S, T, H, D)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        # arguments validated and marshalled once; each run re-issues the C call
+        self.call = gdn.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"],
+                                out=self.out, state_out=self.state_out, workspace=self.ws,
+                                **self.pre)
 
-    def run(self, gdn):
-        d = self.d
-        gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], out=self.out,
-                    state_out=self.state_out, workspace=self.ws, **self.pre)
+    def run(self, gdn, stream=None):
+        """One gdn_forward call on the prepared arguments (on ``stream`` if given, else
+        on the stream current when the slot was made)."""
+        self.call(stream)
 
 
 def clone_dev(d):
@@ -218,12 +222,13 @@ def bench_decode_layers(gdn, torch, wl, reps, n_layers=24):
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):           # warm up outside capture
         for s in slots:
-            s.run(gdn)
+            s.run(gdn, side)
     torch.cuda.current_stream().wait_stream(side)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream()
         for s in slots:
-            s.run(gdn)
+            s.run(gdn, cap)
     dev_us, host_us = [], []
     for _ in range(reps):
         scrub.fill_(1.0)
@@ -243,6 +248,33 @@ def bench_decode_layers(gdn, torch, wl, reps, n_layers=24):
         host_us.append((time.perf_counter() - t0) * 1e6 / n_layers)
         torch.cuda.synchronize()
     return statistics.median(dev_us), min(dev_us), max(dev_us), statistics.median(host_us)
+
+
+def bench_dispatch_floor(torch, n=24, reps=30):
+    """Device time per dispatch of n dependent one-element kernels (torch add_ on a
+    single float) replayed from one HIP graph: the floor any one-kernel layer call
+    pays on this machine, against which the single-token decode is read."""
+    x = torch.zeros(1, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        x.add_(1.0)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(n):
+            x.add_(1.0)
+    us = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us.append(a.elapsed_time(b) * 1e3 / n)
+    return statistics.median(us)
 
 
 def bench_attn(gdn, torch, n_calls=40, reps=7):
@@ -433,26 +465,109 @@ def summarize_mfma(pmc_dir):
     print(json.dumps(rec, indent=1))
 
 
-def cpu_baseline(wl, min_seconds=10.0):
-    """The fp64 oracle on this host's cores over the whole prefill workload, repeated
-    until about min_seconds of CPU time have been spent (one pass takes well under a
-    second), reported as the mean rate."""
+def _oracle_seconds(x, threads, min_seconds, min_reps=1, sub=None):
+    """Mean wall seconds of one oracle pass over x (or x restricted by ``sub``, a
+    (seq slice, head slice) pair), repeated until min_seconds have passed."""
     import oracle
-    from linear_attention_recurrence_03_amd import inputs
-    x = inputs.make(wl)
-    cores = len(os.sched_getaffinity(0))
+    if sub is not None:
+        ss, hs = sub
+        x = {n: (x[n][ss, :, hs] if n in ("q", "k", "v", "g", "beta") else x[n][ss, hs])
+             for n in ("q", "k", "v", "g", "beta", "state")}
+        x = {n: np.ascontiguousarray(a) for n, a in x.items()}
     reps, total = 0, 0.0
-    while total < min_seconds or reps < 3:
+    while total < min_seconds or reps < min_reps:
         t0 = time.perf_counter()
         oracle.gdn_recurrent(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"],
-                             threads=cores)
+                             threads=threads)
         total += time.perf_counter() - t0
         reps += 1
-    return {"value": reps * wl.n_seqs * wl.n_tokens / total, "unit": "tokens/s",
-            "cores": cores, "kind": "oracle", "seconds": round(total, 3),
-            "sample": "the whole workload (%d seq x %d tokens x %d heads, d=%d) %d times, fp64 "
-                      "token recurrence, OpenMP over (seq, head)" % (
-                          wl.n_seqs, wl.n_tokens, wl.n_heads, wl.head_dim, reps)}
+    return total / reps, reps
+
+
+def cpu_baseline(wl, budget=1.0):
+    """The fp64 oracle (plain token recurrence, OpenMP over (seq, head)) timed on this
+    host's cores, at 1 thread and at all the cores this process may use, for each
+    workload: microseconds per layer call for the decodes (the single-token decode
+    as its 24 sequential layer calls) and tokens/s for the prefills.  Where a whole
+    workload would take more than a few seconds of CPU time, a stated sample of its
+    (sequence, head) units is timed and scaled to the whole workload by the unit count
+    (the units are independent and equally long).  ``budget`` scales the repeat
+    times (about 25 s in all at 1.0)."""
+    from linear_attention_recurrence_03_amd import inputs
+    cores = len(os.sched_getaffinity(0))
+    legs = {}
+
+    # single-token decode: 24 layers, each its own inputs and state
+    wl2 = inputs.WORKLOADS[2]
+    xs = [inputs.make(wl2, layer=l) for l in range(24)]
+    for label, th in (("threads_1", 1), ("threads_all", cores)):
+        t_all, reps = 0.0, 0
+        while t_all < 1.0 * budget or reps < 3:
+            t0 = time.perf_counter()
+            for x in xs:
+                _oracle_seconds(x, th, 0.0)
+            t_all += time.perf_counter() - t0
+            reps += 1
+        legs.setdefault("decode_1tok", {})[label] = {
+            "us_per_layer": round(t_all / reps / 24 * 1e6, 2), "threads": th,
+            "sample": "all 24 layer calls, %d times" % reps}
+    del xs
+    # batched decode: 64 seqs x 32 heads, one token
+    wl3 = inputs.WORKLOADS[3]
+    x3 = inputs.make(wl3)
+    for label, th in (("threads_1", 1), ("threads_all", cores)):
+        sec, reps = _oracle_seconds(x3, th, 1.5 * budget, min_reps=3)
+        legs.setdefault("decode_batched", {})[label] = {
+            "us_per_call": round(sec * 1e6, 1), "threads": th,
+            "sample": "the whole call, %d times" % reps}
+    del x3
+    # prefill 1 x 4096 x 32 heads: all cores on the whole workload, 1 thread on 4 heads
+    x4 = inputs.make(wl)
+    sec, reps = _oracle_seconds(x4, cores, 6.0 * budget, min_reps=3)
+    legs["prefill_bf16"] = {"threads_all": {
+        "tokens_per_s": round(wl.n_seqs * wl.n_tokens / sec, 1), "threads": cores,
+        "sample": "the whole workload, %d times" % reps}}
+    h1 = 4
+    sec1, reps1 = _oracle_seconds(x4, 1, 4.0 * budget, sub=(slice(0, 1), slice(0, h1)))
+    whole1 = sec1 * wl.n_heads / h1
+    legs["prefill_bf16"]["threads_1"] = {
+        "tokens_per_s": round(wl.n_seqs * wl.n_tokens / whole1, 1), "threads": 1,
+        "sample": "heads 0-%d of the sequence (%d of %d (seq, head) units), %d times, "
+                  "scaled by %d" % (h1 - 1, h1, wl.n_heads, reps1, wl.n_heads // h1)}
+    headline = {"value": legs["prefill_bf16"]["threads_all"]["tokens_per_s"],
+                "seconds": round(sec * reps, 3), "reps": reps}
+    del x4
+    # long prefill 4 x 32768 x 16 heads: sequence 0 only (all cores), one head (1 thread)
+    wl5 = inputs.WORKLOADS[5]
+    x5 = inputs.make(wl5, seq=0)
+    units = wl5.n_seqs * wl5.n_heads
+    sec, reps = _oracle_seconds(x5, cores, 4.0 * budget)
+    legs["prefill_long"] = {"threads_all": {
+        "tokens_per_s": round(wl5.n_seqs * wl5.n_tokens / (sec * wl5.n_seqs), 1),
+        "threads": cores,
+        "sample": "sequence 0, all %d heads (%d of %d units), %d times, scaled by %d" % (
+            wl5.n_heads, wl5.n_heads, units, reps, wl5.n_seqs)}}
+    sec1, reps1 = _oracle_seconds(x5, 1, 2.0 * budget, sub=(slice(0, 1), slice(0, 1)))
+    legs["prefill_long"]["threads_1"] = {
+        "tokens_per_s": round(wl5.n_seqs * wl5.n_tokens / (sec1 * units), 1), "threads": 1,
+        "sample": "sequence 0, head 0 (1 of %d units), %d times, scaled by %d" % (
+            units, reps1, units)}
+    del x5
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                       None)
+    except OSError:
+        pass
+    return {"value": headline["value"], "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu,
+            "sample": "the headline workload (%d seq x %d tokens x %d heads, d=%d) %d times on "
+                      "%d threads, fp64 token recurrence, OpenMP over (seq, head); every "
+                      "workload at 1 thread and at all cores in legs" % (
+                          wl.n_seqs, wl.n_tokens, wl.n_heads, wl.head_dim, headline["reps"],
+                          cores),
+            "seconds": headline["seconds"], "legs": legs}
 
 
 def main():
@@ -461,6 +576,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="time only the oracle legs (no GPU needed)")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the decode and long-prefill extras")
     ap.add_argument("--profile-pass", action="store_true",
@@ -477,6 +594,10 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)
+        return
+    if args.cpu_baseline_only:
+        from linear_attention_recurrence_03_amd import inputs
+        print(json.dumps(cpu_baseline(inputs.WORKLOADS[4])), flush=True)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -541,6 +662,8 @@ def main():
             "us_per_layer_host": round(host, 3), "bytes_per_call": b2,
             "hbm_frac": round(b2 / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "counters": load_traffic_record("decode_1tok"),
+            "dispatch_floor_us": round(bench_dispatch_floor(torch), 3),
+            "host_path": "prepared call (arguments validated once, C call re-issued)",
             "workload": "1 seq x 1 token x 32 heads x d128 fp32, 24 sequential layer calls "
                         "replayed from one HIP graph, 1 GiB scrub before each replay"}
         # batched decode

@@ -140,7 +140,10 @@ size_t gdn_workspace_size(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens,
  * Size limits (a dispatch counts the work-items of its grid in 32 bits): at most
  * 2^27 state rows, n_seqs * n_heads * head_dim (a 64 GiB state at head_dim 128),
  * and, when the chunked form runs, fewer than 2^24 chunks,
- * n_seqs * n_heads * ceil(n_tokens / 64).  Larger calls return GDN_ERR_BAD_SHAPE;
+ * n_seqs * n_heads * ceil(n_tokens / 64), and 64 token rows of all heads within
+ * 4 GiB, 64 * n_heads * head_dim * (element size) < 2^32 (the kernels address a
+ * row inside one 64-token chunk in 32 bits; at head_dim 128 this allows 131071
+ * heads in fp32, 262143 in bf16).  Larger calls return GDN_ERR_BAD_SHAPE;
  * split the batch or the sequence over several calls (the state carries over). */
 int gdn_forward(gdn_dtype dtype, const void *q, const void *k, const void *v,
                 const float *g, const float *beta, const float *state_in,

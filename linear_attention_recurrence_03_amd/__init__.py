@@ -12,7 +12,7 @@ Mirrors the op pair of the "ggml attention kernels" model card (section
 import ctypes
 import os
 
-__all__ = ["forward", "supports", "workspace_size", "status_string", "library_path",
+__all__ = ["forward", "prepare", "PreparedForward", "supports", "workspace_size", "status_string", "library_path",
            "GdnError", "ALGOS", "flash_attn", "supports_flash_attn",
            "workspace_size_flash_attn"]
 
@@ -97,22 +97,42 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def forward(q, k, v, g, beta, state=None, algo: str = "auto", out=None, state_out=None,
-            workspace=None, stream=None, l2norm_qk: bool = False, raw_gates: bool = False):
-    """Run the gated delta rule over all tokens.  Returns (out, final_state).
+class PreparedForward:
+    """One validated gdn_forward call with its C arguments built once.
 
-    q, k, v: (n_seqs, n_tokens, n_heads, head_dim) float32 or bfloat16 CUDA
-    tensors (same dtype).  q and k may instead hold n_key_heads heads, a
-    divisor of n_heads: value head h then reads key/query head h % n_key_heads
-    (the tiled order; ``gdn_forward_tiled``).  g, beta: (n_seqs, n_tokens,
-    n_heads) float32; state:
-    (n_seqs, n_heads, head_dim, head_dim) float32 stored [value][key], or None
-    for zeros.  ``state_out`` may be ``state`` itself for an in-place update.
-    ``l2norm_qk`` normalises each q and k row inside the op; ``raw_gates`` takes
-    g and beta as pre-activations (g := -softplus(g), beta := sigmoid(beta)).
-    Work is enqueued on ``stream`` (default: torch's current stream); nothing
-    is synchronised.
-    """
+    Calling it re-issues the same C call (the library validates again, in C) on
+    the stream fixed at preparation, and returns ``(out, final_state)``.  It keeps
+    the tensors it was prepared with alive; their contents may change between
+    calls, their storage may not.  This is the cheap path for eager decode loops
+    that call the op on the same buffers every step."""
+
+    __slots__ = ("_fn", "_args", "_keep", "out", "state_out")
+
+    def __init__(self, fn, args, keep, out, state_out):
+        self._fn, self._args, self._keep = fn, args, keep
+        self.out, self.state_out = out, state_out
+
+    def __call__(self, stream=None):
+        """Issue the call; ``stream`` (a torch stream) overrides the prepared one for
+        this call only, e.g. to record it into a HIP graph being captured."""
+        args = self._args
+        if stream is not None:
+            args = args[:-1] + (ctypes.c_void_p(stream.cuda_stream),)
+        rc = self._fn(*args)
+        if rc != 0:
+            raise GdnError(rc, status_string(rc))
+        return self.out, self.state_out
+
+
+def prepare(q, k, v, g, beta, state=None, algo: str = "auto", out=None, state_out=None,
+            workspace=None, stream=None, l2norm_qk: bool = False,
+            raw_gates: bool = False) -> PreparedForward:
+    """Validate the arguments of ``forward`` once, allocate what is missing and
+    return a ``PreparedForward`` that issues the call.  Arguments are those of
+    ``forward``.  Outputs and the workspace are allocated on ``stream`` (the
+    caller's stream, else torch's current stream), the stream the call runs on,
+    so torch's allocator never hands their memory to other work while the
+    library may still use it."""
     import torch
 
     if q.dtype == torch.float32:
@@ -152,35 +172,60 @@ def forward(q, k, v, g, beta, state=None, algo: str = "auto", out=None, state_ou
                                   or not state_out.is_contiguous()):
         raise ValueError("state_out must be a contiguous float32 (n_seqs, n_heads, d, d) "
                          "GPU tensor")
-    if out is None:
-        out = torch.empty_like(v)
-    if state_out is None:
-        state_out = torch.empty((S, H, D, D), dtype=torch.float32, device=dev)
     a = ALGOS[algo]
     lib = _lib()
     need = int(lib.gdn_workspace_size(_DTYPES[dt], S, T, H, D, a))
-    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    with torch.cuda.stream(stream):   # allocations belong to the stream that uses them
+        if out is None:
+            out = torch.empty_like(v)
+        if state_out is None:
+            state_out = torch.empty((S, H, D, D), dtype=torch.float32, device=dev)
+        if need > 0 and (workspace is None or
+                         workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     handle = ctypes.c_void_p(stream.cuda_stream)
     flags = (PRE_L2NORM_QK if l2norm_qk else 0) | (PRE_RAW_GATES if raw_gates else 0)
+    ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out),
+            _ptr(state_out))
+    tail = (_ptr(workspace), ctypes.c_size_t(ws_bytes), ctypes.c_int(a), handle)
+    i64 = ctypes.c_int64
     if flags:
-        rc = lib.gdn_forward_ex(_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                _ptr(state), _ptr(out), _ptr(state_out), S, T, H, HK, D, flags,
-                                _ptr(workspace), ws_bytes, a, handle)
+        fn = lib.gdn_forward_ex
+        args = (_DTYPES[dt],) + ptrs + (i64(S), i64(T), i64(H), i64(HK), ctypes.c_int(D),
+                                        ctypes.c_uint(flags)) + tail
     elif HK == H:
-        rc = lib.gdn_forward(_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                             _ptr(state), _ptr(out), _ptr(state_out), S, T, H, D,
-                             _ptr(workspace), ws_bytes, a, handle)
+        fn = lib.gdn_forward
+        args = (_DTYPES[dt],) + ptrs + (i64(S), i64(T), i64(H), ctypes.c_int(D)) + tail
     else:
-        rc = lib.gdn_forward_tiled(_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                   _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out), S, T,
-                                   H, HK, D, _ptr(workspace), ws_bytes, a, handle)
-    if rc != 0:
-        raise GdnError(rc, status_string(rc))
-    return out, state_out
+        fn = lib.gdn_forward_tiled
+        args = (_DTYPES[dt],) + ptrs + (i64(S), i64(T), i64(H), i64(HK),
+                                        ctypes.c_int(D)) + tail
+    keep = (q, k, v, g, beta, state, workspace, stream)
+    return PreparedForward(fn, args, keep, out, state_out)
+
+
+def forward(q, k, v, g, beta, state=None, algo: str = "auto", out=None, state_out=None,
+            workspace=None, stream=None, l2norm_qk: bool = False, raw_gates: bool = False):
+    """Run the gated delta rule over all tokens.  Returns (out, final_state).
+
+    q, k, v: (n_seqs, n_tokens, n_heads, head_dim) float32 or bfloat16 CUDA
+    tensors (same dtype).  q and k may instead hold n_key_heads heads, a
+    divisor of n_heads: value head h then reads key/query head h % n_key_heads
+    (the tiled order; ``gdn_forward_tiled``).  g, beta: (n_seqs, n_tokens,
+    n_heads) float32; state:
+    (n_seqs, n_heads, head_dim, head_dim) float32 stored [value][key], or None
+    for zeros.  ``state_out`` may be ``state`` itself for an in-place update.
+    ``l2norm_qk`` normalises each q and k row inside the op; ``raw_gates`` takes
+    g and beta as pre-activations (g := -softplus(g), beta := sigmoid(beta)).
+    Work is enqueued on ``stream`` (default: torch's current stream), where the
+    outputs and the workspace are also allocated; nothing is synchronised.
+    """
+    return prepare(q, k, v, g, beta, state, algo=algo, out=out, state_out=state_out,
+                   workspace=workspace, stream=stream, l2norm_qk=l2norm_qk,
+                   raw_gates=raw_gates)()
 
 
 def supports_flash_attn(n_q: int, head_dim_k: int, head_dim_v: int) -> bool:
@@ -222,25 +267,29 @@ def flash_attn(q, k, v, mask=None, scale=None, out=None, workspace=None, stream=
                          "n_kv, d)")
     S, H, NQ, D = q.shape
     HKV, NKV = k.shape[1], k.shape[2]
-    if mask is not None:
-        if mask.shape != (S, 1, NQ, NKV):
-            raise ValueError("mask must be (n_seqs, 1, n_q, n_kv)")
-        mask = mask.to(torch.float32).contiguous()
-    for t in (q, k, v) + ((mask,) if mask is not None else ()):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("all tensors must be contiguous GPU tensors")
-    if out is None:
-        out = torch.empty((S, NQ, H, D), dtype=q.dtype, device=q.device)
-    elif out.shape != (S, NQ, H, D) or out.dtype != q.dtype or not out.is_contiguous():
+    if mask is not None and mask.shape != (S, 1, NQ, NKV):
+        raise ValueError("mask must be (n_seqs, 1, n_q, n_kv)")
+    if out is not None and (out.shape != (S, NQ, H, D) or out.dtype != q.dtype
+                            or not out.is_contiguous()):
         raise ValueError("out must be a contiguous (n_seqs, n_q, n_heads, d) tensor like q")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
     sc = (1.0 / D ** 0.5) if scale is None else float(scale)
     lib = _lib()
     need = int(lib.gdn_flash_attn_workspace_size(S, H, HKV, NQ, NKV, D))
-    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    # the converted mask, the output and the workspace belong to the stream that uses them
+    with torch.cuda.stream(stream):
+        if mask is not None:
+            mask = mask.to(torch.float32).contiguous()
+        if out is None:
+            out = torch.empty((S, NQ, H, D), dtype=q.dtype, device=q.device)
+        if need > 0 and (workspace is None or
+                         workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    for t in (q, k, v, out) + ((mask,) if mask is not None else ()):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous GPU tensors")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
     rc = lib.gdn_flash_attn(_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(out),
                             S, H, HKV, NQ, NKV, D, sc, _ptr(workspace), ws_bytes,
                             ctypes.c_void_p(stream.cuda_stream))

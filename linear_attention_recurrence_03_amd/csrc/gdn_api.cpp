@@ -27,6 +27,7 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;
 // each).  Both bounds lie beyond what fits in device memory at head_dim 128.
 constexpr int64_t kMaxStateRows = int64_t(1) << 27;
 constexpr int64_t kMaxChunks = (int64_t(1) << 24) - 1;
+constexpr int64_t kMaxChunkRowsBytes = int64_t(1) << 32;
 
 bool mul_ok(int64_t a, int64_t b, int64_t *r)
 {
@@ -86,9 +87,13 @@ int check_shape(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens, int64_t n_hea
     if (!mul_ok(n_seqs, n_heads, &b) || !mul_ok(b, int64_t(head_dim) * head_dim, state_elems))
         return GDN_ERR_BAD_SHAPE;
     if (b * head_dim > kMaxStateRows) return GDN_ERR_BAD_SHAPE;
-    if (b > 0 && n_tokens > 0 && pick_algo(algo, n_tokens, dtype) == GDN_ALGO_CHUNKED &&
-        (n_tokens + 63) / 64 > kMaxChunks / b)
-        return GDN_ERR_BAD_SHAPE;
+    if (b > 0 && n_tokens > 0 && pick_algo(algo, n_tokens, dtype) == GDN_ALGO_CHUNKED) {
+        if ((n_tokens + 63) / 64 > kMaxChunks / b) return GDN_ERR_BAD_SHAPE;
+        // The chunked kernels form the byte offset of a token row inside one chunk
+        // of q, k or v in 32 bits: 64 token rows of every head must span < 4 GiB.
+        const int64_t esz = (dtype == GDN_BF16) ? 2 : 4;
+        if (64 * n_heads * head_dim * esz >= kMaxChunkRowsBytes) return GDN_ERR_BAD_SHAPE;
+    }
     return GDN_OK;
 }
 

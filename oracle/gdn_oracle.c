@@ -41,11 +41,12 @@
  * Two forms are provided:
  *   oracle_gdn_recurrent -- the token recurrence above, written out plainly.
  *   oracle_gdn_chunked   -- the same result reorganised into chunks of C
- *                           tokens ("fused Gated Delta Net (chunked)" in the
- *                           velstech page, section "Why this bites AMD users
- *                           specifically": the recurrence rewritten to run in
- *                           parallel blocks).  Used only to check the first
- *                           form and to give stage-by-stage values.
+ *                           tokens: the chunked kernel that the velstech
+ *                           page (section "Why this bites AMD users
+ *                           specifically") says llama.cpp lacks on ROCm,
+ *                           which runs the recurrence in parallel blocks.
+ *                           Used only to check the first form and to give
+ *                           stage-by-stage values.
  *
  * Inputs q, k, v, g, beta are fp32 storage (bf16 inputs arrive already widened
  * to fp32, which is exact); every operation here is fp64.  The initial state is

@@ -292,3 +292,19 @@ def test_size_limits(lib):
     assert fa(S=1 << 24, q=None) == E_SHAPE
     assert fa(S=1 << 22, H=4, HKV=1, NQ=1, q=None) == E_NULL     # four rows per workgroup
     assert fa(S=(1 << 24) + 1, q=None) == E_SHAPE
+
+
+def test_chunk_row_span_limit(lib):
+    """The chunked kernels address a token row inside one 64-token chunk with a
+    32-bit byte offset, so a chunked call whose 64 rows of all heads reach 4 GiB
+    (64 * n_heads * head_dim * element size >= 2^32) is rejected; the token
+    recurrence has no such limit."""
+    for dtype, esz in ((BF16, 2), (F32, 4)):
+        hmax = (1 << 32) // (64 * 128 * esz) - 1        # 262143 (bf16), 131071 (fp32)
+        c = _Call(S=1, T=64, D=128, dtype=dtype)
+        assert c(lib, H=hmax, algo=CHUNK, q=None) == E_NULL
+        assert c(lib, H=hmax + 1, algo=CHUNK, q=None) == E_SHAPE
+        assert c(lib, H=hmax + 1, algo=REC, q=None) == E_NULL
+        name = "bf16" if dtype == BF16 else "f32"
+        assert gdn.workspace_size(name, 1, 64, hmax, 128, "chunked") > 0
+        assert gdn.workspace_size(name, 1, 64, hmax + 1, 128, "chunked") == 0
