@@ -32,9 +32,10 @@
  * q and k are used as given (no normalisation inside the op).
  *
  * Ownership and streams.  Every data pointer is a DEVICE pointer owned by the
- * caller.  The library keeps no pointer after a call returns and never
+ * caller.  The library keeps no pointer after a call returns and no call
  * allocates device memory: scratch space for the chunked algorithm is the
- * caller's workspace.  Work is enqueued on the caller's stream and the call
+ * caller's workspace (gdn_forward_noalloc instead uses a fixed array that the
+ * library holds on each GPU it runs on).  Work is enqueued on the caller's stream and the call
  * returns without synchronising; results are ready when that stream reaches
  * the end of the enqueued work (the model card, section "Where the kernels
  * come from", explains why kernels must join the caller's own queue).
@@ -82,7 +83,9 @@ enum {
     GDN_ERR_ALIASING = -8,             /* out overlaps an input, or state_out
                                           overlaps state_in without being equal */
     GDN_ERR_HIP = -9,                  /* the HIP runtime refused a launch     */
-    GDN_ERR_BAD_FLAGS = -10            /* unknown bits in gdn_forward_ex flags */
+    GDN_ERR_BAD_FLAGS = -10,           /* unknown bits in gdn_forward_ex flags */
+    GDN_ERR_SCRATCH_TOO_SMALL = -11    /* gdn_forward_noalloc: the call needs more
+                                          scratch than the library's fixed array */
 };
 
 /* Input transforms gdn_forward_ex can apply inside the op (bit mask).  They are
@@ -189,6 +192,30 @@ int gdn_forward_ex(gdn_dtype dtype, const void *q, const void *k, const void *v,
                    int64_t n_heads, int64_t n_key_heads, int head_dim,
                    unsigned int flags, void *workspace, size_t workspace_bytes,
                    gdn_algo algo, void *stream);
+
+/* gdn_forward_ex for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  There is
+ * no workspace argument: the chunked algorithm's scratch space is a fixed array
+ * of gdn_noalloc_scratch_bytes() bytes (64 MiB) that the library holds on every
+ * GPU it runs on until the process ends.  The call itself allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); the caller still passes
+ * inputs and outputs, with the meanings, rules and errors of gdn_forward_ex.
+ *
+ * A call whose gdn_workspace_size exceeds that array returns
+ * GDN_ERR_SCRATCH_TOO_SMALL before any HIP call (nothing is launched); smaller
+ * batches or shorter spans fit (the state carries over between calls).  The
+ * array's contents need no initialisation and are overwritten by each call.
+ * Every call on one GPU shares that GPU's array, so calls that overlap in time on
+ * one GPU (on different streams, or from different threads without ordering)
+ * race and may return wrong results: order them on one stream. */
+int gdn_forward_noalloc(gdn_dtype dtype, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, const float *state_in,
+                        void *out, float *state_out, int64_t n_seqs, int64_t n_tokens,
+                        int64_t n_heads, int64_t n_key_heads, int head_dim,
+                        unsigned int flags, gdn_algo algo, void *stream);
+
+/* Bytes of the fixed scratch array gdn_forward_noalloc uses on each GPU. */
+size_t gdn_noalloc_scratch_bytes(void);
 
 /* ---- decode flash attention ("ggml attention kernels" model card, section
  * "flash_attn": the vector variant, a few queries against a key/value cache) ----

@@ -12,9 +12,9 @@ Mirrors the op pair of the "ggml attention kernels" model card (section
 import ctypes
 import os
 
-__all__ = ["forward", "prepare", "PreparedForward", "supports", "workspace_size", "status_string", "library_path",
-           "GdnError", "ALGOS", "flash_attn", "supports_flash_attn",
-           "workspace_size_flash_attn"]
+__all__ = ["forward", "prepare", "PreparedForward", "forward_noalloc", "noalloc_scratch_bytes",
+           "supports", "workspace_size", "status_string", "library_path", "GdnError", "ALGOS",
+           "flash_attn", "supports_flash_attn", "workspace_size_flash_attn"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
@@ -62,6 +62,11 @@ def _lib():
     lib.gdn_forward_ex.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
                                    i64, i64, ctypes.c_int, ctypes.c_uint, vp, ctypes.c_size_t,
                                    ctypes.c_int, vp]
+    lib.gdn_forward_noalloc.restype = ctypes.c_int
+    lib.gdn_forward_noalloc.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
+                                        i64, i64, ctypes.c_int, ctypes.c_uint, ctypes.c_int, vp]
+    lib.gdn_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.gdn_noalloc_scratch_bytes.argtypes = []
     lib.gdn_flash_attn_supports.restype = ctypes.c_int
     lib.gdn_flash_attn_supports.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.gdn_flash_attn_workspace_size.restype = ctypes.c_size_t
@@ -226,6 +231,33 @@ def forward(q, k, v, g, beta, state=None, algo: str = "auto", out=None, state_ou
     return prepare(q, k, v, g, beta, state, algo=algo, out=out, state_out=state_out,
                    workspace=workspace, stream=stream, l2norm_qk=l2norm_qk,
                    raw_gates=raw_gates)()
+
+
+def forward_noalloc(q, k, v, g, beta, state, out, state_out, algo: str = "auto", stream=None,
+                    l2norm_qk: bool = False, raw_gates: bool = False):
+    """``forward`` through gdn_forward_noalloc: no workspace and no allocation, the
+    chunked algorithm's scratch being the library's fixed per-GPU array
+    (``noalloc_scratch_bytes()``).  ``out`` and ``state_out`` must be given (shaped
+    as in ``forward``); the arguments are passed to the C call as they are and the
+    library validates them.  Returns (out, state_out)."""
+    import torch
+    dt = "bf16" if q.dtype == torch.bfloat16 else "f32"
+    S, T, H, D = v.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    flags = (PRE_L2NORM_QK if l2norm_qk else 0) | (PRE_RAW_GATES if raw_gates else 0)
+    rc = _lib().gdn_forward_noalloc(_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(state), _ptr(out), _ptr(state_out), S, T, H,
+                                    q.shape[2], D, flags, ALGOS[algo],
+                                    ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise GdnError(rc, status_string(rc))
+    return out, state_out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the fixed per-GPU scratch array behind gdn_forward_noalloc."""
+    return int(_lib().gdn_noalloc_scratch_bytes())
 
 
 def supports_flash_attn(n_q: int, head_dim_k: int, head_dim_v: int) -> bool:

@@ -139,7 +139,7 @@ int forward_impl(gdn_dtype dtype, const void *q, const void *k, const void *v, c
                  const float *beta, const float *state_in, void *out, float *state_out,
                  int64_t n_seqs, int64_t n_tokens, int64_t n_heads, int64_t n_key_heads,
                  int head_dim, unsigned flags, void *workspace, size_t workspace_bytes,
-                 gdn_algo algo, void *stream);
+                 gdn_algo algo, void *stream, bool use_scratch = false);
 
 }  // namespace
 
@@ -191,6 +191,24 @@ int gdn_forward_ex(gdn_dtype dtype, const void *q, const void *k, const void *v,
     return forward_impl(dtype, q, k, v, g, beta, state_in, out, state_out, n_seqs, n_tokens,
                         n_heads, n_key_heads, head_dim, flags, workspace, workspace_bytes, algo,
                         stream);
+}
+
+int gdn_forward_noalloc(gdn_dtype dtype, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, const float *state_in, void *out,
+                        float *state_out, int64_t n_seqs, int64_t n_tokens, int64_t n_heads,
+                        int64_t n_key_heads, int head_dim, unsigned int flags, gdn_algo algo,
+                        void *stream)
+{
+    // forward_impl validates everything first (a call needing more than the scratch
+    // array is refused there) and looks the array up only once the call is valid
+    return forward_impl(dtype, q, k, v, g, beta, state_in, out, state_out, n_seqs, n_tokens,
+                        n_heads, n_key_heads, head_dim, flags, nullptr,
+                        gdn::kNoAllocScratchBytes, algo, stream, true);
+}
+
+size_t gdn_noalloc_scratch_bytes(void)
+{
+    return gdn::kNoAllocScratchBytes;
 }
 
 int gdn_flash_attn_supports(int n_q, int head_dim_k, int head_dim_v)
@@ -275,6 +293,9 @@ const char *gdn_status_string(int status)
     case GDN_ERR_ALIASING: return "output overlaps an input (only state_out == state_in is allowed)";
     case GDN_ERR_HIP: return "HIP runtime refused a launch";
     case GDN_ERR_BAD_FLAGS: return "unknown bits in the input-transform flags";
+    case GDN_ERR_SCRATCH_TOO_SMALL:
+        return "gdn_forward_noalloc: the call needs more scratch than the library's fixed "
+               "array (gdn_noalloc_scratch_bytes()); use gdn_forward_ex with a workspace";
     default: return "unknown status";
     }
 }
@@ -292,7 +313,7 @@ int forward_impl(gdn_dtype dtype, const void *q, const void *k, const void *v, c
                  const float *beta, const float *state_in, void *out, float *state_out,
                  int64_t n_seqs, int64_t n_tokens, int64_t n_heads, int64_t n_key_heads,
                  int head_dim, unsigned flags, void *workspace, size_t workspace_bytes,
-                 gdn_algo algo, void *stream)
+                 gdn_algo algo, void *stream, bool use_scratch)
 {
     int64_t tok_elems, gate_elems, state_elems;
     int rc = check_shape(dtype, n_seqs, n_tokens, n_heads, head_dim, algo, &tok_elems,
@@ -332,6 +353,12 @@ int forward_impl(gdn_dtype dtype, const void *q, const void *k, const void *v, c
     size_t need = 0;
     if (have_tokens && chosen == GDN_ALGO_CHUNKED) {
         need = gdn::chunk_workspace_bytes(dtype == GDN_BF16, n_seqs, n_tokens, n_heads, head_dim);
+        if (use_scratch) {
+            // gdn_forward_noalloc: the library's fixed array, looked up only now that
+            // the call is known to be valid and to fit (the first HIP call of the entry)
+            if (need > workspace_bytes) return GDN_ERR_SCRATCH_TOO_SMALL;
+            if (gdn::noalloc_scratch(&workspace) != hipSuccess) return GDN_ERR_HIP;
+        }
         if (workspace_bytes < need) return GDN_ERR_WORKSPACE_TOO_SMALL;
         if (need > 0 && !workspace) return GDN_ERR_NULL_POINTER;
         if (need > 0) {

@@ -39,6 +39,11 @@ size_t chunk_workspace_bytes(int bf16, int64_t n_seqs, int64_t n_tokens,
                              int64_t n_heads, int head_dim);
 hipError_t launch_chunked(const Problem &p, void *workspace, hipStream_t stream);
 
+// Size of the library-owned scratch array behind gdn_forward_noalloc (one per
+// device), and its address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 // n_tokens == 0: state_out = state_in (or zeros when state_in is null).
 hipError_t launch_state_copy(const float *state_in, float *state_out,
                              int64_t count, hipStream_t stream);

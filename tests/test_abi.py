@@ -308,3 +308,27 @@ def test_chunk_row_span_limit(lib):
         name = "bf16" if dtype == BF16 else "f32"
         assert gdn.workspace_size(name, 1, 64, hmax, 128, "chunked") > 0
         assert gdn.workspace_size(name, 1, 64, hmax + 1, 128, "chunked") == 0
+
+
+def test_noalloc_refuses_beyond_scratch_before_launch(lib):
+    """gdn_forward_noalloc checks the chunked workspace it would need against its
+    fixed scratch array first: a larger call returns GDN_ERR_SCRATCH_TOO_SMALL with
+    no HIP call (so this runs without a GPU); a fitting call reaches the pointer
+    checks of gdn_forward_ex."""
+    E_SCRATCH = -11
+    cap = lib.gdn_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    base = 1 << 32
+
+    def call(S, T, H, q=base):
+        return lib.gdn_forward_noalloc(BF16, q, base + (1 << 40), base + (2 << 40),
+                                       base + (3 << 40), base + (4 << 40), None,
+                                       base + (5 << 40), base + (6 << 40), S, T, H, H, 128, 0,
+                                       CHUNK, None)
+    per_seq = lib.gdn_workspace_size(BF16, 1, 4096, 32, 128, CHUNK)
+    fits = cap // per_seq
+    assert fits >= 1
+    assert call(fits, 4096, 32, q=None) == E_NULL
+    assert call(fits + 1, 4096, 32) == E_SCRATCH
+    assert "scratch" in lib.gdn_status_string(E_SCRATCH).decode()
+    assert call(1, 4096, 32, q=None) == E_NULL
