@@ -163,6 +163,46 @@ def chunk_stages(q, k, v, g, beta, state=None):
     return res
 
 
+def chunk_lag_terms(k, g, beta, n, chunk: int = 64):
+    """The two state-independent matrices through which chunk n's deltas depend on
+    the deltas of the two chunks before it, for one (sequence, head).
+
+    k: (n_tokens, d) keys; g, beta: (n_tokens,).  With gam the inclusive gate
+    sums inside chunk n, c_m the total gate sum of chunk m, T_n = (I + A_n)^{-1}
+    the chunk's triangular factor (``chunk_stages``) and K_m the key rows of chunk m:
+
+        R1 = -T_n diag(beta e^gam) K_n K_{n-1}^T
+        R2 = -e^{c_{n-1}} T_n diag(beta e^gam) K_n K_{n-2}^T
+
+    (zero when the earlier chunk does not exist).  Then, with S_m the state
+    entering chunk m and Dt_m = diag(e^{c_m - gam}) Delta_m,
+
+        Delta_n = T_n E_n + R1 Dt_{n-1} + R2 Dt_{n-2},
+        E_n = diag(beta)(V_n - e^{c_{n-1} + c_{n-2}} diag(e^gam) K_n S_{n-2}^T),
+
+    which follows from writing S_n = e^{c_{n-1}} S_{n-1} + Dt_{n-1}^T K_{n-1} twice
+    (the chunked form's state pass: Gated Delta Net on AMD, velstech.net, section
+    "Why this bites AMD users specifically", the recurrence run in parallel blocks).
+    Returns (R1, R2), each (rows of chunk n) x chunk, fp64."""
+    k = np.asarray(k, dtype=np.float32)
+    g = np.asarray(g, dtype=np.float32)
+    beta = np.asarray(beta, dtype=np.float32)
+    t0, t1 = n * chunk, min(len(g), (n + 1) * chunk)
+    kn = k[t0:t1].astype(np.float64)
+    st = chunk_stages(k[t0:t1], k[t0:t1], np.zeros_like(k[t0:t1]), g[t0:t1], beta[t0:t1])
+    left = st["T"] @ np.diag(beta[t0:t1].astype(np.float64) * np.exp(st["gam"]))
+    r1 = np.zeros((t1 - t0, chunk))
+    r2 = np.zeros((t1 - t0, chunk))
+    if n >= 1:
+        kp = k[t0 - chunk:t0].astype(np.float64)
+        r1 = -left @ kn @ kp.T
+    if n >= 2:
+        kpp = k[t0 - 2 * chunk:t0 - chunk].astype(np.float64)
+        c_prev = np.sum(g[t0 - chunk:t0].astype(np.float64))
+        r2 = -np.exp(c_prev) * (left @ kn @ kpp.T)
+    return r1, r2
+
+
 # ---- decode flash attention (the model card's second op, vector variant) -------
 
 def flash_attn(q, k, v, mask=None, scale=None):

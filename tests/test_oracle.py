@@ -494,3 +494,94 @@ def test_attn_grouped_head_order_and_empty_rows():
     assert np.all(out[0, 1] == 0.0) and np.any(out[0, 0] != 0.0)
     empty = oracle.flash_attn(q, k[:, :, :0], v[:, :, :0], None)
     assert empty.shape == (1, 2, 6, 8) and np.all(empty == 0.0)
+
+
+@pytest.mark.parametrize("gate", ["standard", "weak", "mixed"])
+@pytest.mark.parametrize("T,d", [(4 * 64, 16), (3 * 64 + 17, 32)])
+def test_chunk_lag_terms_reproduce_chunked_deltas(gate, T, d):
+    """The two-chunk-lag form of the chunk pass: chunk n's deltas equal T_n E_n +
+    R1 Dt_{n-1} + R2 Dt_{n-2}, with E_n formed from the state two chunks back and
+    R1, R2 from ``oracle.chunk_lag_terms``.  The deltas and states come from the
+    oracle's chunked form run chunk by chunk (itself pinned to the token
+    recurrence above), so a wrong sign, decay or chunk index in R1, R2 or E fails."""
+    x = inputs.custom(1, T, 1, d, dtype="f32", state="normal", gate=gate, seed=T + d)
+    k, q, v = x["k"][0, :, 0], x["q"][0, :, 0], x["v"][0, :, 0]
+    g, beta = x["g"][0, :, 0], x["beta"][0, :, 0]
+    C = 64
+    nc = (T + C - 1) // C
+    M = x["state"][0, 0].astype(np.float64)
+    states, deltas, gams, Ts = [M.copy()], [], [], []
+    for n in range(nc):
+        sl = slice(n * C, min(T, (n + 1) * C))
+        st = oracle.chunk_stages(q[sl], k[sl], v[sl], g[sl], beta[sl], M)
+        M = st["state"]
+        states.append(M.copy())
+        deltas.append(st["Delta"])
+        gams.append(st["gam"])
+        Ts.append(st["T"])
+    csum = [gm[-1] for gm in gams]
+    dt = [np.exp(csum[m] - gams[m])[:, None] * deltas[m] for m in range(nc)]
+    for n in range(1, nc):
+        sl = slice(n * C, min(T, (n + 1) * C))
+        m = max(n - 2, 0)
+        f = np.exp(sum(csum[m:n]))
+        E = beta[sl, None].astype(np.float64) * (
+            v[sl].astype(np.float64) -
+            f * np.exp(gams[n])[:, None] * (k[sl].astype(np.float64) @ states[m].T))
+        r1, r2 = oracle.chunk_lag_terms(k, g, beta, n)
+        got = Ts[n] @ E + r1 @ dt[n - 1] + (r2 @ dt[n - 2] if n >= 2 else 0.0)
+        err = np.max(np.abs(got - deltas[n])) / np.max(np.abs(deltas[n]))
+        assert err < 1e-10, (n, err)
+        if n == 1:
+            assert np.all(r2 == 0)
+
+
+def _lag_identity_error(x, r_fn, n):
+    """Relative error of the lag identity at chunk n with lag terms from r_fn."""
+    k, q, v = x["k"][0, :, 0], x["q"][0, :, 0], x["v"][0, :, 0]
+    g, beta = x["g"][0, :, 0], x["beta"][0, :, 0]
+    C = 64
+    M = x["state"][0, 0].astype(np.float64)
+    states, deltas, gams, Ts = [M.copy()], [], [], []
+    for m in range(n + 1):
+        sl = slice(m * C, (m + 1) * C)
+        st = oracle.chunk_stages(q[sl], k[sl], v[sl], g[sl], beta[sl], M)
+        M = st["state"]
+        states.append(M.copy())
+        deltas.append(st["Delta"])
+        gams.append(st["gam"])
+        Ts.append(st["T"])
+    csum = [gm[-1] for gm in gams]
+    dt = [np.exp(csum[m] - gams[m])[:, None] * deltas[m] for m in range(n + 1)]
+    sl = slice(n * C, (n + 1) * C)
+    E = beta[sl, None].astype(np.float64) * (
+        v[sl].astype(np.float64) - np.exp(csum[n - 1] + csum[n - 2]) * np.exp(gams[n])[:, None] *
+        (k[sl].astype(np.float64) @ states[n - 2].T))
+    r1, r2 = r_fn(k, g, beta, n)
+    got = Ts[n] @ E + r1 @ dt[n - 1] + r2 @ dt[n - 2]
+    return np.max(np.abs(got - deltas[n])) / np.max(np.abs(deltas[n]))
+
+
+def test_chunk_lag_terms_planted_mistakes():
+    """Planting a plausible mistake in the lag terms (a transposed cross product,
+    the decay of the wrong chunk in R2, a dropped sign) breaks the identity, on a
+    slowly decaying input where both terms matter, so the pin has teeth."""
+    x = inputs.custom(1, 4 * 64, 1, 16, dtype="f32", state="normal", gate="weak", seed=3)
+    n, C = 3, 64
+    assert _lag_identity_error(x, oracle.chunk_lag_terms, n) < 1e-10
+
+    def transposed(k, g, beta, n):
+        r1, r2 = oracle.chunk_lag_terms(k, g, beta, n)
+        return r1.T, r2
+
+    def wrong_decay(k, g, beta, n):
+        r1, r2 = oracle.chunk_lag_terms(k, g, beta, n)
+        c_prev = np.sum(g[(n - 1) * C:n * C].astype(np.float64))
+        c_this = np.sum(g[n * C:(n + 1) * C].astype(np.float64))
+        return r1, r2 * np.exp(c_this - c_prev)
+
+    def sign(k, g, beta, n):
+        r1, r2 = oracle.chunk_lag_terms(k, g, beta, n)
+        return -r1, r2
+    for bad in (transposed, wrong_decay, sign):
+        assert _lag_identity_error(x, bad, n) > 1e-3, bad.__name__
