@@ -158,19 +158,20 @@ def to_dev(x, dtype, torch):
 class Slot:
     """One resident copy of a workload's inputs plus its output buffers."""
 
-    def __init__(self, gdn, d, torch, pre=None):
+    def __init__(self, gdn, d, torch, pre=None, algo="auto"):
         self.d = d
         self.pre = pre or {}
         v = d["v"]
         S, T, H, D = v.shape
         self.out = torch.empty_like(v)
         self.state_out = torch.empty((S, H, D, D), dtype=torch.float32, device="cuda")
-        need = gdn.workspace_size("bf16" if v.dtype == torch.bfloat16 else "f32", S, T, H, D)
+        need = gdn.workspace_size("bf16" if v.dtype == torch.bfloat16 else "f32", S, T, H, D,
+                                  algo)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
         # arguments validated and marshalled once; each run re-issues the C call
         self.call = gdn.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"],
-                                out=self.out, state_out=self.state_out, workspace=self.ws,
-                                **self.pre)
+                                algo=algo, out=self.out, state_out=self.state_out,
+                                workspace=self.ws, **self.pre)
 
     def run(self, gdn, stream=None):
         """One gdn_forward call on the prepared arguments (on ``stream`` if given, else
@@ -195,11 +196,12 @@ def time_loop(torch, fn, n):
     return a.elapsed_time(b) / n
 
 
-def bench_prefill(gdn, torch, wl, steps, warmup, nbuf, pre=None):
+def bench_prefill(gdn, torch, wl, steps, warmup, nbuf, pre=None, algo="auto"):
     from linear_attention_recurrence_03_amd import inputs
     x = inputs.make(wl)
     base = to_dev(x, wl.dtype, torch)
-    slots = [Slot(gdn, base if i == 0 else clone_dev(base), torch, pre) for i in range(nbuf)]
+    slots = [Slot(gdn, base if i == 0 else clone_dev(base), torch, pre, algo)
+             for i in range(nbuf)]
     del x
     for i in range(warmup):
         slots[i % nbuf].run(gdn)
@@ -715,6 +717,16 @@ def main():
             "hbm_frac": round(bt / (msr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "workload": "as prefill_tiled, with unnormalised q/k rows and raw gate "
                         "pre-activations transformed inside the op"}
+        # the headline workload through the two-chunk-lag form of the chunked pass
+        msl, slots = bench_prefill(gdn, torch, wl, steps=50, warmup=5, nbuf=4,
+                                   algo="chunked_lag")
+        del slots
+        torch.cuda.empty_cache()
+        extras["prefill_lag"] = {
+            "tokens_per_s": round(S * T / (msl * 1e-3), 1), "us_per_call": round(msl * 1e3, 2),
+            "hbm_frac": round(nbytes / (msl * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "workload": "the headline workload with algo chunked_lag (two-chunk-lag chunk "
+                        "pass), 4 rotating input copies"}
         # decode flash attention: the card's measured shape, and a bandwidth-sized cache
         extras["flash_attn_decode"] = bench_attn(gdn, torch)
         line["extras"] = extras

@@ -62,12 +62,22 @@ typedef enum {
 
 /* Algorithm choice.  AUTO takes the chunked form (chunks of 64 tokens) from the
  * length at which it is faster than the token recurrence on MI355X, 16 tokens for
- * bf16 and 40 for fp32, and the token recurrence below that.  The two forced
- * values exist so that tests can run either algorithm on any input. */
+ * bf16 and 40 for fp32, and the token recurrence below that.  The forced values
+ * exist so that tests can run either algorithm on any input.
+ *
+ * CHUNKED_LAG (bf16 only; GDN_ERR_ALGO_UNAVAILABLE for fp32) is the chunked form
+ * with the chunk-to-chunk pass rewritten so that a chunk's deltas depend on those of
+ * the two chunks before it and on the state two chunks old, which takes the state
+ * off the serial chain; its workspace is larger (gdn_workspace_size with this
+ * value).  It computes the same quantities within the same tolerance, is never
+ * chosen by AUTO, and on MI355X it is about twice as slow as CHUNKED at 4,096
+ * tokens x 32 heads (each chunk step moves more operand bytes into every compute
+ * unit); it is kept so that the comparison can be re-run. */
 typedef enum {
     GDN_ALGO_AUTO = 0,
     GDN_ALGO_RECURRENT = 1,
-    GDN_ALGO_CHUNKED = 2
+    GDN_ALGO_CHUNKED = 2,
+    GDN_ALGO_CHUNKED_LAG = 3
 } gdn_algo;
 
 /* Status codes: GDN_OK or a negative error. */
@@ -78,7 +88,8 @@ enum {
     GDN_ERR_NULL_POINTER = -3,         /* a needed pointer is NULL            */
     GDN_ERR_BAD_DTYPE = -4,            /* dtype is not a gdn_dtype value      */
     GDN_ERR_WORKSPACE_TOO_SMALL = -5,  /* workspace_bytes < gdn_workspace_size */
-    GDN_ERR_ALGO_UNAVAILABLE = -6,     /* algo is not a gdn_algo value        */
+    GDN_ERR_ALGO_UNAVAILABLE = -6,     /* algo is not a gdn_algo value, or not
+                                          one the dtype has (CHUNKED_LAG, fp32) */
     GDN_ERR_MISALIGNED = -7,           /* a pointer is not 16-byte aligned    */
     GDN_ERR_ALIASING = -8,             /* out overlaps an input, or state_out
                                           overlaps state_in without being equal */

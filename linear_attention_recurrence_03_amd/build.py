@@ -32,12 +32,20 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+TRACE_LIB = os.path.join(PKG, "libgdn_trace.so")
+
+
+def build(verbose: bool = False, jobs: int = 4, trace: bool = False) -> str:
+    """Compile libgdn.so; with ``trace`` the phase-timestamp variant libgdn_trace.so
+    (-DGDN_PHASE_TRACE: the lag scan records per-wave phase timestamps)."""
+    lib = TRACE_LIB if trace else LIB
     with tempfile.TemporaryDirectory(prefix="gdn_build_") as tmp:
         objs, procs = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             flags = COMMON + (DEVICE if src.endswith(".hip") else ["-D__HIP_PLATFORM_AMD__"])
+            if trace:
+                flags = flags + ["-DGDN_PHASE_TRACE"]
             cmd = [HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
@@ -46,11 +54,11 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         bad = [p.wait() for p in procs]
         if any(bad):
             raise RuntimeError("hipcc failed (exit codes %s)" % bad)
-        tmp_lib = LIB + ".tmp"
+        tmp_lib = lib + ".tmp"
         _run([HIPCC, "-shared", "--offload-arch=" + ARCH, "-fPIC", "-o", tmp_lib] + objs, verbose)
-        os.replace(tmp_lib, LIB)
-    return LIB
+        os.replace(tmp_lib, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, trace="--trace" in sys.argv))

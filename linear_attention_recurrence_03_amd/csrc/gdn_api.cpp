@@ -69,6 +69,8 @@ gdn_algo pick_algo(gdn_algo algo, int64_t n_tokens, gdn_dtype dtype)
     return n_tokens >= from ? GDN_ALGO_CHUNKED : GDN_ALGO_RECURRENT;
 }
 
+bool is_chunked(gdn_algo a) { return a == GDN_ALGO_CHUNKED || a == GDN_ALGO_CHUNKED_LAG; }
+
 // Shape checks shared by gdn_workspace_size and gdn_forward.  On success fills
 // the element counts of a token tensor, a gate tensor and the state.
 int check_shape(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens, int64_t n_heads,
@@ -76,8 +78,10 @@ int check_shape(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens, int64_t n_hea
                 int64_t *state_elems)
 {
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
-    if (algo != GDN_ALGO_AUTO && algo != GDN_ALGO_RECURRENT && algo != GDN_ALGO_CHUNKED)
+    if (algo != GDN_ALGO_AUTO && algo != GDN_ALGO_RECURRENT && algo != GDN_ALGO_CHUNKED &&
+        algo != GDN_ALGO_CHUNKED_LAG)
         return GDN_ERR_ALGO_UNAVAILABLE;
+    if (algo == GDN_ALGO_CHUNKED_LAG && dtype != GDN_BF16) return GDN_ERR_ALGO_UNAVAILABLE;
     if (!gdn_supports(head_dim)) return GDN_ERR_UNSUPPORTED_HEAD_DIM;
     if (n_seqs < 0 || n_tokens < 0 || n_heads < 0) return GDN_ERR_BAD_SHAPE;
     int64_t a, b;
@@ -87,7 +91,7 @@ int check_shape(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens, int64_t n_hea
     if (!mul_ok(n_seqs, n_heads, &b) || !mul_ok(b, int64_t(head_dim) * head_dim, state_elems))
         return GDN_ERR_BAD_SHAPE;
     if (b * head_dim > kMaxStateRows) return GDN_ERR_BAD_SHAPE;
-    if (b > 0 && n_tokens > 0 && pick_algo(algo, n_tokens, dtype) == GDN_ALGO_CHUNKED) {
+    if (b > 0 && n_tokens > 0 && is_chunked(pick_algo(algo, n_tokens, dtype))) {
         if ((n_tokens + 63) / 64 > kMaxChunks / b) return GDN_ERR_BAD_SHAPE;
         // The chunked kernels form the byte offset of a token row inside one chunk
         // of q, k or v in 32 bits: 64 token rows of every head must span < 4 GiB.
@@ -157,8 +161,10 @@ size_t gdn_workspace_size(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens,
     if (check_shape(dtype, n_seqs, n_tokens, n_heads, head_dim, algo, &te, &ge, &se) != GDN_OK)
         return 0;
     if (n_seqs == 0 || n_heads == 0 || n_tokens == 0) return 0;
-    if (pick_algo(algo, n_tokens, dtype) != GDN_ALGO_CHUNKED) return 0;
-    return gdn::chunk_workspace_bytes(dtype == GDN_BF16, n_seqs, n_tokens, n_heads, head_dim);
+    const gdn_algo chosen = pick_algo(algo, n_tokens, dtype);
+    if (!is_chunked(chosen)) return 0;
+    return gdn::chunk_workspace_bytes(dtype == GDN_BF16, chosen == GDN_ALGO_CHUNKED_LAG, n_seqs,
+                                      n_tokens, n_heads, head_dim);
 }
 
 int gdn_forward(gdn_dtype dtype, const void *q, const void *k, const void *v, const float *g,
@@ -288,7 +294,7 @@ const char *gdn_status_string(int status)
     case GDN_ERR_NULL_POINTER: return "required pointer is NULL";
     case GDN_ERR_BAD_DTYPE: return "bad dtype (need GDN_F32 or GDN_BF16)";
     case GDN_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than gdn_workspace_size()";
-    case GDN_ERR_ALGO_UNAVAILABLE: return "algorithm value not recognised";
+    case GDN_ERR_ALGO_UNAVAILABLE: return "algorithm value not recognised, or not available for the dtype";
     case GDN_ERR_MISALIGNED: return "pointer not 16-byte aligned";
     case GDN_ERR_ALIASING: return "output overlaps an input (only state_out == state_in is allowed)";
     case GDN_ERR_HIP: return "HIP runtime refused a launch";
@@ -351,8 +357,9 @@ int forward_impl(gdn_dtype dtype, const void *q, const void *k, const void *v, c
 
     const gdn_algo chosen = pick_algo(algo, n_tokens, dtype);
     size_t need = 0;
-    if (have_tokens && chosen == GDN_ALGO_CHUNKED) {
-        need = gdn::chunk_workspace_bytes(dtype == GDN_BF16, n_seqs, n_tokens, n_heads, head_dim);
+    if (have_tokens && is_chunked(chosen)) {
+        need = gdn::chunk_workspace_bytes(dtype == GDN_BF16, chosen == GDN_ALGO_CHUNKED_LAG,
+                                          n_seqs, n_tokens, n_heads, head_dim);
         if (use_scratch) {
             // gdn_forward_noalloc: the library's fixed array, looked up only now that
             // the call is known to be valid and to fit (the first HIP call of the entry)
@@ -397,8 +404,8 @@ int forward_impl(gdn_dtype dtype, const void *q, const void *k, const void *v, c
     p.l2norm_qk = (flags & GDN_PRE_L2NORM_QK) ? 1 : 0;
     p.raw_gates = (flags & GDN_PRE_RAW_GATES) ? 1 : 0;
     p.head_dim = head_dim;
-    if (chosen == GDN_ALGO_CHUNKED)
-        err = gdn::launch_chunked(p, workspace, st);
+    if (is_chunked(chosen))
+        err = gdn::launch_chunked(p, chosen == GDN_ALGO_CHUNKED_LAG, workspace, st);
     else
         err = gdn::launch_recurrent(p, st);
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;

@@ -34,10 +34,11 @@ struct Problem {
 // Token recurrence, any n_tokens >= 1.
 hipError_t launch_recurrent(const Problem &p, hipStream_t stream);
 
-// Chunked algorithm, n_tokens >= 1.  Needs chunk_workspace_bytes(p) bytes.
-size_t chunk_workspace_bytes(int bf16, int64_t n_seqs, int64_t n_tokens,
+// Chunked algorithm, n_tokens >= 1.  Needs chunk_workspace_bytes(...) bytes.  lag:
+// the two-chunk-lag scan (bf16 rows only).
+size_t chunk_workspace_bytes(int bf16, int lag, int64_t n_seqs, int64_t n_tokens,
                              int64_t n_heads, int head_dim);
-hipError_t launch_chunked(const Problem &p, void *workspace, hipStream_t stream);
+hipError_t launch_chunked(const Problem &p, bool lag, void *workspace, hipStream_t stream);
 
 // Size of the library-owned scratch array behind gdn_forward_noalloc (one per
 // device), and its address on the current device (looked up once per device).

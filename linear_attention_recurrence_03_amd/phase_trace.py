@@ -1,0 +1,126 @@
+"""Per-wave phase timing of the two-chunk-lag scan, from the trace build.
+
+The trace build (``python -m linear_attention_recurrence_03_amd.build --trace``,
+which writes libgdn_trace.so next to libgdn.so) has the lag scan's first eight
+workgroups record, for each of their four waves (C: the chain, G: E one chunk
+ahead, U: the state pass, O: the output) and each phase, the shader clock after
+the barrier that opens the phase, once the wave's operands for the phase have
+landed, and before the barrier that closes it.  This script runs the prefill of
+1 x 4096 tokens x 32 heads, d=128, bf16 with algo "chunked_lag" (four rotating
+input copies, as the benchmark does) on that build and prints, per role, the median and 10th/90th
+percentile over the steady phases of:
+
+  work        closing stamp - opening stamp (everything the wave does in a phase)
+  operands    landed stamp - opening stamp (waiting for the phase's operands)
+  at barrier  next opening stamp - closing stamp (waiting for the other waves)
+
+and the phase length (opening stamp to the next).  Cycles are s_memtime ticks.
+
+Usage: python -m linear_attention_recurrence_03_amd.phase_trace [--json OUT]
+"""
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+
+ROLES = ("C", "G", "U", "O")
+GROUPS, PHASES = 8, 1024
+
+
+def _pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
+
+
+def summarize(raw, n_phases, skip=3):
+    """raw: uint64 array [GROUPS][4][PHASES][3].  Returns per-role statistics over
+    phases skip .. n_phases - skip - 1 of every traced workgroup."""
+    out = {"phase": []}
+    for r in ROLES:
+        out[r] = {"work": [], "operands": [], "at_barrier": []}
+    for wg in range(GROUPS):
+        for p in range(skip, n_phases - skip - 1):
+            out["phase"].append(int(raw[wg][0][p + 1][0]) - int(raw[wg][0][p][0]))
+            for w, r in enumerate(ROLES):
+                s0, s1, s2 = (int(raw[wg][w][p][i]) for i in range(3))
+                nxt = int(raw[wg][w][p + 1][0])
+                out[r]["work"].append(s2 - s0)
+                if s0 <= s1 <= s2:
+                    out[r]["operands"].append(s1 - s0)
+                out[r]["at_barrier"].append(nxt - s2)
+
+    def st(xs):
+        return {"median": statistics.median(xs), "p10": _pct(xs, 0.1), "p90": _pct(xs, 0.9)} \
+            if xs else None
+    res = {"phase": st(out["phase"])}
+    for r in ROLES:
+        res[r] = {k: st(v) for k, v in out[r].items()}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--json", help="also write the statistics to this file")
+    ap.add_argument("--lib", help="trace build to load (default: libgdn_trace.so here)")
+    args = ap.parse_args()
+    here = os.path.dirname(os.path.abspath(__file__))
+    lib_path = args.lib or os.path.join(here, "libgdn_trace.so")
+    if not os.path.exists(lib_path):
+        sys.exit("libgdn_trace.so is not built (python -m linear_attention_recurrence_03_amd.build "
+                 "--trace)")
+    os.environ["LIBGDN_PATH"] = lib_path
+    sys.path.insert(0, os.path.dirname(here))
+    import numpy as np
+    import torch
+    import linear_attention_recurrence_03_amd as gdn
+    from linear_attention_recurrence_03_amd import inputs
+
+    lib = gdn._lib()
+    lib.gdn_phase_trace_read.restype = ctypes.c_int
+    lib.gdn_phase_trace_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    wl = inputs.WORKLOADS[4]
+    x = inputs.make(wl)
+    S, T, H, D = wl.shape()
+    sets = []
+    for i in range(4):
+        d = {n: torch.from_numpy(x[n]).cuda().to(torch.bfloat16) for n in ("q", "k", "v")}
+        d.update({n: torch.from_numpy(x[n]).cuda() for n in ("g", "beta")})
+        sets.append(d)
+    out = torch.empty_like(sets[0]["v"])
+    fin = torch.empty((S, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gdn.workspace_size("bf16", S, T, H, D, "chunked_lag"), dtype=torch.uint8,
+                     device="cuda")
+    calls = [gdn.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], None, algo="chunked_lag",
+                         out=out, state_out=fin, workspace=ws) for d in sets]
+    for i in range(12):
+        calls[i % 4]()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    calls[1]()
+    b.record()
+    torch.cuda.synchronize()
+    raw = np.zeros((GROUPS, 4, PHASES, 3), dtype=np.uint64)
+    assert lib.gdn_phase_trace_read(raw.ctypes.data, raw.nbytes) == 0
+    n_phases = (T + 63) // 64 + 2
+    res = summarize(raw, n_phases)
+    res["call_us"] = a.elapsed_time(b) * 1e3
+    res["n_phases"] = n_phases
+    print("traced call (prep + lag scan): %.1f us, %d phases" % (res["call_us"], n_phases))
+    ph = res["phase"]
+    print("phase length: median %d, p10 %d, p90 %d cycles" % (ph["median"], ph["p10"], ph["p90"]))
+    print("%-4s %-11s %8s %8s %8s" % ("wave", "", "median", "p10", "p90"))
+    for r in ROLES:
+        for k in ("work", "operands", "at_barrier"):
+            v = res[r][k]
+            if v:
+                print("%-4s %-11s %8d %8d %8d" % (r, k, v["median"], v["p10"], v["p90"]))
+    if args.json:
+        with open(args.json, "w") as f:
+            json.dump(res, f, indent=1)
+
+
+if __name__ == "__main__":
+    main()

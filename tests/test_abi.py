@@ -82,6 +82,11 @@ def test_workspace_size(lib):
     assert big >= small >= 0
     assert lib.gdn_workspace_size(7, 1, 64, 1, 32, 0) == 0               # bad dtype
     assert lib.gdn_workspace_size(0, 1, 64, 1, 32, 9) == 0               # bad algo
+    # the two-chunk-lag form: bf16 only, 30 KiB per (seq, head, chunk) against 14 KiB
+    assert gdn.workspace_size("f32", 1, 4096, 32, 128, "chunked_lag") == 0
+    lag = gdn.workspace_size("bf16", 1, 4096, 32, 128, "chunked_lag")
+    assert lag == 32 * 64 * 30 * 1024 and big == 32 * 64 * 14 * 1024
+    assert gdn.workspace_size("bf16", 1, 4096 + 1, 32, 128, "chunked_lag") == 32 * 65 * 30 * 1024
 
 
 class _Call:
@@ -118,7 +123,9 @@ def test_forward_rejects_before_launch(lib):
     assert c(lib, D=48) == E_HD
     assert c(lib, D=256) == E_HD
     assert c(lib, dtype=5) == E_DTYPE
-    assert c(lib, algo=3) == E_ALGO
+    assert c(lib, algo=3) == E_ALGO          # the lag form has no fp32 variant
+    assert c(lib, algo=4) == E_ALGO
+    assert c(lib, algo=3, dtype=BF16) == E_WS  # bf16: accepted, needs its workspace
     assert c(lib, S=-1) == E_SHAPE
     assert c(lib, T=-2) == E_SHAPE
     assert c(lib, H=1 << 62) == E_SHAPE

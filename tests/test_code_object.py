@@ -58,7 +58,7 @@ def kernels(tmp_path_factory):
 
 def test_every_kernel_is_found(kernels):
     names = " ".join(kernels)
-    for k in ("chunk_prep_kernel", "chunk_scan_kernel", "recurrent_kernel",
+    for k in ("chunk_prep_kernel", "chunk_scan_kernel", "chunk_lag_kernel", "recurrent_kernel",
               "attn_split_mma_kernel", "attn_combine_kernel"):
         assert k in names, k
 
@@ -89,9 +89,22 @@ def test_attention_register_budget(kernels):
 
 
 def test_prep_register_budget(kernels):
-    """bf16 rows of 128 (the headline prefill): five prep workgroups per CU, one
-    wave per SIMD each."""
-    prep = [m for n, m in kernels.items() if "chunk_prep_kernelILi128ELb1E" in n]
-    assert len(prep) == 2, sorted(kernels)
-    for m in prep:
-        assert _waves_per_simd(m) >= 5, m
+    """bf16 rows of 128 (the headline prefill): five prep workgroups per CU, one wave
+    per SIMD each; the lag form's prep, which also forms the cross-chunk matrices,
+    three (two when the op normalises q and k)."""
+    prep = {n: m for n, m in kernels.items() if "chunk_prep_kernelILi128ELb1E" in n}
+    assert len(prep) == 4, sorted(kernels)
+    for n, m in prep.items():
+        # template arguments after <128, true>: NORM, LAG
+        norm, lag = (n.split("chunk_prep_kernelILi128ELb1E")[1][i] == "1" for i in (2, 6))
+        want = (2 if norm else 3) if lag else 5
+        assert _waves_per_simd(m) >= want, (n, m, want)
+
+
+def test_lag_scan_register_budget(kernels):
+    """The lag scan keeps two register sets of operands and runs two waves per SIMD
+    (one workgroup of five waves per CU), for every width."""
+    lag = {n: m for n, m in kernels.items() if "chunk_lag_kernel" in n}
+    assert len(lag) == 4, sorted(kernels)
+    for n, m in lag.items():
+        assert _waves_per_simd(m) >= 2, (n, m)

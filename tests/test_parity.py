@@ -86,21 +86,22 @@ def test_workload3_batched_decode(gdn):
     print("ERR batched_decode_f32: out %.3e state %.3e" % (eo, ef), flush=True)
 
 
-@pytest.mark.parametrize("algo", ["auto", "recurrent"])
+@pytest.mark.parametrize("algo", ["auto", "recurrent", "chunked_lag"])
 def test_workload4_prefill(gdn, algo):
     eo, ef = check(gdn, inputs.make(inputs.WORKLOADS[4]), "bf16", algo, what="prefill 4096")
     print("ERR prefill_bf16 %s: out %.3e state %.3e" % (algo, eo, ef), flush=True)
 
 
-def test_workload5_long_prefill_all_heads(gdn):
+@pytest.mark.parametrize("algo", ["auto", "chunked_lag"])
+def test_workload5_long_prefill_all_heads(gdn, algo):
     """The full long prefill on the GPU (all 4 sequences in one call, the launch the
     benchmark times), then every (sequence, head) compared with the oracle, one
     sequence at a time so that host memory stays near half a GB of fp64."""
     wl = inputs.WORKLOADS[5]
     x = inputs.make(wl)
-    print("case: long prefill full", flush=True)
+    print("case: long prefill full", algo, flush=True)
     d = to_dev(x, "bf16")
-    out, fin = gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"])
+    out, fin = gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], algo=algo)
     torch.cuda.synchronize()
     out = out.float().cpu()
     fin = fin.cpu().numpy().astype(np.float64)
@@ -118,8 +119,8 @@ def test_workload5_long_prefill_all_heads(gdn):
             assert eo <= TOL["bf16"] and ef <= TOL["bf16"], (s, h, eo, ef)
             worst_o, worst_f = max(worst_o, eo), max(worst_f, ef)
         del ro, rf, o
-    print("ERR long_prefill_bf16 (64 seq-heads): out %.3e state %.3e" % (worst_o, worst_f),
-          flush=True)
+    print("ERR long_prefill_bf16 %s (64 seq-heads): out %.3e state %.3e"
+          % (algo, worst_o, worst_f), flush=True)
 
 
 # ---- tails, widths, decay regimes -------------------------------------------
@@ -152,6 +153,62 @@ def test_many_row_blocks(gdn, dtype):
     there are compute units."""
     x = inputs.custom(2, 130, 20, 128, dtype=dtype, state="normal", seed=77)
     check(gdn, x, dtype, "chunked", what="many row blocks")
+
+
+# ---- the two-chunk-lag form of the chunked pass (bf16 rows) ----------------------
+
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
+@pytest.mark.parametrize("T", [1, 2, 63, 65, 130, 200])
+def test_lag_tails_and_widths(gdn, D, T):
+    """One, two and three chunks (the chain reaches back two), full and partial."""
+    x = inputs.custom(2, T, 3, D, dtype="bf16", state="normal", seed=T * 1000 + D + 5)
+    check(gdn, x, "bf16", "chunked_lag", what="lag tail T=%d D=%d" % (T, D))
+
+
+@pytest.mark.parametrize("gate", ["weak", "mixed"])
+def test_lag_decay_regimes(gdn, gate):
+    """Weak decay keeps the two earlier chunks' terms large; the mixed recipe has
+    chunk gate sums far below -70 (the cross-chunk factors underflow to zero)."""
+    x = inputs.custom(1, 1000, 4, 128, dtype="bf16", state="normal", gate=gate,
+                      beta_std=2.0, seed=42)
+    check(gdn, x, "bf16", "chunked_lag", what="lag gate " + gate)
+
+
+def test_lag_many_row_blocks(gdn):
+    x = inputs.custom(2, 130, 20, 128, dtype="bf16", state="normal", seed=77)
+    check(gdn, x, "bf16", "chunked_lag", what="lag many row blocks")
+
+
+@pytest.mark.parametrize("HK", [1, 2])
+def test_lag_tiled_key_heads(gdn, HK):
+    x = inputs.custom(2, 200, 6, 64, dtype="bf16", state="normal", seed=950 + HK,
+                      key_heads=HK)
+    check(gdn, x, "bf16", "chunked_lag", what="lag tiled key heads HK=%d" % HK)
+
+
+@pytest.mark.parametrize("l2,gates", [(True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("D", [32, 128])
+def test_lag_input_transforms(gdn, l2, gates, D):
+    x = _mixed_raw(2, 200, 3, D, "bf16", seed=750 + D, l2=l2, gates=gates)
+    check(gdn, x, "bf16", "chunked_lag", what="lag transforms D=%d" % D, l2norm_qk=l2,
+          raw_gates=gates)
+
+
+def test_lag_agrees_with_chunked(gdn):
+    """Both chunked forms compute the same quantities: their outputs differ by no more
+    than bf16 operand rounding, and each value channel depends only on its own
+    channel of v (perturbing one changes nothing else)."""
+    x = inputs.custom(1, 300, 4, 128, dtype="bf16", state="normal", gate="weak", seed=61)
+    a = run_gpu(gdn, x, "bf16", "chunked")
+    b = run_gpu(gdn, x, "bf16", "chunked_lag")
+    assert rel_err(b[0], a[0]) < 2e-2 and rel_err(b[1], a[1]) < 2e-2
+    y = dict(x)
+    y["v"] = x["v"].copy()
+    y["v"][..., 17] = inputs.bf16_round(y["v"][..., 17] + 1.0)
+    c = run_gpu(gdn, y, "bf16", "chunked_lag")
+    other = [j for j in range(128) if j != 17]
+    assert np.array_equal(b[0][..., other], c[0][..., other])
+    assert np.array_equal(b[1][:, :, other, :], c[1][:, :, other, :])
 
 
 # ---- q and k with fewer (key) heads, tiled over the value heads ---------------------
