@@ -717,6 +717,21 @@ def main():
             "hbm_frac": round(bt / (msr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "workload": "as prefill_tiled, with unnormalised q/k rows and raw gate "
                         "pre-activations transformed inside the op"}
+        # a batch of prefills with a (seq, head) pair per compute unit: AUTO (the
+        # whole-head pass) against the per-tile pass forced
+        wlb = inputs.BATCHED_PREFILL
+        Sb, Tb, Hb, Db = wlb.shape()
+        bb = algorithmic_bytes(Sb, Tb, Hb, Db, 2)
+        rec = {"workload": "8 seqs x 2048 tokens x 32 heads x d128 bf16, zero state, "
+                           "2 rotating input copies", "bytes_per_call": bb}
+        for key, algo in (("auto", "auto"), ("per_tile", "chunked")):
+            msb, slots = bench_prefill(gdn, torch, wlb, steps=20, warmup=3, nbuf=2, algo=algo)
+            del slots
+            torch.cuda.empty_cache()
+            rec[key] = {"us_per_call": round(msb * 1e3, 2),
+                        "tokens_per_s": round(Sb * Tb / (msb * 1e-3), 1),
+                        "hbm_frac": round(bb / (msb * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        extras["prefill_batched"] = rec
         # the headline workload through the two-chunk-lag form of the chunked pass
         msl, slots = bench_prefill(gdn, torch, wl, steps=50, warmup=5, nbuf=4,
                                    algo="chunked_lag")

@@ -65,6 +65,15 @@ typedef enum {
  * bf16 and 40 for fp32, and the token recurrence below that.  The forced values
  * exist so that tests can run either algorithm on any input.
  *
+ * The chunked form's chunk-to-chunk pass has two kernels for bf16 rows: one that
+ * spreads each (seq, head)'s value rows over several workgroups (fewest steps in
+ * sequence per compute unit: AUTO's choice while there are fewer (seq, head) pairs
+ * than compute units), and one whole-head workgroup per (seq, head) that brings
+ * each chunk's shared operands in once for all value rows (AUTO's choice from one
+ * pair per compute unit on; 18-31% faster there on MI355X).  Both give the same
+ * bits.  CHUNKED forces the first (and is the only chunked pass for fp32),
+ * CHUNKED_HEAD (bf16 only) the second.
+ *
  * CHUNKED_LAG (bf16 only; GDN_ERR_ALGO_UNAVAILABLE for fp32) is the chunked form
  * with the chunk-to-chunk pass rewritten so that a chunk's deltas depend on those of
  * the two chunks before it and on the state two chunks old, which takes the state
@@ -77,7 +86,8 @@ typedef enum {
     GDN_ALGO_AUTO = 0,
     GDN_ALGO_RECURRENT = 1,
     GDN_ALGO_CHUNKED = 2,
-    GDN_ALGO_CHUNKED_LAG = 3
+    GDN_ALGO_CHUNKED_LAG = 3,
+    GDN_ALGO_CHUNKED_HEAD = 4
 } gdn_algo;
 
 /* Status codes: GDN_OK or a negative error. */
@@ -89,7 +99,8 @@ enum {
     GDN_ERR_BAD_DTYPE = -4,            /* dtype is not a gdn_dtype value      */
     GDN_ERR_WORKSPACE_TOO_SMALL = -5,  /* workspace_bytes < gdn_workspace_size */
     GDN_ERR_ALGO_UNAVAILABLE = -6,     /* algo is not a gdn_algo value, or not
-                                          one the dtype has (CHUNKED_LAG, fp32) */
+                                          one the dtype has (CHUNKED_LAG and
+                                          CHUNKED_HEAD with fp32) */
     GDN_ERR_MISALIGNED = -7,           /* a pointer is not 16-byte aligned    */
     GDN_ERR_ALIASING = -8,             /* out overlaps an input, or state_out
                                           overlaps state_in without being equal */

@@ -17,7 +17,7 @@ __all__ = ["forward", "prepare", "PreparedForward", "forward_noalloc", "noalloc_
            "flash_attn", "supports_flash_attn", "workspace_size_flash_attn"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2, "chunked_lag": 3}
+ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2, "chunked_lag": 3, "chunked_head": 4}
 # input transforms (gdn.h GDN_PRE_*)
 PRE_L2NORM_QK = 1
 PRE_RAW_GATES = 2

@@ -69,7 +69,10 @@ gdn_algo pick_algo(gdn_algo algo, int64_t n_tokens, gdn_dtype dtype)
     return n_tokens >= from ? GDN_ALGO_CHUNKED : GDN_ALGO_RECURRENT;
 }
 
-bool is_chunked(gdn_algo a) { return a == GDN_ALGO_CHUNKED || a == GDN_ALGO_CHUNKED_LAG; }
+bool is_chunked(gdn_algo a)
+{
+    return a == GDN_ALGO_CHUNKED || a == GDN_ALGO_CHUNKED_LAG || a == GDN_ALGO_CHUNKED_HEAD;
+}
 
 // Shape checks shared by gdn_workspace_size and gdn_forward.  On success fills
 // the element counts of a token tensor, a gate tensor and the state.
@@ -79,9 +82,10 @@ int check_shape(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens, int64_t n_hea
 {
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
     if (algo != GDN_ALGO_AUTO && algo != GDN_ALGO_RECURRENT && algo != GDN_ALGO_CHUNKED &&
-        algo != GDN_ALGO_CHUNKED_LAG)
+        algo != GDN_ALGO_CHUNKED_LAG && algo != GDN_ALGO_CHUNKED_HEAD)
         return GDN_ERR_ALGO_UNAVAILABLE;
-    if (algo == GDN_ALGO_CHUNKED_LAG && dtype != GDN_BF16) return GDN_ERR_ALGO_UNAVAILABLE;
+    if ((algo == GDN_ALGO_CHUNKED_LAG || algo == GDN_ALGO_CHUNKED_HEAD) && dtype != GDN_BF16)
+        return GDN_ERR_ALGO_UNAVAILABLE;
     if (!gdn_supports(head_dim)) return GDN_ERR_UNSUPPORTED_HEAD_DIM;
     if (n_seqs < 0 || n_tokens < 0 || n_heads < 0) return GDN_ERR_BAD_SHAPE;
     int64_t a, b;
@@ -404,6 +408,8 @@ int forward_impl(gdn_dtype dtype, const void *q, const void *k, const void *v, c
     p.l2norm_qk = (flags & GDN_PRE_L2NORM_QK) ? 1 : 0;
     p.raw_gates = (flags & GDN_PRE_RAW_GATES) ? 1 : 0;
     p.head_dim = head_dim;
+    // AUTO picks the chunk-to-chunk pass by grid size; the forced values keep theirs
+    p.head_scan = algo == GDN_ALGO_CHUNKED_HEAD ? 1 : algo == GDN_ALGO_CHUNKED ? -1 : 0;
     if (is_chunked(chosen))
         err = gdn::launch_chunked(p, chosen == GDN_ALGO_CHUNKED_LAG, workspace, st);
     else

@@ -29,6 +29,7 @@ struct Problem {
     int head_dim;
     int l2norm_qk;          // 1: q and k rows are divided by sqrt(|row|^2 + 1e-6)
     int raw_gates;          // 1: g <- -softplus(g), beta <- sigmoid(beta)
+    int head_scan = 0;      // chunked bf16: 1 whole-head pass, -1 per-tile pass, 0 by size
 };
 
 // Token recurrence, any n_tokens >= 1.

@@ -89,6 +89,12 @@ WORKLOADS = {
 GQA_PREFILL = Workload("prefill_tiled_bf16", 1, 4096, 32, 128, "bf16", "zeros", "standard",
                        seed=6000, key_heads=16)
 
+# A batch of prefills with one (seq, head) pair per compute unit of MI355X (8
+# sequences x 32 heads), otherwise the prefill recipe: the size from which the
+# whole-head chunk-to-chunk pass is chosen.
+BATCHED_PREFILL = Workload("prefill_batched_bf16", 8, 2048, 32, 128, "bf16", "zeros",
+                           "standard", seed=7000)
+
 
 def _draw(rng, shape, dtype, state_kind, gate, beta_std, head_dim, key_heads=None, raw=False):
     S, T, H, d = shape

@@ -87,6 +87,9 @@ def test_workspace_size(lib):
     lag = gdn.workspace_size("bf16", 1, 4096, 32, 128, "chunked_lag")
     assert lag == 32 * 64 * 30 * 1024 and big == 32 * 64 * 14 * 1024
     assert gdn.workspace_size("bf16", 1, 4096 + 1, 32, 128, "chunked_lag") == 32 * 65 * 30 * 1024
+    # the whole-head pass reads the same workspace as the per-tile one
+    assert gdn.workspace_size("bf16", 1, 4096, 32, 128, "chunked_head") == big
+    assert gdn.workspace_size("f32", 1, 4096, 32, 128, "chunked_head") == 0
 
 
 class _Call:
@@ -124,7 +127,9 @@ def test_forward_rejects_before_launch(lib):
     assert c(lib, D=256) == E_HD
     assert c(lib, dtype=5) == E_DTYPE
     assert c(lib, algo=3) == E_ALGO          # the lag form has no fp32 variant
-    assert c(lib, algo=4) == E_ALGO
+    assert c(lib, algo=4) == E_ALGO          # nor the whole-head pass
+    assert c(lib, algo=5) == E_ALGO
+    assert c(lib, algo=4, dtype=BF16) == E_WS
     assert c(lib, algo=3, dtype=BF16) == E_WS  # bf16: accepted, needs its workspace
     assert c(lib, S=-1) == E_SHAPE
     assert c(lib, T=-2) == E_SHAPE

@@ -108,3 +108,12 @@ def test_lag_scan_register_budget(kernels):
     assert len(lag) == 4, sorted(kernels)
     for n, m in lag.items():
         assert _waves_per_simd(m) >= 2, (n, m)
+
+
+def test_head_scan_register_budget(kernels):
+    """The whole-head pass keeps every value in vector registers (no copies to and
+    from accumulation registers) at two or more waves per SIMD, for every width."""
+    head = {n: m for n, m in kernels.items() if "chunk_head_kernel" in n}
+    assert len(head) == 8, sorted(kernels)
+    for n, m in head.items():
+        assert m.get("agpr_count", 0) == 0 and _waves_per_simd(m) >= 2, (n, m)

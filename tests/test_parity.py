@@ -211,6 +211,61 @@ def test_lag_agrees_with_chunked(gdn):
     assert np.array_equal(b[1][:, :, other, :], c[1][:, :, other, :])
 
 
+# ---- the whole-head chunk-to-chunk pass (bf16 rows) -------------------------------
+
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
+@pytest.mark.parametrize("T", [1, 2, 63, 65, 130, 200])
+def test_head_tails_and_widths(gdn, D, T):
+    x = inputs.custom(2, T, 3, D, dtype="bf16", state="normal", seed=T * 1000 + D + 9)
+    check(gdn, x, "bf16", "chunked_head", what="head tail T=%d D=%d" % (T, D))
+
+
+@pytest.mark.parametrize("gate", ["weak", "mixed"])
+def test_head_decay_regimes(gdn, gate):
+    x = inputs.custom(1, 1000, 4, 128, dtype="bf16", state="normal", gate=gate,
+                      beta_std=2.0, seed=42)
+    check(gdn, x, "bf16", "chunked_head", what="head gate " + gate)
+
+
+@pytest.mark.parametrize("HK", [1, 2])
+def test_head_tiled_key_heads(gdn, HK):
+    x = inputs.custom(2, 200, 6, 64, dtype="bf16", state="normal", seed=960 + HK,
+                      key_heads=HK)
+    check(gdn, x, "bf16", "chunked_head", what="head tiled key heads HK=%d" % HK)
+
+
+@pytest.mark.parametrize("l2,gates", [(True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("D", [32, 128])
+def test_head_input_transforms(gdn, l2, gates, D):
+    x = _mixed_raw(2, 200, 3, D, "bf16", seed=760 + D, l2=l2, gates=gates)
+    check(gdn, x, "bf16", "chunked_head", what="head transforms D=%d" % D, l2norm_qk=l2,
+          raw_gates=gates)
+
+
+@pytest.mark.parametrize("D,pre", [(128, {}), (64, {"l2norm_qk": True, "raw_gates": True})])
+def test_head_equals_per_tile_scan(gdn, D, pre):
+    """The two chunk-to-chunk passes round at the same points: identical bits."""
+    x = (_mixed_raw(2, 300, 4, D, "bf16", seed=71, l2=True, gates=True) if pre
+         else inputs.custom(2, 300, 4, D, dtype="bf16", state="normal", gate="weak", seed=71))
+    a = run_gpu(gdn, x, "bf16", "chunked", **pre)
+    b = run_gpu(gdn, x, "bf16", "chunked_head", **pre)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_head_chosen_for_large_grids(gdn):
+    """256 (seq, head) pairs or more: AUTO runs the whole-head pass (one pair per
+    compute unit); checked against the oracle, with a ragged last chunk and key
+    heads tiled over value heads."""
+    x = inputs.custom(8, 130, 32, 128, dtype="bf16", state="normal", seed=88, key_heads=16)
+    eo, ef = check(gdn, x, "bf16", "auto", what="large grid auto")
+    a = run_gpu(gdn, x, "bf16", "auto")
+    b = run_gpu(gdn, x, "bf16", "chunked_head")
+    c = run_gpu(gdn, x, "bf16", "chunked")       # the per-tile pass, forced
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+    print("ERR large_grid_bf16 auto: out %.3e state %.3e" % (eo, ef), flush=True)
+
+
 # ---- q and k with fewer (key) heads, tiled over the value heads ---------------------
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
