@@ -13,14 +13,17 @@ SRC = os.path.join(HERE, "gdn_oracle.c")
 LIB = os.environ.get("GDN_ORACLE_PATH", os.path.join(HERE, "libgdn_oracle.so"))
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, mutant: int = 0, out: str = None) -> str:
+    """Compile the oracle to ``out`` (default LIB).  ``mutant`` > 0 plants that
+    numbered mistake (ORACLE_MUTANT in gdn_oracle.c) for the mutation test only."""
+    out = out or LIB
     cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c99",
-           "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
+           "-Wall", "-Wextra", "-DORACLE_MUTANT=%d" % mutant, "-o", out + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -51,7 +51,16 @@
  * Inputs q, k, v, g, beta are fp32 storage (bf16 inputs arrive already widened
  * to fp32, which is exact); every operation here is fp64.  The initial state is
  * fp64 so that a carried state is passed on without rounding.
+ *
+ * ORACLE_MUTANT (a compile-time number, 0 and absent in every normal build)
+ * plants one plausible mistake in the token recurrence, so that a test can show
+ * each of them is caught by the pins: 1 readout before the token's write,
+ * 2 no 1/sqrt(head_dim), 3 the state read transposed, 4 the gate applied after
+ * the retrieval, 5 the delta's sign flipped, 6 beta dropped from the delta.
  */
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -101,6 +110,18 @@ static double softplus(double x)
     return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
 }
 
+/* out_t = scale * M q_t for one (seq, head) and token t. */
+static void readout(const double *M, const double *qt, double *out, double scale, long s,
+                    long t, long h, long T, long H, long d)
+{
+    for (long i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (long j = 0; j < d; ++j)
+            acc += M[i * d + j] * qt[j];
+        out[idx_tok(s, t, h, i, T, H, d)] = scale * acc;
+    }
+}
+
 /* Token-sequential recurrence for one (seq, head).  M is d*d doubles, u is 3*d
  * doubles of scratch. */
 static void recur_one(const float *q, const float *k, const float *v,
@@ -108,7 +129,7 @@ static void recur_one(const float *q, const float *k, const float *v,
                       double *M, double *u, long s, long h, long T, long H,
                       long d, int flags)
 {
-    const double scale = 1.0 / sqrt((double)d);
+    const double scale = ORACLE_MUTANT == 2 ? 1.0 : 1.0 / sqrt((double)d);
     double *kt = u + d, *qt = u + 2 * d;
     for (long t = 0; t < T; ++t) {
         for (long j = 0; j < d; ++j) {
@@ -128,25 +149,31 @@ static void recur_one(const float *q, const float *k, const float *v,
         }
         const double alpha = exp(gt);
 
-        for (long i = 0; i < d * d; ++i)
-            M[i] *= alpha;
+        if (ORACLE_MUTANT != 4)
+            for (long i = 0; i < d * d; ++i)
+                M[i] *= alpha;
         for (long i = 0; i < d; ++i) {
             double acc = 0.0;
             for (long j = 0; j < d; ++j)
-                acc += M[i * d + j] * kt[j];
+                acc += (ORACLE_MUTANT == 3 ? M[j * d + i] : M[i * d + j]) * kt[j];
             u[i] = acc;
         }
+        if (ORACLE_MUTANT == 4)
+            for (long i = 0; i < d * d; ++i)
+                M[i] *= alpha;
+        if (ORACLE_MUTANT == 1)
+            readout(M, qt, out, scale, s, t, h, T, H, d);
         for (long i = 0; i < d; ++i) {
-            const double delta = b * ((double)vt[i] - u[i]);
+            double delta = b * ((double)vt[i] - u[i]);
+            if (ORACLE_MUTANT == 5)
+                delta = -delta;
+            if (ORACLE_MUTANT == 6)
+                delta = (double)vt[i] - u[i];
             for (long j = 0; j < d; ++j)
                 M[i * d + j] += delta * kt[j];
         }
-        for (long i = 0; i < d; ++i) {
-            double acc = 0.0;
-            for (long j = 0; j < d; ++j)
-                acc += M[i * d + j] * qt[j];
-            out[idx_tok(s, t, h, i, T, H, d)] = scale * acc;
-        }
+        if (ORACLE_MUTANT != 1)
+            readout(M, qt, out, scale, s, t, h, T, H, d);
     }
 }
 
