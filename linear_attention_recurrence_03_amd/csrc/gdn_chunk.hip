@@ -1440,6 +1440,70 @@ __device__ __forceinline__ void producer_loop(const ScanPtrs &pt, unsigned char 
     }
 }
 
+// ---- phase timestamps (trace builds only) ----------------------------------------
+// Off by default.  Built with -DGDN_PHASE_TRACE, the first kTraceGroups workgroups
+// of a chunk-to-chunk pass record the shader clock (s_memtime) at fixed points of
+// every chunk step into a device array that gdn_phase_trace_read (lag) or
+// gdn_scan_trace_read (per-tile) copies out
+// (linear_attention_recurrence_03_amd/phase_trace.py prints per-role statistics):
+//   the lag pass (g_phase_trace), for waves C, G, U, O and each phase: after the
+//   barrier that opens it (slot 0), once the wave's operands have landed (slot 1;
+//   the wave then waits for them explicitly) and before the barrier that closes it
+//   (slot 2);
+//   the per-tile pass (g_scan_trace, bf16 rows), for waves X_0, U_0, O_0 and each
+//   chunk: arriving at and leaving barrier A (slots 0, 1), arriving at and leaving
+//   barrier B (slots 2, 3).
+#ifdef GDN_PHASE_TRACE
+constexpr int kTraceGroups = 8, kTracePhases = 1024;
+__device__ uint64_t g_phase_trace[kTraceGroups][4][kTracePhases][3];
+__device__ uint64_t g_scan_trace[kTraceGroups][4][kTracePhases][4];
+#endif
+
+struct LagTrace {
+    int wg, wave;
+    __device__ __forceinline__ void mark(int t, int slot, int lane) const
+    {
+#ifdef GDN_PHASE_TRACE
+        const int p = t + 1;   // phases -1 .. n_chunks at 0 ..
+        if (wg < kTraceGroups && lane == 0 && p < kTracePhases)
+            g_phase_trace[wg][wave][p][slot] = __builtin_amdgcn_s_memtime();
+#else
+        (void)t;
+        (void)slot;
+        (void)lane;
+#endif
+    }
+    // operands landed: an explicit wait only when tracing (the compiler places its
+    // own waits otherwise).  The opening stamp's store, issued last, may stay in
+    // flight: its acknowledgement is not what is measured.
+    __device__ __forceinline__ void landed(int t, int lane) const
+    {
+#ifdef GDN_PHASE_TRACE
+        wait_vmem_le<1>();
+        mark(t, 1, lane);
+#else
+        (void)t;
+        (void)lane;
+#endif
+    }
+};
+
+struct ScanTrace {
+    int64_t wg;
+    int role;      // 0 X, 1 U, 2 O; waves of value tile 0 only
+    __device__ __forceinline__ void mark(int n, int slot, int lane) const
+    {
+#ifdef GDN_PHASE_TRACE
+        if (wg < kTraceGroups && role >= 0 && lane == 0 && n < kTracePhases)
+            g_scan_trace[wg][role][n][slot] = __builtin_amdgcn_s_memtime();
+#else
+        (void)n;
+        (void)slot;
+        (void)lane;
+#endif
+    }
+};
+
 enum { kRoleX = 0, kRoleU = 1, kRoleO = 2, kRoleProd = 3 };
 
 // Wave order: X_0.., U_0.., then O and the producers arranged so that, with
@@ -1523,15 +1587,20 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
         return;
     }
 
+    const ScanTrace tr{b, (vt == 0 && role != kRoleProd && PIPE) ? role : -1};
     if (role == kRoleX) {
         XOps<D, BF16> ops;
         if constexpr (PIPE) lds_barrier();  // B_{-1}
         for (int n = 0; n < nc; ++n) {
             if constexpr (!PIPE) lds_barrier();  // L_n
             x_load<D, BF16, VT>(ops, kt_slot(n), vt, lane);
+            tr.mark(n, 0, lane);
             lds_barrier();  // A_n
+            tr.mark(n, 1, lane);
             x_step<D, BF16, VT>(ops, kt_slot(n), smem, vt, lane);
+            tr.mark(n, 2, lane);
             lds_barrier();  // B_n
+            tr.mark(n, 3, lane);
         }
     } else if (role == kRoleU) {
         // Mt[t][j] = M[v0 + 16 vt + lane%16][16 t + 4 (lane/16) + j]
@@ -1552,11 +1621,15 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
         if constexpr (PIPE) lds_barrier();  // B_{-1}
         for (int n = 0; n < nc; ++n) {
             if constexpr (!PIPE) lds_barrier();  // L_n
+            tr.mark(n, 0, lane);
             lds_barrier();  // A_n
+            tr.mark(n, 1, lane);
             u_load<D, BF16, VT>(akt, eC, kt_slot(n), lane);
 #pragma unroll
             for (int t = 0; t < D / 16; ++t) Mt[t] *= eC;
+            tr.mark(n, 2, lane);
             lds_barrier();  // B_n
+            tr.mark(n, 3, lane);
             u_step<D, BF16, VT>(Mt, akt, smem, vt, lane);
         }
 #pragma unroll
@@ -1571,10 +1644,14 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
         if constexpr (PIPE) lds_barrier();  // B_{-1}
         for (int n = 0; n < nc; ++n) {
             if constexpr (!PIPE) lds_barrier();  // L_n
+            tr.mark(n, 0, lane);
             lds_barrier();  // A_n
+            tr.mark(n, 1, lane);
             o_load<D, BF16, VT>(ops, kt_slot(n), qp_slot(n), eg_row, lane);
             o_xq<D, BF16, VT>(ops, qp_slot(n), smem, vt, lane, acc);
+            tr.mark(n, 2, lane);
             lds_barrier();  // B_n
+            tr.mark(n, 3, lane);
             o_finish<D, BF16, VT>(ops, smem, vt, lane, acc, obase + int64_t(n) * C * hd, hd,
                                   nv_of(n));
         }
@@ -1957,47 +2034,6 @@ struct LagScan {
     static_assert(C * RK % 1024 == 0 && C * RV % 1024 == 0, "DMA blocks");
     static_assert(NBK + 2 * (NBV + NBG) < 64, "vmcnt range");
     static_assert(WsLag::kBytes - WsLag::kGates == 2048, "gates block");
-};
-
-// Phase timestamps, off by default.  Built with -DGDN_PHASE_TRACE, the first
-// kTraceGroups workgroups of the lag scan record for each wave and phase the shader
-// clock (s_memtime) after the barrier that opens the phase (slot 0), once the wave's
-// operands for the phase have landed (slot 1; the wave then waits for them
-// explicitly) and before the barrier that closes it (slot 2), into a device array
-// that gdn_phase_trace_read copies out (linear_attention_recurrence_03_amd/
-// phase_trace.py prints the per-role statistics).
-#ifdef GDN_PHASE_TRACE
-constexpr int kTraceGroups = 8, kTracePhases = 1024;
-__device__ uint64_t g_phase_trace[kTraceGroups][4][kTracePhases][3];
-#endif
-
-struct LagTrace {
-    int wg, wave;
-    __device__ __forceinline__ void mark(int t, int slot, int lane) const
-    {
-#ifdef GDN_PHASE_TRACE
-        const int p = t + 1;   // phases -1 .. n_chunks at 0 ..
-        if (wg < kTraceGroups && lane == 0 && p < kTracePhases)
-            g_phase_trace[wg][wave][p][slot] = __builtin_amdgcn_s_memtime();
-#else
-        (void)t;
-        (void)slot;
-        (void)lane;
-#endif
-    }
-    // operands landed: an explicit wait only when tracing (the compiler places its
-    // own waits otherwise).  The opening stamp's store, issued last, may stay in
-    // flight: its acknowledgement is not what is measured.
-    __device__ __forceinline__ void landed(int t, int lane) const
-    {
-#ifdef GDN_PHASE_TRACE
-        wait_vmem_le<1>();
-        mark(t, 1, lane);
-#else
-        (void)t;
-        (void)lane;
-#endif
-    }
 };
 
 struct LagPtrs {
@@ -2654,12 +2690,20 @@ size_t chunk_workspace_bytes(int bf16, int lag, int64_t n_seqs, int64_t n_tokens
 }
 
 #ifdef GDN_PHASE_TRACE
-// Copies the phase timestamps of the last lag scan out (trace builds only; not part
-// of the installed interface).
+// Copy the timestamps of the last lag pass, or of the last per-tile pass, out (trace
+// builds only; not part of the installed interface).
 extern "C" int gdn_phase_trace_read(void *host, size_t bytes)
 {
     if (bytes > sizeof(g_phase_trace)) bytes = sizeof(g_phase_trace);
     return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_trace), bytes, 0, hipMemcpyDeviceToHost) ==
+                   hipSuccess
+               ? 0
+               : -1;
+}
+extern "C" int gdn_scan_trace_read(void *host, size_t bytes)
+{
+    if (bytes > sizeof(g_scan_trace)) bytes = sizeof(g_scan_trace);
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_scan_trace), bytes, 0, hipMemcpyDeviceToHost) ==
                    hipSuccess
                ? 0
                : -1;

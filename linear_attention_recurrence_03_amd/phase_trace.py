@@ -1,22 +1,31 @@
-"""Per-wave phase timing of the two-chunk-lag scan, from the trace build.
+"""Per-wave timing of the chunk-to-chunk passes, from the trace build.
 
 The trace build (``python -m linear_attention_recurrence_03_amd.build --trace``,
-which writes libgdn_trace.so next to libgdn.so) has the lag scan's first eight
-workgroups record, for each of their four waves (C: the chain, G: E one chunk
-ahead, U: the state pass, O: the output) and each phase, the shader clock after
-the barrier that opens the phase, once the wave's operands for the phase have
-landed, and before the barrier that closes it.  This script runs the prefill of
-1 x 4096 tokens x 32 heads, d=128, bf16 with algo "chunked_lag" (four rotating
-input copies, as the benchmark does) on that build and prints, per role, the median and 10th/90th
-percentile over the steady phases of:
+which writes libgdn_trace.so next to libgdn.so) has the first eight workgroups of
+a chunk-to-chunk pass record the shader clock (s_memtime ticks) at fixed points of
+every chunk step.  This script runs the prefill of 1 x 4096 tokens x 32 heads,
+d=128, bf16 (four rotating input copies, as the benchmark does) on that build and
+prints medians and 10th/90th percentiles over the steady chunks.
+
+``--pass scan`` (default): the per-tile pass that AUTO runs for this shape, waves
+X (K M^T, E, Delta = T E), U (the state update) and O (the output) of value tile
+0, two workgroup barriers (A, B) per chunk:
+
+  step        from leaving barrier A to leaving it again (X's stamps)
+  A->B, B->A  work of each wave between leaving one barrier and arriving at the next
+  wait A/B    arriving at a barrier to leaving it
+  last at A/B how often each wave is the last of the three to arrive
+
+``--pass lag``: the two-chunk-lag pass (algo "chunked_lag"), waves C, G, U, O and
+one barrier per phase:
 
   work        closing stamp - opening stamp (everything the wave does in a phase)
   operands    landed stamp - opening stamp (waiting for the phase's operands)
   at barrier  next opening stamp - closing stamp (waiting for the other waves)
 
-and the phase length (opening stamp to the next).  Cycles are s_memtime ticks.
+and the phase length (opening stamp to the next).
 
-Usage: python -m linear_attention_recurrence_03_amd.phase_trace [--json OUT]
+Usage: python -m linear_attention_recurrence_03_amd.phase_trace [--pass scan|lag] [--json OUT]
 """
 import argparse
 import ctypes
@@ -26,6 +35,7 @@ import statistics
 import sys
 
 ROLES = ("C", "G", "U", "O")
+SCAN_ROLES = ("X", "U", "O")
 GROUPS, PHASES = 8, 1024
 
 
@@ -60,8 +70,43 @@ def summarize(raw, n_phases, skip=3):
     return res
 
 
+def summarize_scan(raw, n_chunks, skip=3):
+    """raw: uint64 array [GROUPS][4][PHASES][4] (arrive A, leave A, arrive B, leave B
+    per role and chunk).  Statistics over chunks skip .. n_chunks - skip - 2."""
+    out = {"step": []}
+    for r in SCAN_ROLES:
+        out[r] = {"A->B": [], "B->A": [], "wait A": [], "wait B": []}
+    last = {"A": {r: 0 for r in SCAN_ROLES}, "B": {r: 0 for r in SCAN_ROLES}}
+    release = {"A": [], "B": []}
+    for wg in range(GROUPS):
+        for n in range(skip, n_chunks - skip - 1):
+            st = [[int(x) for x in raw[wg][w][n]] for w in range(3)]
+            nx = [[int(x) for x in raw[wg][w][n + 1]] for w in range(3)]
+            out["step"].append(nx[0][1] - st[0][1])
+            for w, r in enumerate(SCAN_ROLES):
+                out[r]["A->B"].append(st[w][2] - st[w][1])
+                out[r]["B->A"].append(nx[w][0] - st[w][3])
+                out[r]["wait A"].append(st[w][1] - st[w][0])
+                out[r]["wait B"].append(st[w][3] - st[w][2])
+            for bar, ia, il in (("A", 0, 1), ("B", 2, 3)):
+                arrive = [st[w][ia] for w in range(3)]
+                last[bar][SCAN_ROLES[arrive.index(max(arrive))]] += 1
+                release[bar].append(min(st[w][il] for w in range(3)) - max(arrive))
+
+    def stat(xs):
+        return {"median": statistics.median(xs), "p10": _pct(xs, 0.1), "p90": _pct(xs, 0.9)} \
+            if xs else None
+    res = {"step": stat(out["step"]), "last_at": last,
+           "release_after_last_traced_arrival": {k: stat(v) for k, v in release.items()}}
+    for r in SCAN_ROLES:
+        res[r] = {k: stat(v) for k, v in out[r].items()}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--pass", dest="which", choices=("scan", "lag"), default="scan",
+                    help="which chunk-to-chunk pass to trace")
     ap.add_argument("--json", help="also write the statistics to this file")
     ap.add_argument("--lib", help="trace build to load (default: libgdn_trace.so here)")
     args = ap.parse_args()
@@ -78,8 +123,10 @@ def main():
     from linear_attention_recurrence_03_amd import inputs
 
     lib = gdn._lib()
-    lib.gdn_phase_trace_read.restype = ctypes.c_int
-    lib.gdn_phase_trace_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    read = lib.gdn_scan_trace_read if args.which == "scan" else lib.gdn_phase_trace_read
+    read.restype = ctypes.c_int
+    read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    algo = "chunked" if args.which == "scan" else "chunked_lag"
     wl = inputs.WORKLOADS[4]
     x = inputs.make(wl)
     S, T, H, D = wl.shape()
@@ -90,9 +137,9 @@ def main():
         sets.append(d)
     out = torch.empty_like(sets[0]["v"])
     fin = torch.empty((S, H, D, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(gdn.workspace_size("bf16", S, T, H, D, "chunked_lag"), dtype=torch.uint8,
+    ws = torch.empty(gdn.workspace_size("bf16", S, T, H, D, algo), dtype=torch.uint8,
                      device="cuda")
-    calls = [gdn.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], None, algo="chunked_lag",
+    calls = [gdn.prepare(d["q"], d["k"], d["v"], d["g"], d["beta"], None, algo=algo,
                          out=out, state_out=fin, workspace=ws) for d in sets]
     for i in range(12):
         calls[i % 4]()
@@ -102,21 +149,41 @@ def main():
     calls[1]()
     b.record()
     torch.cuda.synchronize()
-    raw = np.zeros((GROUPS, 4, PHASES, 3), dtype=np.uint64)
-    assert lib.gdn_phase_trace_read(raw.ctypes.data, raw.nbytes) == 0
-    n_phases = (T + 63) // 64 + 2
-    res = summarize(raw, n_phases)
-    res["call_us"] = a.elapsed_time(b) * 1e3
-    res["n_phases"] = n_phases
-    print("traced call (prep + lag scan): %.1f us, %d phases" % (res["call_us"], n_phases))
-    ph = res["phase"]
-    print("phase length: median %d, p10 %d, p90 %d cycles" % (ph["median"], ph["p10"], ph["p90"]))
-    print("%-4s %-11s %8s %8s %8s" % ("wave", "", "median", "p10", "p90"))
-    for r in ROLES:
-        for k in ("work", "operands", "at_barrier"):
-            v = res[r][k]
-            if v:
-                print("%-4s %-11s %8d %8d %8d" % (r, k, v["median"], v["p10"], v["p90"]))
+    n_chunks = (T + 63) // 64
+    if args.which == "scan":
+        raw = np.zeros((GROUPS, 4, PHASES, 4), dtype=np.uint64)
+        assert read(raw.ctypes.data, raw.nbytes) == 0
+        res = summarize_scan(raw, n_chunks)
+        res["call_us"] = a.elapsed_time(b) * 1e3
+        res["n_chunks"] = n_chunks
+        print("traced call (prep + per-tile pass): %.1f us, %d chunks" % (res["call_us"], n_chunks))
+        st = res["step"]
+        print("chunk step: median %d, p10 %d, p90 %d cycles" % (st["median"], st["p10"], st["p90"]))
+        print("%-4s %-8s %8s %8s %8s" % ("wave", "", "median", "p10", "p90"))
+        for r in SCAN_ROLES:
+            for k in ("A->B", "wait B", "B->A", "wait A"):
+                v = res[r][k]
+                print("%-4s %-8s %8d %8d %8d" % (r, k, v["median"], v["p10"], v["p90"]))
+        for bar in ("A", "B"):
+            rel = res["release_after_last_traced_arrival"][bar]
+            print("barrier %s: last traced arrival %s; release after it: median %d cycles" % (
+                bar, ", ".join("%s %d" % kv for kv in res["last_at"][bar].items()), rel["median"]))
+    else:
+        raw = np.zeros((GROUPS, 4, PHASES, 3), dtype=np.uint64)
+        assert read(raw.ctypes.data, raw.nbytes) == 0
+        n_phases = n_chunks + 2
+        res = summarize(raw, n_phases)
+        res["call_us"] = a.elapsed_time(b) * 1e3
+        res["n_phases"] = n_phases
+        print("traced call (prep + lag scan): %.1f us, %d phases" % (res["call_us"], n_phases))
+        ph = res["phase"]
+        print("phase length: median %d, p10 %d, p90 %d cycles" % (ph["median"], ph["p10"], ph["p90"]))
+        print("%-4s %-11s %8s %8s %8s" % ("wave", "", "median", "p10", "p90"))
+        for r in ROLES:
+            for k in ("work", "operands", "at_barrier"):
+                v = res[r][k]
+                if v:
+                    print("%-4s %-11s %8d %8d %8d" % (r, k, v["median"], v["p10"], v["p90"]))
     if args.json:
         with open(args.json, "w") as f:
             json.dump(res, f, indent=1)

@@ -1,0 +1,39 @@
+"""Host logic of the phase-trace summaries (no GPU): known stamps give known
+statistics."""
+import numpy as np
+
+from linear_attention_recurrence_03_amd import phase_trace as pt
+
+
+def test_scan_summary_of_synthetic_stamps():
+    raw = np.zeros((pt.GROUPS, 4, pt.PHASES, 4), dtype=np.uint64)
+    n_chunks = 20
+    for wg in range(pt.GROUPS):
+        for n in range(n_chunks):
+            t0 = 10_000 + 2_000 * n                # every wave leaves A at t0
+            # X arrives at B last (t0 + 1100), U at t0 + 300, O at t0 + 900; all leave
+            # B at t0 + 1200; they arrive at the next A at t0 + 1900, 1990, 1500
+            for w, (b_arr, a_next) in enumerate(((1100, 1900), (300, 1990), (900, 1500))):
+                raw[wg, w, n] = [t0 - (2000 - a_next), t0, t0 + b_arr, t0 + 1200]
+    res = pt.summarize_scan(raw, n_chunks)
+    assert res["step"]["median"] == 2000
+    assert res["X"]["A->B"]["median"] == 1100 and res["X"]["wait B"]["median"] == 100
+    assert res["U"]["B->A"]["median"] == 790 and res["O"]["wait A"]["median"] == 500
+    assert res["last_at"]["B"]["X"] == res["last_at"]["B"]["X"] > 0
+    assert res["last_at"]["B"]["U"] == 0 and res["last_at"]["A"]["U"] > 0
+    assert res["release_after_last_traced_arrival"]["B"]["median"] == 100
+    assert res["release_after_last_traced_arrival"]["A"]["median"] == 10
+
+
+def test_lag_summary_of_synthetic_stamps():
+    raw = np.zeros((pt.GROUPS, 4, pt.PHASES, 3), dtype=np.uint64)
+    n_phases = 20
+    for wg in range(pt.GROUPS):
+        for p in range(n_phases):
+            t0 = 5_000 + 4_000 * p
+            for w in range(4):
+                raw[wg, w, p] = [t0, t0 + 100 * (w + 1), t0 + 1000 * (w + 1)]
+    res = pt.summarize(raw, n_phases)
+    assert res["phase"]["median"] == 4000
+    assert res["C"]["work"]["median"] == 1000 and res["O"]["work"]["median"] == 4000
+    assert res["G"]["operands"]["median"] == 200 and res["U"]["at_barrier"]["median"] == 1000
