@@ -279,6 +279,47 @@ def bench_dispatch_floor(torch, n=24, reps=30):
     return statistics.median(us)
 
 
+def bench_state_copy_floor(gdn, torch, wl, reps=30, n_layers=24):
+    """Device time per layer of 24 zero-token gdn_forward calls on the single-token
+    decode's states (each launches the library's plain state copy: the same 2 MB
+    read and written, no token arithmetic), replayed from one HIP graph after the
+    same 1 GiB scrub as the decode timing: what reading and writing a layer's state
+    costs on this machine, between the dispatch floor and the decode."""
+    from linear_attention_recurrence_03_amd import inputs
+    S, _, H, D = wl.shape()
+    states = [torch.from_numpy(inputs.make(wl, layer=l)["state"]).cuda() for l in range(n_layers)]
+    outs = [torch.empty_like(st) for st in states]
+    empty = torch.empty((S, 0, H, D), dtype=torch.float32, device="cuda")
+    gates = torch.empty((S, 0, H), dtype=torch.float32, device="cuda")
+    calls = [gdn.prepare(empty, empty, empty, gates, gates, st, out=empty, state_out=o)
+             for st, o in zip(states, outs)]
+    scrub = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in calls:
+            c(side)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream()
+        for c in calls:
+            c(cap)
+    us = []
+    for _ in range(reps):
+        scrub.fill_(1.0)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us.append(a.elapsed_time(b) * 1e3 / n_layers)
+    assert all(torch.equal(o, st) for o, st in zip(outs, states))
+    return statistics.median(us)
+
+
 def bench_attn(gdn, torch, n_calls=40, reps=7):
     """Decode attention, one query per head: the card's shape (16 query heads over 4
     key/value heads, head_dim 256, 141 and 512 cached positions; warm, as a decode
@@ -665,6 +706,7 @@ def main():
             "hbm_frac": round(b2 / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "counters": load_traffic_record("decode_1tok"),
             "dispatch_floor_us": round(bench_dispatch_floor(torch), 3),
+            "state_copy_us": round(bench_state_copy_floor(gdn, torch, wl2), 3),
             "host_path": "prepared call (arguments validated once, C call re-issued)",
             "workload": "1 seq x 1 token x 32 heads x d128 fp32, 24 sequential layer calls "
                         "replayed from one HIP graph, 1 GiB scrub before each replay"}

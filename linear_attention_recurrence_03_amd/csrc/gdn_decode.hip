@@ -277,14 +277,16 @@ hipError_t launch_rec_t(const Problem &p, hipStream_t stream)
     }
 }
 
-__global__ __launch_bounds__(256) void state_copy_kernel(const float *__restrict__ src,
-                                                         float *__restrict__ dst,
-                                                         int64_t count)
+// Copies (or zeroes) count4 float4s: the state is a whole number of 16-byte
+// groups (head_dim^2 floats per head) at 16-byte aligned addresses.
+__global__ __launch_bounds__(256) void state_copy_kernel(const float4 *__restrict__ src,
+                                                         float4 *__restrict__ dst,
+                                                         int64_t count4)
 {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count4;
          i += stride)
-        dst[i] = src ? src[i] : 0.f;
+        dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 }  // namespace
@@ -298,10 +300,12 @@ hipError_t launch_state_copy(const float *state_in, float *state_out, int64_t co
                              hipStream_t stream)
 {
     if (count <= 0) return hipSuccess;
-    int64_t blocks = (count + 255) / 256;
+    const int64_t count4 = count / 4;   // count = n_seqs * n_heads * head_dim^2, head_dim % 32 == 0
+    int64_t blocks = (count4 + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(state_copy_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                       stream, state_in, state_out, count);
+                       stream, reinterpret_cast<const float4 *>(state_in),
+                       reinterpret_cast<float4 *>(state_out), count4);
     return hipGetLastError();
 }
 
