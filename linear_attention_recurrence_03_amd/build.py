@@ -16,8 +16,8 @@ LIB = os.path.join(PKG, "libgdn.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_chunk.hip", "gdn_attn.hip",
-           "gdn_noalloc.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_chunk.hip", "gdn_chunk_head.hip",
+           "gdn_chunk_lag.hip", "gdn_attn.hip", "gdn_noalloc.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 # Device code: gfx950 only; packed-fp32 instruction selection disabled.

@@ -38,275 +38,16 @@
 //                         transposing LDS reads); the next chunk's loads
 //                         are in flight while the current one is computed.
 //   chunk_head_kernel  -- (bf16, from one (seq, head) per compute unit on) one
-//                         workgroup per (seq, head) carrying all its value rows.
-//   chunk_lag_kernel   -- (bf16, on request) the two-chunk-lag form of the pass.
-//
-// MFMA fragments.  An A operand (16 rows x 32 k) gives lane l row l%16 and eight
-// k values; a B operand (32 k x 16 cols) gives lane l column l%16 and eight k
-// values; the hardware pairs element j of lane group g = l/16 in A with the same
-// element of B.  The accumulator gives lane l column l%16 and rows 4g..4g+3.
-// Two stacked accumulator tiles therefore form a B operand directly if element
-// j of group g stands for row 4g+j (j < 4) or 16+4g+j-4 (j >= 4) of the 32; every
-// A operand here is loaded with that same k order, so no data moves between
-// lanes when a product feeds the next one.
-#include <atomic>
-
-#include "gdn_common.h"
-#include "gdn_internal.h"
+//                         workgroup per (seq, head) carrying all its value rows
+//                         (gdn_chunk_head.hip).
+//   chunk_lag_kernel   -- (bf16, on request) the two-chunk-lag form of the pass
+//                         (gdn_chunk_lag.hip).
+// This file holds the prep, the per-tile pass and the choice between the passes;
+// the MFMA fragment conventions and helpers they share are in gdn_chunk_common.h.
+#include "gdn_chunk_common.h"
 
 namespace gdn {
 namespace {
-
-constexpr int C = kChunk;
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-template <bool BF16>
-struct Elem;
-template <>
-struct Elem<true> {
-    using T = uint16_t;
-};
-template <>
-struct Elem<false> {
-    using T = float;
-};
-
-template <class T>
-__device__ __forceinline__ T from_f(float x);
-template <>
-__device__ __forceinline__ uint16_t from_f<uint16_t>(float x)
-{
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-}
-template <>
-__device__ __forceinline__ float from_f<float>(float x)
-{
-    return x;
-}
-
-// ---- fragments ---------------------------------------------------------------
-
-template <bool BF16>
-struct Frag;
-template <>
-struct Frag<true> {
-    uint4 u;  // eight bf16
-};
-template <>
-struct Frag<false> {
-    float v[8];
-};
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-
-// Two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack2(float a, float b)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf16x2_t));
-}
-
-// k order of a fragment: element j of lane group g is k = 4g+j (j<4), 16+4g+j-4.
-// Row `row` of a row-major LDS matrix with leading dimension ld, k offset k0.
-template <bool BF16>
-__device__ __forceinline__ Frag<BF16> lds_frag(const typename Elem<BF16>::T *base, int ld, int row,
-                                               int k0, int g)
-{
-    Frag<BF16> f;
-    const typename Elem<BF16>::T *p = base + row * ld + k0 + 4 * g;
-    if constexpr (BF16) {
-        const uint2 lo = *reinterpret_cast<const uint2 *>(p);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(p + 16);
-        f.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    } else {
-        const float4 lo = *reinterpret_cast<const float4 *>(p);
-        const float4 hi = *reinterpret_cast<const float4 *>(p + 16);
-        f.v[0] = lo.x; f.v[1] = lo.y; f.v[2] = lo.z; f.v[3] = lo.w;
-        f.v[4] = hi.x; f.v[5] = hi.y; f.v[6] = hi.z; f.v[7] = hi.w;
-    }
-    return f;
-}
-
-typedef short short4_t __attribute__((ext_vector_type(4)));
-
-// A operand whose rows are the key channels of a token-major LDS matrix: lane
-// (g, i) gets base[t0 + k(g, j)][key0 + i] for the eight j, i.e. eight tokens of
-// one key.  For bf16 this is two ds_read_b64_tr_b16: inside each group of 16
-// lanes, lane i receives element j = (i mod 4)-th 16-bit value fetched by lane
-// 4j + i/4, so lane p of group g fetches row t0 + 4g + p/4 (then 16 rows lower),
-// keys key0 + 4 (p mod 4) .. +3.
-template <bool BF16>
-__device__ __forceinline__ Frag<BF16> lds_frag_tr(const typename Elem<BF16>::T *base, int ld,
-                                                  int t0, int key0, int lane)
-{
-    Frag<BF16> f;
-    const int g = lane >> 4, p = lane & 15;
-    if constexpr (BF16) {
-        const uint16_t *a1 = base + (t0 + 4 * g + (p >> 2)) * ld + key0 + 4 * (p & 3);
-        const uint16_t *a2 = a1 + 16 * ld;
-        typedef __attribute__((address_space(3))) short4_t lds_short4;
-        const short4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a1));
-        const short4_t r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a2));
-        const uint2 u1 = __builtin_bit_cast(uint2, r1);
-        const uint2 u2 = __builtin_bit_cast(uint2, r2);
-        f.u = make_uint4(u1.x, u1.y, u2.x, u2.y);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f.v[j] = base[(t0 + 4 * g + j) * ld + key0 + p];
-            f.v[4 + j] = base[(t0 + 16 + 4 * g + j) * ld + key0 + p];
-        }
-    }
-    return f;
-}
-
-// B operand from two stacked accumulator tiles (rows 0-15 and 16-31 of the k range).
-template <bool BF16>
-__device__ __forceinline__ Frag<BF16> acc_frag(const floatx4 &c0, const floatx4 &c1)
-{
-    Frag<BF16> f;
-    if constexpr (BF16) {
-        f.u = make_uint4(pack2(c0[0], c0[1]), pack2(c0[2], c0[3]), pack2(c1[0], c1[1]),
-                         pack2(c1[2], c1[3]));
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f.v[j] = c0[j];
-            f.v[4 + j] = c1[j];
-        }
-    }
-    return f;
-}
-
-__device__ __forceinline__ floatx4 mma(const Frag<true> &a, const Frag<true> &b, floatx4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.u),
-                                                   __builtin_bit_cast(bf16x8_t, b.u), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ floatx4 mma(const Frag<false> &a, const Frag<false> &b, floatx4 c)
-{
-#pragma unroll
-    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
-    return c;
-}
-
-// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
-// outstanding global load and store of the wave, which would stall on the next
-// chunk's prefetch and on output stores that nothing in the workgroup reads.
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// ---- fragment blocks -------------------------------------------------------------
-// A fragment block is the image of one 16-row x 32-k A operand, laid out so that
-// each lane's fragment is one contiguous unit (its eight elements: 16 bytes for
-// bf16, 32 for fp32) and a wave's read of the whole operand touches every LDS
-// bank equally: the unit of row r for lane group g sits at position
-// 4 r + (g ^ (r >> 2)).  Inside a unit the elements follow the fragment k order
-// (4g+j for j < 4, 16+4g+j-4 for j >= 4), so the block multiplies B operands
-// built from accumulator tiles.  The lower-triangular T and P are stored as the
-// six blocks (row tile tt, k half h) with 32 h <= 16 tt + 15, in the order
-// (0,0) (1,0) (2,0) (2,1) (3,0) (3,1); the other two are zero.
-template <bool BF16>
-constexpr int kFragBytes = BF16 ? 16 : 32;
-template <bool BF16>
-constexpr int kBlkBytes = 64 * kFragBytes<BF16>;
-
-__device__ __forceinline__ int blk_unit(int r, int g) { return 4 * r + (g ^ (r >> 2)); }
-
-template <bool BF16>
-__device__ __forceinline__ Frag<BF16> frag_blk(const unsigned char *blk, int lane)
-{
-    return *reinterpret_cast<const Frag<BF16> *>(blk + kFragBytes<BF16> * blk_unit(lane & 15, lane >> 4));
-}
-
-// ---- workspace layout, per (seq, head, chunk) ----------------------------------
-//   T     six fragment blocks (elements like q/k/v: fp32 or bf16)
-//   P     six fragment blocks, holding P / sqrt(d)
-//   gates [4][C] fp32: beta_r, e^{gam_r}, e^{gam_last - gam_r}, then e^{gam_last}
-//                      repeated C times
-// Rows past the end of a partial last chunk carry beta = e^gam = 0, so they add
-// nothing to the state or to valid outputs.
-template <bool BF16>
-struct WsLayout {
-    static constexpr int64_t kT = 0;
-    static constexpr int64_t kP = 6 * kBlkBytes<BF16>;
-    static constexpr int64_t kGates = 2 * kP;
-    // gates: four rows of C floats (1 KiB); five with normalised q/k rows, which
-    // then take a 2 KiB area
-    static constexpr int64_t kBytes = kGates + 4 * C * 4;
-    static constexpr int64_t kBytesNorm = kGates + 8 * C * 4;
-    static constexpr int64_t stride(int l2norm_qk) { return l2norm_qk ? kBytesNorm : kBytes; }
-};
-
-// Workspace of the two-chunk-lag path (bf16 rows), per (seq, head, chunk):
-//   T, P     six fragment blocks each, as above (P holds P / sqrt(d))
-//   R1, R2   eight fragment blocks each (row tile tt, k half h) at 2 tt + h: the full
-//            64 x 64 matrices R1 = -T diag(beta e^gam) K_n K_{n-1}^T and
-//            R2 = -e^{c_{n-1}} T diag(beta e^gam) K_n K_{n-2}^T (zero when the
-//            earlier chunk does not exist), bf16
-//   gates    [8][C] fp32 rows: beta; e^gam; e^{gam_last - gam}; e^{gam_last}
-//            repeated; e^gam for the output; rows 1 and 2 carry 1 / |k_r| and row 4
-//            carries 1 / |q_r| when the op normalises q and k
-struct WsLag {
-    static constexpr int kBlk = kBlkBytes<true>;
-    static constexpr int64_t kT = 0;
-    static constexpr int64_t kP = 6 * kBlk;
-    static constexpr int64_t kR1 = 12 * kBlk;
-    static constexpr int64_t kR2 = 20 * kBlk;
-    static constexpr int64_t kGates = 28 * kBlk;
-    static constexpr int64_t kBytes = kGates + 8 * C * 4;
-};
-
-// A operand from rows of a padded row-major LDS matrix: lane (g, r) gets row
-// row0 + r, k = k0 + 8g .. k0 + 8g + 7 (contiguous).
-template <bool BF16>
-__device__ __forceinline__ Frag<BF16> row_frag(const unsigned char *base, int stride, int row,
-                                               int k0, int g)
-{
-    return *reinterpret_cast<const Frag<BF16> *>(base + row * stride + (k0 + 8 * g) * (BF16 ? 2 : 4));
-}
-
-constexpr int kPrepThreads = 256;
-
-// LDS of the prep kernel (one workgroup per (seq, head, chunk)).  Region R holds
-// the chunk's K rows (16-byte padded) while the products are formed; after that
-// it is reused for T and A (as MFMA input type).  Q rows never pass through LDS:
-// the two waves that form Q K^T load their row tiles straight into MFMA operand
-// registers.
-template <int D, bool BF16>
-struct PrepSmem {
-    using E = typename Elem<BF16>::T;
-    static constexpr int ES = sizeof(E);
-    static constexpr int RK = D * ES + 16;               // K, Q row stride (bytes)
-    static constexpr int LDT = C + 16 / ES;              // T and A rows (elements)
-    static constexpr int LDD = 16;                       // transposed diagonal blocks (floats)
-    static constexpr int kMat = C * LDT * ES;            // one C x C matrix of E
-    static constexpr int kK = 0;                         // during the products
-    static constexpr int kT = 0, kAe = kMat;             // afterwards
-    static constexpr int kR = (C * RK > 2 * kMat) ? C * RK : 2 * kMat;
-    static constexpr int kD = kR;                        // 4 x [16][LDD] fp32
-    static constexpr int kG = kD + 4 * 16 * LDD * 4;     // gates
-    static constexpr int kN = kG + (4 * C + 4) * 4;      // 1/|k_r|, 1/|q_r| (normalised rows)
-    static constexpr int kBytes = kN + 2 * C * 4;
-    static constexpr int NBK = C * RK / 1024;            // DMA blocks of the K rows
-    // Workgroups per CU that 160 KiB of LDS allows, at most five; the kernel's
-    // register budget is set for that many (one wave per SIMD each).
-    static constexpr int kPerCU = (160 * 1024 / kBytes < 5) ? 160 * 1024 / kBytes : 5;
-    static_assert(C * RK % 1024 == 0 && kMat % 16 == 0 && kR % 16 == 0 && kPerCU >= 1, "layout");
-};
-
-// The output's factor 1/sqrt(d), applied where P is formed (and by the scan's
-// output wave to e^gam), so that the output needs no scaling of its own.
-template <int D>
-constexpr float kOutScale = D == 32 ? 0.17677669529663687f : D == 64 ? 0.125f
-                          : D == 96 ? 0.10206207261596575f : 0.08838834764831845f;
 
 // The products of one prep wave: the lower tiles of row tiles R0 and R1 of
 // K K^T (KK) or Q K^T, kept in registers across the barrier that frees the K
@@ -1048,65 +789,6 @@ __device__ __forceinline__ void issue_qp(const ScanPtrs &pt, unsigned char *slot
         dma16(i < F::NBK ? pt.q + tbk : wsc + W::kP, po.qp[(i - PART) / kProducers], slot + 1024 * i);
 }
 
-
-// Operand whose rows are columns c0 + (lane mod 16) of a row-major LDS matrix and
-// whose k values are rows t0 + {4g..4g+3}, t0 + 16 + {4g..4g+3} (eight rows of
-// one column).  bf16: two ds_read_b64_tr_b16; inside each group of 16 lanes
-// this instruction hands lane i the (i mod 4)-th 16-bit value fetched by lane
-// 4j + i/4 as its element j, so lane p fetches row t0 + 4g + p/4 (then 16 rows
-// lower), columns c0 + 4 (p mod 4) .. +3.
-template <bool BF16>
-__device__ __forceinline__ Frag<BF16> frag_cols(const unsigned char *base, int stride, int t0,
-                                                int c0, int lane)
-{
-    Frag<BF16> f;
-    const int g = lane >> 4, p = lane & 15;
-    if constexpr (BF16) {
-        const unsigned char *a1 = base + (t0 + 4 * g + (p >> 2)) * stride + (c0 + 4 * (p & 3)) * 2;
-        typedef __attribute__((address_space(3))) short4_t lds_short4;
-        const short4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a1));
-        const short4_t r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a1 + 16 * stride));
-        const uint2 u1 = __builtin_bit_cast(uint2, r1);
-        const uint2 u2 = __builtin_bit_cast(uint2, r2);
-        f.u = make_uint4(u1.x, u1.y, u2.x, u2.y);
-    } else {
-        const float *col = reinterpret_cast<const float *>(base + (c0 + p) * 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f.v[j] = *reinterpret_cast<const float *>(reinterpret_cast<const unsigned char *>(col) +
-                                                      (t0 + 4 * g + j) * stride);
-            f.v[4 + j] = *reinterpret_cast<const float *>(reinterpret_cast<const unsigned char *>(col) +
-                                                          (t0 + 16 + 4 * g + j) * stride);
-        }
-    }
-    return f;
-}
-
-// Values of one LDS column at four consecutive rows t..t+3 (accumulator layout
-// rows 4g+j of a tile): lane (g, i) gets base[t0 + 4g + j][c0 + i], j = 0..3.
-template <bool BF16>
-__device__ __forceinline__ floatx4 col4(const unsigned char *base, int stride, int t0, int c0,
-                                        int lane)
-{
-    const int g = lane >> 4, p = lane & 15;
-    floatx4 r;
-    if constexpr (BF16) {
-        // one transposing read: lane 4j + i/4 fetches row t0 + 4g + j, columns
-        // c0 + 4 (i/4) .. +3; lane i receives column c0 + i of the four rows
-        const unsigned char *a = base + (t0 + 4 * g + (p >> 2)) * stride + (c0 + 4 * (p & 3)) * 2;
-        typedef __attribute__((address_space(3))) short4_t lds_short4;
-        const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = bf16_to_f32(static_cast<uint16_t>(v[j]));
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            r[j] = *reinterpret_cast<const float *>(base + (t0 + 4 * g + j) * stride + (c0 + p) * 4);
-    }
-    return r;
-}
-
-
 // ---- wave roles ---------------------------------------------------------------
 
 // X operands of one chunk.  The bf16 path holds the K and T fragments in
@@ -1145,18 +827,6 @@ __device__ __forceinline__ void x_load(XOps<D, BF16> &o, const unsigned char *kt
         o.edec[tt] = floatx4{d4.x, d4.y, d4.z, d4.w};
         o.bv[tt] = bt * col4<BF16>(kt + F::kV, F::RV, 16 * tt, 16 * vt, lane);
     }
-}
-
-// Lower-triangular block matrix (six fragment blocks) times the 64-row B operand
-// given as two k halves: rows tt of the product.
-template <bool BF16>
-__device__ __forceinline__ void tri_mul(const Frag<BF16> (&a)[6], const Frag<BF16> &b0,
-                                        const Frag<BF16> &b1, floatx4 (&acc)[4])
-{
-    acc[0] = mma(a[0], b0, acc[0]);
-    acc[1] = mma(a[1], b0, acc[1]);
-    acc[2] = mma(a[3], b1, mma(a[2], b0, acc[2]));
-    acc[3] = mma(a[5], b1, mma(a[4], b0, acc[3]));
 }
 
 // X_vt, one chunk (between barriers A and B): X = K M^T from the published M^T
@@ -1440,53 +1110,12 @@ __device__ __forceinline__ void producer_loop(const ScanPtrs &pt, unsigned char 
     }
 }
 
-// ---- phase timestamps (trace builds only) ----------------------------------------
-// Off by default.  Built with -DGDN_PHASE_TRACE, the first kTraceGroups workgroups
-// of a chunk-to-chunk pass record the shader clock (s_memtime) at fixed points of
-// every chunk step into a device array that gdn_phase_trace_read (lag) or
-// gdn_scan_trace_read (per-tile) copies out
-// (linear_attention_recurrence_03_amd/phase_trace.py prints per-role statistics):
-//   the lag pass (g_phase_trace), for waves C, G, U, O and each phase: after the
-//   barrier that opens it (slot 0), once the wave's operands have landed (slot 1;
-//   the wave then waits for them explicitly) and before the barrier that closes it
-//   (slot 2);
-//   the per-tile pass (g_scan_trace, bf16 rows), for waves X_0, U_0, O_0 and each
-//   chunk: arriving at and leaving barrier A (slots 0, 1), arriving at and leaving
-//   barrier B (slots 2, 3).
+// Per-tile pass timestamps (trace builds only): for waves X_0, U_0, O_0 and each
+// chunk, arriving at and leaving barrier A (slots 0, 1), arriving at and leaving
+// barrier B (slots 2, 3); gdn_scan_trace_read copies them out.
 #ifdef GDN_PHASE_TRACE
-constexpr int kTraceGroups = 8, kTracePhases = 1024;
-__device__ uint64_t g_phase_trace[kTraceGroups][4][kTracePhases][3];
 __device__ uint64_t g_scan_trace[kTraceGroups][4][kTracePhases][4];
 #endif
-
-struct LagTrace {
-    int wg, wave;
-    __device__ __forceinline__ void mark(int t, int slot, int lane) const
-    {
-#ifdef GDN_PHASE_TRACE
-        const int p = t + 1;   // phases -1 .. n_chunks at 0 ..
-        if (wg < kTraceGroups && lane == 0 && p < kTracePhases)
-            g_phase_trace[wg][wave][p][slot] = __builtin_amdgcn_s_memtime();
-#else
-        (void)t;
-        (void)slot;
-        (void)lane;
-#endif
-    }
-    // operands landed: an explicit wait only when tracing (the compiler places its
-    // own waits otherwise).  The opening stamp's store, issued last, may stay in
-    // flight: its acknowledgement is not what is measured.
-    __device__ __forceinline__ void landed(int t, int lane) const
-    {
-#ifdef GDN_PHASE_TRACE
-        wait_vmem_le<1>();
-        mark(t, 1, lane);
-#else
-        (void)t;
-        (void)lane;
-#endif
-    }
-};
 
 struct ScanTrace {
     int64_t wg;
@@ -1658,856 +1287,6 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
     }
 }
 
-// ---- the whole-head scan (bf16 rows) ------------------------------------------------
-//
-// One workgroup carries every value row of one (seq, head) through its chunks, so
-// a chunk's shared operands (K, Q, T, P, gates) are brought into the compute unit
-// once for all value rows instead of once per row block.  D / 16 waves (two per
-// SIMD at D = 128) each own one value tile (16 rows) and do the whole chunk step
-// for it with no hand-off between waves:
-//   X = K M^T and (M Q^T) from the state's own accumulators, turned into bf16
-//   operands in registers (the state's key order is permuted so that two stacked
-//   accumulator tiles are a B operand with eight consecutive keys per lane);
-//   E = beta V - beta e^gam X; Delta = T E; the output tile
-//   O^T = e^gam (M Q^T) + Delta^T P^T stored from registers; and
-//   M^T <- e^{gam_last} M^T + K^T diag(e^{gam_last - gam}) Delta (K^T from
-//   transposing LDS reads that deliver the permuted key order).
-// The chunk's data pass through two LDS slots: every wave copies a share of chunk
-// n + 1 from global memory into registers during chunk n - 1 and writes it into
-// the free slot at the end of chunk n, so one workgroup barrier per chunk suffices.
-// A wave's registers then hold its own state rows, its operands and one staging
-// share (171 at D = 128, two waves per SIMD); holding two value tiles per wave
-// (four waves) halves the LDS operand reads but needs ~350 registers, and the
-// copies between accumulation and vector registers that this forces made it slower
-// (242 against 190 us per 4,096 x 32 call on MI355X).
-//
-// Row r of state tile t holds key 32 (t/2) + 8 (r/4) + 4 (t%2) + r%4.
-template <int D>
-struct HeadCfg {
-    static constexpr int NVT = D / 16;                  // value tiles of a head
-    static constexpr int NT = 1;                        // value tiles per wave
-    static constexpr int NW = NVT / NT;                 // waves
-    static constexpr int KT = D / 16, KS = D / 32;      // key tiles, 32-key steps
-    static constexpr int RK = 2 * D + 32;               // K, Q, V row stride in LDS
-    static_assert((RK / 16) % 4 == 2, "row stride");
-    static constexpr int kK = 0, kQ = C * RK, kV = 2 * C * RK;
-    static constexpr int kT = 3 * C * RK;               // T, P, gates as in the workspace
-    static constexpr int kP = kT + 6 * kBlkBytes<true>;
-    static constexpr int kG = kP + 6 * kBlkBytes<true>;
-    static constexpr int kSlot = kG + 2048;
-    static constexpr int kBytes = 2 * kSlot;
-    static_assert(kBytes <= 160 * 1024, "LDS budget");
-    // staging: per matrix (K, Q, V) PR = D/8 pieces of 16 bytes per row, spread over
-    // the 64 NW lanes; then the T/P/gates bytes as a contiguous copy
-    static constexpr int PR = D / 8;
-    static constexpr int LANES = 64 * NW;
-    static constexpr int RPS = LANES / PR;              // rows per staging round
-    static constexpr int NR = C / RPS;                  // rounds per matrix
-    static_assert(LANES % PR == 0 && C % RPS == 0, "staging rows");
-    static constexpr int NWS = (WsLayout<true>::kBytesNorm / 16 + LANES - 1) / LANES;  // workspace pieces
-    static constexpr int NSTAGE = 3 * NR + NWS;
-};
-
-// A operand of K^T for state tile t: row r is key 32 (t/2) + 8 (r/4) + 4 (t%2) + r%4,
-// k is tokens t0 + 4g + j, t0 + 16 + 4g + j.  Two transposing reads: lane p of a group
-// fetches row t0 + 4g + p/4 (then 16 rows lower) at keys kb + 8 (p mod 4) .. +3, and
-// lane i receives the (i mod 4)-th value fetched by lane 4j + i/4.
-__device__ __forceinline__ Frag<true> head_kt_frag(const unsigned char *base, int stride, int t0,
-                                                   int t, int lane)
-{
-    const int g = lane >> 4, p = lane & 15;
-    const int key = 32 * (t >> 1) + 4 * (t & 1) + 8 * (p & 3);
-    const unsigned char *a1 = base + (t0 + 4 * g + (p >> 2)) * stride + 2 * key;
-    typedef __attribute__((address_space(3))) short4_t lds_short4;
-    const short4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a1));
-    const short4_t r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a1 + 16 * stride));
-    Frag<true> f;
-    const uint2 u1 = __builtin_bit_cast(uint2, r1);
-    const uint2 u2 = __builtin_bit_cast(uint2, r2);
-    f.u = make_uint4(u1.x, u1.y, u2.x, u2.y);
-    return f;
-}
-
-// One chunk's data in flight to LDS: each lane's 16-byte pieces (a native vector
-// type, so that the array lives in registers).
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-template <int D>
-struct HeadStage {
-    u32x4_t x[HeadCfg<D>::NSTAGE];
-};
-
-// Issues the loads of chunk m (nv valid rows) into st.
-template <int D>
-__device__ __forceinline__ void head_stage_load(HeadStage<D> &st, const unsigned char *k,
-                                                const unsigned char *q, const unsigned char *v,
-                                                const unsigned char *wsc, int64_t kq_bytes,
-                                                int64_t hd_bytes, int ws_bytes, int m, int nv,
-                                                int tid)
-{
-    using H = HeadCfg<D>;
-    // wave-uniform chunk bases plus 32-bit lane offsets (64 token rows of all heads
-    // span less than 4 GiB)
-    const uint32_t row0 = tid / H::PR, col = (tid % H::PR) * 16;
-    const uint32_t kqb = static_cast<uint32_t>(kq_bytes), hdb = static_cast<uint32_t>(hd_bytes);
-    const unsigned char *kb = k + int64_t(m) * C * kq_bytes;
-    const unsigned char *qb = q + int64_t(m) * C * kq_bytes;
-    const unsigned char *vb = v + int64_t(m) * C * hd_bytes;
-#pragma unroll
-    for (int r = 0; r < H::NR; ++r) {
-        const uint32_t row = min(row0 + r * H::RPS, uint32_t(nv - 1));
-        st.x[r] = *reinterpret_cast<const u32x4_t *>(kb + (row * kqb + col));
-        st.x[H::NR + r] = *reinterpret_cast<const u32x4_t *>(qb + (row * kqb + col));
-        st.x[2 * H::NR + r] = *reinterpret_cast<const u32x4_t *>(vb + (row * hdb + col));
-    }
-#pragma unroll
-    for (int r = 0; r < H::NWS; ++r) {
-        // pieces past the chunk's bytes re-read its last piece and are not stored
-        const int o = min(16 * (tid + r * H::LANES), ws_bytes - 16);
-        st.x[3 * H::NR + r] = *reinterpret_cast<const u32x4_t *>(wsc + o);
-    }
-}
-
-// Writes the staged chunk into an LDS slot.
-template <int D>
-__device__ __forceinline__ void head_stage_store(const HeadStage<D> &st, unsigned char *slot,
-                                                 int ws_bytes, int tid)
-{
-    using H = HeadCfg<D>;
-    const int row0 = tid / H::PR, col = (tid % H::PR) * 16;
-#pragma unroll
-    for (int r = 0; r < H::NR; ++r) {
-        const int off = (row0 + r * H::RPS) * H::RK + col;
-        *reinterpret_cast<u32x4_t *>(slot + H::kK + off) = st.x[r];
-        *reinterpret_cast<u32x4_t *>(slot + H::kQ + off) = st.x[H::NR + r];
-        *reinterpret_cast<u32x4_t *>(slot + H::kV + off) = st.x[2 * H::NR + r];
-    }
-#pragma unroll
-    for (int r = 0; r < H::NWS; ++r) {
-        const int o = 16 * (tid + r * H::LANES);
-        if (o < ws_bytes) *reinterpret_cast<u32x4_t *>(slot + H::kT + o) = st.x[3 * H::NR + r];
-    }
-}
-
-// The whole-head scan over chunks [c0, c1) of one (seq, head).  m_in: the state
-// entering chunk c0 ([value][key] fp32, or null for zeros); m_out: where the state
-// after chunk c1 - 1 goes.
-template <int D, bool NORM>
-__global__ __launch_bounds__(64 * HeadCfg<D>::NW) __attribute__((amdgpu_waves_per_eu(2)))
-void chunk_head_kernel(const void *__restrict__ q, const void *__restrict__ k,
-                       const void *__restrict__ v, const float *state_in, void *__restrict__ out,
-                       float *state_out, const unsigned char *__restrict__ ws, int64_t n_tokens,
-                       int64_t n_heads, int64_t n_k_heads, int n_chunks)
-{
-    using H = HeadCfg<D>;
-    using W = WsLayout<true>;
-    constexpr int NT = H::NT, KT = H::KT, KS = H::KS;
-    constexpr int ws_bytes = NORM ? int(W::kBytesNorm) : int(W::kBytes);
-    constexpr int eg_row = NORM ? 4 : 1;
-    extern __shared__ __align__(16) unsigned char smem[];
-
-    const int64_t sh = blockIdx.x;
-    const int64_t s = sh / n_heads, h = sh - s * n_heads;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int gq = lane >> 4, cl = lane & 15;
-    const int64_t kq_bytes = n_k_heads * D * 2, hd_bytes = n_heads * D * 2;
-    const int64_t ktok0 = (s * n_tokens * n_k_heads + h % n_k_heads) * D;
-    const int64_t tok0 = (s * n_tokens * n_heads + h) * D;
-    const unsigned char *kp = static_cast<const unsigned char *>(k) + ktok0 * 2;
-    const unsigned char *qp = static_cast<const unsigned char *>(q) + ktok0 * 2;
-    const unsigned char *vp = static_cast<const unsigned char *>(v) + tok0 * 2;
-    const int64_t ws_stride = W::stride(NORM);
-    const unsigned char *wsh = ws + sh * n_chunks * ws_stride;
-    auto nv_of = [&](int m) { return static_cast<int>(min<int64_t>(C, n_tokens - int64_t(m) * C)); };
-    const int nc = n_chunks;
-
-    // state: Mt[i][t] = M[16 (wave NT + i) + cl][32 (t/2) + 8 gq + 4 (t%2) + j]
-    floatx4 Mt[NT][KT];
-    const int64_t st0 = sh * D * D;
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-        const int vrow = 16 * (wave * NT + i) + cl;
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            const int key = 32 * (t >> 1) + 8 * gq + 4 * (t & 1);
-            if (state_in) {
-                const float4 m = *reinterpret_cast<const float4 *>(state_in + st0 + int64_t(vrow) * D + key);
-                Mt[i][t] = floatx4{m.x, m.y, m.z, m.w};
-            } else {
-                Mt[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-    }
-
-    HeadStage<D> st;
-    head_stage_load<D>(st, kp, qp, vp, wsh, kq_bytes, hd_bytes, ws_bytes, 0, nv_of(0), tid);
-    head_stage_store<D>(st, smem, ws_bytes, tid);
-    {
-        const int m1 = min(1, nc - 1);
-        head_stage_load<D>(st, kp, qp, vp, wsh + m1 * ws_stride, kq_bytes, hd_bytes, ws_bytes, m1,
-                           nv_of(m1), tid);
-    }
-    lds_barrier();
-
-    uint16_t *obase = static_cast<uint16_t *>(out) + tok0;
-    for (int n = 0; n < nc; ++n) {
-        const unsigned char *S = smem + (n & 1) * H::kSlot;
-        const float *G = reinterpret_cast<const float *>(S + H::kG);
-        // the state entering chunk n as bf16 operands (B of M^T, A of M)
-        Frag<true> mb[NT][KS];
-#pragma unroll
-        for (int i = 0; i < NT; ++i)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) mb[i][ks] = acc_frag<true>(Mt[i][2 * ks], Mt[i][2 * ks + 1]);
-        // X = K M^T
-        floatx4 X[NT][4];
-#pragma unroll
-        for (int i = 0; i < NT; ++i)
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) X[i][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            Frag<true> kf[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) kf[tt] = row_frag<true>(S + H::kK, H::RK, 16 * tt + cl, 32 * ks, gq);
-#pragma unroll
-            for (int i = 0; i < NT; ++i)
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) X[i][tt] = mma(kf[tt], mb[i][ks], X[i][tt]);
-        }
-        // E = beta V - beta e^gam X; Delta = T E
-        Frag<true> tf[6];
-#pragma unroll
-        for (int b = 0; b < 6; ++b) tf[b] = frag_blk<true>(S + H::kT + b * kBlkBytes<true>, lane);
-        floatx4 dl[NT][4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int r = 16 * tt + 4 * gq;
-            const float4 b4 = *reinterpret_cast<const float4 *>(G + r);
-            const float4 e4 = *reinterpret_cast<const float4 *>(G + C + r);
-            const floatx4 bb = floatx4{b4.x, b4.y, b4.z, b4.w};
-            const floatx4 be = bb * floatx4{e4.x, e4.y, e4.z, e4.w};
-#pragma unroll
-            for (int i = 0; i < NT; ++i) {
-                const floatx4 vv = col4<true>(S + H::kV, H::RK, 16 * tt, 16 * (wave * NT + i), lane);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) X[i][tt][j] = fmaf(-be[j], X[i][tt][j], bb[j] * vv[j]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) dl[i][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-            tri_mul<true>(tf, acc_frag<true>(X[i][0], X[i][1]), acc_frag<true>(X[i][2], X[i][3]), dl[i]);
-        }
-        // output: O^T = e^gam (M Q^T) + Delta^T P^T (1/sqrt(d) in e^gam and P)
-        floatx4 O[NT][4];
-#pragma unroll
-        for (int i = 0; i < NT; ++i)
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) O[i][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            Frag<true> qf[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) qf[tt] = row_frag<true>(S + H::kQ, H::RK, 16 * tt + cl, 32 * ks, gq);
-#pragma unroll
-            for (int i = 0; i < NT; ++i)
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) O[i][tt] = mma(mb[i][ks], qf[tt], O[i][tt]);
-        }
-        Frag<true> pf[6];
-#pragma unroll
-        for (int b = 0; b < 6; ++b) pf[b] = frag_blk<true>(S + H::kP + b * kBlkBytes<true>, lane);
-        float eg[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) eg[tt] = kOutScale<D> * G[eg_row * C + 16 * tt + cl];
-        const int nv = nv_of(n);
-        uint16_t *ob = obase + int64_t(n) * C * (hd_bytes / 2);
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            const Frag<true> d0 = acc_frag<true>(dl[i][0], dl[i][1]);
-            const Frag<true> d1 = acc_frag<true>(dl[i][2], dl[i][3]);
-            floatx4 a[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) a[tt] = O[i][tt] * eg[tt];
-            a[0] = mma(d0, pf[0], a[0]);
-            a[1] = mma(d0, pf[1], a[1]);
-            a[2] = mma(d1, pf[3], mma(d0, pf[2], a[2]));
-            a[3] = mma(d1, pf[5], mma(d0, pf[4], a[3]));
-            const int c0 = 16 * (wave * NT + i) + 4 * gq;
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                if (nv == C || 16 * tt + cl < nv)
-                    *reinterpret_cast<uint2 *>(ob + (16 * tt + cl) * (hd_bytes / 2) + c0) =
-                        make_uint2(pack2(a[tt][0], a[tt][1]), pack2(a[tt][2], a[tt][3]));
-            }
-        }
-        floatx4 ed[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const float4 d4 = *reinterpret_cast<const float4 *>(G + 2 * C + 16 * tt + 4 * gq);
-            ed[tt] = floatx4{d4.x, d4.y, d4.z, d4.w};
-        }
-        const float ec = G[3 * C];
-        // M^T <- e^{gam_last} M^T + K^T diag(e^{gam_last - gam}) Delta
-        Frag<true> dt[NT][2];
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            dt[i][0] = acc_frag<true>(ed[0] * dl[i][0], ed[1] * dl[i][1]);
-            dt[i][1] = acc_frag<true>(ed[2] * dl[i][2], ed[3] * dl[i][3]);
-        }
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            const Frag<true> k0 = head_kt_frag(S + H::kK, H::RK, 0, t, lane);
-            const Frag<true> k1 = head_kt_frag(S + H::kK, H::RK, 32, t, lane);
-#pragma unroll
-            for (int i = 0; i < NT; ++i) Mt[i][t] = mma(k1, dt[i][1], mma(k0, dt[i][0], Mt[i][t] * ec));
-        }
-        // chunk n + 1 into the other slot, then the loads of chunk n + 2 (the last
-        // chunk again near the end: loaded, never stored)
-        if (n + 1 < nc) head_stage_store<D>(st, smem + ((n + 1) & 1) * H::kSlot, ws_bytes, tid);
-        const int m2 = min(n + 2, nc - 1);
-        head_stage_load<D>(st, kp, qp, vp, wsh + m2 * ws_stride, kq_bytes, hd_bytes, ws_bytes, m2,
-                           nv_of(m2), tid);
-        lds_barrier();
-    }
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-        const int vrow = 16 * (wave * NT + i) + cl;
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            const int key = 32 * (t >> 1) + 8 * gq + 4 * (t & 1);
-            *reinterpret_cast<float4 *>(state_out + st0 + int64_t(vrow) * D + key) =
-                make_float4(Mt[i][t][0], Mt[i][t][1], Mt[i][t][2], Mt[i][t][3]);
-        }
-    }
-}
-
-// ---- the two-chunk-lag scan (bf16 rows) --------------------------------------------
-//
-// With S_n the state entering chunk n (value rows x key columns), c_n the gate sum
-// of chunk n and Dt_n = diag(e^{c_n - gam}) Delta_n the scaled deltas the state
-// update uses, writing S_n = e^{c_{n-1}} S_{n-1} + Dt_{n-1}^T K_{n-1} twice gives
-//
-//   Delta_n = T_n E_n + R1_n Dt_{n-1} + R2_n Dt_{n-2},
-//   E_n     = diag(beta) (V_n - e^{c_{n-1} + c_{n-2}} diag(e^gam) K_n S_{n-2}^T),
-//
-// with R1, R2 the state-independent 64 x 64 matrices the prep kernel stores (WsLag).
-// The serial chain from one chunk's deltas to the next is then three small products
-// (R2 Dt, R1 Dt, T E) in one wave, and everything that needs the state runs with a
-// chunk of slack.  One workgroup per (seq, head, 16 value rows), five waves, one
-// workgroup barrier per phase; every wave's inputs in phase t were published in
-// phase t - 1 (buffers alternate by parity):
-//   C  phase t:      Delta_t from E_t, Dt_{t-1}, Dt_{t-2}; publishes Delta_t, Dt_t
-//   G  phase t:      E_{t+1} from S_{max(t-1,0)} (K_{t+1} rows, V_{t+1}, gates)
-//   U  phase t >= 1: S_t = e^{c_{t-1}} S_{t-1} + K_{t-1}^T Dt_{t-1} (S^T in fp32
-//                    accumulators, K^T from transposing LDS reads); publishes S_t;
-//                    the final state after the last chunk
-//   O  phase t >= 1: output rows of chunk t-1 from S_{t-1}, Delta_{t-1}, Q, P
-//   P                K, V and gates moves into LDS rings (LDS-DMA)
-// for t = -1 .. n_chunks.  C, G and O load their chunk operands two phases ahead
-// straight into MFMA operand registers (fragment blocks and key/query rows, 16 bytes
-// per lane; two register sets, so the kernel runs one workgroup per compute unit).
-// The LDS-DMA moves are kept in a wave that reads no LDS: a wave with such moves in
-// flight is made to wait for all of them before any LDS read of its own.
-template <int D>
-struct LagScan {
-    static constexpr int KS = D / 32;        // 32-wide k steps over the key channels
-    static constexpr int KT = D / 16;        // 16-key tiles of S^T
-    static constexpr int NRB = D / 16;       // value tiles (workgroups) per (seq, head)
-    static constexpr int RK = 2 * D + 32;    // K row stride in LDS: 2 mod 4 16-byte units
-    static_assert((RK / 16) % 4 == 2, "K row stride");
-    static constexpr int RV = 2 * 16 + 16;   // V row stride (the tile's 16 values)
-    static constexpr int SK = 2, SV = 3;     // ring slots
-    static constexpr int SG = 5;             // gates slots: chunk m is read in phases m-1 .. m+1
-    static constexpr int kPubS = 0;                       // S^T: KS B-operand blocks, x 2
-    static constexpr int kPubE = kPubS + 2 * KS * 1024;   // E: two B fragments, x 2
-    static constexpr int kPubD = kPubE + 2 * 2048;        // Delta
-    static constexpr int kPubDs = kPubD + 2 * 2048;       // Dt
-    static constexpr int kK = kPubDs + 2 * 2048;
-    static constexpr int kV = kK + SK * C * RK;
-    static constexpr int kGt = kV + SV * C * RV;           // gates blocks (2 KiB each)
-    static constexpr int kBytes = kGt + SG * 2048;
-    static constexpr int NBK = C * RK / 1024;             // DMA blocks of one K slot
-    static constexpr int NBV = C * RV / 1024;
-    static constexpr int NBG = 2;
-    static_assert(C * RK % 1024 == 0 && C * RV % 1024 == 0, "DMA blocks");
-    static_assert(NBK + 2 * (NBV + NBG) < 64, "vmcnt range");
-    static_assert(WsLag::kBytes - WsLag::kGates == 2048, "gates block");
-};
-
-struct LagPtrs {
-    const unsigned char *k, *q;   // token 0 of (seq, key head)
-    const unsigned char *v;       // token 0 of (seq, head), the tile's first value
-    const unsigned char *ws;      // chunk 0 of (seq, head) in the workspace
-    int64_t kq_bytes, hd_bytes;   // token strides of k/q and of v/out
-    int64_t n_tokens;
-    int nc;
-    __device__ int nv(int m) const { return static_cast<int>(min<int64_t>(C, n_tokens - int64_t(m) * C)); }
-    __device__ const unsigned char *wsc(int m) const { return ws + int64_t(m) * WsLag::kBytes; }
-};
-
-// Workgroup barrier of the lag scan: waits for this wave's LDS accesses only (the
-// LDS-DMA loads in flight write slots nobody reads before their issuer has waited
-// for them), and keeps the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lag_barrier()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Keeps the compiler from moving memory accesses across this point: a wave issues
-// its next chunk's operand loads only after this chunk's products have read the
-// registers they replace (hoisting them would keep two sets of operands live).
-__device__ __forceinline__ void lag_order() { asm volatile("" ::: "memory"); }
-
-// Rows 16 tt + (lane mod 16) of a token-major matrix as A operands (k = 8g .. 8g + 7
-// of each 32-wide step), rows at or past nv repeating row nv - 1.
-template <int D>
-__device__ __forceinline__ void load_row_frags(Frag<true> (&f)[4][D / 32], const unsigned char *base,
-                                               int64_t stride, int nv, int lane)
-{
-    const int g = lane >> 4, r = lane & 15;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const unsigned char *p = base + int64_t(min(16 * tt + r, nv - 1)) * stride + 16 * g;
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) f[tt][ks] = *reinterpret_cast<const Frag<true> *>(p + 64 * ks);
-    }
-}
-
-// Gates row `row` of chunk m in the LDS ring.
-template <int D>
-__device__ __forceinline__ const float *lag_gates(const unsigned char *smem, int m, int row)
-{
-    return reinterpret_cast<const float *>(smem + LagScan<D>::kGt + (m % LagScan<D>::SG) * 2048) + row * C;
-}
-
-// Four gate values of the accumulator rows 16 tt + 4g .. 4g + 3 of one gates row.
-__device__ __forceinline__ floatx4 gate4(const float *row, int tt, int lane)
-{
-    const float4 x = *reinterpret_cast<const float4 *>(row + 16 * tt + 4 * (lane >> 4));
-    return floatx4{x.x, x.y, x.z, x.w};
-}
-
-// ---- C: the chain ----
-struct LagCOps {
-    Frag<true> ta[6], r1[8], r2[8];
-};
-
-__device__ __forceinline__ void lag_c_load(LagCOps &o, const LagPtrs &pp, int m, int lane)
-{
-    const unsigned char *wc = pp.wsc(m);
-#pragma unroll
-    for (int b = 0; b < 6; ++b) o.ta[b] = frag_blk<true>(wc + WsLag::kT + b * WsLag::kBlk, lane);
-    if (m >= 1) {
-#pragma unroll
-        for (int b = 0; b < 8; ++b) o.r1[b] = frag_blk<true>(wc + WsLag::kR1 + b * WsLag::kBlk, lane);
-    }
-    if (m >= 2) {
-#pragma unroll
-        for (int b = 0; b < 8; ++b) o.r2[b] = frag_blk<true>(wc + WsLag::kR2 + b * WsLag::kBlk, lane);
-    }
-}
-
-// The phase loops of C, G and O run two phases per iteration so that the operands
-// of chunk m and m + 1 sit in two fixed register sets: the loads of chunk m + 2
-// replace chunk m's set right after its products, two phases before use.
-template <int D>
-__device__ void lag_role_c(const LagPtrs &pp, unsigned char *smem, int lane, const LagTrace &tr)
-{
-    using F = LagScan<D>;
-    const int nc = pp.nc;
-    LagCOps oa, ob;
-    Frag<true> dt1[2], dt2[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        dt1[i].u = make_uint4(0u, 0u, 0u, 0u);
-        dt2[i].u = make_uint4(0u, 0u, 0u, 0u);
-    }
-    lag_c_load(oa, pp, 0, lane);
-    if (1 < nc) lag_c_load(ob, pp, 1, lane);
-    auto step = [&](int t, LagCOps &o) {
-        tr.mark(t, 0, lane);
-        if (t >= 0 && t < nc) {
-            tr.landed(t, lane);
-            floatx4 acc[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) acc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-            if (t >= 2) {
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
-                    acc[tt] = mma(o.r2[2 * tt + 1], dt2[1], mma(o.r2[2 * tt], dt2[0], acc[tt]));
-            }
-            if (t >= 1) {
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
-                    acc[tt] = mma(o.r1[2 * tt + 1], dt1[1], mma(o.r1[2 * tt], dt1[0], acc[tt]));
-            }
-            const Frag<true> *pe = reinterpret_cast<const Frag<true> *>(smem + F::kPubE + (t & 1) * 2048);
-            tri_mul<true>(o.ta, pe[lane], pe[64 + lane], acc);
-            // Dt = diag(e^{c - gam} (/|k|)) Delta
-            const float *ed = lag_gates<D>(smem, t, 2);
-            floatx4 ds[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) ds[tt] = gate4(ed, tt, lane) * acc[tt];
-            Frag<true> *pd = reinterpret_cast<Frag<true> *>(smem + F::kPubD + (t & 1) * 2048);
-            Frag<true> *ps = reinterpret_cast<Frag<true> *>(smem + F::kPubDs + (t & 1) * 2048);
-            pd[lane] = acc_frag<true>(acc[0], acc[1]);
-            pd[64 + lane] = acc_frag<true>(acc[2], acc[3]);
-            dt2[0] = dt1[0];
-            dt2[1] = dt1[1];
-            dt1[0] = acc_frag<true>(ds[0], ds[1]);
-            dt1[1] = acc_frag<true>(ds[2], ds[3]);
-            ps[lane] = dt1[0];
-            ps[64 + lane] = dt1[1];
-            lag_order();   // the next operands replace this chunk's, not join them
-            if (t + 2 < nc) lag_c_load(o, pp, t + 2, lane);
-        }
-        tr.mark(t, 2, lane);
-        lag_barrier();
-    };
-    lag_barrier();                      // prologue
-    // chunk m's operands are in oa for even m, ob for odd m
-    for (int t = -1; t <= nc; t += 2) {
-        step(t, ob);
-        if (t + 1 <= nc) step(t + 1, oa);
-    }
-}
-
-// ---- G: E one chunk ahead of the chain ----
-template <int D>
-struct LagGOps {
-    Frag<true> gk[4][D / 32];      // K rows of the chunk
-};
-
-template <int D>
-__device__ __forceinline__ void lag_g_load(LagGOps<D> &o, const LagPtrs &pp, int m, int lane)
-{
-    load_row_frags<D>(o.gk, pp.k + int64_t(m) * C * pp.kq_bytes, pp.kq_bytes, pp.nv(m), lane);
-}
-
-template <int D>
-__device__ __forceinline__ void lag_g_dma_v(const LagPtrs &pp, unsigned char *smem, int m, int lane)
-{
-    using F = LagScan<D>;
-    const uint32_t hdb = static_cast<uint32_t>(pp.hd_bytes);
-    const unsigned char *vb = pp.v + int64_t(m) * C * pp.hd_bytes;
-    unsigned char *slot = smem + F::kV + (m % F::SV) * C * F::RV;
-#pragma unroll
-    for (int i = 0; i < F::NBV; ++i)
-        dma16(vb, dma_src_offset(i, lane, 16 * 2, F::RV, hdb, pp.nv(m)), slot + 1024 * i);
-}
-
-template <int D>
-__device__ void lag_role_g(const LagPtrs &pp, unsigned char *smem, int lane, const LagTrace &tr)
-{
-    using F = LagScan<D>;
-    const int nc = pp.nc;
-    LagGOps<D> oa, ob;
-    lag_g_load<D>(oa, pp, 0, lane);
-    if (1 < nc) lag_g_load<D>(ob, pp, 1, lane);
-    auto step = [&](int t, LagGOps<D> &o) {
-        tr.mark(t, 0, lane);
-        if (t <= nc - 2) {
-            const int m = t + 1;        // chunk whose E is formed
-            tr.landed(t, lane);
-            const int src = t - 1 > 0 ? t - 1 : 0;   // S_{max(m-2, 0)}
-            Frag<true> bs[F::KS];
-#pragma unroll
-            for (int ks = 0; ks < F::KS; ++ks)
-                bs[ks] = frag_blk<true>(smem + F::kPubS + ((src & 1) * F::KS + ks) * 1024, lane);
-            floatx4 x[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                x[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < F::KS; ++ks) x[tt] = mma(o.gk[tt][ks], bs[ks], x[tt]);
-            }
-            const unsigned char *vs = smem + F::kV + (m % F::SV) * C * F::RV;
-            // e^{c_{m-1} + c_{m-2}} (fewer factors for the first chunks)
-            const float f = (m >= 1 ? lag_gates<D>(smem, m - 1, 3)[0] : 1.f) *
-                            (m >= 2 ? lag_gates<D>(smem, m - 2, 3)[0] : 1.f);
-            const float *gb = lag_gates<D>(smem, m, 0), *ge = lag_gates<D>(smem, m, 1);
-            floatx4 e[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const floatx4 vv = col4<true>(vs, F::RV, 16 * tt, 0, lane);
-                const floatx4 b4 = gate4(gb, tt, lane), e4 = gate4(ge, tt, lane);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) e[tt][j] = b4[j] * fmaf(-f * e4[j], x[tt][j], vv[j]);
-            }
-            Frag<true> *pe = reinterpret_cast<Frag<true> *>(smem + F::kPubE + (m & 1) * 2048);
-            pe[lane] = acc_frag<true>(e[0], e[1]);
-            pe[64 + lane] = acc_frag<true>(e[2], e[3]);
-            lag_order();
-            if (m + 2 < nc) lag_g_load<D>(o, pp, m + 2, lane);
-        }
-        tr.mark(t, 2, lane);
-        lag_barrier();
-    };
-    lag_barrier();                      // prologue
-    // phase t forms E of chunk t + 1: even chunks in oa, odd in ob
-    for (int t = -1; t <= nc; t += 2) {
-        step(t, oa);
-        if (t + 1 <= nc) step(t + 1, ob);
-    }
-}
-
-// ---- U: the state pass ----
-template <int D>
-__device__ __forceinline__ void lag_publish_s(const floatx4 (&Mt)[D / 16], unsigned char *blocks, int lane)
-{
-    const int gq = lane >> 4, cl = lane & 15;
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-        // keys 16t + 4gq + 0..3: block t/2, unit group 2 (t & 1) + gq / 2, elements 4 (gq & 1) ..
-        unsigned char *u = blocks + (t >> 1) * 1024 + 16 * blk_unit(cl, 2 * (t & 1) + (gq >> 1)) +
-                           8 * (gq & 1);
-        *reinterpret_cast<uint2 *>(u) = make_uint2(pack2(Mt[t][0], Mt[t][1]), pack2(Mt[t][2], Mt[t][3]));
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void lag_u_dma_k(const LagPtrs &pp, unsigned char *smem, int m, int lane)
-{
-    using F = LagScan<D>;
-    const unsigned char *kb = pp.k + int64_t(m) * C * pp.kq_bytes;
-    unsigned char *slot = smem + F::kK + (m % F::SK) * C * F::RK;
-    const uint32_t kqb = static_cast<uint32_t>(pp.kq_bytes);
-#pragma unroll
-    for (int i = 0; i < F::NBK; ++i)
-        dma16(kb, dma_src_offset(i, lane, 2 * D, F::RK, kqb, pp.nv(m)), slot + 1024 * i);
-}
-
-template <int D>
-__device__ void lag_role_u(const LagPtrs &pp, unsigned char *smem, const float *state_in,
-                           float *state_out, int64_t st_off, int lane, const LagTrace &tr)
-{
-    using F = LagScan<D>;
-    const int nc = pp.nc;
-    floatx4 Mt[F::KT];
-#pragma unroll
-    for (int t = 0; t < F::KT; ++t) {
-        if (state_in) {
-            const float4 m = *reinterpret_cast<const float4 *>(state_in + st_off + 16 * t);
-            Mt[t] = floatx4{m.x, m.y, m.z, m.w};
-        } else {
-            Mt[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-    lag_publish_s<D>(Mt, smem + F::kPubS, lane);
-    Frag<true> akt[F::KT][2];
-    lag_barrier();                      // prologue
-    for (int t = -1; t <= nc; ++t) {
-        tr.mark(t, 0, lane);
-        if (t >= 1) {
-            const Frag<true> *ps = reinterpret_cast<const Frag<true> *>(smem + F::kPubDs + ((t - 1) & 1) * 2048);
-            const Frag<true> d0 = ps[lane], d1 = ps[64 + lane];
-            const float ec = lag_gates<D>(smem, t - 1, 3)[0];
-#pragma unroll
-            for (int kt = 0; kt < F::KT; ++kt) Mt[kt] *= ec;
-#pragma unroll
-            for (int kt = 0; kt < F::KT; ++kt) Mt[kt] = mma(akt[kt][0], d0, Mt[kt]);
-#pragma unroll
-            for (int kt = 0; kt < F::KT; ++kt) Mt[kt] = mma(akt[kt][1], d1, Mt[kt]);
-            lag_publish_s<D>(Mt, smem + F::kPubS + (t & 1) * F::KS * 1024, lane);
-        }
-        if (t >= 0 && t < nc) {
-            // K_t was moved in by P before this phase began
-            tr.mark(t, 1, lane);
-            const unsigned char *kslot = smem + F::kK + (t % F::SK) * C * F::RK;
-#pragma unroll
-            for (int kt = 0; kt < F::KT; ++kt) {
-                akt[kt][0] = frag_cols<true>(kslot, F::RK, 0, 16 * kt, lane);
-                akt[kt][1] = frag_cols<true>(kslot, F::RK, 32, 16 * kt, lane);
-            }
-        }
-        tr.mark(t, 2, lane);
-        lag_barrier();
-    }
-#pragma unroll
-    for (int t = 0; t < F::KT; ++t)
-        *reinterpret_cast<float4 *>(state_out + st_off + 16 * t) =
-            make_float4(Mt[t][0], Mt[t][1], Mt[t][2], Mt[t][3]);
-}
-
-// ---- P: K and V moves into LDS ----
-// Phase t moves K_{t+1} (U reads it at the end of phase t+1; two slots, the rows
-// are in L2 already, G having loaded them in phase t-1), V_{t+3} (G reads it in
-// phase t+2; three slots) and the gates block of chunk t+3 (read by G, C, U and O
-// in phases t+2 .. t+4; five slots), then waits for K_{t+1}, which with the issue
-// order also covers chunk t+2's moves: every move is complete before the barrier
-// after which it is read.
-// P reads no LDS itself, so no wait on its moves is forced anywhere else.
-template <int D>
-__device__ __forceinline__ void lag_p_dma_vg(const LagPtrs &pp, unsigned char *smem, int m, int lane)
-{
-    using F = LagScan<D>;
-    lag_g_dma_v<D>(pp, smem, m, lane);
-    const unsigned char *gb = pp.wsc(m) + WsLag::kGates;
-    unsigned char *slot = smem + F::kGt + (m % F::SG) * 2048;
-#pragma unroll
-    for (int i = 0; i < F::NBG; ++i) dma16(gb, 1024u * i + 16u * lane, slot + 1024 * i);
-}
-
-template <int D>
-__device__ void lag_role_p(const LagPtrs &pp, unsigned char *smem, int lane)
-{
-    const int nc = pp.nc;
-    constexpr int NVG = LagScan<D>::NBV + LagScan<D>::NBG;
-    lag_p_dma_vg<D>(pp, smem, 0, lane);
-    if (1 < nc) lag_p_dma_vg<D>(pp, smem, 1, lane);
-    if (1 < nc) wait_vmem_le<NVG>(); else wait_vmem_le<0>();   // V_0, gates_0 (phase -1)
-    lag_barrier();                      // prologue
-    for (int t = -1; t <= nc; ++t) {
-        if (t + 1 < nc) lag_u_dma_k<D>(pp, smem, t + 1, lane);
-        if (t + 3 < nc) lag_p_dma_vg<D>(pp, smem, t + 3, lane);
-        if (t + 3 < nc) wait_vmem_le<NVG>(); else wait_vmem_le<0>();
-        lag_barrier();
-    }
-}
-
-// ---- O: the output ----
-template <int D>
-struct LagOOps {
-    Frag<true> oq[4][D / 32];      // Q rows
-    Frag<true> op[6];              // P / sqrt(d) blocks
-};
-
-template <int D>
-__device__ __forceinline__ void lag_o_load(LagOOps<D> &o, const LagPtrs &pp, int m, int lane)
-{
-    load_row_frags<D>(o.oq, pp.q + int64_t(m) * C * pp.kq_bytes, pp.kq_bytes, pp.nv(m), lane);
-    const unsigned char *wc = pp.wsc(m);
-#pragma unroll
-    for (int b = 0; b < 6; ++b) o.op[b] = frag_blk<true>(wc + WsLag::kP + b * WsLag::kBlk, lane);
-}
-
-template <int D>
-__device__ void lag_role_o(const LagPtrs &pp, unsigned char *smem, uint16_t *obase, int lane,
-                           const LagTrace &tr)
-{
-    using F = LagScan<D>;
-    const int nc = pp.nc;
-    const int gq = lane >> 4, cl = lane & 15;
-    const int64_t hd = pp.hd_bytes / 2;
-    LagOOps<D> oa, ob;
-    lag_o_load<D>(oa, pp, 0, lane);
-    if (1 < nc) lag_o_load<D>(ob, pp, 1, lane);
-    auto step = [&](int t, LagOOps<D> &o) {
-        tr.mark(t, 0, lane);
-        if (t >= 1) {
-            tr.landed(t, lane);
-            const int m = t - 1;        // chunk whose rows are written
-            Frag<true> bm[F::KS];
-#pragma unroll
-            for (int ks = 0; ks < F::KS; ++ks)
-                bm[ks] = frag_blk<true>(smem + F::kPubS + ((m & 1) * F::KS + ks) * 1024, lane);
-            const float *eg = lag_gates<D>(smem, m, 4);   // e^gam (/|q|)
-            floatx4 acc[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                floatx4 xq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < F::KS; ++ks) xq = mma(bm[ks], o.oq[tt][ks], xq);
-                acc[tt] = xq * (kOutScale<D> * eg[16 * tt + cl]);
-            }
-            const Frag<true> *pd = reinterpret_cast<const Frag<true> *>(smem + F::kPubD + (m & 1) * 2048);
-            const Frag<true> d0 = pd[lane], d1 = pd[64 + lane];
-            acc[0] = mma(d0, o.op[0], acc[0]);
-            acc[1] = mma(d0, o.op[1], acc[1]);
-            acc[2] = mma(d1, o.op[3], mma(d0, o.op[2], acc[2]));
-            acc[3] = mma(d1, o.op[5], mma(d0, o.op[4], acc[3]));
-            // the next operand loads go out before the stores: loads issued after them
-            // could be given the stores' data registers and would wait for the stores
-            lag_order();
-            if (m + 2 < nc) lag_o_load<D>(o, pp, m + 2, lane);
-            uint16_t *ob_ = obase + int64_t(m) * C * hd;
-            const int nv = pp.nv(m);
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                if (nv == C || 16 * tt + cl < nv)
-                    *reinterpret_cast<uint2 *>(ob_ + (16 * tt + cl) * hd + 4 * gq) =
-                        make_uint2(pack2(acc[tt][0], acc[tt][1]), pack2(acc[tt][2], acc[tt][3]));
-            }
-        }
-        tr.mark(t, 2, lane);
-        lag_barrier();
-    };
-    lag_barrier();                      // prologue
-    // phase t writes chunk t - 1: even chunks in oa, odd in ob
-    for (int t = -1; t <= nc; t += 2) {
-        step(t, oa);
-        if (t + 1 <= nc) step(t + 1, ob);
-    }
-}
-
-// Workgroups are numbered so that the NRB row blocks of one (seq, head) share the
-// low three bits of the block id and land on one XCD (shared L2).
-constexpr int kLagWaves = 5;
-
-// Two register sets of operands per wave (up to 256 registers): one workgroup per
-// compute unit.
-template <int D>
-__global__ __launch_bounds__(64 * kLagWaves) __attribute__((amdgpu_waves_per_eu(2))) void chunk_lag_kernel(
-    const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
-    const float *state_in, void *__restrict__ out, float *state_out,
-    const unsigned char *__restrict__ ws, int64_t n_tokens, int64_t n_heads, int64_t n_k_heads,
-    int64_t n_sh, int n_chunks)
-{
-    using F = LagScan<D>;
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int64_t b = blockIdx.x;
-    const int64_t sh = (b / (8 * F::NRB)) * 8 + (b & 7);
-    const int rb = static_cast<int>((b >> 3) % F::NRB);
-    if (sh >= n_sh) return;   // whole workgroup leaves before any barrier
-    const int64_t s = sh / n_heads, h = sh - s * n_heads;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int v0 = 16 * rb;
-    LagPtrs pp;
-    pp.kq_bytes = n_k_heads * D * 2;
-    pp.hd_bytes = n_heads * D * 2;
-    const int64_t ktok0 = (s * n_tokens * n_k_heads + h % n_k_heads) * D;
-    const int64_t tok0 = (s * n_tokens * n_heads + h) * D;
-    pp.k = static_cast<const unsigned char *>(k) + ktok0 * 2;
-    pp.q = static_cast<const unsigned char *>(q) + ktok0 * 2;
-    pp.v = static_cast<const unsigned char *>(v) + (tok0 + v0) * 2;
-    pp.ws = ws + sh * n_chunks * WsLag::kBytes;
-    pp.n_tokens = n_tokens;
-    pp.nc = n_chunks;
-    const LagTrace tr{static_cast<int>(b), wave};
-    if (wave == 0) {
-        lag_role_c<D>(pp, smem, lane, tr);
-    } else if (wave == 1) {
-        lag_role_g<D>(pp, smem, lane, tr);
-    } else if (wave == 2) {
-        const int64_t st_off = sh * D * D + int64_t(v0 + (lane & 15)) * D + 4 * (lane >> 4);
-        lag_role_u<D>(pp, smem, state_in, state_out, st_off, lane, tr);
-    } else if (wave == 3) {
-        lag_role_o<D>(pp, smem, static_cast<uint16_t *>(out) + tok0 + v0, lane, tr);
-    } else {
-        lag_role_p<D>(pp, smem, lane);
-    }
-}
-
-// Raises the dynamic-LDS limit of `kern` to `bytes`, once per device (bit d of
-// `done` records device d; concurrent first calls may both set it, harmlessly).
-template <typename K>
-hipError_t ensure_lds_limit(K kern, int bytes, std::atomic<uint64_t> &done)
-{
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
-    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
-    return e;
-}
-
 template <int D, bool BF16, bool NORM, bool LAG>
 hipError_t launch_prep(const Problem &p, unsigned char *ws, int n_chunks, hipStream_t stream)
 {
@@ -2547,54 +1326,6 @@ hipError_t launch_scan(const Problem &p, const unsigned char *ws, int n_chunks, 
     return hipGetLastError();
 }
 
-template <int D>
-int64_t lag_blocks(int64_t n_sh)
-{
-    return (n_sh + 7) / 8 * 8 * LagScan<D>::NRB;
-}
-
-// The whole-head scan: one workgroup per (seq, head), one wave per SIMD.
-template <int D, bool NORM>
-hipError_t launch_head(const Problem &p, const unsigned char *ws, int n_chunks, hipStream_t stream)
-{
-    using H = HeadCfg<D>;
-    auto kern = chunk_head_kernel<D, NORM>;
-    static std::atomic<uint64_t> lds_set{0};
-    const hipError_t e = ensure_lds_limit(kern, H::kBytes, lds_set);
-    if (e != hipSuccess) return e;
-    const int64_t blocks = p.n_seqs * p.n_heads;
-    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(64 * H::NW), H::kBytes,
-                       stream, p.q, p.k, p.v, p.state_in, p.out, p.state_out, ws, p.n_tokens,
-                       p.n_heads, p.n_k_heads, n_chunks);
-    return hipGetLastError();
-}
-
-// The lag scan: one workgroup per compute unit (its registers allow no second one;
-// the LDS request says so as well).
-template <int D>
-hipError_t launch_lag(const Problem &p, const unsigned char *ws, int n_chunks, hipStream_t stream)
-{
-    using F = LagScan<D>;
-    constexpr int kAlone = 80 * 1024 + 256;
-    static_assert(F::kBytes <= kAlone, "LDS of the lag scan");
-    auto kern = chunk_lag_kernel<D>;
-    static std::atomic<uint64_t> lds_set{0};
-    const hipError_t e = ensure_lds_limit(kern, kAlone, lds_set);
-    if (e != hipSuccess) return e;
-    const int64_t blocks = lag_blocks<D>(p.n_seqs * p.n_heads);
-    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(64 * kLagWaves), kAlone,
-                       stream, p.q, p.k, p.v, p.state_in, p.out, p.state_out, ws, p.n_tokens,
-                       p.n_heads, p.n_k_heads, p.n_seqs * p.n_heads, n_chunks);
-    return hipGetLastError();
-}
-
-// The prep, then the scan.  Default (and fp32, the parity path): the two-barrier
-// scan, for bf16 with two value tiles per workgroup once one tile each would give
-// more workgroups than compute units; fp32 keeps one tile and one ring slot.  lag
-// (bf16 only): the prep with the lag form's cross-chunk matrices, then the lag scan.
-// Normalised q/k rows are a prep (and two-barrier scan) variant of their own (NORM),
-// so that the plain kernels carry none of that mode's code; the lag scan reads the
-// normalisation through the gate rows and has no such variant.
 // Compute units of the current device (looked up once per device).
 int cu_count()
 {
@@ -2610,6 +1341,14 @@ int cu_count()
     return n;
 }
 
+// The prep, then the chunk-to-chunk pass.  The whole-head pass (bf16) when forced,
+// or under AUTO from one (seq, head) per compute unit on; else the two-barrier
+// scan, for bf16 with two value tiles per workgroup once one tile each would give
+// more workgroups than compute units; fp32 keeps one tile and one ring slot.  lag
+// (bf16 only): the prep with the lag form's cross-chunk matrices, then the lag scan.
+// Normalised q/k rows are a prep (and two-barrier scan) variant of their own (NORM),
+// so that the plain kernels carry none of that mode's code; the lag scan reads the
+// normalisation through the gate rows and has no such variant.
 template <int D, bool BF16, bool NORM>
 hipError_t launch_chunk_dn(const Problem &p, bool lag, unsigned char *ws, hipStream_t stream)
 {
@@ -2623,11 +1362,11 @@ hipError_t launch_chunk_dn(const Problem &p, bool lag, unsigned char *ws, hipStr
             const int64_t n_chunks64 = (p.n_tokens + C - 1) / C;
             const int64_t n_sh = p.n_seqs * p.n_heads;
             if (n_chunks64 > INT32_MAX || !grid_fits(n_sh * n_chunks64, kPrepThreads) ||
-                !grid_fits(n_sh, 64 * HeadCfg<D>::NW))
+                !head_pass_fits(n_sh, D))
                 return hipErrorInvalidConfiguration;
             const int n_chunks = static_cast<int>(n_chunks64);
             const hipError_t e = launch_prep<D, BF16, NORM, false>(p, ws, n_chunks, stream);
-            return e != hipSuccess ? e : launch_head<D, NORM>(p, ws, n_chunks, stream);
+            return e != hipSuccess ? e : launch_head_pass(p, ws, n_chunks, stream);
         }
     }
     const int64_t n_chunks64 = (p.n_tokens + C - 1) / C;
@@ -2635,7 +1374,7 @@ hipError_t launch_chunk_dn(const Problem &p, bool lag, unsigned char *ws, hipStr
     const bool vt1 = !BF16 || n_sh * (D / 16) <= 256;
     // both grids are checked before either kernel is launched
     const bool scan_fits =
-        lag ? grid_fits(lag_blocks<D>(n_sh), 64 * kLagWaves)
+        lag ? lag_pass_fits(n_sh, D)
         : vt1 ? grid_fits(scan_blocks<D, BF16, 1>(n_sh), 64 * ScanCfg<D, BF16, 1>::kWaves)
               : grid_fits(scan_blocks<D, BF16, 2>(n_sh), 64 * ScanCfg<D, BF16, 2>::kWaves);
     if (n_chunks64 > INT32_MAX || !grid_fits(n_sh * n_chunks64, kPrepThreads) || !scan_fits)
@@ -2644,7 +1383,7 @@ hipError_t launch_chunk_dn(const Problem &p, bool lag, unsigned char *ws, hipStr
     if constexpr (BF16) {
         if (lag) {
             const hipError_t e = launch_prep<D, BF16, NORM, true>(p, ws, n_chunks, stream);
-            return e != hipSuccess ? e : launch_lag<D>(p, ws, n_chunks, stream);
+            return e != hipSuccess ? e : launch_lag_pass(p, ws, n_chunks, stream);
         }
     } else if (lag) {
         return hipErrorInvalidValue;   // refused by the API before this point
@@ -2690,16 +1429,8 @@ size_t chunk_workspace_bytes(int bf16, int lag, int64_t n_seqs, int64_t n_tokens
 }
 
 #ifdef GDN_PHASE_TRACE
-// Copy the timestamps of the last lag pass, or of the last per-tile pass, out (trace
-// builds only; not part of the installed interface).
-extern "C" int gdn_phase_trace_read(void *host, size_t bytes)
-{
-    if (bytes > sizeof(g_phase_trace)) bytes = sizeof(g_phase_trace);
-    return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_trace), bytes, 0, hipMemcpyDeviceToHost) ==
-                   hipSuccess
-               ? 0
-               : -1;
-}
+// Copies the timestamps of the last per-tile pass out (trace builds only; not part
+// of the installed interface).
 extern "C" int gdn_scan_trace_read(void *host, size_t bytes)
 {
     if (bytes > sizeof(g_scan_trace)) bytes = sizeof(g_scan_trace);

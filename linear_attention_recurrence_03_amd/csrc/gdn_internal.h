@@ -41,6 +41,17 @@ size_t chunk_workspace_bytes(int bf16, int lag, int64_t n_seqs, int64_t n_tokens
                              int64_t n_heads, int head_dim);
 hipError_t launch_chunked(const Problem &p, bool lag, void *workspace, hipStream_t stream);
 
+// The chunk-to-chunk passes kept in files of their own (bf16 rows), run after the
+// prep kernel has filled the workspace: the whole-head pass (gdn_chunk_head.hip) and
+// the two-chunk-lag pass (gdn_chunk_lag.hip), with the grid checks done before any
+// kernel of a call is launched.
+bool head_pass_fits(int64_t n_sh, int head_dim);
+hipError_t launch_head_pass(const Problem &p, const unsigned char *ws, int n_chunks,
+                            hipStream_t stream);
+bool lag_pass_fits(int64_t n_sh, int head_dim);
+hipError_t launch_lag_pass(const Problem &p, const unsigned char *ws, int n_chunks,
+                           hipStream_t stream);
+
 // Size of the library-owned scratch array behind gdn_forward_noalloc (one per
 // device), and its address on the current device (looked up once per device).
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;

@@ -45,7 +45,12 @@ def capture(fn):
 @pytest.mark.parametrize("dtype,T,algo,pre", [("bf16", 300, "chunked", {}),
                                               ("f32", 5, "recurrent", {}),
                                               ("bf16", 200, "chunked",
-                                               {"l2norm_qk": True, "raw_gates": True})])
+                                               {"l2norm_qk": True, "raw_gates": True}),
+                                              ("bf16", 300, "chunked_head", {}),
+                                              ("bf16", 200, "chunked_head",
+                                               {"l2norm_qk": True, "raw_gates": True}),
+                                              ("bf16", 300, "chunked_lag", {}),
+                                              ("f32", 200, "chunked", {})])
 def test_forward_graph_replays(gdn, dtype, T, algo, pre):
     x = inputs.custom(2, T, 4, 128, dtype=dtype, state="normal", seed=T, raw=bool(pre))
     d = dev(x, dtype)
