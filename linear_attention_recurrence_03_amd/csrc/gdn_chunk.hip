@@ -229,7 +229,7 @@ __device__ __forceinline__ float sumsq16(const uint4 &u, float acc)
 // keeps the result as two bf16 A operands (k = the rows s of chunk n), and once T
 // is final multiplies by T: (T Y)^T = Y^T T^T, whose accumulator hands lane (g, i)
 // four consecutive columns of row i, i.e. half of a fragment unit.
-template <int D, bool BF16, bool NORM, bool LAG>
+template <int D, bool BF16, bool NORM, bool LAG, bool PQ>
 __global__ __launch_bounds__(kPrepThreads)
 __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM, LAG>()))) void chunk_prep_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const float *__restrict__ g,
@@ -240,7 +240,10 @@ __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM, LAG>()))) void chu
     using E = typename Elem<BF16>::T;
     using L = PrepSmem<D, BF16>;
     using W = WsLayout<BF16>;
-    constexpr int64_t kStride = LAG ? WsLag::kBytes : W::stride(NORM);
+    static_assert(PQ || (BF16 && !NORM && !LAG), "P is left to the pass only for plain bf16 rows");
+    // without P (the whole-head pass forms it) the gates take the 2 KiB area, with a
+    // sixth row holding gam itself
+    constexpr int64_t kStride = LAG ? WsLag::kBytes : !PQ ? W::kBytesNorm : W::stride(NORM);
     constexpr int64_t kWsP = LAG ? WsLag::kP : W::kP;
     constexpr int64_t kWsT = LAG ? WsLag::kT : W::kT;
     constexpr int64_t kWsG = LAG ? WsLag::kGates : W::kGates;
@@ -280,7 +283,7 @@ __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM, LAG>()))) void chu
         const uint32_t hdb = static_cast<uint32_t>(n_k_heads * D * L::ES);
         for (int i = wave; i < L::NBK; i += kPrepThreads / 64)
             dma16(kb, dma_src_offset(i, lane, D * L::ES, L::RK, hdb, nv), smem + L::kK + 1024 * i);
-        if (wave >= 2) {
+        if (PQ && wave >= 2) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int tr = (wave == 2) ? (i ? 3 : 0) : (i ? 2 : 1);
@@ -436,14 +439,18 @@ __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM, LAG>()))) void chu
         }
     } else {
         if (wave == 2) {
-            PrepTiles<0, 3> pt;
-            prep_products<D, BF16, false, 0, 3>(pt, smem, sG, sD, sN, lane, fq);
-            emit_p<BF16, 0, 3>(pt, dst + kWsP, lane);
+            if constexpr (PQ) {
+                PrepTiles<0, 3> pt;
+                prep_products<D, BF16, false, 0, 3>(pt, smem, sG, sD, sN, lane, fq);
+                emit_p<BF16, 0, 3>(pt, dst + kWsP, lane);
+            }
             lds_barrier();
         } else {
-            PrepTiles<1, 2> pt;
-            prep_products<D, BF16, false, 1, 2>(pt, smem, sG, sD, sN, lane, fq);
-            emit_p<BF16, 1, 2>(pt, dst + kWsP, lane);
+            if constexpr (PQ) {
+                PrepTiles<1, 2> pt;
+                prep_products<D, BF16, false, 1, 2>(pt, smem, sG, sD, sN, lane, fq);
+                emit_p<BF16, 1, 2>(pt, dst + kWsP, lane);
+            }
             lds_barrier();
             // beta, e^gam, e^{last-gam}, e^last; with normalised rows the second and
             // third carry 1/|k| and a fifth row holds e^gam / |q|
@@ -454,6 +461,7 @@ __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM, LAG>()))) void chu
             wG[2 * C + lane] = sG[3 * C + lane] * rk;
             wG[3 * C + lane] = sG[4 * C];
             if (LAG || sN) wG[4 * C + lane] = sG[2 * C + lane] * (sN ? sN[C + lane] : 1.f);
+            if (!PQ) wG[5 * C + lane] = sG[lane];
         }
     }
     if (wave == 0) {
@@ -1287,11 +1295,11 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
     }
 }
 
-template <int D, bool BF16, bool NORM, bool LAG>
+template <int D, bool BF16, bool NORM, bool LAG, bool PQ = true>
 hipError_t launch_prep(const Problem &p, unsigned char *ws, int n_chunks, hipStream_t stream)
 {
     using L = PrepSmem<D, BF16>;
-    auto kern = chunk_prep_kernel<D, BF16, NORM, LAG>;
+    auto kern = chunk_prep_kernel<D, BF16, NORM, LAG, PQ>;
     static std::atomic<uint64_t> lds_set{0};
     const hipError_t e = ensure_lds_limit(kern, L::kBytes, lds_set);
     if (e != hipSuccess) return e;
@@ -1365,7 +1373,10 @@ hipError_t launch_chunk_dn(const Problem &p, bool lag, unsigned char *ws, hipStr
                 !head_pass_fits(n_sh, D))
                 return hipErrorInvalidConfiguration;
             const int n_chunks = static_cast<int>(n_chunks64);
-            const hipError_t e = launch_prep<D, BF16, NORM, false>(p, ws, n_chunks, stream);
+            // plain rows: the pass forms P itself, and the prep skips Q
+            const hipError_t e = NORM ? launch_prep<D, BF16, NORM, false>(p, ws, n_chunks, stream)
+                                      : launch_prep<D, BF16, false, false, false>(p, ws, n_chunks,
+                                                                                  stream);
             return e != hipSuccess ? e : launch_head_pass(p, ws, n_chunks, stream);
         }
     }

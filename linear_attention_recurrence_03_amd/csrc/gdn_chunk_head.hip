@@ -46,14 +46,24 @@ struct HeadCfg {
     static constexpr int kBytes = 2 * kSlot;
     static_assert(kBytes <= 160 * 1024, "LDS budget");
     // staging: per matrix (K, Q, V) PR = D/8 pieces of 16 bytes per row, spread over
-    // the 64 NW lanes; then the T/P/gates bytes as a contiguous copy
+    // the 64 NW lanes; then the workspace's T, P and gates (PIN: P in the workspace)
+    // or its T and gates (P formed by the pass), in 16-byte pieces
     static constexpr int PR = D / 8;
     static constexpr int LANES = 64 * NW;
     static constexpr int RPS = LANES / PR;              // rows per staging round
     static constexpr int NR = C / RPS;                  // rounds per matrix
     static_assert(LANES % PR == 0 && C % RPS == 0, "staging rows");
-    static constexpr int NWS = (WsLayout<true>::kBytesNorm / 16 + LANES - 1) / LANES;  // workspace pieces
-    static constexpr int NSTAGE = 3 * NR + NWS;
+    static constexpr int ws_pieces(bool pin)
+    {
+        return pin ? int(WsLayout<true>::kBytesNorm / 16) : (6 * kBlkBytes<true> + 2048) / 16;
+    }
+    static constexpr int nws(bool pin) { return (ws_pieces(pin) + LANES - 1) / LANES; }
+    // byte offset of workspace piece i (the same offset in the LDS slot, from kT)
+    static constexpr int ws_offset(bool pin, int i)
+    {
+        return (pin || 16 * i < 6 * kBlkBytes<true>) ? 16 * i : 16 * i + 6 * kBlkBytes<true>;
+    }
+    static constexpr int NSTAGE = 3 * NR + nws(true);
 };
 
 // A operand of K^T for state tile t: row r is key 32 (t/2) + 8 (r/4) + 4 (t%2) + r%4,
@@ -85,12 +95,11 @@ struct HeadStage {
 };
 
 // Issues the loads of chunk m (nv valid rows) into st.
-template <int D>
+template <int D, bool PIN>
 __device__ __forceinline__ void head_stage_load(HeadStage<D> &st, const unsigned char *k,
                                                 const unsigned char *q, const unsigned char *v,
                                                 const unsigned char *wsc, int64_t kq_bytes,
-                                                int64_t hd_bytes, int ws_bytes, int m, int nv,
-                                                int tid)
+                                                int64_t hd_bytes, int m, int nv, int tid)
 {
     using H = HeadCfg<D>;
     // wave-uniform chunk bases plus 32-bit lane offsets (64 token rows of all heads
@@ -108,17 +117,17 @@ __device__ __forceinline__ void head_stage_load(HeadStage<D> &st, const unsigned
         st.x[2 * H::NR + r] = *reinterpret_cast<const u32x4_t *>(vb + (row * hdb + col));
     }
 #pragma unroll
-    for (int r = 0; r < H::NWS; ++r) {
-        // pieces past the chunk's bytes re-read its last piece and are not stored
-        const int o = min(16 * (tid + r * H::LANES), ws_bytes - 16);
-        st.x[3 * H::NR + r] = *reinterpret_cast<const u32x4_t *>(wsc + o);
+    for (int r = 0; r < H::nws(PIN); ++r) {
+        // pieces past the chunk's last re-read it and are not stored
+        const int i = min(tid + r * H::LANES, H::ws_pieces(PIN) - 1);
+        st.x[3 * H::NR + r] = *reinterpret_cast<const u32x4_t *>(wsc + H::ws_offset(PIN, i));
     }
 }
 
 // Writes the staged chunk into an LDS slot.
-template <int D>
+template <int D, bool PIN>
 __device__ __forceinline__ void head_stage_store(const HeadStage<D> &st, unsigned char *slot,
-                                                 int ws_bytes, int tid)
+                                                 int tid)
 {
     using H = HeadCfg<D>;
     const int row0 = tid / H::PR, col = (tid % H::PR) * 16;
@@ -130,9 +139,45 @@ __device__ __forceinline__ void head_stage_store(const HeadStage<D> &st, unsigne
         *reinterpret_cast<u32x4_t *>(slot + H::kV + off) = st.x[2 * H::NR + r];
     }
 #pragma unroll
-    for (int r = 0; r < H::NWS; ++r) {
-        const int o = 16 * (tid + r * H::LANES);
-        if (o < ws_bytes) *reinterpret_cast<u32x4_t *>(slot + H::kT + o) = st.x[3 * H::NR + r];
+    for (int r = 0; r < H::nws(PIN); ++r) {
+        const int i = tid + r * H::LANES;
+        if (i < H::ws_pieces(PIN))
+            *reinterpret_cast<u32x4_t *>(slot + H::kT + H::ws_offset(PIN, i)) = st.x[3 * H::NR + r];
+    }
+}
+
+// P = e^{gam_r - gam_s} (q_r . k_s) / sqrt(d) for s <= r (zero above the diagonal)
+// from the chunk's K and Q rows in an LDS slot, written as the prep writes it: the
+// ten lower 16 x 16 tiles, tile (tt, tc) as half tc % 2 of the fragment units of
+// block (tt, tc / 2) (blocks in the order (0,0), (1,0), (2,0), (2,1), (3,0), (3,1)).
+// Wave w forms tiles w, w + nw, ...; the same products, scaling and rounding as
+// the prep, so P is identical bit for bit.  gam: the chunk's cumulative log gates.
+template <int D>
+__device__ __forceinline__ void head_form_p(unsigned char *slot, const float *gam, int wave,
+                                            int nw, int lane)
+{
+    using H = HeadCfg<D>;
+    const int gq = lane >> 4, cl = lane & 15;
+    for (int i = wave; i < 10; i += nw) {
+        const int tt = i < 1 ? 0 : i < 3 ? 1 : i < 6 ? 2 : 3;
+        const int tc = i - tt * (tt + 1) / 2;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < H::KS; ++ks)
+            acc = mma(row_frag<true>(slot + H::kK, H::RK, 16 * tc + cl, 32 * ks, gq),
+                      row_frag<true>(slot + H::kQ, H::RK, 16 * tt + cl, 32 * ks, gq), acc);
+        const int row = 16 * tt + cl, col0 = 16 * tc + 4 * gq;
+        const float g_row = gam[row];
+        const float4 gc = *reinterpret_cast<const float4 *>(gam + col0);
+        const float gcol[4] = {gc.x, gc.y, gc.z, gc.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float e = __expf(g_row - gcol[j]);
+            acc[j] = (col0 + j <= row) ? kOutScale<D> * e * acc[j] : 0.f;
+        }
+        const int b = tt < 2 ? tt : 2 * tt - 2 + (tc >> 1);
+        *reinterpret_cast<uint2 *>(slot + H::kP + b * kBlkBytes<true> + kFragBytes<true> * blk_unit(cl, gq) +
+                                   8 * (tc & 1)) = make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
     }
 }
 
@@ -149,7 +194,9 @@ void chunk_head_kernel(const void *__restrict__ q, const void *__restrict__ k,
     using H = HeadCfg<D>;
     using W = WsLayout<true>;
     constexpr int NT = H::NT, KT = H::KT, KS = H::KS;
-    constexpr int ws_bytes = NORM ? int(W::kBytesNorm) : int(W::kBytes);
+    // normalised rows keep P in the workspace (it needs the q row norms the prep
+    // forms); plain rows have the pass form P from the K and Q rows it stages anyway
+    constexpr bool PIN = NORM;
     constexpr int eg_row = NORM ? 4 : 1;
     extern __shared__ __align__(16) unsigned char smem[];
 
@@ -163,7 +210,7 @@ void chunk_head_kernel(const void *__restrict__ q, const void *__restrict__ k,
     const unsigned char *kp = static_cast<const unsigned char *>(k) + ktok0 * 2;
     const unsigned char *qp = static_cast<const unsigned char *>(q) + ktok0 * 2;
     const unsigned char *vp = static_cast<const unsigned char *>(v) + tok0 * 2;
-    const int64_t ws_stride = W::stride(NORM);
+    const int64_t ws_stride = W::kBytesNorm;   // the prep's stride for this pass
     const unsigned char *wsh = ws + sh * n_chunks * ws_stride;
     auto nv_of = [&](int m) { return static_cast<int>(min<int64_t>(C, n_tokens - int64_t(m) * C)); };
     const int nc = n_chunks;
@@ -186,20 +233,33 @@ void chunk_head_kernel(const void *__restrict__ q, const void *__restrict__ k,
         }
     }
 
+    if constexpr (!PIN) {
+        // the zero halves of P (tiles (0, 1) and (2, 3)), which no step writes
+        const int u = kFragBytes<true> * blk_unit(cl, gq) + 8;
+        if (wave == 0) {
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                unsigned char *pz = smem + sl * H::kSlot + H::kP;
+                *reinterpret_cast<uint2 *>(pz + u) = make_uint2(0u, 0u);
+                *reinterpret_cast<uint2 *>(pz + 3 * kBlkBytes<true> + u) = make_uint2(0u, 0u);
+            }
+        }
+    }
     HeadStage<D> st;
-    head_stage_load<D>(st, kp, qp, vp, wsh, kq_bytes, hd_bytes, ws_bytes, 0, nv_of(0), tid);
-    head_stage_store<D>(st, smem, ws_bytes, tid);
+    head_stage_load<D, PIN>(st, kp, qp, vp, wsh, kq_bytes, hd_bytes, 0, nv_of(0), tid);
+    head_stage_store<D, PIN>(st, smem, tid);
     {
         const int m1 = min(1, nc - 1);
-        head_stage_load<D>(st, kp, qp, vp, wsh + m1 * ws_stride, kq_bytes, hd_bytes, ws_bytes, m1,
-                           nv_of(m1), tid);
+        head_stage_load<D, PIN>(st, kp, qp, vp, wsh + m1 * ws_stride, kq_bytes, hd_bytes, m1,
+                                nv_of(m1), tid);
     }
     lds_barrier();
 
     uint16_t *obase = static_cast<uint16_t *>(out) + tok0;
     for (int n = 0; n < nc; ++n) {
-        const unsigned char *S = smem + (n & 1) * H::kSlot;
+        unsigned char *S = smem + (n & 1) * H::kSlot;
         const float *G = reinterpret_cast<const float *>(S + H::kG);
+        if constexpr (!PIN) head_form_p<D>(S, G + 5 * C, wave, H::NW, lane);
         // the state entering chunk n as bf16 operands (B of M^T, A of M)
         Frag<true> mb[NT][KS];
 #pragma unroll
@@ -263,6 +323,7 @@ void chunk_head_kernel(const void *__restrict__ q, const void *__restrict__ k,
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) O[i][tt] = mma(mb[i][ks], qf[tt], O[i][tt]);
         }
+        if constexpr (!PIN) lds_barrier();   // P formed by every wave
         Frag<true> pf[6];
 #pragma unroll
         for (int b = 0; b < 6; ++b) pf[b] = frag_blk<true>(S + H::kP + b * kBlkBytes<true>, lane);
@@ -313,10 +374,10 @@ void chunk_head_kernel(const void *__restrict__ q, const void *__restrict__ k,
         }
         // chunk n + 1 into the other slot, then the loads of chunk n + 2 (the last
         // chunk again near the end: loaded, never stored)
-        if (n + 1 < nc) head_stage_store<D>(st, smem + ((n + 1) & 1) * H::kSlot, ws_bytes, tid);
+        if (n + 1 < nc) head_stage_store<D, PIN>(st, smem + ((n + 1) & 1) * H::kSlot, tid);
         const int m2 = min(n + 2, nc - 1);
-        head_stage_load<D>(st, kp, qp, vp, wsh + m2 * ws_stride, kq_bytes, hd_bytes, ws_bytes, m2,
-                           nv_of(m2), tid);
+        head_stage_load<D, PIN>(st, kp, qp, vp, wsh + m2 * ws_stride, kq_bytes, hd_bytes, m2,
+                                nv_of(m2), tid);
         lds_barrier();
     }
 #pragma unroll

@@ -90,12 +90,13 @@ def test_attention_register_budget(kernels):
 
 def test_prep_register_budget(kernels):
     """bf16 rows of 128 (the headline prefill): five prep workgroups per CU, one wave
-    per SIMD each; the lag form's prep, which also forms the cross-chunk matrices,
-    three (two when the op normalises q and k)."""
+    per SIMD each (also the variant that leaves P to the whole-head pass); the lag
+    form's prep, which also forms the cross-chunk matrices, three (two when the op
+    normalises q and k)."""
     prep = {n: m for n, m in kernels.items() if "chunk_prep_kernelILi128ELb1E" in n}
-    assert len(prep) == 4, sorted(kernels)
+    assert len(prep) == 5, sorted(kernels)
     for n, m in prep.items():
-        # template arguments after <128, true>: NORM, LAG
+        # template arguments after <128, true>: NORM, LAG, PQ
         norm, lag = (n.split("chunk_prep_kernelILi128ELb1E")[1][i] == "1" for i in (2, 6))
         want = (2 if norm else 3) if lag else 5
         assert _waves_per_simd(m) >= want, (n, m, want)
