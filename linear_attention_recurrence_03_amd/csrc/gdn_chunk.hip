@@ -175,6 +175,29 @@ __device__ __forceinline__ void emit_p(const PrepTiles<R0, R1> &pt, unsigned cha
     }
 }
 
+// Prep timestamps (trace builds only): wave 0 of each of the first kPrepTraceGroups
+// workgroups records the shader clock at the start, when the chunk's rows have
+// landed, after the products, after the diagonal inverses, after the two levels of
+// off-diagonal blocks and at the end; gdn_prep_trace_read copies them out.
+#ifdef GDN_PHASE_TRACE
+constexpr int kPrepTraceGroups = 4096;
+__device__ uint64_t g_prep_trace[kPrepTraceGroups][8];
+#endif
+
+struct PrepTrace {
+    __device__ __forceinline__ void mark(int slot, int wave, int lane) const
+    {
+#ifdef GDN_PHASE_TRACE
+        if (blockIdx.x < kPrepTraceGroups && wave == 0 && lane == 0)
+            g_prep_trace[blockIdx.x][slot] = __builtin_amdgcn_s_memtime();
+#else
+        (void)slot;
+        (void)wave;
+        (void)lane;
+#endif
+    }
+};
+
 // One workgroup per (seq, head, chunk): the state-independent part of the chunk.
 //   0. K rows -> LDS by LDS-DMA (all waves); Q rows -> operand registers
 //      (waves 2, 3); gate sums (wave 0)
@@ -268,6 +291,8 @@ __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM, LAG>()))) void chu
     const int64_t t0 = int64_t(n) * C;
     const int nv = static_cast<int>(min<int64_t>(C, n_tokens - t0));
     unsigned char *dst = ws + chunk_id * kStride;
+    const PrepTrace ptr;
+    ptr.mark(0, wave, lane);
 
     // 0. K rows of key head h % n_k_heads into LDS; waves 2 and 3 load the Q rows
     //    of their row tiles ({0, 3} and {1, 2}) as MFMA operands (lane (g, i): row
@@ -358,6 +383,7 @@ __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM, LAG>()))) void chu
     }
     wait_vmem_le<0>();
     lds_barrier();
+    ptr.mark(1, wave, lane);
 
     // 0b. normalised rows: 1 / sqrt(|x_r|^2 + eps) for the K rows (waves 0, 1: 32
     //     rows each, two lanes per row, from LDS) and the Q rows (waves 2, 3: their
@@ -431,6 +457,7 @@ __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM, LAG>()))) void chu
             prep_products<D, BF16, true, 0, 3>(pt, smem, sG, sD, sN, lane, nullptr);
             lds_barrier();
             store_tiles<BF16, 0, 3>(pt, sAe, LDT, lane);
+            ptr.mark(2, wave, lane);
         } else {
             PrepTiles<1, 2> pt;
             prep_products<D, BF16, true, 1, 2>(pt, smem, sG, sD, sN, lane, nullptr);
@@ -493,6 +520,7 @@ __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM, LAG>()))) void chu
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) sT[(16 * b + r) * LDT + 16 * b + c] = from_f<E>(x[r]);
+        ptr.mark(3, wave, lane);
     } else if (wave == 1) {
         // blocks (1,0), (3,2), (0,1), (2,3) of T are read (as zeros) before they
         // are formed or as the upper triangle: 16 rows x 16 elements each
@@ -522,6 +550,7 @@ __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM, LAG>()))) void chu
     }
     lds_barrier();
 
+    ptr.mark(4, wave, lane);
     // 4. column tile j = wave of the lower-left 32x32 block
     if (wave < 2) {
         const int j = wave;
@@ -539,6 +568,7 @@ __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM, LAG>()))) void chu
     }
     lds_barrier();
 
+    ptr.mark(5, wave, lane);
     // 5. T as six fragment blocks.  Every entry of sT above the diagonal that a
     //    block covers is zero: the diagonal blocks' upper triangles come out of
     //    the substitution as zeros and blocks (0,1), (2,3) were cleared.
@@ -555,6 +585,7 @@ __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM, LAG>()))) void chu
         for (int x = 0; x < FB / 16; ++x) ub[x] = w[x];
     }
 
+    ptr.mark(6, wave, lane);
     // 6. LAG: R = T Y for row tiles tr of T (B operand: T's rows, k = rows of Y in
     //    fragment order; blocks of T above the diagonal are zero and skipped).  The
     //    accumulator of (tj = wave, tr) gives lane (g, i) R[16 tr + i][16 w + 4g + jj],
@@ -1440,6 +1471,17 @@ size_t chunk_workspace_bytes(int bf16, int lag, int64_t n_seqs, int64_t n_tokens
 }
 
 #ifdef GDN_PHASE_TRACE
+// Copies the timestamps of the last prep out (trace builds only; not part of the
+// installed interface).
+extern "C" int gdn_prep_trace_read(void *host, size_t bytes)
+{
+    if (bytes > sizeof(g_prep_trace)) bytes = sizeof(g_prep_trace);
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_prep_trace), bytes, 0, hipMemcpyDeviceToHost) ==
+                   hipSuccess
+               ? 0
+               : -1;
+}
+
 // Copies the timestamps of the last per-tile pass out (trace builds only; not part
 // of the installed interface).
 extern "C" int gdn_scan_trace_read(void *host, size_t bytes)

@@ -329,6 +329,51 @@ __device__ __forceinline__ floatx4 col4(const unsigned char *base, int stride, i
     return r;
 }
 
+// P = e^{gam_r - gam_s} (q_r . k_s) / sqrt(d) for s <= r (zero above the diagonal),
+// for a pass that forms P itself from a chunk's K and Q rows in LDS (bf16, rows of
+// `rk` bytes, k order 8g..8g+7 per lane group), written as the prep writes it: the
+// ten lower 16 x 16 tiles, tile (tt, tc) as half tc % 2 of the fragment units of
+// block (tt, tc / 2) of `pdst`.  The caller forms tiles first, first + step, ...;
+// the products, scaling and rounding are the prep's, so P is identical bit for
+// bit.  gam: the chunk's cumulative log gates.
+template <int D>
+__device__ __forceinline__ void form_p(const unsigned char *kb, const unsigned char *qb, int rk,
+                                       const float *gam, unsigned char *pdst, int first, int step,
+                                       int lane)
+{
+    const int gq = lane >> 4, cl = lane & 15;
+    for (int i = first; i < 10; i += step) {
+        const int tt = i < 1 ? 0 : i < 3 ? 1 : i < 6 ? 2 : 3;
+        const int tc = i - tt * (tt + 1) / 2;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            acc = mma(row_frag<true>(kb, rk, 16 * tc + cl, 32 * ks, gq),
+                      row_frag<true>(qb, rk, 16 * tt + cl, 32 * ks, gq), acc);
+        const int row = 16 * tt + cl, col0 = 16 * tc + 4 * gq;
+        const float g_row = gam[row];
+        const float4 gc = *reinterpret_cast<const float4 *>(gam + col0);
+        const float gcol[4] = {gc.x, gc.y, gc.z, gc.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float e = __expf(g_row - gcol[j]);
+            acc[j] = (col0 + j <= row) ? kOutScale<D> * e * acc[j] : 0.f;
+        }
+        const int b = tt < 2 ? tt : 2 * tt - 2 + (tc >> 1);
+        *reinterpret_cast<uint2 *>(pdst + b * kBlkBytes<true> + kFragBytes<true> * blk_unit(cl, gq) +
+                                   8 * (tc & 1)) = make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
+    }
+}
+
+// The halves of P's fragment units that form_p never writes (tiles (0, 1) and
+// (2, 3), above the diagonal), set to zero.
+__device__ __forceinline__ void zero_p_halves(unsigned char *pdst, int lane)
+{
+    const int u = kFragBytes<true> * blk_unit(lane & 15, lane >> 4) + 8;
+    *reinterpret_cast<uint2 *>(pdst + u) = make_uint2(0u, 0u);
+    *reinterpret_cast<uint2 *>(pdst + 3 * kBlkBytes<true> + u) = make_uint2(0u, 0u);
+}
+
 // Lower-triangular block matrix (six fragment blocks) times the 64-row B operand
 // given as two k halves: rows tt of the product.
 template <bool BF16>

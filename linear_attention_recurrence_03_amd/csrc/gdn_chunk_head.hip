@@ -146,41 +146,6 @@ __device__ __forceinline__ void head_stage_store(const HeadStage<D> &st, unsigne
     }
 }
 
-// P = e^{gam_r - gam_s} (q_r . k_s) / sqrt(d) for s <= r (zero above the diagonal)
-// from the chunk's K and Q rows in an LDS slot, written as the prep writes it: the
-// ten lower 16 x 16 tiles, tile (tt, tc) as half tc % 2 of the fragment units of
-// block (tt, tc / 2) (blocks in the order (0,0), (1,0), (2,0), (2,1), (3,0), (3,1)).
-// Wave w forms tiles w, w + nw, ...; the same products, scaling and rounding as
-// the prep, so P is identical bit for bit.  gam: the chunk's cumulative log gates.
-template <int D>
-__device__ __forceinline__ void head_form_p(unsigned char *slot, const float *gam, int wave,
-                                            int nw, int lane)
-{
-    using H = HeadCfg<D>;
-    const int gq = lane >> 4, cl = lane & 15;
-    for (int i = wave; i < 10; i += nw) {
-        const int tt = i < 1 ? 0 : i < 3 ? 1 : i < 6 ? 2 : 3;
-        const int tc = i - tt * (tt + 1) / 2;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < H::KS; ++ks)
-            acc = mma(row_frag<true>(slot + H::kK, H::RK, 16 * tc + cl, 32 * ks, gq),
-                      row_frag<true>(slot + H::kQ, H::RK, 16 * tt + cl, 32 * ks, gq), acc);
-        const int row = 16 * tt + cl, col0 = 16 * tc + 4 * gq;
-        const float g_row = gam[row];
-        const float4 gc = *reinterpret_cast<const float4 *>(gam + col0);
-        const float gcol[4] = {gc.x, gc.y, gc.z, gc.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float e = __expf(g_row - gcol[j]);
-            acc[j] = (col0 + j <= row) ? kOutScale<D> * e * acc[j] : 0.f;
-        }
-        const int b = tt < 2 ? tt : 2 * tt - 2 + (tc >> 1);
-        *reinterpret_cast<uint2 *>(slot + H::kP + b * kBlkBytes<true> + kFragBytes<true> * blk_unit(cl, gq) +
-                                   8 * (tc & 1)) = make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
-    }
-}
-
 // The whole-head scan over chunks [c0, c1) of one (seq, head).  m_in: the state
 // entering chunk c0 ([value][key] fp32, or null for zeros); m_out: where the state
 // after chunk c1 - 1 goes.
@@ -234,15 +199,10 @@ void chunk_head_kernel(const void *__restrict__ q, const void *__restrict__ k,
     }
 
     if constexpr (!PIN) {
-        // the zero halves of P (tiles (0, 1) and (2, 3)), which no step writes
-        const int u = kFragBytes<true> * blk_unit(cl, gq) + 8;
+        // the zero halves of P, which no step writes
         if (wave == 0) {
 #pragma unroll
-            for (int sl = 0; sl < 2; ++sl) {
-                unsigned char *pz = smem + sl * H::kSlot + H::kP;
-                *reinterpret_cast<uint2 *>(pz + u) = make_uint2(0u, 0u);
-                *reinterpret_cast<uint2 *>(pz + 3 * kBlkBytes<true> + u) = make_uint2(0u, 0u);
-            }
+            for (int sl = 0; sl < 2; ++sl) zero_p_halves(smem + sl * H::kSlot + H::kP, lane);
         }
     }
     HeadStage<D> st;
@@ -259,7 +219,7 @@ void chunk_head_kernel(const void *__restrict__ q, const void *__restrict__ k,
     for (int n = 0; n < nc; ++n) {
         unsigned char *S = smem + (n & 1) * H::kSlot;
         const float *G = reinterpret_cast<const float *>(S + H::kG);
-        if constexpr (!PIN) head_form_p<D>(S, G + 5 * C, wave, H::NW, lane);
+        if constexpr (!PIN) form_p<D>(S + H::kK, S + H::kQ, H::RK, G + 5 * C, S + H::kP, wave, H::NW, lane);
         // the state entering chunk n as bf16 operands (B of M^T, A of M)
         Frag<true> mb[NT][KS];
 #pragma unroll

@@ -16,6 +16,13 @@ X (K M^T, E, Delta = T E), U (the state update) and O (the output) of value tile
   wait A/B    arriving at a barrier to leaving it
   last at A/B how often each wave is the last of the three to arrive
 
+``--pass prep``: the prep kernel of the same call (the per-tile pass's variant),
+wave 0 of each of its first 4,096 workgroups: the phases of a workgroup (rows
+landed, products, diagonal inverses, the two levels of off-diagonal blocks, the T
+stores) and when workgroups start and end relative to the first start on their XCD
+(consecutive workgroups go to the eight XCDs in turn, and each XCD's shader clock
+has its own origin).
+
 ``--pass lag``: the two-chunk-lag pass (algo "chunked_lag"), waves C, G, U, O and
 one barrier per phase:
 
@@ -25,7 +32,7 @@ one barrier per phase:
 
 and the phase length (opening stamp to the next).
 
-Usage: python -m linear_attention_recurrence_03_amd.phase_trace [--pass scan|lag] [--json OUT]
+Usage: python -m linear_attention_recurrence_03_amd.phase_trace [--pass scan|prep|lag] [--json OUT]
 """
 import argparse
 import ctypes
@@ -103,9 +110,33 @@ def summarize_scan(raw, n_chunks, skip=3):
     return res
 
 
+PREP_GROUPS = 4096
+PREP_PHASES = ("rows landed", "products", "inverse", "level 1", "level 2", "T stored")
+
+
+def summarize_prep(raw, n_groups):
+    """raw: uint64 array [PREP_GROUPS][8], stamps 0..6 of each workgroup's wave 0.
+    Statistics over the first n_groups workgroups."""
+    n = min(n_groups, PREP_GROUPS)
+    rows = [[int(x) for x in raw[i][:7]] for i in range(n)]
+    # per-XCD origin: workgroup i runs on XCD i % 8
+    t0 = {x: min(rows[i][0] for i in range(x, n, 8)) for x in range(min(8, n))}
+
+    def stat(xs):
+        return {"median": statistics.median(xs), "p10": _pct(xs, 0.1), "p90": _pct(xs, 0.9),
+                "max": max(xs)} if xs else None
+    res = {"groups": n}
+    for i, name in enumerate(PREP_PHASES):
+        res[name] = stat([r[i + 1] - r[i] for r in rows])
+    res["total"] = stat([r[6] - r[0] for r in rows])
+    res["start"] = stat([r[0] - t0[i % 8] for i, r in enumerate(rows)])
+    res["end"] = stat([r[6] - t0[i % 8] for i, r in enumerate(rows)])
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--pass", dest="which", choices=("scan", "lag"), default="scan",
+    ap.add_argument("--pass", dest="which", choices=("scan", "prep", "lag"), default="scan",
                     help="which chunk-to-chunk pass to trace")
     ap.add_argument("--json", help="also write the statistics to this file")
     ap.add_argument("--lib", help="trace build to load (default: libgdn_trace.so here)")
@@ -123,10 +154,11 @@ def main():
     from linear_attention_recurrence_03_amd import inputs
 
     lib = gdn._lib()
-    read = lib.gdn_scan_trace_read if args.which == "scan" else lib.gdn_phase_trace_read
+    read = {"scan": lib.gdn_scan_trace_read, "prep": lib.gdn_prep_trace_read,
+            "lag": lib.gdn_phase_trace_read}[args.which]
     read.restype = ctypes.c_int
     read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
-    algo = "chunked" if args.which == "scan" else "chunked_lag"
+    algo = "chunked_lag" if args.which == "lag" else "chunked"
     wl = inputs.WORKLOADS[4]
     x = inputs.make(wl)
     S, T, H, D = wl.shape()
@@ -168,6 +200,18 @@ def main():
             rel = res["release_after_last_traced_arrival"][bar]
             print("barrier %s: last traced arrival %s; release after it: median %d cycles" % (
                 bar, ", ".join("%s %d" % kv for kv in res["last_at"][bar].items()), rel["median"]))
+    elif args.which == "prep":
+        raw = np.zeros((PREP_GROUPS, 8), dtype=np.uint64)
+        assert read(raw.ctypes.data, raw.nbytes) == 0
+        n_groups = S * H * n_chunks
+        res = summarize_prep(raw, n_groups)
+        res["call_us"] = a.elapsed_time(b) * 1e3
+        print("traced call (prep + per-tile pass): %.1f us, %d prep workgroups, %d traced" % (
+            res["call_us"], n_groups, res["groups"]))
+        print("%-12s %8s %8s %8s %8s (cycles)" % ("", "median", "p10", "p90", "max"))
+        for k in PREP_PHASES + ("total", "start", "end"):
+            v = res[k]
+            print("%-12s %8d %8d %8d %8d" % (k, v["median"], v["p10"], v["p90"], v["max"]))
     else:
         raw = np.zeros((GROUPS, 4, PHASES, 3), dtype=np.uint64)
         assert read(raw.ctypes.data, raw.nbytes) == 0

@@ -37,3 +37,17 @@ def test_lag_summary_of_synthetic_stamps():
     assert res["phase"]["median"] == 4000
     assert res["C"]["work"]["median"] == 1000 and res["O"]["work"]["median"] == 4000
     assert res["G"]["operands"]["median"] == 200 and res["U"]["at_barrier"]["median"] == 1000
+
+
+def test_prep_summary_of_synthetic_stamps():
+    raw = np.zeros((pt.PREP_GROUPS, 8), dtype=np.uint64)
+    n_groups = 100
+    for i in range(n_groups):
+        t0 = 1_000 + 50 * i
+        steps = [0, 400, 900, 1700, 1800, 1900, 2000]   # cumulative stamps
+        raw[i, :7] = [t0 + x for x in steps]
+    res = pt.summarize_prep(raw, n_groups)
+    assert res["rows landed"]["median"] == 400 and res["inverse"]["median"] == 800
+    assert res["total"]["median"] == 2000
+    # starts are taken from the first start on each XCD (workgroup i on XCD i % 8)
+    assert res["start"]["max"] == 50 * (99 - 3) and res["end"]["max"] == 50 * 96 + 2000
