@@ -32,7 +32,12 @@ one barrier per phase:
 
 and the phase length (opening stamp to the next).
 
-Usage: python -m linear_attention_recurrence_03_amd.phase_trace [--pass scan|prep|lag] [--json OUT]
+``--shape S,T,H`` traces another size (d=128, bf16): e.g. 2,4096,32 has more value tiles
+than compute units, so the per-tile pass runs two tiles per workgroup (waves X_0, U_0,
+O_0 of tile 0 are traced).
+
+Usage: python -m linear_attention_recurrence_03_amd.phase_trace [--pass scan|prep|lag]
+       [--shape S,T,H] [--json OUT]
 """
 import argparse
 import ctypes
@@ -139,6 +144,7 @@ def main():
     ap.add_argument("--pass", dest="which", choices=("scan", "prep", "lag"), default="scan",
                     help="which chunk-to-chunk pass to trace")
     ap.add_argument("--json", help="also write the statistics to this file")
+    ap.add_argument("--shape", help="n_seqs,n_tokens,n_heads (default 1,4096,32)")
     ap.add_argument("--lib", help="trace build to load (default: libgdn_trace.so here)")
     args = ap.parse_args()
     here = os.path.dirname(os.path.abspath(__file__))
@@ -160,6 +166,9 @@ def main():
     read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     algo = "chunked_lag" if args.which == "lag" else "chunked"
     wl = inputs.WORKLOADS[4]
+    if args.shape:
+        s_, t_, h_ = (int(v) for v in args.shape.split(","))
+        wl = inputs.Workload("traced", s_, t_, h_, 128, "bf16", "zeros", "standard", seed=11)
     x = inputs.make(wl)
     S, T, H, D = wl.shape()
     sets = []
