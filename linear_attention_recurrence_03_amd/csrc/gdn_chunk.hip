@@ -924,25 +924,40 @@ __device__ __forceinline__ void x_step(const XOps<D, BF16> &o, const unsigned ch
     pD[64 + lane] = acc_frag<BF16>(dl[2], dl[3]);
 }
 
-// U_vt: publishes its M^T tiles as fragment blocks with k (key) order 8g..8g+7:
-// tile t (keys 16t..16t+15) fills half of the units of block t/2.
+// U_vt: publishes its M^T tiles as fragment blocks with k (key) order 8g..8g+7.
+// bf16: U's tiles hold keys in the permuted order of the whole-head pass (tile t,
+// lane (gq, cl): keys 32 (t/2) + 8 gq + 4 (t%2) + 0..3), so tiles 2 ks and 2 ks + 1
+// together are the lane's whole unit of block ks.  fp32: tile t holds keys
+// 16t + 4gq + 0..3 and fills half of the units of block t/2.
 template <int D, bool BF16, int VT>
 __device__ __forceinline__ void publish_mt(const floatx4 (&Mt)[D / 16], unsigned char *smem, int vt,
                                            int lane)
 {
     using F = ScanCfg<D, BF16, VT>;
     const int gq = lane >> 4, cl = lane & 15;
+    if constexpr (BF16) {
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-        // lane (gq, cl) holds keys 16t + 4gq + 0..3: unit group 2 (t & 1) + gq / 2,
-        // elements 4 (gq & 1) .. +3
-        unsigned char *u = smem + F::kPubM + (vt * F::KS + (t >> 1)) * F::BLK +
-                           F::FB * blk_unit(cl, 2 * (t & 1) + (gq >> 1)) + 4 * F::ES * (gq & 1);
-        if constexpr (BF16)
-            *reinterpret_cast<uint2 *>(u) = make_uint2(pack2(Mt[t][0], Mt[t][1]), pack2(Mt[t][2], Mt[t][3]));
-        else
+        for (int ks = 0; ks < F::KS; ++ks)
+            *reinterpret_cast<Frag<true> *>(smem + F::kPubM + (vt * F::KS + ks) * F::BLK +
+                                            F::FB * blk_unit(cl, gq)) =
+                acc_frag<true>(Mt[2 * ks], Mt[2 * ks + 1]);
+    } else {
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+            // lane (gq, cl) holds keys 16t + 4gq + 0..3: unit group 2 (t & 1) + gq / 2,
+            // elements 4 (gq & 1) .. +3
+            unsigned char *u = smem + F::kPubM + (vt * F::KS + (t >> 1)) * F::BLK +
+                               F::FB * blk_unit(cl, 2 * (t & 1) + (gq >> 1)) + 4 * F::ES * (gq & 1);
             *reinterpret_cast<float4 *>(u) = make_float4(Mt[t][0], Mt[t][1], Mt[t][2], Mt[t][3]);
+        }
     }
+}
+
+// Key of element j of U's state tile t in lane group gq (see publish_mt).
+template <bool BF16>
+__device__ __forceinline__ int u_key(int t, int gq)
+{
+    return BF16 ? 32 * (t >> 1) + 8 * gq + 4 * (t & 1) : 16 * t + 4 * gq;
 }
 
 // U_vt operands of one chunk (read between barriers A and B): K^T fragments
@@ -954,8 +969,13 @@ __device__ __forceinline__ void u_load(Frag<BF16> (&akt)[D / 16][2], float &eC,
     using F = ScanCfg<D, BF16, VT>;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
-        akt[t][0] = frag_cols<BF16>(kt + F::kK, F::RK, 0, 16 * t, lane);
-        akt[t][1] = frag_cols<BF16>(kt + F::kK, F::RK, 32, 16 * t, lane);
+        if constexpr (BF16) {
+            akt[t][0] = key_tr_frag(kt + F::kK, F::RK, 0, t, lane);
+            akt[t][1] = key_tr_frag(kt + F::kK, F::RK, 32, t, lane);
+        } else {
+            akt[t][0] = frag_cols<BF16>(kt + F::kK, F::RK, 0, 16 * t, lane);
+            akt[t][1] = frag_cols<BF16>(kt + F::kK, F::RK, 32, 16 * t, lane);
+        }
     }
     eC = reinterpret_cast<const float *>(kt + F::kG)[3 * C];
 }
@@ -1271,13 +1291,13 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
             tr.mark(n, 3, lane);
         }
     } else if (role == kRoleU) {
-        // Mt[t][j] = M[v0 + 16 vt + lane%16][16 t + 4 (lane/16) + j]
-        const int64_t st_off = sh * D * D + int64_t(v0 + 16 * vt + (lane & 15)) * D + 4 * (lane >> 4);
+        // Mt[t][j] = M[v0 + 16 vt + lane%16][u_key(t, lane/16) + j]
+        const int64_t st_off = sh * D * D + int64_t(v0 + 16 * vt + (lane & 15)) * D;
         floatx4 Mt[D / 16];
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
             if (state_in) {
-                const float4 m = *reinterpret_cast<const float4 *>(state_in + st_off + 16 * t);
+                const float4 m = *reinterpret_cast<const float4 *>(state_in + st_off + u_key<BF16>(t, lane >> 4));
                 Mt[t] = floatx4{m.x, m.y, m.z, m.w};
             } else {
                 Mt[t] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -1302,7 +1322,7 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
         }
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
-            *reinterpret_cast<float4 *>(state_out + st_off + 16 * t) =
+            *reinterpret_cast<float4 *>(state_out + st_off + u_key<BF16>(t, lane >> 4)) =
                 make_float4(Mt[t][0], Mt[t][1], Mt[t][2], Mt[t][3]);
     } else {
         E *obase = static_cast<E *>(out) + tok0 + v0 + 16 * vt;

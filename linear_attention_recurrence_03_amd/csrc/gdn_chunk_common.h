@@ -374,6 +374,27 @@ __device__ __forceinline__ void zero_p_halves(unsigned char *pdst, int lane)
     *reinterpret_cast<uint2 *>(pdst + 3 * kBlkBytes<true> + u) = make_uint2(0u, 0u);
 }
 
+// A operand of K^T for state tile t in the permuted key order of the whole-head pass
+// and the per-tile pass's U waves: row r is key 32 (t/2) + 8 (r/4) + 4 (t%2) + r%4,
+// k is tokens t0 + 4g + j, t0 + 16 + 4g + j.  Two transposing reads: lane p of a group
+// fetches row t0 + 4g + p/4 (then 16 rows lower) at keys kb + 8 (p mod 4) .. +3, and
+// lane i receives the (i mod 4)-th value fetched by lane 4j + i/4.
+__device__ __forceinline__ Frag<true> key_tr_frag(const unsigned char *base, int stride, int t0,
+                                                   int t, int lane)
+{
+    const int g = lane >> 4, p = lane & 15;
+    const int key = 32 * (t >> 1) + 4 * (t & 1) + 8 * (p & 3);
+    const unsigned char *a1 = base + (t0 + 4 * g + (p >> 2)) * stride + 2 * key;
+    typedef __attribute__((address_space(3))) short4_t lds_short4;
+    const short4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a1));
+    const short4_t r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a1 + 16 * stride));
+    Frag<true> f;
+    const uint2 u1 = __builtin_bit_cast(uint2, r1);
+    const uint2 u2 = __builtin_bit_cast(uint2, r2);
+    f.u = make_uint4(u1.x, u1.y, u2.x, u2.y);
+    return f;
+}
+
 // Lower-triangular block matrix (six fragment blocks) times the 64-row B operand
 // given as two k halves: rows tt of the product.
 template <bool BF16>

@@ -66,26 +66,6 @@ struct HeadCfg {
     static constexpr int NSTAGE = 3 * NR + nws(true);
 };
 
-// A operand of K^T for state tile t: row r is key 32 (t/2) + 8 (r/4) + 4 (t%2) + r%4,
-// k is tokens t0 + 4g + j, t0 + 16 + 4g + j.  Two transposing reads: lane p of a group
-// fetches row t0 + 4g + p/4 (then 16 rows lower) at keys kb + 8 (p mod 4) .. +3, and
-// lane i receives the (i mod 4)-th value fetched by lane 4j + i/4.
-__device__ __forceinline__ Frag<true> head_kt_frag(const unsigned char *base, int stride, int t0,
-                                                   int t, int lane)
-{
-    const int g = lane >> 4, p = lane & 15;
-    const int key = 32 * (t >> 1) + 4 * (t & 1) + 8 * (p & 3);
-    const unsigned char *a1 = base + (t0 + 4 * g + (p >> 2)) * stride + 2 * key;
-    typedef __attribute__((address_space(3))) short4_t lds_short4;
-    const short4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a1));
-    const short4_t r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(a1 + 16 * stride));
-    Frag<true> f;
-    const uint2 u1 = __builtin_bit_cast(uint2, r1);
-    const uint2 u2 = __builtin_bit_cast(uint2, r2);
-    f.u = make_uint4(u1.x, u1.y, u2.x, u2.y);
-    return f;
-}
-
 // One chunk's data in flight to LDS: each lane's 16-byte pieces (a native vector
 // type, so that the array lives in registers).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -327,8 +307,8 @@ void chunk_head_kernel(const void *__restrict__ q, const void *__restrict__ k,
         }
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-            const Frag<true> k0 = head_kt_frag(S + H::kK, H::RK, 0, t, lane);
-            const Frag<true> k1 = head_kt_frag(S + H::kK, H::RK, 32, t, lane);
+            const Frag<true> k0 = key_tr_frag(S + H::kK, H::RK, 0, t, lane);
+            const Frag<true> k1 = key_tr_frag(S + H::kK, H::RK, 32, t, lane);
 #pragma unroll
             for (int i = 0; i < NT; ++i) Mt[i][t] = mma(k1, dt[i][1], mma(k0, dt[i][0], Mt[i][t] * ec));
         }
