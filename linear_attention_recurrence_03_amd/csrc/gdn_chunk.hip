@@ -71,27 +71,40 @@ __device__ __forceinline__ void prep_products(PrepTiles<R0, R1> &pt, const unsig
                                               const float *sG, float *sD, const float *sN,
                                               int lane, const Frag<BF16> *fq)
 {
+    static_assert(R0 < R1, "row tiles");
     using L = PrepSmem<D, BF16>;
     constexpr int KS = D / 32;
     const int gq = lane >> 4, cl = lane & 15;
     const unsigned char *sK = smem + L::kK;
+    // operands of the two row tiles: K rows (K K^T) or the Q rows already in registers
+    Frag<BF16> fa[2][KS];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int tr = i ? R1 : R0;
-        Frag<BF16> fa[KS];
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if constexpr (KK) fa[ks] = row_frag<BF16>(sK, L::RK, 16 * tr + cl, 32 * ks, gq);
-            else fa[ks] = fq[i * KS + ks];   // Q rows, already in registers
+            if constexpr (KK) fa[i][ks] = row_frag<BF16>(sK, L::RK, 16 * (i ? R1 : R0) + cl, 32 * ks, gq);
+            else fa[i][ks] = fq[i * KS + ks];
         }
-        const int row = 16 * tr + cl;
-        const float g_row = sG[row];
+    // column tiles in order, each column tile's K rows read once for both row tiles
+    // (for K K^T the row tiles' own operands serve as their column tiles)
 #pragma unroll
-        for (int tc = 0; tc <= (i ? R1 : R0); ++tc) {
+    for (int tc = 0; tc <= R1; ++tc) {
+        Frag<BF16> kc[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (KK && tc == R0) kc[ks] = fa[0][ks];
+            else if (KK && tc == R1) kc[ks] = fa[1][ks];
+            else kc[ks] = row_frag<BF16>(sK, L::RK, 16 * tc + cl, 32 * ks, gq);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int tr = i ? R1 : R0;
+            if (tc > tr) continue;
+            const int row = 16 * tr + cl;
+            const float g_row = sG[row];
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                acc = mma(row_frag<BF16>(sK, L::RK, 16 * tc + cl, 32 * ks, gq), fa[ks], acc);
+            for (int ks = 0; ks < KS; ++ks) acc = mma(kc[ks], fa[i][ks], acc);
             const int col0 = 16 * tc + 4 * gq;
             if (sN) {  // normalised rows: (x_r / |x_r|) . (k_s / |k_s|)
                 const float rr = sN[(KK ? 0 : C) + row];
