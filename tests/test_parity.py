@@ -155,6 +155,32 @@ def test_many_row_blocks(gdn, dtype):
     check(gdn, x, dtype, "chunked", what="many row blocks")
 
 
+# Degenerate gates and betas, where the recurrence reduces to a simpler one (the
+# oracle is pinned to these closed forms in test_oracle.py): beta = 0 (no write,
+# the state only decays; gates a hundredth of the standard recipe's, so that the
+# state stays far above fp32's smallest normal numbers, which the kernels flush to
+# zero below), g = 0 (no decay: the plain delta rule), beta = 1 with g = 0 (each
+# write replaces the value stored along its key), and g = -40 (every token forgets
+# all before it: exp underflows to zero inside the chunked forms).
+_DEGENERATE = {
+    "beta0": lambda g, b: (0.01 * g, np.zeros_like(b)),
+    "g0": lambda g, b: (np.zeros_like(g), b),
+    "beta1_g0": lambda g, b: (np.zeros_like(g), np.ones_like(b)),
+    "forget": lambda g, b: (np.full_like(g, -40.0), b),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_DEGENERATE))
+@pytest.mark.parametrize("dtype,algo", [("f32", "recurrent"), ("f32", "chunked"),
+                                        ("bf16", "recurrent"), ("bf16", "chunked"),
+                                        ("bf16", "chunked_head"), ("bf16", "chunked_lag")])
+def test_degenerate_gates_and_betas(gdn, case, dtype, algo):
+    x = inputs.custom(1, 130, 3, 64, dtype=dtype, state="normal", seed=31)
+    x["g"], x["beta"] = (np.ascontiguousarray(a, dtype=np.float32)
+                         for a in _DEGENERATE[case](x["g"], x["beta"]))
+    check(gdn, x, dtype, algo, what="degenerate " + case)
+
+
 # ---- the two-chunk-lag form of the chunked pass (bf16 rows) ----------------------
 
 @pytest.mark.parametrize("D", [32, 64, 96, 128])
