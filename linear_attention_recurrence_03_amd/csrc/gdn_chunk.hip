@@ -1184,9 +1184,14 @@ __device__ __forceinline__ void producer_loop(const ScanPtrs &pt, unsigned char 
 
 // Per-tile pass timestamps (trace builds only): for waves X_0, U_0, O_0 and each
 // chunk, arriving at and leaving barrier A (slots 0, 1), arriving at and leaving
-// barrier B (slots 2, 3); gdn_scan_trace_read copies them out.
+// barrier B (slots 2, 3); row [3][0] holds the workgroup's edges: X_0 starting,
+// X_0 leaving the first barrier, U_0 done storing the state, O_0 done storing the
+// last output; gdn_scan_trace_read copies them out.
 #ifdef GDN_PHASE_TRACE
 __device__ uint64_t g_scan_trace[kTraceGroups][4][kTracePhases][4];
+// every workgroup's X_0 start, U_0 end and O_0 end on the chip-wide 100 MHz clock
+constexpr int kSpanGroups = 4096;
+__device__ uint64_t g_scan_span[kSpanGroups][4];
 #endif
 
 struct ScanTrace {
@@ -1200,6 +1205,19 @@ struct ScanTrace {
 #else
         (void)n;
         (void)slot;
+        (void)lane;
+#endif
+    }
+    __device__ __forceinline__ void edge(int which, int lane) const
+    {
+#ifdef GDN_PHASE_TRACE
+        if (which >= 2) __builtin_amdgcn_s_waitcnt(0);  // the stores have left the wave
+        if (wg < kTraceGroups && role >= 0 && lane == 0)
+            g_scan_trace[wg][3][0][which] = __builtin_amdgcn_s_memtime();
+        if (wg < kSpanGroups && role >= 0 && lane == 0 && which != 1)
+            g_scan_span[wg][which == 0 ? 0 : which - 1] = __builtin_amdgcn_s_memrealtime();
+#else
+        (void)which;
         (void)lane;
 #endif
     }
@@ -1291,7 +1309,9 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
     const ScanTrace tr{b, (vt == 0 && role != kRoleProd && PIPE) ? role : -1};
     if (role == kRoleX) {
         XOps<D, BF16> ops;
+        tr.edge(0, lane);
         if constexpr (PIPE) lds_barrier();  // B_{-1}
+        tr.edge(1, lane);
         for (int n = 0; n < nc; ++n) {
             if constexpr (!PIPE) lds_barrier();  // L_n
             x_load<D, BF16, VT>(ops, kt_slot(n), vt, lane);
@@ -1337,6 +1357,7 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
         for (int t = 0; t < D / 16; ++t)
             *reinterpret_cast<float4 *>(state_out + st_off + u_key<BF16>(t, lane >> 4)) =
                 make_float4(Mt[t][0], Mt[t][1], Mt[t][2], Mt[t][3]);
+        tr.edge(2, lane);
     } else {
         E *obase = static_cast<E *>(out) + tok0 + v0 + 16 * vt;
         constexpr int eg_row = NORM ? 4 : 1;  // e^gam, or e^gam / |q| for normalised rows
@@ -1356,6 +1377,7 @@ __global__ __launch_bounds__(64 * (3 * VT + kProducers)) void chunk_scan_kernel(
             o_finish<D, BF16, VT>(ops, smem, vt, lane, acc, obase + int64_t(n) * C * hd, hd,
                                   nv_of(n));
         }
+        tr.edge(3, lane);
     }
 }
 
@@ -1510,6 +1532,17 @@ extern "C" int gdn_prep_trace_read(void *host, size_t bytes)
 {
     if (bytes > sizeof(g_prep_trace)) bytes = sizeof(g_prep_trace);
     return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_prep_trace), bytes, 0, hipMemcpyDeviceToHost) ==
+                   hipSuccess
+               ? 0
+               : -1;
+}
+
+// Copies every workgroup's start and end stamps of the last per-tile pass out (trace
+// builds only; not part of the installed interface).
+extern "C" int gdn_scan_span_read(void *host, size_t bytes)
+{
+    if (bytes > sizeof(g_scan_span)) bytes = sizeof(g_scan_span);
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_scan_span), bytes, 0, hipMemcpyDeviceToHost) ==
                    hipSuccess
                ? 0
                : -1;

@@ -16,6 +16,11 @@ X (K M^T, E, Delta = T E), U (the state update) and O (the output) of value tile
   wait A/B    arriving at a barrier to leaving it
   last at A/B how often each wave is the last of the three to arrive
 
+and each traced workgroup's edges (start to the first barrier, to chunk 0, the chunk
+steps, after the last barrier until the state and the output are stored), then every
+workgroup's start, end and life on the chip-wide 100 MHz clock (s_memrealtime), in
+microseconds from the first start: the kernel ends with its slowest workgroup.
+
 ``--pass prep``: the prep kernel of the same call (the per-tile pass's variant),
 wave 0 of each of its first 4,096 workgroups: the phases of a workgroup (rows
 landed, products, diagonal inverses, the two levels of off-diagonal blocks, the T
@@ -112,7 +117,48 @@ def summarize_scan(raw, n_chunks, skip=3):
            "release_after_last_traced_arrival": {k: stat(v) for k, v in release.items()}}
     for r in SCAN_ROLES:
         res[r] = {k: stat(v) for k, v in out[r].items()}
+    # workgroup edges (row [3][0]: X starts, X leaves the first barrier, U has stored
+    # the state, O has stored the last output), against X's stamps at chunk 0's
+    # barrier A and the last chunk's barrier B
+    edges = {k: [] for k in ("start to first barrier", "first barrier to chunk 0 A",
+                             "chunk steps", "last B to state stored",
+                             "last B to output stored", "span")}
+    for wg in range(GROUPS):
+        e = [int(x) for x in raw[wg][3][0]]
+        if n_chunks > PHASES or not all(e):
+            continue
+        a0 = int(raw[wg][0][0][0])
+        bl = int(raw[wg][0][n_chunks - 1][3])
+        edges["start to first barrier"].append(e[1] - e[0])
+        edges["first barrier to chunk 0 A"].append(a0 - e[1])
+        edges["chunk steps"].append(bl - a0)
+        edges["last B to state stored"].append(e[2] - bl)
+        edges["last B to output stored"].append(e[3] - bl)
+        edges["span"].append(max(e[2], e[3]) - e[0])
+    res["edges"] = {k: stat(v) for k, v in edges.items()}
     return res
+
+
+SPAN_GROUPS = 4096
+
+
+def summarize_span(raw, n_groups):
+    """raw: uint64 array [SPAN_GROUPS][4] of each per-tile-pass workgroup's start, U
+    end and O end on the 100 MHz clock.  Microseconds from the earliest start."""
+    rows = [[int(x) for x in raw[i][:3]] for i in range(min(n_groups, SPAN_GROUPS))]
+    rows = [r for r in rows if r[0]]
+    if not rows:
+        return None
+    t0 = min(r[0] for r in rows)
+    us = lambda t: (t - t0) / 100.0
+    starts = [us(r[0]) for r in rows]
+    ends = [us(max(r[1], r[2])) for r in rows]
+    lives = [e - s for s, e in zip(starts, ends)]
+    def stat(xs):
+        return {"min": min(xs), "median": statistics.median(xs), "p90": _pct(xs, 0.9),
+                "max": max(xs)}
+    return {"groups": len(rows), "start": stat(starts), "end": stat(ends), "life": stat(lives),
+            "extent": max(ends)}
 
 
 PREP_GROUPS = 4096
@@ -209,6 +255,23 @@ def main():
             rel = res["release_after_last_traced_arrival"][bar]
             print("barrier %s: last traced arrival %s; release after it: median %d cycles" % (
                 bar, ", ".join("%s %d" % kv for kv in res["last_at"][bar].items()), rel["median"]))
+        for k, v in res["edges"].items():
+            if v:
+                print("workgroup %-27s median %8d, p10 %8d, p90 %8d cycles" % (
+                    k, v["median"], v["p10"], v["p90"]))
+        if hasattr(lib, "gdn_scan_span_read"):
+            lib.gdn_scan_span_read.restype = ctypes.c_int
+            lib.gdn_scan_span_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+            span = np.zeros((SPAN_GROUPS, 4), dtype=np.uint64)
+            assert lib.gdn_scan_span_read(span.ctypes.data, span.nbytes) == 0
+            res["span"] = summarize_span(span, SPAN_GROUPS)
+            if res["span"]:
+                sp = res["span"]
+                print("all %d workgroups (100 MHz clock, us from the first start): extent %.2f"
+                      % (sp["groups"], sp["extent"]))
+                for k in ("start", "end", "life"):
+                    print("  %-5s min %7.2f median %7.2f p90 %7.2f max %7.2f" % (
+                        k, sp[k]["min"], sp[k]["median"], sp[k]["p90"], sp[k]["max"]))
     elif args.which == "prep":
         raw = np.zeros((PREP_GROUPS, 8), dtype=np.uint64)
         assert read(raw.ctypes.data, raw.nbytes) == 0
