@@ -294,6 +294,45 @@ def test_head_chosen_for_large_grids(gdn):
 
 # ---- q and k with fewer (key) heads, tiled over the value heads ---------------------
 
+def _carve(t, off_bytes):
+    """A copy of t that starts off_bytes past a 4 KiB boundary inside a larger buffer
+    (returned too, to keep it alive)."""
+    n = t.numel() * t.element_size()
+    buf = torch.empty(n + off_bytes + 8192, dtype=torch.uint8, device=t.device)
+    base = (-buf.data_ptr()) % 4096 + off_bytes
+    view = buf[base:base + n].view(t.dtype).view(t.shape)
+    view.copy_(t)
+    return view, buf
+
+
+@pytest.mark.parametrize("dtype,algo", [("f32", "recurrent"), ("f32", "chunked"),
+                                        ("bf16", "recurrent"), ("bf16", "chunked"),
+                                        ("bf16", "chunked_lag"), ("bf16", "chunked_head")])
+def test_any_16_byte_placement(gdn, dtype, algo):
+    """The result does not depend on where the tensors lie: every input and output
+    placed at a different 16-byte offset from a 4 KiB boundary gives bit for bit the
+    result of the same call on torch's own (aligned) allocations.  The kernels read
+    rows as 16-byte pieces at per-lane offsets from a wave-wide base, so an odd
+    16-byte base takes other address paths than an aligned one."""
+    x = inputs.make(inputs.Workload("placement", 2, 130, 4, 128, dtype, "normal", "mixed",
+                                    seed=23))
+    d = to_dev(x, dtype)
+    print("case: placement", dtype, algo, flush=True)
+    ref_out, ref_fin = gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"],
+                                   algo=algo)
+    keep, c = [], {}
+    for n, off in (("q", 16), ("k", 272), ("v", 4112), ("g", 48), ("beta", 80), ("state", 144)):
+        c[n], b = _carve(d[n], off)
+        keep.append(b)
+    out, b_out = _carve(torch.zeros_like(ref_out), 528)
+    fin, b_fin = _carve(torch.zeros_like(ref_fin), 1040)
+    gdn.forward(c["q"], c["k"], c["v"], c["g"], c["beta"], c["state"], algo=algo, out=out,
+                state_out=fin)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out), "out differs with moved tensors (%s %s)" % (dtype, algo)
+    assert torch.equal(fin, ref_fin), "state differs with moved tensors (%s %s)" % (dtype, algo)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("HK", [1, 2, 3])
 @pytest.mark.parametrize("T,algo", [(1, "recurrent"), (7, "recurrent"), (63, "chunked"),
