@@ -104,3 +104,16 @@ def test_more_than_one_gpu_is_refused():
                            capture_output=True, text=True, timeout=120)
         assert r.returncode == 2, r.stderr
         assert "exactly one GPU" in r.stderr
+
+
+def test_moved_copy_starts_past_a_2mib_boundary():
+    # the placement helper of the bench's prefill_placement record: a copy of the
+    # tensor, equal in value, starting exactly off bytes past a 2 MiB boundary
+    import torch
+    t = torch.arange(3 * 1000, dtype=torch.float32).reshape(3, 1000)
+    for off in (0, 256, 768):
+        v, buf = bench.moved(torch, t, off)
+        assert v.data_ptr() % (2 << 20) == off
+        assert torch.equal(v, t) and v.is_contiguous()
+        assert buf.data_ptr() <= v.data_ptr()
+        assert v.data_ptr() + t.numel() * 4 <= buf.data_ptr() + buf.numel()
