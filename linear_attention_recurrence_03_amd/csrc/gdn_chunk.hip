@@ -25,18 +25,20 @@
 //                         K K^T and Q K^T run on MFMA; T comes from a blocked
 //                         triangular inverse in LDS (16x16 diagonal blocks by
 //                         forward substitution, then the off-diagonal blocks).
-//                         Writes T, P and the gate vectors to the workspace.
+//                         Writes T, the gate vectors and (unless the pass forms
+//                         it itself) P to the workspace.
 //   chunk_scan_kernel  -- one workgroup per (seq, head, block of value rows),
 //                         walking the chunks in order and carrying its rows of
 //                         M in registers.  Value rows of M are independent given
 //                         k, q, g, beta, so splitting them across workgroups
-//                         needs no communication.  Each wave owns 16 value rows
-//                         and does K M^T, Q M^T, T E, P Delta and the state
-//                         update on MFMA (16x16x32 bf16 for bf16 inputs,
-//                         16x16x4 fp32 for fp32 inputs), with the chunk's K, Q, T,
-//                         P and V staged in LDS (K^T operands come from
-//                         transposing LDS reads); the next chunk's loads
-//                         are in flight while the current one is computed.
+//                         needs no communication.  Each 16-row value tile has
+//                         three waves on MFMA (16x16x32 bf16 for bf16 inputs,
+//                         16x16x4 fp32 for fp32 inputs): X forms K M^T, E and
+//                         T E, U holds the tile's rows of M and updates them, O
+//                         forms Q M^T and P Delta.  Four producer waves move the
+//                         chunk's K, Q, T, P, V and gates into LDS by LDS-DMA
+//                         (K^T operands come from transposing LDS reads), the
+//                         next chunks' loads in flight while one is computed.
 //   chunk_head_kernel  -- (bf16, from one (seq, head) per compute unit on) one
 //                         workgroup per (seq, head) carrying all its value rows
 //                         (gdn_chunk_head.hip).
@@ -650,9 +652,9 @@ __attribute__((amdgpu_waves_per_eu(prep_per_cu<D, BF16, NORM, LAG>()))) void chu
 // in slot m mod S.  The K/T slot of chunk m is read during [B_{m-1}, B_m) and
 // refilled with chunk m+SK from B_m on; the Q/P slot is read during [A_m, B_m)
 // and refilled with chunk m+SQ from A_{m+1} on.  A load thus has SK - 1 (SQ - 1)
-// chunk steps to land, and the two kinds of loads are issued half a step apart.  The fp32 variant (parity path) keeps
-// one slot of each: a third barrier L_n per chunk marks the slot as loaded and
-// the phases of a chunk run back to back.
+// chunk steps to land, and the two kinds of loads are issued half a step apart.
+// The fp32 variant (parity path) keeps one slot of each: a third barrier L_n per
+// chunk marks the slot as loaded and the phases of a chunk run back to back.
 //
 // K and Q rows are padded by 32 bytes, which makes both the 16-byte row reads
 // (k order 8g..8g+7 per lane group, matched by the key order of the published
