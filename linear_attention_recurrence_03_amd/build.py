@@ -26,6 +26,12 @@ DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-fgpu-flush-denormals-to-zero", "-munsafe-fp-atomics"]
 
 
+# The decode kernel has the hardware preload its first 16 dwords of arguments into
+# scalar registers at wave launch (gfx950; the code keeps a fallback entry that
+# loads them itself where the firmware does not).
+PER_FILE = {"gdn_decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -44,6 +50,7 @@ def build(verbose: bool = False, jobs: int = 4, trace: bool = False) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             flags = COMMON + (DEVICE if src.endswith(".hip") else ["-D__HIP_PLATFORM_AMD__"])
+            flags = flags + PER_FILE.get(src, [])
             if trace:
                 flags = flags + ["-DGDN_PHASE_TRACE"]
             cmd = [HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]

@@ -110,14 +110,26 @@ __device__ __forceinline__ void store_scalar_out(void *base, int64_t off, float 
 
 // One workgroup = kWaves waves = kWaves*2*NP consecutive value rows of one
 // (seq, head).  Grid: n_seqs * n_heads * (D / rows_per_block) workgroups.
-template <int D, int NP, bool BF16>
+// Everything the first loads need comes first, in 14 dwords: this file is built to
+// have the hardware preload them into scalar registers at wave launch, so the
+// state and token loads go out without waiting on argument loads (the kernel's
+// life at one token per call is a few such round trips).  With PK the token
+// count (< 2^31) and both head counts (< 2^16) are packed into two of them
+// (tok32, heads16); otherwise the full-width counts further on are used and read
+// like any argument.  Head counts fit in 32 bits: the grid, one workgroup per
+// group of rows of each (seq, head), does.
+template <int D, int NP, bool BF16, bool PK>
 __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
-    const void *__restrict__ q, const void *__restrict__ k,
-    const void *__restrict__ v, const float *__restrict__ g,
-    const float *__restrict__ beta, const float *state_in, void *__restrict__ out,
-    float *state_out, int64_t n_tokens, int64_t n_heads, int64_t n_k_heads, float scale,
-    int l2norm_qk, int raw_gates)
+    const void *__restrict__ k, const void *__restrict__ q, const float *state_in,
+    const void *__restrict__ v, const float *__restrict__ g, const float *__restrict__ beta,
+    uint32_t tok32, uint32_t heads16, int64_t n_tokens_full, int n_heads_full,
+    int n_k_heads_full, void *__restrict__ out, float *state_out, float scale, int l2norm_qk,
+    int raw_gates)
 {
+    const int64_t n_tokens = PK ? int64_t(tok32) : n_tokens_full;
+    const int n_heads32 = PK ? int(heads16 & 0xffffu) : n_heads_full;
+    const int n_k_heads32 = PK ? int(heads16 >> 16) : n_k_heads_full;
+    const int64_t n_heads = n_heads32, n_k_heads = n_k_heads32;
     constexpr int NV = D / 32;
     constexpr int kRowsPerWave = 2 * NP;
     constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
@@ -126,10 +138,11 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int col = (lane & 31) * NV;
-    const int64_t sh = blockIdx.x / kBlocksPerHead;   // s * n_heads + h
+    const uint32_t shu = blockIdx.x / kBlocksPerHead;   // s * n_heads + h
     const int rb = blockIdx.x % kBlocksPerHead;
-    const int64_t s = sh / n_heads;
-    const int64_t h = sh - s * n_heads;
+    const uint32_t su = shu / static_cast<uint32_t>(n_heads32);
+    const uint32_t hu = shu - su * static_cast<uint32_t>(n_heads32);
+    const int64_t sh = shu, s = su, h = hu;
     // rows of this lane: row0 + 2p, p < NP (the two half-waves interleave)
     const int row0 = rb * kRowsPerBlock + wave * kRowsPerWave + (lane >> 5);
     const int64_t st_base = sh * D * D;
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
     // token t of (s, h): v and out at ((s*T + t)*H + h)*D, gates at (s*T + t)*H + h,
     // q and k at ((s*T + t)*Hk + h % Hk)*D
     int64_t gi = s * n_tokens * n_heads + h;
-    int64_t ki = s * n_tokens * n_k_heads + h % n_k_heads;
+    int64_t ki = s * n_tokens * n_k_heads + hu % static_cast<uint32_t>(n_k_heads32);
     Vec<NV> kv = load_in<NV, BF16>(k, ki * D + col);
     Vec<NV> qv = load_in<NV, BF16>(q, ki * D + col);
     float vr[NP];
@@ -241,15 +254,20 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
 template <int D, int NP, bool BF16>
 hipError_t launch_rec(const Problem &p, hipStream_t stream)
 {
+    const bool pk = p.n_tokens < (int64_t(1) << 31) && p.n_heads < (1 << 16) &&
+                    p.n_k_heads < (1 << 16);
     constexpr int kRowsPerBlock = kWaves * 2 * NP;
     static_assert(D % kRowsPerBlock == 0, "rows per block must divide head_dim");
     const int64_t blocks = p.n_seqs * p.n_heads * (D / kRowsPerBlock);
     if (!grid_fits(blocks, kWaves * 64)) return hipErrorInvalidConfiguration;
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
-    hipLaunchKernelGGL((recurrent_kernel<D, NP, BF16>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kWaves * 64), 0, stream, p.q, p.k, p.v, p.g, p.beta,
-                       p.state_in, p.out, p.state_out, p.n_tokens, p.n_heads, p.n_k_heads, scale,
-                       p.l2norm_qk, p.raw_gates);
+    const uint32_t tok32 = pk ? static_cast<uint32_t>(p.n_tokens) : 0u;
+    const uint32_t heads16 = pk ? static_cast<uint32_t>(p.n_heads | (p.n_k_heads << 16)) : 0u;
+    auto kern = pk ? recurrent_kernel<D, NP, BF16, true> : recurrent_kernel<D, NP, BF16, false>;
+    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kWaves * 64), 0, stream,
+                       p.k, p.q, p.state_in, p.v, p.g, p.beta, tok32, heads16, p.n_tokens,
+                       static_cast<int>(p.n_heads), static_cast<int>(p.n_k_heads), p.out,
+                       p.state_out, scale, p.l2norm_qk, p.raw_gates);
     return hipGetLastError();
 }
 

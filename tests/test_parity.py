@@ -146,6 +146,17 @@ def test_decay_regimes(gdn, gate, algo):
     check(gdn, xf, "f32", algo, what="gate f32 " + gate)
 
 
+def test_token_recurrence_with_65536_heads(gdn):
+    """The token recurrence reads its token and head counts from arguments packed
+    into the launch's preloaded registers while they fit in 32 and 16 bits; 65,536
+    heads take the variant that reads the full-width counts.  Both against the
+    oracle, and the packed one (65,535 heads, the largest) too."""
+    for H in (65535, 65536):
+        x = inputs.make(inputs.Workload("heads", 1, 2, H, 32, "f32", "normal", "standard",
+                                        seed=31))
+        check(gdn, x, "f32", "recurrent", what="%d heads" % H)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_many_row_blocks(gdn, dtype):
     """More (sequence, head, 16 value rows) blocks than compute units: the bf16 scan
