@@ -277,8 +277,9 @@ size_t gdn_flash_attn_workspace_size(int64_t n_seqs, int64_t n_heads, int64_t n_
  * n_heads_kv), a non-finite scale (GDN_ERR_BAD_SHAPE), null or misaligned
  * pointers, out overlapping an input, a too small workspace.  n_seqs == 0 or
  * n_heads == 0 is a no-op; n_kv == 0 writes zeros.  Size limits: at most 2^24
- * query rows (n_seqs * n_heads * n_q), and grids that fit one dispatch each
- * (their work-items are counted in 32 bits); else GDN_ERR_BAD_SHAPE. */
+ * query rows (n_seqs * n_heads * n_q), fewer than 2^31 cached positions (n_kv),
+ * and grids that fit one dispatch each (their work-items are counted in 32 bits);
+ * else GDN_ERR_BAD_SHAPE. */
 int gdn_flash_attn(gdn_dtype dtype, const void *q, const void *k, const void *v,
                    const float *mask, void *out, int64_t n_seqs, int64_t n_heads,
                    int64_t n_heads_kv, int64_t n_q, int64_t n_kv, int head_dim, float scale,

@@ -26,10 +26,12 @@ DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-fgpu-flush-denormals-to-zero", "-munsafe-fp-atomics"]
 
 
-# The decode kernel has the hardware preload its first 16 dwords of arguments into
-# scalar registers at wave launch (gfx950; the code keeps a fallback entry that
-# loads them itself where the firmware does not).
-PER_FILE = {"gdn_decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+# The decode and attention kernels have the hardware preload their leading kernel
+# arguments (as many dwords as the user-SGPR budget leaves, 14 here) into scalar
+# registers at wave launch (gfx950; the code keeps a fallback entry that loads
+# them itself where the firmware does not).
+_PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
+PER_FILE = {"gdn_decode.hip": _PRELOAD, "gdn_attn.hip": _PRELOAD}
 
 
 def _run(cmd, verbose):

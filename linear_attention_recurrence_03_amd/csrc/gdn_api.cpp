@@ -130,6 +130,8 @@ int attn_check(int64_t n_seqs, int64_t n_heads, int64_t n_heads_kv, int64_t n_q,
     // work-items, then one wave per (seq, query, head) row to merge the ranges; a
     // dispatch counts work-items in 32 bits
     if (n_seqs * n_heads * n_q > (int64_t(1) << 24)) return GDN_ERR_BAD_SHAPE;
+    // the kernels index cache positions in 32 bits
+    if (n_kv >= (int64_t(1) << 31)) return GDN_ERR_BAD_SHAPE;
     if (n_seqs > 0 && n_heads > 0 && !gdn::attn_grid_fits(n_seqs, n_heads, n_heads_kv, n_q, n_kv))
         return GDN_ERR_BAD_SHAPE;
     if (sizes) {

@@ -93,20 +93,34 @@ __device__ __forceinline__ float exp_diff(float a, float b)
     return (a == -INFINITY) ? 0.f : __expf(a - b);
 }
 
+// The kernels take these as separate arguments in this order (a struct passed by
+// value is not preloaded): the first 14 dwords are what a workgroup's first loads
+// need, and this file is built to have the hardware preload them into scalar
+// registers at wave launch.  Counts are 32-bit (the rows, the grids and the cache
+// length are bounded below 2^31).
 struct AttnArgs {
     const void *q, *k, *v;
+    uint32_t n_split, groups;   // token ranges per row; row groups per (seq, kv head)
+    uint32_t n_heads_kv, hg;    // key/value heads; query heads per key/value head
+    uint32_t n_q, n_kv;
+    uint32_t split_len;         // tokens per range
+    float scale;
     const float *mask;          // (S, 1, n_q, n_kv) or null
     void *out;                  // (S, n_q, H, D)
     float *part;                // per (row, split): D weighted sums, max, sum
-    float scale;
-    int64_t n_heads, n_heads_kv, n_q, n_kv;
-    int groups;                 // row groups per (seq, key/value head)
-    int n_split, split_len;     // token ranges per row and their length
 };
+#define ATTN_ARGS(a)                                                                          \
+    (a).q, (a).k, (a).v, (a).n_split, (a).groups, (a).n_heads_kv, (a).hg, (a).n_q, (a).n_kv, \
+        (a).split_len, (a).scale, (a).mask, (a).out, (a).part
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
+__global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
+    const void *q_, const void *k_, const void *v_, uint32_t n_split_, uint32_t groups_,
+    uint32_t n_heads_kv_, uint32_t hg_, uint32_t n_q_, uint32_t n_kv_, uint32_t split_len_,
+    float scale_, const float *mask_, void *out_, float *part_)
 {
+    const AttnArgs a{q_, k_, v_, n_split_, groups_, n_heads_kv_, hg_, n_q_, n_kv_, split_len_,
+                     scale_, mask_, out_, part_};
     using E = typename AttnElem<BF16>::T;
     constexpr int QW = D / 4;            // key elements per scoring thread
     constexpr int LPR = D / 8;           // lanes covering one value row
@@ -122,13 +136,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
     __shared__ __align__(16) float sAcc[STREAMS][kAttnRows][D];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t b = blockIdx.x;
+    // block -> (seq, key/value head, row group, token range), in 32 bits
+    const uint32_t b = blockIdx.x;
     const int split = static_cast<int>(b % a.n_split);
-    const int64_t u = b / a.n_split;
+    const uint32_t u = b / a.n_split;
     const int grp = static_cast<int>(u % a.groups);
-    const int64_t sj = u / a.groups;                  // s * n_heads_kv + j
-    const int64_t s = sj / a.n_heads_kv, j = sj - s * a.n_heads_kv;
-    const int64_t hg = a.n_heads / a.n_heads_kv;      // query heads per key/value head
+    const uint32_t sj = u / a.groups;                 // s * n_heads_kv + j
+    const uint32_t s32 = sj / a.n_heads_kv;
+    const int64_t s = s32, j = sj - s32 * a.n_heads_kv;
+    const int64_t n_heads = int64_t(a.hg) * a.n_heads_kv;
+    const int64_t hg = a.hg;                          // query heads per key/value head
     const int64_t rows_here = hg * a.n_q;
 
     // row r of this group: query head j*hg + R / n_q, query R % n_q
@@ -138,8 +155,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
     for (int r = 0; r < kAttnRows; ++r) {
         const int64_t R = int64_t(grp) * kAttnRows + r;
         rv[r] = R < rows_here;
-        rh[r] = rv[r] ? j * hg + R / a.n_q : 0;
-        ri[r] = rv[r] ? R % a.n_q : 0;
+        rh[r] = rv[r] ? j * hg + uint32_t(R) / a.n_q : 0;
+        ri[r] = rv[r] ? uint32_t(R) % a.n_q : 0;
     }
 
     // scaled query rows (zeros for unused rows)
@@ -147,7 +164,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
         const int r = x / D, c = x - r * D;
         float val = 0.f;
         if (rv[r]) {
-            const int64_t off = ((s * a.n_heads + rh[r]) * a.n_q + ri[r]) * D + c;
+            const int64_t off = ((s * n_heads + rh[r]) * a.n_q + ri[r]) * D + c;
             if constexpr (BF16)
                 val = bf16_to_f32(static_cast<const uint16_t *>(a.q)[off]);
             else
@@ -294,7 +311,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a)
 #pragma unroll
         for (int st = 0; st < STREAMS; ++st) sum += sAcc[st][r][c];
         const float m = sS[r][0], l = sS[r][1];
-        const int64_t row = (s * a.n_q + ri[r]) * a.n_heads + rh[r];   // (s, i, h)
+        const int64_t row = (s * a.n_q + ri[r]) * n_heads + rh[r];   // (s, i, h)
         if (a.n_split == 1) {
             const float o = (l > 0.f) ? sum / l : 0.f;
             if constexpr (BF16)
@@ -359,8 +376,13 @@ __device__ __forceinline__ uint32_t attn_pack_bf16(float a, float b)
 }
 
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_split_mma_kernel(AttnArgs a)
+__global__ __launch_bounds__(kAttnThreads) void attn_split_mma_kernel(
+    const void *q_, const void *k_, const void *v_, uint32_t n_split_, uint32_t groups_,
+    uint32_t n_heads_kv_, uint32_t hg_, uint32_t n_q_, uint32_t n_kv_, uint32_t split_len_,
+    float scale_, const float *mask_, void *out_, float *part_)
 {
+    const AttnArgs a{q_, k_, v_, n_split_, groups_, n_heads_kv_, hg_, n_q_, n_kv_, split_len_,
+                     scale_, mask_, out_, part_};
     using F = AttnMmaCfg<D>;
     __shared__ __align__(16) unsigned char sV[kAttnTile * F::RS];
     __shared__ __align__(16) float sS[kAttnRows][kAttnTile];
@@ -369,13 +391,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_mma_kernel(AttnArgs a
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
-    const int64_t b = blockIdx.x;
+    // block -> (seq, key/value head, row group, token range), in 32 bits
+    const uint32_t b = blockIdx.x;
     const int split = static_cast<int>(b % a.n_split);
-    const int64_t u = b / a.n_split;
+    const uint32_t u = b / a.n_split;
     const int grp = static_cast<int>(u % a.groups);
-    const int64_t sj = u / a.groups;                  // s * n_heads_kv + j
-    const int64_t s = sj / a.n_heads_kv, j = sj - s * a.n_heads_kv;
-    const int64_t hg = a.n_heads / a.n_heads_kv;
+    const uint32_t sj = u / a.groups;                 // s * n_heads_kv + j
+    const uint32_t s32 = sj / a.n_heads_kv;
+    const int64_t s = s32, j = sj - s32 * a.n_heads_kv;
+    const int64_t n_heads = int64_t(a.hg) * a.n_heads_kv;
+    const int64_t hg = a.hg;
     const int64_t rows_here = hg * a.n_q;
 
     bool rv[kAttnRows];
@@ -384,7 +409,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_mma_kernel(AttnArgs a
     for (int r = 0; r < kAttnRows; ++r) {
         const int64_t R = int64_t(grp) * kAttnRows + r;
         rv[r] = R < rows_here;
-        ri[r] = rv[r] ? R % a.n_q : 0;
+        ri[r] = rv[r] ? uint32_t(R) % a.n_q : 0;
     }
 
     // query rows as the A operand of the scores (lane row n of the group)
@@ -392,7 +417,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_mma_kernel(AttnArgs a
     {
         const int64_t R = int64_t(grp) * kAttnRows + n;
         const bool ok = n < kAttnRows && R < rows_here;
-        const int64_t off = ok ? ((s * a.n_heads + j * hg + R / a.n_q) * a.n_q + R % a.n_q) * D : 0;
+        const int64_t off =
+            ok ? ((s * n_heads + j * hg + uint32_t(R) / a.n_q) * a.n_q + uint32_t(R) % a.n_q) * D : 0;
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks)
             aq[ks] = ok ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + off +
@@ -520,7 +546,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_mma_kernel(AttnArgs a
         for (int r = 0; r < kAttnRows; ++r)
             if (r == n) {
                 ok = rv[r];
-                row = (s * a.n_q + ri[r]) * a.n_heads + j * hg + (int64_t(grp) * kAttnRows + r) / a.n_q;
+                row = (s * a.n_q + ri[r]) * n_heads + j * hg + uint32_t(grp * kAttnRows + r) / a.n_q;
             }
         if (ok) {
             const float m = sML[n][0], l = sML[n][1];
@@ -551,12 +577,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_mma_kernel(AttnArgs a
 // weighted partial sums of its D/64 columns with the weights taken from the lanes
 // that hold them.
 template <int D, bool BF16>
-__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a)
+__global__ __launch_bounds__(64) void attn_combine_kernel(const float *part, void *out,
+                                                          uint32_t n_split)
 {
     const int64_t row = blockIdx.x;
     const int lane = threadIdx.x;
-    const int ns = a.n_split;
-    const float *pp = a.part + row * ns * (D + 2);
+    const int ns = n_split;
+    const float *pp = part + row * ns * (D + 2);
     float M = -INFINITY;
     for (int i0 = 0; i0 < ns; i0 += 64)
         if (i0 + lane < ns) M = fmaxf(M, pp[(i0 + lane) * (D + 2) + D]);
@@ -597,9 +624,9 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a)
         const float o = (den > 0.f) ? num[e] / den : 0.f;
         const int64_t idx = row * D + lane + 64 * e;
         if constexpr (BF16)
-            static_cast<uint16_t *>(a.out)[idx] = f32_to_bf16(o);
+            static_cast<uint16_t *>(out)[idx] = f32_to_bf16(o);
         else
-            static_cast<float *>(a.out)[idx] = o;
+            static_cast<float *>(out)[idx] = o;
     }
 }
 
@@ -614,26 +641,26 @@ hipError_t launch_attn_d(const AttnProblem &p, void *ws, hipStream_t stream)
     a.out = p.out;
     a.part = static_cast<float *>(ws);
     a.scale = p.scale;
-    a.n_heads = p.n_heads;
-    a.n_heads_kv = p.n_heads_kv;
-    a.n_q = p.n_q;
-    a.n_kv = p.n_kv;
+    a.n_heads_kv = static_cast<uint32_t>(p.n_heads_kv);
+    a.hg = static_cast<uint32_t>(p.n_heads / p.n_heads_kv);
+    a.n_q = static_cast<uint32_t>(p.n_q);
+    a.n_kv = static_cast<uint32_t>(p.n_kv);
     const AttnSplit sp = attn_split(p.n_seqs, p.n_heads, p.n_heads_kv, p.n_q, p.n_kv);
-    a.groups = sp.groups;
-    a.n_split = sp.n_split;
-    a.split_len = sp.split_len;
+    a.groups = static_cast<uint32_t>(sp.groups);
+    a.n_split = static_cast<uint32_t>(sp.n_split);
+    a.split_len = static_cast<uint32_t>(sp.split_len);
     const int64_t blocks = p.n_seqs * p.n_heads_kv * sp.groups * int64_t(sp.n_split);
     const int64_t rows = p.n_seqs * p.n_q * p.n_heads;
     if (!grid_fits(blocks, kAttnThreads) || !grid_fits(rows, 64)) return hipErrorInvalidConfiguration;
     if constexpr (BF16)
         hipLaunchKernelGGL((attn_split_mma_kernel<D>), dim3(static_cast<uint32_t>(blocks)),
-                           dim3(kAttnThreads), 0, stream, a);
+                           dim3(kAttnThreads), 0, stream, ATTN_ARGS(a));
     else
         hipLaunchKernelGGL((attn_split_kernel<D, false>), dim3(static_cast<uint32_t>(blocks)),
-                           dim3(kAttnThreads), 0, stream, a);
+                           dim3(kAttnThreads), 0, stream, ATTN_ARGS(a));
     if (sp.n_split > 1) {
         hipLaunchKernelGGL((attn_combine_kernel<D, BF16>), dim3(static_cast<uint32_t>(rows)),
-                           dim3(64), 0, stream, a);
+                           dim3(64), 0, stream, static_cast<const float *>(a.part), a.out, a.n_split);
     }
     return hipGetLastError();
 }

@@ -304,6 +304,9 @@ def test_size_limits(lib):
     assert fa(S=1 << 24, q=None) == E_SHAPE
     assert fa(S=1 << 22, H=4, HKV=1, NQ=1, q=None) == E_NULL     # four rows per workgroup
     assert fa(S=(1 << 24) + 1, q=None) == E_SHAPE
+    # cache positions are indexed in 32 bits: fewer than 2^31
+    assert fa(S=1, NKV=(1 << 31) - 1, q=None) == E_NULL
+    assert fa(S=1, NKV=1 << 31, q=None) == E_SHAPE
 
 
 def test_chunk_row_span_limit(lib):
