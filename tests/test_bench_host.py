@@ -89,6 +89,12 @@ def test_traffic_records_calibrate_each_counter(tmp_path):
     assert abs(d["seconds_under_counters"] - 50e-6) < 1e-12
     assert abs(d["counted_GBs"] - round(250 * mb / 50e-6 / 1e9, 1)) < 0.06
     assert "decode_1tok" not in rec
+    # the single-token layer calls: any other row count of the d = 128 recurrence
+    one = "void gdn::recurrent_kernel<128, 2, false, true>(...)"
+    _counter_csv(tmp_path / "f1", "FETCH_SIZE", [(copy, 256 * mib, 10), (one, 2 * mib, 4_000)])
+    _counter_csv(tmp_path / "w1", "WRITE_SIZE", [(copy, 512 * mib, 10), (one, 2 * mib, 4_000)])
+    rec1 = bench.traffic_records(str(tmp_path / "f1"), str(tmp_path / "w1"))
+    assert rec1["decode_1tok"]["bytes_per_launch"] == round((4 + 2) * mb)
 
 
 def test_more_than_one_gpu_is_refused():
