@@ -21,6 +21,8 @@
 // partials plus a 32-lane DPP reduction; k.q is reduced alongside.  Since
 // M_new q = exp(g) M q + delta (k.q), the readout needs no second pass over
 // the row.
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
@@ -28,6 +30,11 @@ namespace gdn {
 namespace {
 
 constexpr int kWaves = 4;   // waves per workgroup
+
+// One state row of zeros (the widest head): a call without an initial state reads
+// its rows from here, so that the state loads are unconditional and no branch
+// joins them (a join makes the compiler wait for them before anything else issues).
+__device__ float kZeroRow[128] = {};
 
 template <int NV>
 struct Vec {
@@ -90,6 +97,115 @@ __device__ __forceinline__ Vec<NV> load_in(const void *base, int64_t off)
     }
 }
 
+// A copy of x in a register other than x's own (early-clobber output), made at this
+// point of the program: once a loaded value has been copied, the next load can
+// land in its register while the copy is in use, and no copy of a load still in
+// flight is ever needed.
+__device__ __forceinline__ float fresh(float x)
+{
+    float y;
+    asm volatile("v_mov_b32 %0, %1" : "=&v"(y) : "v"(x) : "memory");
+    return y;
+}
+
+// x, computed from loaded bits, fixed at this point of the program: its inputs are
+// dead from here on, and no later load is moved above it.
+__device__ __forceinline__ float pin(float x)
+{
+    asm volatile("" : "+v"(x) : : "memory");
+    return x;
+}
+
+// A token's q or k slice as loaded (bf16: the raw bits), converted when used, so
+// that the next token's loads can be in flight across the current token's work.
+template <int NV, bool BF16>
+struct RawIn;
+template <int NV>
+struct RawIn<NV, false> {
+    Vec<NV> x;
+};
+template <int NV>
+struct RawIn<NV, true> {
+    // The aligned 32-bit words that hold the slice (two values each). An odd width
+    // starts at the high half of its first word on odd lanes (odd = 1), and reads one
+    // value past its end on even lanes: in bounds, as 32 lanes cover the whole row.
+    uint32_t w[(NV + 1) / 2];
+    uint32_t odd;
+};
+
+template <int NV, bool BF16>
+__device__ __forceinline__ RawIn<NV, BF16> load_raw(const void *base, int64_t off)
+{
+    RawIn<NV, BF16> r;
+    if constexpr (!BF16) {
+        r.x = load_f32<NV>(static_cast<const float *>(base) + off);
+    } else {
+        const uint16_t *p = static_cast<const uint16_t *>(base) + off;
+        if constexpr (NV == 4) {
+            const uint2 t = *reinterpret_cast<const uint2 *>(p);
+            r.w[0] = t.x;
+            r.w[1] = t.y;
+        } else if constexpr (NV == 2) {
+            r.w[0] = *reinterpret_cast<const uint32_t *>(p);
+        } else {
+            const uint32_t *pw = static_cast<const uint32_t *>(base) + (off >> 1);
+#pragma unroll
+            for (int j = 0; j < (NV + 1) / 2; ++j) r.w[j] = pw[j];
+            r.odd = static_cast<uint32_t>(off & 1);
+        }
+    }
+    return r;
+}
+
+template <int NV, bool BF16>
+__device__ __forceinline__ Vec<NV> cvt_in(const RawIn<NV, BF16> &r)
+{
+    if constexpr (!BF16) {
+        Vec<NV> v;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v.x[i] = fresh(r.x.x[i]);
+        return v;
+    } else {
+        // half j of the words as a float
+        auto half = [&](int j) {
+            return __uint_as_float((j & 1) ? (r.w[j >> 1] & 0xffff0000u) : (r.w[j >> 1] << 16));
+        };
+        Vec<NV> v;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            if constexpr (NV % 2 == 0)
+                v.x[i] = pin(half(i));
+            else
+                v.x[i] = pin(r.odd ? half(i + 1) : half(i));
+        }
+        return v;
+    }
+}
+
+// One v element as loaded: bf16 loads the aligned 32-bit pair that holds it (in
+// bounds: rows have an even width), so no narrow load needs widening later.
+template <bool BF16>
+using RawScalar = typename std::conditional<BF16, uint32_t, float>::type;
+
+template <bool BF16>
+__device__ __forceinline__ RawScalar<BF16> load_scalar_raw(const void *base, int64_t off)
+{
+    if constexpr (BF16)
+        return static_cast<const uint32_t *>(base)[off >> 1];
+    else
+        return static_cast<const float *>(base)[off];
+}
+
+// sh: 16 when the element is the pair's low half (an even offset), else 0
+template <bool BF16>
+__device__ __forceinline__ float cvt_scalar(RawScalar<BF16> x, uint32_t sh)
+{
+    if constexpr (BF16)
+        return pin(__uint_as_float((x << sh) & 0xffff0000u));
+    else
+        return fresh(x);
+}
+
 template <bool BF16>
 __device__ __forceinline__ float load_scalar_in(const void *base, int64_t off)
 {
@@ -118,7 +234,7 @@ __device__ __forceinline__ void store_scalar_out(void *base, int64_t off, float 
 // (tok32, heads16); otherwise the full-width counts further on are used and read
 // like any argument.  Head counts fit in 32 bits: the grid, one workgroup per
 // group of rows of each (seq, head), does.
-template <int D, int NP, bool BF16, bool PK>
+template <int D, int NP, bool BF16, bool PK, bool ONE>
 __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
     const void *__restrict__ k, const void *__restrict__ q, const float *state_in,
     const void *__restrict__ v, const float *__restrict__ g, const float *__restrict__ beta,
@@ -147,43 +263,21 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
     const int row0 = rb * kRowsPerBlock + wave * kRowsPerWave + (lane >> 5);
     const int64_t st_base = sh * D * D;
 
+    static_assert(D <= 128, "the zero row covers head_dim <= 128");
     Vec<NV> M[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-        if (state_in) {
-            M[p] = load_f32<NV>(state_in + st_base + (int64_t)(row0 + 2 * p) * D + col);
-        } else {
-#pragma unroll
-            for (int i = 0; i < NV; ++i) M[p].x[i] = 0.f;
-        }
+        const float *row = state_in ? state_in + st_base + (int64_t)(row0 + 2 * p) * D : kZeroRow;
+        M[p] = load_f32<NV>(row + col);
     }
 
     // token t of (s, h): v and out at ((s*T + t)*H + h)*D, gates at (s*T + t)*H + h,
     // q and k at ((s*T + t)*Hk + h % Hk)*D
     int64_t gi = s * n_tokens * n_heads + h;
     int64_t ki = s * n_tokens * n_k_heads + hu % static_cast<uint32_t>(n_k_heads32);
-    Vec<NV> kv = load_in<NV, BF16>(k, ki * D + col);
-    Vec<NV> qv = load_in<NV, BF16>(q, ki * D + col);
-    float vr[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) vr[p] = load_scalar_in<BF16>(v, gi * D + row0 + 2 * p);
-    float gt = g[gi], bt = beta[gi];
-
-    for (int64_t t = 0; t < n_tokens; ++t) {
-        // prefetch the next token's inputs while this one is computed
-        const int64_t gn = gi + n_heads, kn_i = ki + n_k_heads;
-        const bool more = (t + 1 < n_tokens);
-        Vec<NV> kn, qn;
-        float vn[NP], gnext = 0.f, bnext = 0.f;
-        if (more) {
-            kn = load_in<NV, BF16>(k, kn_i * D + col);
-            qn = load_in<NV, BF16>(q, kn_i * D + col);
-#pragma unroll
-            for (int p = 0; p < NP; ++p) vn[p] = load_scalar_in<BF16>(v, gn * D + row0 + 2 * p);
-            gnext = g[gn];
-            bnext = beta[gn];
-        }
-
+    // One token of (s, h): decay, delta update and read-out of the rows held here,
+    // with out at token offset go.
+    auto token = [&](Vec<NV> kv, Vec<NV> qv, const float *vr, float gt, float bt, int64_t go) {
         if (l2norm_qk) {
             // both 32-lane halves hold the whole rows: one reduction each
             float sk = 0.f, sq = 0.f;
@@ -231,19 +325,79 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
 #pragma unroll
             for (int i = 0; i < NV; ++i) M[p].x[i] = fmaf(alpha, M[p].x[i], delta * kv.x[i]);
             const float o = scale * fmaf(alpha, b[p], delta * kq);
-            if ((lane & 31) == 0) store_scalar_out<BF16>(out, gi * D + row0 + 2 * p, o);
+            if ((lane & 31) == 0) store_scalar_out<BF16>(out, go * D + row0 + 2 * p, o);
         }
+    };
 
-        if (more) {
-            kv = kn;
-            qv = qn;
+    if constexpr (ONE) {
+        // a single token: straight-line loads, the gates through the scalar path
+        float vr[NP];
 #pragma unroll
-            for (int p = 0; p < NP; ++p) vr[p] = vn[p];
-            gt = gnext;
-            bt = bnext;
+        for (int p = 0; p < NP; ++p) vr[p] = load_scalar_in<BF16>(v, gi * D + row0 + 2 * p);
+        token(load_in<NV, BF16>(k, ki * D + col), load_in<NV, BF16>(q, ki * D + col), vr, g[gi],
+              beta[gi], gi);
+    } else {
+        // Two tokens in flight: stages A and B hold the raw bits of the next two
+        // tokens' inputs. Each stage is converted, then at once reloaded with the
+        // token two places on, and only then is its token worked on, so a load has
+        // two tokens' arithmetic to land. The loop handles two tokens per pass, so
+        // that no register of an in-flight load is ever copied (a copy would wait
+        // for it). The gates go through the vector path (a lane-varying zero
+        // offset) so that the waits on the cross-lane sums never also wait on them.
+        int zoff;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(zoff));
+        struct Raw {
+            RawIn<NV, BF16> k, q;
+            RawScalar<BF16> v[NP];
+            float g, b;
+        };
+        const int64_t gi0 = gi, ki0 = ki;
+        const uint32_t vsh = (row0 & 1) ? 0u : 16u;   // rows row0 + 2p share row0's parity
+        auto fetch = [&](int64_t t) {
+            const int64_t gx = gi0 + t * n_heads, kx = ki0 + t * n_k_heads;
+            Raw r;
+            r.k = load_raw<NV, BF16>(k, kx * D + col);
+            r.q = load_raw<NV, BF16>(q, kx * D + col);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) r.v[p] = load_scalar_raw<BF16>(v, gx * D + row0 + 2 * p);
+            r.g = g[gx + zoff];
+            r.b = beta[gx + zoff];
+            return r;
+        };
+        struct Tok {
+            Vec<NV> k, q;
+            float v[NP];
+            float g, b;
+        };
+        auto convert = [&](const Raw &r) {
+            Tok c;
+            c.k = cvt_in<NV, BF16>(r.k);
+            c.q = cvt_in<NV, BF16>(r.q);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) c.v[p] = cvt_scalar<BF16>(r.v[p], vsh);
+            c.g = fresh(r.g);
+            c.b = fresh(r.b);
+            return c;
+        };
+        const int64_t last = n_tokens - 1;
+        Raw A = fetch(0);
+        Raw B = fetch(last < 1 ? last : 1);
+        int64_t t = 0;
+        for (; t + 2 < n_tokens; t += 2) {
+            const Tok ca = convert(A);
+            A = fetch(t + 2);
+            token(ca.k, ca.q, ca.v, ca.g, ca.b, gi0 + t * n_heads);
+            const Tok cb = convert(B);
+            B = fetch(t + 3 < last ? t + 3 : last);   // past the end: the last token again
+            token(cb.k, cb.q, cb.v, cb.g, cb.b, gi0 + (t + 1) * n_heads);
         }
-        gi = gn;
-        ki = kn_i;
+        // one or two tokens left, in A and B
+        const Tok ca = convert(A);
+        token(ca.k, ca.q, ca.v, ca.g, ca.b, gi0 + t * n_heads);
+        if (t + 1 < n_tokens) {
+            const Tok cb = convert(B);
+            token(cb.k, cb.q, cb.v, cb.g, cb.b, gi0 + (t + 1) * n_heads);
+        }
     }
 
 #pragma unroll
@@ -251,7 +405,7 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
         store_f32<NV>(state_out + st_base + (int64_t)(row0 + 2 * p) * D + col, M[p]);
 }
 
-template <int D, int NP, bool BF16>
+template <int D, int NP, bool BF16, bool ONE>
 hipError_t launch_rec(const Problem &p, hipStream_t stream)
 {
     const bool pk = p.n_tokens < (int64_t(1) << 31) && p.n_heads < (1 << 16) &&
@@ -263,7 +417,8 @@ hipError_t launch_rec(const Problem &p, hipStream_t stream)
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
     const uint32_t tok32 = pk ? static_cast<uint32_t>(p.n_tokens) : 0u;
     const uint32_t heads16 = pk ? static_cast<uint32_t>(p.n_heads | (p.n_k_heads << 16)) : 0u;
-    auto kern = pk ? recurrent_kernel<D, NP, BF16, true> : recurrent_kernel<D, NP, BF16, false>;
+    auto kern = pk ? recurrent_kernel<D, NP, BF16, true, ONE>
+                   : recurrent_kernel<D, NP, BF16, false, ONE>;
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kWaves * 64), 0, stream,
                        p.k, p.q, p.state_in, p.v, p.g, p.beta, tok32, heads16, p.n_tokens,
                        static_cast<int>(p.n_heads), static_cast<int>(p.n_k_heads), p.out,
@@ -280,11 +435,13 @@ template <int D, bool BF16>
 hipError_t launch_rec_d(const Problem &p, hipStream_t stream)
 {
     const int64_t rows = p.n_seqs * p.n_heads * D;
+    const bool one = (p.n_tokens == 1);
     if (rows >= 256 * 32 * 4)
-        return launch_rec<D, 4, BF16>(p, stream);
-    if (p.n_tokens == 1)
-        return launch_rec<D, 2, BF16>(p, stream);
-    return launch_rec<D, 1, BF16>(p, stream);
+        return one ? launch_rec<D, 4, BF16, true>(p, stream)
+                   : launch_rec<D, 4, BF16, false>(p, stream);
+    if (one)
+        return launch_rec<D, 2, BF16, true>(p, stream);
+    return launch_rec<D, 1, BF16, false>(p, stream);
 }
 
 template <bool BF16>

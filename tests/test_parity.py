@@ -431,6 +431,19 @@ def test_zero_initial_state_pointer(gdn):
     check(gdn, x, "f32", "auto", state=False, what="state None")
 
 
+@pytest.mark.parametrize("n_seqs,n_tokens,n_heads,head_dim,dtype", [
+    (1, 1, 4, 128, "bf16"),      # one token, four rows per wave
+    (1, 7, 3, 96, "f32"),        # several tokens, two rows per wave
+    (8, 1, 32, 128, "f32"),      # one token, eight rows per wave
+    (8, 3, 32, 128, "bf16"),     # several tokens, eight rows per wave
+])
+def test_zero_initial_state_pointer_recurrent(gdn, n_seqs, n_tokens, n_heads, head_dim, dtype):
+    """Without an initial state the token recurrence starts from zeros in every
+    kernel shape (rows per wave, single and several tokens)."""
+    x = inputs.custom(n_seqs, n_tokens, n_heads, head_dim, dtype=dtype, state="zeros", seed=2)
+    check(gdn, x, dtype, "recurrent", state=False, what="state None")
+
+
 # ---- contract properties ------------------------------------------------------
 
 def test_in_place_state_update(gdn):
