@@ -62,10 +62,22 @@ bool aligned16(const void *p)
 // on MI355X (one sequence, 8 or 32 heads, d=128, device time per call): bf16 at 16
 // tokens (10.4 vs 10.2 us; 14.1 vs 10.2 at 24), fp32 at 40 (16.3 vs 17.9 us at 32,
 // 22.6 vs 18.0 at 48; the fp32 chunked path keeps one ring slot).
-gdn_algo pick_algo(gdn_algo algo, int64_t n_tokens, gdn_dtype dtype)
+// AUTO: the chunked form from the token count at which it overtakes the token
+// recurrence on MI355X. The recurrence costs a fixed latency per token while few
+// state rows are in flight and ALU time proportional to the rows once they fill
+// the chip, so the crossover falls as the work per token grows; the work is
+// counted in d = 128 heads (n_seqs * n_heads * (d / 128)^2, measured at d = 128).
+gdn_algo pick_algo(gdn_algo algo, int64_t n_seqs, int64_t n_tokens, int64_t n_heads,
+                   int head_dim, gdn_dtype dtype)
 {
     if (algo != GDN_ALGO_AUTO) return algo;
-    const int64_t from = (dtype == GDN_BF16) ? 16 : 40;
+    const double units = static_cast<double>(n_seqs) * static_cast<double>(n_heads) *
+                         (head_dim / 128.0) * (head_dim / 128.0);
+    int64_t from;
+    if (dtype == GDN_BF16)
+        from = units <= 40 ? 20 : units <= 96 ? 14 : units <= 192 ? 12 : 11;
+    else   // the fp32 chunked form runs fp32 MFMA: a later crossover
+        from = units <= 40 ? 44 : units <= 96 ? 48 : 52;
     return n_tokens >= from ? GDN_ALGO_CHUNKED : GDN_ALGO_RECURRENT;
 }
 
@@ -95,7 +107,8 @@ int check_shape(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens, int64_t n_hea
     if (!mul_ok(n_seqs, n_heads, &b) || !mul_ok(b, int64_t(head_dim) * head_dim, state_elems))
         return GDN_ERR_BAD_SHAPE;
     if (b * head_dim > kMaxStateRows) return GDN_ERR_BAD_SHAPE;
-    if (b > 0 && n_tokens > 0 && is_chunked(pick_algo(algo, n_tokens, dtype))) {
+    if (b > 0 && n_tokens > 0 &&
+        is_chunked(pick_algo(algo, n_seqs, n_tokens, n_heads, head_dim, dtype))) {
         if ((n_tokens + 63) / 64 > kMaxChunks / b) return GDN_ERR_BAD_SHAPE;
         // The chunked kernels form the byte offset of a token row inside one chunk
         // of q, k or v in 32 bits: 64 token rows of every head must span < 4 GiB.
@@ -167,7 +180,7 @@ size_t gdn_workspace_size(gdn_dtype dtype, int64_t n_seqs, int64_t n_tokens,
     if (check_shape(dtype, n_seqs, n_tokens, n_heads, head_dim, algo, &te, &ge, &se) != GDN_OK)
         return 0;
     if (n_seqs == 0 || n_heads == 0 || n_tokens == 0) return 0;
-    const gdn_algo chosen = pick_algo(algo, n_tokens, dtype);
+    const gdn_algo chosen = pick_algo(algo, n_seqs, n_tokens, n_heads, head_dim, dtype);
     if (!is_chunked(chosen)) return 0;
     return gdn::chunk_workspace_bytes(dtype == GDN_BF16, chosen == GDN_ALGO_CHUNKED_LAG, n_seqs,
                                       n_tokens, n_heads, head_dim);
@@ -361,7 +374,7 @@ int forward_impl(gdn_dtype dtype, const void *q, const void *k, const void *v, c
         if (overlap(r_out, r_state_in) || overlap(r_out, r_state_out)) return GDN_ERR_ALIASING;
     }
 
-    const gdn_algo chosen = pick_algo(algo, n_tokens, dtype);
+    const gdn_algo chosen = pick_algo(algo, n_seqs, n_tokens, n_heads, head_dim, dtype);
     size_t need = 0;
     if (have_tokens && is_chunked(chosen)) {
         need = gdn::chunk_workspace_bytes(dtype == GDN_BF16, chosen == GDN_ALGO_CHUNKED_LAG,

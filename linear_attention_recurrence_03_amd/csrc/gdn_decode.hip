@@ -426,21 +426,22 @@ hipError_t launch_rec(const Problem &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Rows per wave: 8 (NP = 4) once there are enough rows to fill the chip with
-// workgroups; otherwise 4 (NP = 2) for a single token, where half as many waves
-// each issue two state loads (3.71 against 3.94 us per layer for 1 x 32 heads,
-// d = 128), and 2 (NP = 1) for several tokens, where a wave's per-token chain of
-// reductions grows with its rows (8 tokens: 6.1 against 6.5 us).
+// Rows per wave (2 NP). A single token: 8 (NP = 4) once there are enough rows to
+// fill the chip with workgroups, else 4 (NP = 2: half as many waves, each issuing
+// two state loads; 3.71 against 3.94 us per layer for 1 x 32 heads, d = 128).
+// Several tokens trade a wave's per-token chain, which grows with its rows, against
+// the work per row (each wave reduces and converts its own k and q): 2 rows below
+// 8192 rows in all, 4 below 16384, else 8 (32 tokens, d = 128, bf16: 15.2 / 17.3 /
+// 26.6 us at 4096 rows, 23.2 / 21.1 / 27.7 at 8192, 39.8 / 33.4 / 32.8 at 16384).
 template <int D, bool BF16>
 hipError_t launch_rec_d(const Problem &p, hipStream_t stream)
 {
     const int64_t rows = p.n_seqs * p.n_heads * D;
-    const bool one = (p.n_tokens == 1);
-    if (rows >= 256 * 32 * 4)
-        return one ? launch_rec<D, 4, BF16, true>(p, stream)
-                   : launch_rec<D, 4, BF16, false>(p, stream);
-    if (one)
-        return launch_rec<D, 2, BF16, true>(p, stream);
+    if (p.n_tokens == 1)
+        return rows >= 256 * 32 * 4 ? launch_rec<D, 4, BF16, true>(p, stream)
+                                    : launch_rec<D, 2, BF16, true>(p, stream);
+    if (rows >= 16384) return launch_rec<D, 4, BF16, false>(p, stream);
+    if (rows >= 8192) return launch_rec<D, 2, BF16, false>(p, stream);
     return launch_rec<D, 1, BF16, false>(p, stream);
 }
 
