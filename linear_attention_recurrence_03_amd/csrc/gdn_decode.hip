@@ -133,25 +133,28 @@ struct RawIn<NV, true> {
     uint32_t odd;
 };
 
+// The raw loads take a token's row start (the same in every lane) and a lane's
+// 32-bit offset in elements.
 template <int NV, bool BF16>
-__device__ __forceinline__ RawIn<NV, BF16> load_raw(const void *base, int64_t off)
+__device__ __forceinline__ RawIn<NV, BF16> load_raw(const void *base, uint32_t off)
 {
+    // byte offsets formed in 32 bits, so that the address is base + zero-extended offset
+    const char *b = static_cast<const char *>(base);
     RawIn<NV, BF16> r;
     if constexpr (!BF16) {
-        r.x = load_f32<NV>(static_cast<const float *>(base) + off);
+        r.x = load_f32<NV>(reinterpret_cast<const float *>(b + off * 4u));
     } else {
-        const uint16_t *p = static_cast<const uint16_t *>(base) + off;
         if constexpr (NV == 4) {
-            const uint2 t = *reinterpret_cast<const uint2 *>(p);
+            const uint2 t = *reinterpret_cast<const uint2 *>(b + off * 2u);
             r.w[0] = t.x;
             r.w[1] = t.y;
         } else if constexpr (NV == 2) {
-            r.w[0] = *reinterpret_cast<const uint32_t *>(p);
+            r.w[0] = *reinterpret_cast<const uint32_t *>(b + off * 2u);
         } else {
-            const uint32_t *pw = static_cast<const uint32_t *>(base) + (off >> 1);
+            const uint32_t *pw = reinterpret_cast<const uint32_t *>(b + (off >> 1) * 4u);
 #pragma unroll
             for (int j = 0; j < (NV + 1) / 2; ++j) r.w[j] = pw[j];
-            r.odd = static_cast<uint32_t>(off & 1);
+            r.odd = off & 1u;
         }
     }
     return r;
@@ -188,12 +191,13 @@ template <bool BF16>
 using RawScalar = typename std::conditional<BF16, uint32_t, float>::type;
 
 template <bool BF16>
-__device__ __forceinline__ RawScalar<BF16> load_scalar_raw(const void *base, int64_t off)
+__device__ __forceinline__ RawScalar<BF16> load_scalar_raw(const void *base, uint32_t off)
 {
+    const char *b = static_cast<const char *>(base);
     if constexpr (BF16)
-        return static_cast<const uint32_t *>(base)[off >> 1];
+        return *reinterpret_cast<const uint32_t *>(b + (off >> 1) * 4u);
     else
-        return static_cast<const float *>(base)[off];
+        return *reinterpret_cast<const float *>(b + off * 4u);
 }
 
 // sh: 16 when the element is the pair's low half (an even offset), else 0
@@ -222,6 +226,13 @@ __device__ __forceinline__ void store_scalar_out(void *base, int64_t off, float 
         static_cast<uint16_t *>(base)[off] = f32_to_bf16(x);
     else
         static_cast<float *>(base)[off] = x;
+}
+
+// element e of a bf16 (BF16) or fp32 array, as a byte pointer
+template <bool BF16>
+__device__ __forceinline__ const char *elem(const void *base, int64_t e)
+{
+    return static_cast<const char *>(base) + e * (BF16 ? 2 : 4);
 }
 
 // One workgroup = kWaves waves = kWaves*2*NP consecutive value rows of one
@@ -298,7 +309,8 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
             gt = neg_softplus(gt);
             bt = sigmoid(bt);
         }
-        const float alpha = expf(gt);
+        const float alpha = __expf(gt);
+        char *const orow = static_cast<char *>(out) + go * D * (BF16 ? 2 : 4);   // token's out row
         float a[NP], b[NP], kq = 0.f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) kq = fmaf(kv.x[i], qv.x[i], kq);
@@ -325,7 +337,13 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
 #pragma unroll
             for (int i = 0; i < NV; ++i) M[p].x[i] = fmaf(alpha, M[p].x[i], delta * kv.x[i]);
             const float o = scale * fmaf(alpha, b[p], delta * kq);
-            if ((lane & 31) == 0) store_scalar_out<BF16>(out, go * D + row0 + 2 * p, o);
+            if ((lane & 31) == 0) {
+                char *dst = orow + static_cast<uint32_t>(row0 + 2 * p) * (BF16 ? 2u : 4u);
+                if constexpr (BF16)
+                    *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16(o);
+                else
+                    *reinterpret_cast<float *>(dst) = o;
+            }
         }
     };
 
@@ -353,15 +371,18 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
         };
         const int64_t gi0 = gi, ki0 = ki;
         const uint32_t vsh = (row0 & 1) ? 0u : 16u;   // rows row0 + 2p share row0's parity
+        const uint32_t colu = static_cast<uint32_t>(col), zoff4 = static_cast<uint32_t>(zoff) * 4u;
         auto fetch = [&](int64_t t) {
             const int64_t gx = gi0 + t * n_heads, kx = ki0 + t * n_k_heads;
             Raw r;
-            r.k = load_raw<NV, BF16>(k, kx * D + col);
-            r.q = load_raw<NV, BF16>(q, kx * D + col);
+            r.k = load_raw<NV, BF16>(elem<BF16>(k, kx * D), colu);
+            r.q = load_raw<NV, BF16>(elem<BF16>(q, kx * D), colu);
+            const char *vrow = elem<BF16>(v, gx * D);
 #pragma unroll
-            for (int p = 0; p < NP; ++p) r.v[p] = load_scalar_raw<BF16>(v, gx * D + row0 + 2 * p);
-            r.g = g[gx + zoff];
-            r.b = beta[gx + zoff];
+            for (int p = 0; p < NP; ++p)
+                r.v[p] = load_scalar_raw<BF16>(vrow, static_cast<uint32_t>(row0 + 2 * p));
+            r.g = *reinterpret_cast<const float *>(elem<false>(g, gx) + zoff4);
+            r.b = *reinterpret_cast<const float *>(elem<false>(beta, gx) + zoff4);
             return r;
         };
         struct Tok {
