@@ -244,7 +244,9 @@ __device__ __forceinline__ const char *elem(const void *base, int64_t e)
 // count (< 2^31) and both head counts (< 2^16) are packed into two of them
 // (tok32, heads16); otherwise the full-width counts further on are used and read
 // like any argument.  Head counts fit in 32 bits: the grid, one workgroup per
-// group of rows of each (seq, head), does.
+// group of rows of each (seq, head), does.  ONE: the call has a single token
+// (straight-line code); otherwise a software pipeline keeps two tokens' inputs in
+// flight.
 template <int D, int NP, bool BF16, bool PK, bool ONE>
 __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
     const void *__restrict__ k, const void *__restrict__ q, const float *state_in,
