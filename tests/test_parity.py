@@ -134,6 +134,21 @@ def test_tails_and_widths(gdn, dtype, D, T, algo):
     check(gdn, x, dtype, algo, what="tail T=%d D=%d" % (T, D))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [32, 96, 128])
+@pytest.mark.parametrize("rows", [4096, 8192, 16384])
+@pytest.mark.parametrize("T", [2, 3, 6])
+def test_recurrence_rows_per_wave(gdn, dtype, D, rows, T):
+    """Several tokens through the token recurrence in each of its shapes: two, four
+    and eight state rows per wave (chosen by the total row count), odd and even
+    numbers of tokens (the loop takes two per pass), and widths whose lanes hold an
+    odd or even number of keys (bf16 words straddle lanes at d = 32 and 96)."""
+    n_heads = -(-rows // (2 * D))               # at least `rows` rows in all
+    x = inputs.custom(2, T, n_heads, D, dtype=dtype, state="normal", gate="weak",
+                      seed=rows + T * 10 + D)
+    check(gdn, x, dtype, "recurrent", what="rows %d T=%d D=%d" % (rows, T, D))
+
+
 @pytest.mark.parametrize("gate", ["weak", "mixed"])
 @pytest.mark.parametrize("algo", ["recurrent", "chunked"])
 def test_decay_regimes(gdn, gate, algo):
