@@ -64,9 +64,10 @@ typedef enum {
  * length at which it is faster than the token recurrence on MI355X, and the token
  * recurrence below that.  The crossover falls as the work per token grows: with
  * w = n_seqs * n_heads * (head_dim / 128)^2, bf16 switches at 20 tokens for
- * w <= 40, 14 for w <= 96, 12 for w <= 192 and 11 above; fp32 (whose chunked form
- * runs fp32 matrix products) at 44 tokens for w <= 40, 48 for w <= 96 and 52 above.
- * The forced values exist so that tests can run either algorithm on any input.
+ * w <= 96, 18 for w <= 192, 16 for w <= 512 and 14 above; fp32 (whose chunked form
+ * runs fp32 matrix products) at 48 tokens for w <= 40, 60 for w <= 96, 104 for
+ * w <= 192 and 120 above.  The forced values exist so that tests can run either
+ * algorithm on any input.
  *
  * The chunked form's chunk-to-chunk pass has two kernels for bf16 rows: one that
  * spreads each (seq, head)'s value rows over several workgroups (fewest steps in

@@ -75,9 +75,9 @@ gdn_algo pick_algo(gdn_algo algo, int64_t n_seqs, int64_t n_tokens, int64_t n_he
                          (head_dim / 128.0) * (head_dim / 128.0);
     int64_t from;
     if (dtype == GDN_BF16)
-        from = units <= 40 ? 20 : units <= 96 ? 14 : units <= 192 ? 12 : 11;
-    else   // the fp32 chunked form runs fp32 MFMA: a later crossover
-        from = units <= 40 ? 44 : units <= 96 ? 48 : 52;
+        from = units <= 96 ? 20 : units <= 192 ? 18 : units <= 512 ? 16 : 14;
+    else   // the fp32 chunked form runs fp32 MFMA, a step per 64 tokens: a later crossover
+        from = units <= 40 ? 48 : units <= 96 ? 60 : units <= 192 ? 104 : 120;
     return n_tokens >= from ? GDN_ALGO_CHUNKED : GDN_ALGO_RECURRENT;
 }
 

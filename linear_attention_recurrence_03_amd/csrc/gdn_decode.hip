@@ -10,17 +10,18 @@
 // order").
 //
 // Value rows of M are independent given (k, q, g, beta) of the token, so each
-// state row is one unit of work.  A row of d fp32 values is held by 32 lanes
-// with d/32 consecutive values each (the width rule of the model card's
-// supports predicate), so one wave64 load instruction covers two adjacent rows
-// -- 2*d*4 contiguous bytes, fully coalesced.  A wave keeps 2*NP rows in
-// registers for the whole call: the state is read once and written once, which
-// is all of the HBM traffic that matters (the model card notes that a 2 MB
-// state copy per layer per token is most of the cost).  Per token each row
-// needs two dot products over its keys (M_i.k and M_i.q), done as lane
-// partials plus a 32-lane DPP reduction; k.q is reduced alongside.  Since
-// M_new q = exp(g) M q + delta (k.q), the readout needs no second pass over
-// the row.
+// state row is one unit of work.  A row of d fp32 values is held by LPR = 32 or
+// 16 lanes with d/LPR consecutive values each (the width rule of the model
+// card's supports predicate: d a multiple of 32), so one wave64 load instruction
+// covers 64/LPR adjacent rows -- contiguous bytes, fully coalesced.  A wave keeps
+// (64/LPR)*NP rows in registers for the whole call: the state is read once and
+// written once, which is all of the HBM traffic that matters (the model card
+// notes that a 2 MB state copy per layer per token is most of the cost).  Per
+// token each row needs two dot products over its keys (M_i.k and M_i.q), done as
+// lane partials plus a DPP reduction over the row's lanes (and a swizzle across
+// the two 16-lane rows of a half-wave at LPR = 32); k.q is reduced alongside.
+// Since M_new q = exp(g) M q + delta (k.q), the readout needs no second pass
+// over the row.
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -44,13 +45,21 @@ struct Vec {
 template <int NV>
 __device__ __forceinline__ Vec<NV> load_f32(const float *p)
 {
+    // a lane's NV floats start at a multiple of NV floats: 16-byte pieces when NV is
+    // a multiple of four, 8-byte ones when it is even
     Vec<NV> r;
-    if constexpr (NV == 4) {
-        const float4 t = *reinterpret_cast<const float4 *>(p);
-        r.x[0] = t.x; r.x[1] = t.y; r.x[2] = t.z; r.x[3] = t.w;
-    } else if constexpr (NV == 2) {
-        const float2 t = *reinterpret_cast<const float2 *>(p);
-        r.x[0] = t.x; r.x[1] = t.y;
+    if constexpr (NV % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < NV / 4; ++j) {
+            const float4 t = reinterpret_cast<const float4 *>(p)[j];
+            r.x[4 * j] = t.x; r.x[4 * j + 1] = t.y; r.x[4 * j + 2] = t.z; r.x[4 * j + 3] = t.w;
+        }
+    } else if constexpr (NV % 2 == 0) {
+#pragma unroll
+        for (int j = 0; j < NV / 2; ++j) {
+            const float2 t = reinterpret_cast<const float2 *>(p)[j];
+            r.x[2 * j] = t.x; r.x[2 * j + 1] = t.y;
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < NV; ++i) r.x[i] = p[i];
@@ -61,13 +70,41 @@ __device__ __forceinline__ Vec<NV> load_f32(const float *p)
 template <int NV>
 __device__ __forceinline__ void store_f32(float *p, const Vec<NV> &r)
 {
-    if constexpr (NV == 4) {
-        *reinterpret_cast<float4 *>(p) = make_float4(r.x[0], r.x[1], r.x[2], r.x[3]);
-    } else if constexpr (NV == 2) {
-        *reinterpret_cast<float2 *>(p) = make_float2(r.x[0], r.x[1]);
+    if constexpr (NV % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < NV / 4; ++j)
+            reinterpret_cast<float4 *>(p)[j] =
+                make_float4(r.x[4 * j], r.x[4 * j + 1], r.x[4 * j + 2], r.x[4 * j + 3]);
+    } else if constexpr (NV % 2 == 0) {
+#pragma unroll
+        for (int j = 0; j < NV / 2; ++j)
+            reinterpret_cast<float2 *>(p)[j] = make_float2(r.x[2 * j], r.x[2 * j + 1]);
     } else {
 #pragma unroll
         for (int i = 0; i < NV; ++i) p[i] = r.x[i];
+    }
+}
+
+// NW 32-bit words from p, which is aligned to 16 bytes when NW is a multiple of four
+// and to 8 when NW is even (a lane's slice of NV = 2 NW bf16 values)
+template <int NW>
+__device__ __forceinline__ void load_words(const char *p, uint32_t (&w)[NW])
+{
+    if constexpr (NW % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < NW / 4; ++j) {
+            const uint4 t = reinterpret_cast<const uint4 *>(p)[j];
+            w[4 * j] = t.x; w[4 * j + 1] = t.y; w[4 * j + 2] = t.z; w[4 * j + 3] = t.w;
+        }
+    } else if constexpr (NW % 2 == 0) {
+#pragma unroll
+        for (int j = 0; j < NW / 2; ++j) {
+            const uint2 t = reinterpret_cast<const uint2 *>(p)[j];
+            w[2 * j] = t.x; w[2 * j + 1] = t.y;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) w[j] = reinterpret_cast<const uint32_t *>(p)[j];
     }
 }
 
@@ -79,16 +116,14 @@ __device__ __forceinline__ Vec<NV> load_in(const void *base, int64_t off)
     } else {
         const uint16_t *p = static_cast<const uint16_t *>(base) + off;
         Vec<NV> r;
-        if constexpr (NV == 4) {
-            const uint2 t = *reinterpret_cast<const uint2 *>(p);
-            r.x[0] = __uint_as_float(t.x << 16);
-            r.x[1] = __uint_as_float(t.x & 0xffff0000u);
-            r.x[2] = __uint_as_float(t.y << 16);
-            r.x[3] = __uint_as_float(t.y & 0xffff0000u);
-        } else if constexpr (NV == 2) {
-            const uint32_t t = *reinterpret_cast<const uint32_t *>(p);
-            r.x[0] = __uint_as_float(t << 16);
-            r.x[1] = __uint_as_float(t & 0xffff0000u);
+        if constexpr (NV % 2 == 0) {
+            uint32_t w[NV / 2];
+            load_words<NV / 2>(reinterpret_cast<const char *>(p), w);
+#pragma unroll
+            for (int j = 0; j < NV / 2; ++j) {
+                r.x[2 * j] = __uint_as_float(w[j] << 16);
+                r.x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < NV; ++i) r.x[i] = bf16_to_f32(p[i]);
@@ -144,12 +179,8 @@ __device__ __forceinline__ RawIn<NV, BF16> load_raw(const void *base, uint32_t o
     if constexpr (!BF16) {
         r.x = load_f32<NV>(reinterpret_cast<const float *>(b + off * 4u));
     } else {
-        if constexpr (NV == 4) {
-            const uint2 t = *reinterpret_cast<const uint2 *>(b + off * 2u);
-            r.w[0] = t.x;
-            r.w[1] = t.y;
-        } else if constexpr (NV == 2) {
-            r.w[0] = *reinterpret_cast<const uint32_t *>(b + off * 2u);
+        if constexpr (NV % 2 == 0) {
+            load_words<NV / 2>(b + off * 2u, r.w);
         } else {
             const uint32_t *pw = reinterpret_cast<const uint32_t *>(b + (off >> 1) * 4u);
 #pragma unroll
@@ -235,7 +266,23 @@ __device__ __forceinline__ const char *elem(const void *base, int64_t e)
     return static_cast<const char *>(base) + e * (BF16 ? 2 : 4);
 }
 
-// One workgroup = kWaves waves = kWaves*2*NP consecutive value rows of one
+// Sum over the L lanes of a row: 16 lanes (one DPP row) in four DPP steps, 32 with
+// a swizzle across the two rows of a half-wave besides.
+template <int L>
+__device__ __forceinline__ float sum_lanes(float x)
+{
+    if constexpr (L == 32) {
+        return sum32(x);
+    } else {
+        x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+        x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+        x += dpp_mov<0x141>(x);  // row_half_mirror
+        x += dpp_mov<0x140>(x);  // row_mirror
+        return x;
+    }
+}
+
+// One workgroup = kWaves waves = kWaves*(64/LPR)*NP consecutive value rows of one
 // (seq, head).  Grid: n_seqs * n_heads * (D / rows_per_block) workgroups.
 // Everything the first loads need comes first, in 14 dwords: this file is built to
 // have the hardware preload them into scalar registers at wave launch, so the
@@ -247,7 +294,7 @@ __device__ __forceinline__ const char *elem(const void *base, int64_t e)
 // group of rows of each (seq, head), does.  ONE: the call has a single token
 // (straight-line code); otherwise a software pipeline keeps two tokens' inputs in
 // flight.
-template <int D, int NP, bool BF16, bool PK, bool ONE>
+template <int D, int LPR, int NP, bool BF16, bool PK, bool ONE>
 __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
     const void *__restrict__ k, const void *__restrict__ q, const float *state_in,
     const void *__restrict__ v, const float *__restrict__ g, const float *__restrict__ beta,
@@ -259,28 +306,30 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
     const int n_heads32 = PK ? int(heads16 & 0xffffu) : n_heads_full;
     const int n_k_heads32 = PK ? int(heads16 >> 16) : n_k_heads_full;
     const int64_t n_heads = n_heads32, n_k_heads = n_k_heads32;
-    constexpr int NV = D / 32;
-    constexpr int kRowsPerWave = 2 * NP;
+    static_assert(LPR == 16 || LPR == 32, "a row spans 16 or 32 lanes");
+    constexpr int NV = D / LPR;          // keys per lane
+    constexpr int G = 64 / LPR;          // rows side by side in a wave
+    constexpr int kRowsPerWave = G * NP;
     constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
     constexpr int kBlocksPerHead = D / kRowsPerBlock;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int col = (lane & 31) * NV;
+    const int col = (lane % LPR) * NV;
     const uint32_t shu = blockIdx.x / kBlocksPerHead;   // s * n_heads + h
     const int rb = blockIdx.x % kBlocksPerHead;
     const uint32_t su = shu / static_cast<uint32_t>(n_heads32);
     const uint32_t hu = shu - su * static_cast<uint32_t>(n_heads32);
     const int64_t sh = shu, s = su, h = hu;
     // rows of this lane: row0 + 2p, p < NP (the two half-waves interleave)
-    const int row0 = rb * kRowsPerBlock + wave * kRowsPerWave + (lane >> 5);
+    const int row0 = rb * kRowsPerBlock + wave * kRowsPerWave + lane / LPR;
     const int64_t st_base = sh * D * D;
 
     static_assert(D <= 128, "the zero row covers head_dim <= 128");
     Vec<NV> M[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-        const float *row = state_in ? state_in + st_base + (int64_t)(row0 + 2 * p) * D : kZeroRow;
+        const float *row = state_in ? state_in + st_base + (int64_t)(row0 + G * p) * D : kZeroRow;
         M[p] = load_f32<NV>(row + col);
     }
 
@@ -292,15 +341,15 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
     // with out at token offset go.
     auto token = [&](Vec<NV> kv, Vec<NV> qv, const float *vr, float gt, float bt, int64_t go) {
         if (l2norm_qk) {
-            // both 32-lane halves hold the whole rows: one reduction each
+            // every row's lanes hold the whole k and q rows: one reduction each
             float sk = 0.f, sq = 0.f;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 sk = fmaf(kv.x[i], kv.x[i], sk);
                 sq = fmaf(qv.x[i], qv.x[i], sq);
             }
-            const float rk = 1.f / sqrtf(sum32(sk) + kL2Eps);
-            const float rq = 1.f / sqrtf(sum32(sq) + kL2Eps);
+            const float rk = 1.f / sqrtf(sum_lanes<LPR>(sk) + kL2Eps);
+            const float rq = 1.f / sqrtf(sum_lanes<LPR>(sq) + kL2Eps);
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 kv.x[i] *= rk;
@@ -326,11 +375,11 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
                 b[p] = fmaf(M[p].x[i], qv.x[i], b[p]);
             }
         }
-        kq = sum32(kq);
+        kq = sum_lanes<LPR>(kq);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            a[p] = sum32(a[p]);
-            b[p] = sum32(b[p]);
+            a[p] = sum_lanes<LPR>(a[p]);
+            b[p] = sum_lanes<LPR>(b[p]);
         }
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -339,8 +388,8 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
 #pragma unroll
             for (int i = 0; i < NV; ++i) M[p].x[i] = fmaf(alpha, M[p].x[i], delta * kv.x[i]);
             const float o = scale * fmaf(alpha, b[p], delta * kq);
-            if ((lane & 31) == 0) {
-                char *dst = orow + static_cast<uint32_t>(row0 + 2 * p) * (BF16 ? 2u : 4u);
+            if (lane % LPR == 0) {
+                char *dst = orow + static_cast<uint32_t>(row0 + G * p) * (BF16 ? 2u : 4u);
                 if constexpr (BF16)
                     *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16(o);
                 else
@@ -353,7 +402,7 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
         // a single token: straight-line loads, the gates through the scalar path
         float vr[NP];
 #pragma unroll
-        for (int p = 0; p < NP; ++p) vr[p] = load_scalar_in<BF16>(v, gi * D + row0 + 2 * p);
+        for (int p = 0; p < NP; ++p) vr[p] = load_scalar_in<BF16>(v, gi * D + row0 + G * p);
         token(load_in<NV, BF16>(k, ki * D + col), load_in<NV, BF16>(q, ki * D + col), vr, g[gi],
               beta[gi], gi);
     } else {
@@ -382,7 +431,7 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
             const char *vrow = elem<BF16>(v, gx * D);
 #pragma unroll
             for (int p = 0; p < NP; ++p)
-                r.v[p] = load_scalar_raw<BF16>(vrow, static_cast<uint32_t>(row0 + 2 * p));
+                r.v[p] = load_scalar_raw<BF16>(vrow, static_cast<uint32_t>(row0 + G * p));
             r.g = *reinterpret_cast<const float *>(elem<false>(g, gx) + zoff4);
             r.b = *reinterpret_cast<const float *>(elem<false>(beta, gx) + zoff4);
             return r;
@@ -425,23 +474,23 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
 
 #pragma unroll
     for (int p = 0; p < NP; ++p)
-        store_f32<NV>(state_out + st_base + (int64_t)(row0 + 2 * p) * D + col, M[p]);
+        store_f32<NV>(state_out + st_base + (int64_t)(row0 + G * p) * D + col, M[p]);
 }
 
-template <int D, int NP, bool BF16, bool ONE>
+template <int D, int LPR, int NP, bool BF16, bool ONE>
 hipError_t launch_rec(const Problem &p, hipStream_t stream)
 {
     const bool pk = p.n_tokens < (int64_t(1) << 31) && p.n_heads < (1 << 16) &&
                     p.n_k_heads < (1 << 16);
-    constexpr int kRowsPerBlock = kWaves * 2 * NP;
+    constexpr int kRowsPerBlock = kWaves * (64 / LPR) * NP;
     static_assert(D % kRowsPerBlock == 0, "rows per block must divide head_dim");
     const int64_t blocks = p.n_seqs * p.n_heads * (D / kRowsPerBlock);
     if (!grid_fits(blocks, kWaves * 64)) return hipErrorInvalidConfiguration;
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
     const uint32_t tok32 = pk ? static_cast<uint32_t>(p.n_tokens) : 0u;
     const uint32_t heads16 = pk ? static_cast<uint32_t>(p.n_heads | (p.n_k_heads << 16)) : 0u;
-    auto kern = pk ? recurrent_kernel<D, NP, BF16, true, ONE>
-                   : recurrent_kernel<D, NP, BF16, false, ONE>;
+    auto kern = pk ? recurrent_kernel<D, LPR, NP, BF16, true, ONE>
+                   : recurrent_kernel<D, LPR, NP, BF16, false, ONE>;
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kWaves * 64), 0, stream,
                        p.k, p.q, p.state_in, p.v, p.g, p.beta, tok32, heads16, p.n_tokens,
                        static_cast<int>(p.n_heads), static_cast<int>(p.n_k_heads), p.out,
@@ -449,23 +498,27 @@ hipError_t launch_rec(const Problem &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Rows per wave (2 NP). A single token: 8 (NP = 4) once there are enough rows to
-// fill the chip with workgroups, else 4 (NP = 2: half as many waves, each issuing
-// two state loads; 3.71 against 3.94 us per layer for 1 x 32 heads, d = 128).
-// Several tokens trade a wave's per-token chain, which grows with its rows, against
-// the work per row (each wave reduces and converts its own k and q): 2 rows below
-// 8192 rows in all, 4 below 16384, else 8 (32 tokens, d = 128, bf16: 15.2 / 17.3 /
-// 26.6 us at 4096 rows, 23.2 / 21.1 / 27.7 at 8192, 39.8 / 33.4 / 32.8 at 16384).
+// Lanes per row and rows per wave. A single token: 32 lanes per row, 8 rows per
+// wave (NP = 4) once there are enough rows to fill the chip with workgroups, else 4
+// (NP = 2: half as many waves, each issuing two state loads; 3.71 against 3.94 us
+// per layer for 1 x 32 heads, d = 128); 16 lanes per row measured slower there
+// (3.62 against 3.56 us, batched 50.1 against 48.2). Several tokens are bound by
+// each wave's instructions per token: from 8192 rows, 16 lanes per row (no swizzle
+// in the reductions, half the per-row share of converting and reducing k and q)
+// with 4 rows per wave, and 8 from 16384 (32 tokens, d = 128, bf16: 16.4 against
+// 20.1 us at 8192 rows, 23.9 against 30.8 at 16384, 40.7 against 50.6 at 32768);
+// below 8192 rows, 32 lanes and 2 rows per wave keep twice the waves in flight
+// (14.5 against 14.8 us at 4096 rows).
 template <int D, bool BF16>
 hipError_t launch_rec_d(const Problem &p, hipStream_t stream)
 {
     const int64_t rows = p.n_seqs * p.n_heads * D;
     if (p.n_tokens == 1)
-        return rows >= 256 * 32 * 4 ? launch_rec<D, 4, BF16, true>(p, stream)
-                                    : launch_rec<D, 2, BF16, true>(p, stream);
-    if (rows >= 16384) return launch_rec<D, 4, BF16, false>(p, stream);
-    if (rows >= 8192) return launch_rec<D, 2, BF16, false>(p, stream);
-    return launch_rec<D, 1, BF16, false>(p, stream);
+        return rows >= 256 * 32 * 4 ? launch_rec<D, 32, 4, BF16, true>(p, stream)
+                                    : launch_rec<D, 32, 2, BF16, true>(p, stream);
+    if (rows >= 16384) return launch_rec<D, 16, 2, BF16, false>(p, stream);
+    if (rows >= 8192) return launch_rec<D, 16, 1, BF16, false>(p, stream);
+    return launch_rec<D, 32, 1, BF16, false>(p, stream);
 }
 
 template <bool BF16>
