@@ -315,14 +315,14 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int col = (lane % LPR) * NV;
+    const int col = (lane & (LPR - 1)) * NV;
     const uint32_t shu = blockIdx.x / kBlocksPerHead;   // s * n_heads + h
     const int rb = blockIdx.x % kBlocksPerHead;
     const uint32_t su = shu / static_cast<uint32_t>(n_heads32);
     const uint32_t hu = shu - su * static_cast<uint32_t>(n_heads32);
     const int64_t sh = shu, s = su, h = hu;
     // rows of this lane: row0 + 2p, p < NP (the two half-waves interleave)
-    const int row0 = rb * kRowsPerBlock + wave * kRowsPerWave + lane / LPR;
+    const int row0 = rb * kRowsPerBlock + wave * kRowsPerWave + (lane >> (LPR == 16 ? 4 : 5));
     const int64_t st_base = sh * D * D;
 
     static_assert(D <= 128, "the zero row covers head_dim <= 128");
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
 #pragma unroll
             for (int i = 0; i < NV; ++i) M[p].x[i] = fmaf(alpha, M[p].x[i], delta * kv.x[i]);
             const float o = scale * fmaf(alpha, b[p], delta * kq);
-            if (lane % LPR == 0) {
+            if ((lane & (LPR - 1)) == 0) {
                 char *dst = orow + static_cast<uint32_t>(row0 + G * p) * (BF16 ? 2u : 4u);
                 if constexpr (BF16)
                     *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16(o);
