@@ -439,8 +439,9 @@ def traffic_records(fetch_dir, write_dir):
                 "chunk_scan" if "chunk_scan" in name else
                 "chunk_prep" if "chunk_prep" in name else
                 # the profile pass runs the token recurrence twice: the batched decode
-                # (eight rows per wave) and the single-token layer calls (fewer)
-                "decode_batched" if "recurrent_kernel<128, 4" in name else
+                # (32 lanes per row, eight rows per wave: recurrent_kernel<128, 32, 4, ...>)
+                # and the single-token layer calls (fewer rows per wave)
+                "decode_batched" if "recurrent_kernel<128, 32, 4," in name else
                 "decode_1tok" if "recurrent_kernel<128, " in name else None)
 
     def per_kernel(d, counter, dur):

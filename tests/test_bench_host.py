@@ -68,7 +68,7 @@ def test_traffic_records_calibrate_each_counter(tmp_path):
     copy = "void at::native::vectorized_elementwise_kernel<4, at::native::MulFunctor<float>>"
     scan = "void gdn::chunk_scan_kernel<128, true, 1, false>(...)"
     prep = "void gdn::chunk_prep_kernel<128, true, false>(...)"
-    dec = "void gdn::recurrent_kernel<128, 4, false, true, true>(...)"
+    dec = "void gdn::recurrent_kernel<128, 32, 4, false, true, true>(...)"
     _counter_csv(tmp_path / "f", "FETCH_SIZE",
                  [(copy, 256 * mib, 10), (prep, 10 * mib, 10), (scan, 20 * mib, 10),
                   (scan, 22 * mib, 10), (scan, 21 * mib, 10), (dec, 60 * mib, 50_000)])
@@ -90,7 +90,7 @@ def test_traffic_records_calibrate_each_counter(tmp_path):
     assert abs(d["counted_GBs"] - round(250 * mb / 50e-6 / 1e9, 1)) < 0.06
     assert "decode_1tok" not in rec
     # the single-token layer calls: any other row count of the d = 128 recurrence
-    one = "void gdn::recurrent_kernel<128, 2, false, true, true>(...)"
+    one = "void gdn::recurrent_kernel<128, 32, 2, false, true, true>(...)"
     _counter_csv(tmp_path / "f1", "FETCH_SIZE", [(copy, 256 * mib, 10), (one, 2 * mib, 4_000)])
     _counter_csv(tmp_path / "w1", "WRITE_SIZE", [(copy, 512 * mib, 10), (one, 2 * mib, 4_000)])
     rec1 = bench.traffic_records(str(tmp_path / "f1"), str(tmp_path / "w1"))
