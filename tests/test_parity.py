@@ -136,7 +136,7 @@ def test_tails_and_widths(gdn, dtype, D, T, algo):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("D", [32, 96, 128])
-@pytest.mark.parametrize("rows", [4096, 8192, 16384])
+@pytest.mark.parametrize("rows", [4096, 8192, 16384, 65536])
 @pytest.mark.parametrize("T", [2, 3, 6])
 def test_recurrence_rows_per_wave(gdn, dtype, D, rows, T):
     """Several tokens through the token recurrence in each of its shapes: two, four
