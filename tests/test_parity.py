@@ -406,6 +406,18 @@ def _mixed_raw(n_seqs, n_tokens, n_heads, head_dim, dtype, seed, l2, gates, key_
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [96, 128])
+@pytest.mark.parametrize("rows", [8192, 16384])
+def test_input_transforms_rows_per_wave(gdn, dtype, D, rows):
+    """Normalised q/k rows and raw gates in the several-token shapes with 16 lanes
+    per state row (four and eight rows per wave)."""
+    n_heads = -(-rows // (2 * D))
+    x = _mixed_raw(2, 5, n_heads, D, dtype, seed=800 + D + rows // 1024, l2=True, gates=True)
+    check(gdn, x, dtype, "recurrent", what="transforms rows %d D=%d" % (rows, D),
+          l2norm_qk=True, raw_gates=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("l2,gates", [(True, False), (False, True), (True, True)])
 @pytest.mark.parametrize("D", [32, 128])
 @pytest.mark.parametrize("T,algo", [(1, "recurrent"), (9, "recurrent"), (65, "chunked"),
