@@ -406,6 +406,17 @@ def _mixed_raw(n_seqs, n_tokens, n_heads, head_dim, dtype, seed, l2, gates, key_
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows", [4096, 8192, 16384])
+def test_tiled_key_heads_rows_per_wave(gdn, dtype, rows):
+    """Query/key heads shared by four value heads each (value head h reads key head
+    h mod n_k) in every several-token shape of the token recurrence."""
+    n_heads = rows // (2 * 128)
+    x = inputs.custom(2, 4, n_heads, 128, dtype=dtype, state="normal", seed=900 + rows // 1024,
+                      key_heads=n_heads // 4)
+    check(gdn, x, dtype, "recurrent", what="tiled rows %d" % rows)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("D", [96, 128])
 @pytest.mark.parametrize("rows", [8192, 16384])
 def test_input_transforms_rows_per_wave(gdn, dtype, D, rows):
