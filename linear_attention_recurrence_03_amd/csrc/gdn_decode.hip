@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
     const uint32_t su = shu / static_cast<uint32_t>(n_heads32);
     const uint32_t hu = shu - su * static_cast<uint32_t>(n_heads32);
     const int64_t sh = shu, s = su, h = hu;
-    // rows of this lane: row0 + 2p, p < NP (the two half-waves interleave)
+    // rows of this lane: row0 + G p, p < NP (the wave's G groups of LPR lanes interleave)
     const int row0 = rb * kRowsPerBlock + wave * kRowsPerWave + (lane >> (LPR == 16 ? 4 : 5));
     const int64_t st_base = sh * D * D;
 
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(kWaves * 64) void recurrent_kernel(
             float g, b;
         };
         const int64_t gi0 = gi, ki0 = ki;
-        const uint32_t vsh = (row0 & 1) ? 0u : 16u;   // rows row0 + 2p share row0's parity
+        const uint32_t vsh = (row0 & 1) ? 0u : 16u;   // rows row0 + G p share row0's parity
         const uint32_t colu = static_cast<uint32_t>(col), zoff4 = static_cast<uint32_t>(zoff) * 4u;
         auto fetch = [&](int64_t t) {
             const int64_t gx = gi0 + t * n_heads, kx = ki0 + t * n_k_heads;
